@@ -1,0 +1,339 @@
+"""Plain fp64 CPU oracle for training-free block-sparse attention (test infrastructure only).
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may use this module.
+
+Sources (page title, then the section on it):
+  [LoSA]   scholarbro author page (Changming Sun), LoSA abstract: exact block attention masses at one
+           early dense step; per head and query block the smallest key/value block set meeting a
+           99% retained-mass threshold; the frozen indices are reused for the remaining steps.
+  [SCOPE]  mlsift "sparse attention" listing, SCOPE abstract: hybrid top-p / fixed top-k; a
+           head-specific k from the initial retained counts averaged with query-cluster-size
+           weights; extra keys only for clusters whose initial count falls below it.
+  [VMoBA]  pith.science review of "VMoBA: Mixture-of-Block Attention for Video Diffusion Models":
+           "What carries the argument" (non-overlapping key blocks, mean key per block, queries score
+           the block means, only the top blocks contribute; global selection pools a head's scores;
+           the threshold rule), the referee report's major comment 1 (Sec. 3.3 Eq. 3 global
+           TopkMask over the query-by-block matrix, Sec. 3.4 Eq. 4 smallest k' whose cumulative
+           normalised similarity reaches tau; empty query rows are possible), the circularity
+           check (Eq. 1-2 constructive block partition), Figure 2 caption (block means; attention
+           over the selected blocks only).
+
+The method is an approximation, so the oracle follows its steps in the pages' order rather than a
+closed form. Points the pages leave open take these readings (each one is also listed with its
+reasoning in the design notes):
+  * block-mean scores are normalised by a softmax over the kv blocks of one query block, without
+    block-size weights (parity unpinned against the |J|-weighted alternative);
+  * the head-global pool normalises one softmax over all (I, J) pairs of a head, each pair weighted
+    by the query-block size |I| (parity unpinned);
+  * "reaches" / "meeting" means >=; ties in score go to the lower block (pair) index; when the
+    cumulative sum never reaches the threshold, or the threshold is >= 1, everything is selected;
+  * indices within a row are returned ascending;
+  * SCOPE's head k is the integer ceiling of the |I|-weighted mean count, capped at the block count;
+  * a query block with no selected block outputs O = 0 and LSE = -inf, with zero gradients;
+  * the selection is a hard, stop-gradient gate in the backward pass.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "partition", "block_sizes", "pool", "block_logits", "score_row", "score_head",
+    "exact_mass", "exact_mass_row", "select_topp", "select_row", "head_min_k",
+    "select_hybrid", "select_head", "to_csr", "csr_rows", "attention_rows", "attention_fwd",
+    "attention_bwd", "row_backward", "density",
+]
+
+
+# ---------------------------------------------------------------------------------------------
+# O1. Block partition of the frame-major token sequence
+# ---------------------------------------------------------------------------------------------
+
+def partition(grid: Sequence[int], part) -> List[np.ndarray]:
+    """Non-overlapping blocks over the (T, Hg, Wg) token grid ([VMoBA] Eq. 1-2 as the
+    circularity check describes them; 1D temporal, 2D spatial, 3D spatio-temporal blocks).
+
+    part = ("flat", s): block j is tokens [j*s, min((j+1)*s, N)) of the frame-major sequence.
+    part = ("tile", (bt, bh, bw)): block (a, b, c), numbered (a*nbh + b)*nbw + c, holds every token
+    (t, h, w) with t in [a*bt, (a+1)*bt) and likewise for h, w, clipped at the grid edge.
+    Tokens of a block are listed in ascending frame-major index n = (t*Hg + h)*Wg + w.
+    """
+    T, Hg, Wg = (int(v) for v in grid)
+    N = T * Hg * Wg
+    kind, arg = part
+    if kind == "flat":
+        s = int(arg)
+        return [np.arange(j * s, min((j + 1) * s, N)) for j in range(-(-N // s))]
+    bt, bh, bw = (int(v) for v in arg)
+    nbh, nbw = -(-Hg // bh), -(-Wg // bw)
+    nblk = -(-T // bt) * nbh * nbw
+    members: List[List[int]] = [[] for _ in range(nblk)]
+    for n in range(N):
+        t, rem = divmod(n, Hg * Wg)
+        h, w = divmod(rem, Wg)
+        members[((t // bt) * nbh + h // bh) * nbw + w // bw].append(n)
+    return [np.asarray(m, dtype=np.int64) for m in members]
+
+
+def block_sizes(blocks: Sequence[np.ndarray]) -> np.ndarray:
+    return np.asarray([len(b) for b in blocks], dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------------------------
+# O2. Block means
+# ---------------------------------------------------------------------------------------------
+
+def pool(X: np.ndarray, blocks: Sequence[np.ndarray]) -> np.ndarray:
+    """Mean vector of each block ([VMoBA] "What carries the argument", Figure 2 caption: each key
+    block is represented by the mean of its keys; queries are pooled the same way).
+    X: [B, H, N, d] -> [B, H, nblk, d] in fp64."""
+    X = np.asarray(X, dtype=np.float64)
+    out = np.empty(X.shape[:2] + (len(blocks), X.shape[3]), np.float64)
+    for j, idx in enumerate(blocks):
+        out[:, :, j, :] = X[:, :, idx, :].sum(axis=2) / len(idx)
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# O3. Scores
+# ---------------------------------------------------------------------------------------------
+
+def block_logits(Qbar: np.ndarray, Kbar: np.ndarray, head_scale: np.ndarray) -> np.ndarray:
+    """L[b, h, I, J] = sigma_h * <qbar_I, kbar_J> (query-to-block-mean similarity, [VMoBA])."""
+    sig = np.asarray(head_scale, np.float64)[None, :, None, None]
+    return sig * np.einsum("bhid,bhjd->bhij", Qbar, Kbar)
+
+
+def score_row(Qbar, Kbar, head_scale) -> np.ndarray:
+    """Normalised similarity per query block: softmax over the kv blocks J of each row (I)
+    ([VMoBA] Eq. 4's cumulative normalised similarity, read per query block)."""
+    L = block_logits(Qbar, Kbar, head_scale)
+    m = L.max(axis=-1, keepdims=True)
+    e = np.exp(L - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def score_head(Qbar, Kbar, head_scale, qsizes) -> np.ndarray:
+    """Head-global normalisation for the global pool ([VMoBA] Eq. 3: one ranking over the whole
+    query-by-block matrix of a head): W_IJ = |I| exp(L_IJ) / sum_{I',J'} |I'| exp(L_I'J')."""
+    L = block_logits(Qbar, Kbar, head_scale)
+    wq = np.asarray(qsizes, np.float64)[None, None, :, None]
+    m = L.max(axis=(2, 3), keepdims=True)
+    e = wq * np.exp(L - m)
+    return e / e.sum(axis=(2, 3), keepdims=True)
+
+
+def exact_mass_row(q_rows: np.ndarray, K: np.ndarray, sigma: float,
+                   kvblocks: Sequence[np.ndarray]) -> np.ndarray:
+    """One query block's exact block masses ([LoSA]): softmax of sigma*q_i.k_j over all N keys,
+    summed over the keys of each kv block J and averaged over the block's queries.
+    q_rows: [|I|, d], K: [N, d] -> [nkv]."""
+    s = sigma * (q_rows @ K.T)
+    s = s - s.max(axis=1, keepdims=True)
+    P = np.exp(s)
+    P /= P.sum(axis=1, keepdims=True)
+    return np.asarray([P[:, idx].sum() for idx in kvblocks]) / q_rows.shape[0]
+
+
+def exact_mass(Q, K, head_scale, qblocks, kvblocks,
+               rows: Optional[Iterable[Tuple[int, int, int]]] = None) -> np.ndarray:
+    """Exact block masses M[b, h, I, J] from one dense step ([LoSA]); rows of M not listed in
+    `rows` (b, h, I) are left as NaN so that a sampled computation is never mistaken for a
+    full one."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    B, H = Q.shape[:2]
+    M = np.full((B, H, len(qblocks), len(kvblocks)), np.nan)
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(len(qblocks))]
+    for b, h, i in rows:
+        M[b, h, i] = exact_mass_row(Q[b, h, qblocks[i]], K[b, h], float(head_scale[h]),
+                                    kvblocks)
+    return M
+
+
+# ---------------------------------------------------------------------------------------------
+# O4. Selection
+# ---------------------------------------------------------------------------------------------
+
+def select_topp(scores: np.ndarray, p: float) -> np.ndarray:
+    """Smallest prefix, in (score descending, index ascending) order, whose cumulative sum
+    reaches p ([VMoBA] Eq. 4; [LoSA] the smallest block set meeting the mass threshold).
+    Returns the chosen indices ascending. p >= 1, or a sum that never reaches p, keeps all."""
+    s = np.asarray(scores, np.float64)
+    n = s.shape[0]
+    order = np.lexsort((np.arange(n), -s))
+    if p >= 1.0:
+        k = n
+    else:
+        c = np.cumsum(s[order])
+        hit = np.flatnonzero(c >= p)
+        k = int(hit[0]) + 1 if hit.size else n
+    return np.sort(order[:k])
+
+
+def select_row(S: np.ndarray, p: float) -> List[np.ndarray]:
+    """Top-p per (b, h, I) row of S [B, H, nq, nkv]; rows in (b*H + h)*nq + I order."""
+    B, H, nq, _ = S.shape
+    return [select_topp(S[b, h, i], p) for b in range(B) for h in range(H) for i in range(nq)]
+
+
+def head_min_k(counts: Sequence[int], qsizes: Sequence[int], nkv: int) -> int:
+    """[SCOPE] head-specific k: the query-block-size weighted mean of the initial retained
+    counts, as an exact integer ceiling, capped at the number of kv blocks."""
+    num = sum(int(c) * int(w) for c, w in zip(counts, qsizes))
+    den = sum(int(w) for w in qsizes)
+    return min(-(-num // den), int(nkv))
+
+
+def select_hybrid(S: np.ndarray, p: float, qsizes) -> Tuple[List[np.ndarray], np.ndarray]:
+    """[SCOPE] top-p, then rows whose retained count is below the head's k are extended with the
+    next blocks of the same (score desc, index asc) order up to k. Returns (rows, k per (b, h))."""
+    B, H, nq, nkv = S.shape
+    rows: List[np.ndarray] = []
+    head_k = np.zeros(B * H, np.int64)
+    for b in range(B):
+        for h in range(H):
+            base = [select_topp(S[b, h, i], p) for i in range(nq)]
+            k = head_min_k([len(r) for r in base], qsizes, nkv)
+            head_k[b * H + h] = k
+            for i in range(nq):
+                f = max(len(base[i]), k)
+                if f == len(base[i]):
+                    rows.append(base[i])
+                else:
+                    s = S[b, h, i]
+                    order = np.lexsort((np.arange(nkv), -s))
+                    rows.append(np.sort(order[:f]))
+    return rows, head_k
+
+
+def select_head(W: np.ndarray, tau: float) -> List[np.ndarray]:
+    """[VMoBA] global selection: per head, rank every (I, J) pair of the query-by-block matrix by
+    weight (ties: lower pair index I*nkv + J first) and keep the smallest prefix whose cumulative
+    weight reaches tau. A query block may end up with no pair at all (an empty row, referee
+    report major comment 1)."""
+    B, H, nq, nkv = W.shape
+    rows: List[np.ndarray] = []
+    for b in range(B):
+        for h in range(H):
+            pairs = select_topp(W[b, h].reshape(-1), tau)
+            I, J = np.divmod(pairs, nkv)
+            for i in range(nq):
+                rows.append(np.sort(J[I == i]))
+    return rows
+
+
+def to_csr(rows: Sequence[np.ndarray]) -> Tuple[np.ndarray, np.ndarray]:
+    counts = np.asarray([len(r) for r in rows], np.int64)
+    row_ptr = np.zeros(len(rows) + 1, np.int64)
+    np.cumsum(counts, out=row_ptr[1:])
+    col_idx = np.concatenate([np.asarray(r, np.int64) for r in rows]) if rows else np.zeros(0)
+    return row_ptr.astype(np.int32), col_idx.astype(np.int32)
+
+
+def csr_rows(row_ptr, col_idx) -> List[np.ndarray]:
+    return [np.asarray(col_idx[row_ptr[r]:row_ptr[r + 1]]) for r in range(len(row_ptr) - 1)]
+
+
+def density(rows: Sequence[np.ndarray], qsizes, kvsizes, H: int, B: int = 1) -> float:
+    """Selected fraction of the N x N query-key pairs: sum over rows of |I| * sum_J |J| / N^2."""
+    nq = len(qsizes)
+    N = float(np.sum(qsizes))
+    tot = 0.0
+    for r, sel in enumerate(rows):
+        tot += float(qsizes[r % nq]) * float(np.sum(np.asarray(kvsizes)[sel])) if len(sel) else 0
+    return tot / (B * H * N * N)
+
+
+# ---------------------------------------------------------------------------------------------
+# O5. Attention over the selected blocks
+# ---------------------------------------------------------------------------------------------
+
+def _selected_keys(sel: np.ndarray, kvblocks) -> np.ndarray:
+    if len(sel) == 0:
+        return np.zeros(0, np.int64)
+    return np.concatenate([kvblocks[j] for j in sel])
+
+
+def attention_rows(q_rows, K, V, sigma: float, keys: np.ndarray):
+    """Softmax attention of query rows over the given key tokens only ([VMoBA] Figure 2 caption:
+    attention is computed with the selected blocks only). Returns (O [|I|, d], LSE [|I|]).
+    No keys: O = 0, LSE = -inf."""
+    if keys.size == 0:
+        return np.zeros((q_rows.shape[0], V.shape[1])), np.full(q_rows.shape[0], -np.inf)
+    s = sigma * (q_rows @ K[keys].T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    O = (e @ V[keys]) / l
+    return O, (m + np.log(l))[:, 0]
+
+
+def attention_fwd(Q, K, V, head_scale, qblocks, kvblocks, row_ptr, col_idx,
+                  rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """O[b, h, i] and LSE[b, h, i] for every query token (or only the (b, h, I) blocks listed in
+    `rows`; other entries stay NaN). CSR row r = (b*H + h)*nq + I lists the selected kv blocks."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    B, H, N, d = Q.shape
+    nq = len(qblocks)
+    O = np.full((B, H, N, V.shape[3]), np.nan)
+    LSE = np.full((B, H, N), np.nan)
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(nq)]
+    for b, h, i in rows:
+        r = (b * H + h) * nq + i
+        keys = _selected_keys(col_idx[row_ptr[r]:row_ptr[r + 1]], kvblocks)
+        o, lse = attention_rows(Q[b, h, qblocks[i]], K[b, h], V[b, h], float(head_scale[h]), keys)
+        O[b, h, qblocks[i]] = o
+        LSE[b, h, qblocks[i]] = lse
+    return O, LSE
+
+
+# ---------------------------------------------------------------------------------------------
+# O6. Backward through the selected blocks (selection is a stop-gradient gate)
+# ---------------------------------------------------------------------------------------------
+
+def row_backward(q_rows, dO_rows, K, V, sigma: float, keys: np.ndarray):
+    """Gradients of sum(dO * O) for one query block's rows over its selected keys.
+    Returns (dQ_rows, dK_keys, dV_keys). With P = softmax(sigma q k^T):
+    dV = P^T dO; dP = dO V^T; D = rowsum(dO * O); dS = P * (dP - D); dQ = sigma dS K;
+    dK = sigma dS^T Q."""
+    if keys.size == 0:
+        return np.zeros_like(q_rows), np.zeros((0, K.shape[1])), np.zeros((0, V.shape[1]))
+    s = sigma * (q_rows @ K[keys].T)
+    s = s - s.max(axis=1, keepdims=True)
+    P = np.exp(s)
+    P /= P.sum(axis=1, keepdims=True)
+    O = P @ V[keys]
+    dV = P.T @ dO_rows
+    dP = dO_rows @ V[keys].T
+    D = (dO_rows * O).sum(axis=1, keepdims=True)
+    dS = P * (dP - D)
+    return sigma * dS @ K[keys], sigma * dS.T @ q_rows, dV
+
+
+def attention_bwd(Q, K, V, dO, head_scale, qblocks, kvblocks, row_ptr, col_idx):
+    """dQ, dK, dV of the block-sparse attention for every token (fp64)."""
+    Q, K, V, dO = (np.asarray(x, np.float64) for x in (Q, K, V, dO))
+    B, H, N, d = Q.shape
+    nq = len(qblocks)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nq):
+                r = (b * H + h) * nq + i
+                keys = _selected_keys(col_idx[row_ptr[r]:row_ptr[r + 1]], kvblocks)
+                gq, gk, gv = row_backward(Q[b, h, qblocks[i]], dO[b, h, qblocks[i]], K[b, h],
+                                          V[b, h], float(head_scale[h]), keys)
+                dQ[b, h, qblocks[i]] = gq
+                if keys.size:
+                    np.add.at(dK[b, h], keys, gk)
+                    np.add.at(dV[b, h], keys, gv)
+    return dQ, dK, dV
