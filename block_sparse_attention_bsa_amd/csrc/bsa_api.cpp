@@ -1,0 +1,354 @@
+// Host side of the C ABI declared in include/bsa.h: argument validation, partition and plan
+// construction, workspace layouts, and dispatch to the HIP kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "bsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return BSA_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_partition(const bsa_partition* part, const char* name) {
+  if (part->kind == BSA_PART_FLAT) {
+    if (part->flat < 1) return fail(BSA_EINVAL, "%s: flat block size must be >= 1", name);
+  } else if (part->kind == BSA_PART_TILE) {
+    if (part->bt < 1 || part->bh < 1 || part->bw < 1)
+      return fail(BSA_EINVAL, "%s: tile extents must be >= 1", name);
+  } else {
+    return fail(BSA_EINVAL, "%s: unknown partition kind %d", name, part->kind);
+  }
+  return BSA_OK;
+}
+
+int64_t partition_count(int T, int Hg, int Wg, const bsa_partition* part) {
+  const int64_t N = (int64_t)T * Hg * Wg;
+  if (part->kind == BSA_PART_FLAT) return ceil_div(N, part->flat);
+  return ceil_div(T, part->bt) * ceil_div(Hg, part->bh) * ceil_div(Wg, part->bw);
+}
+
+// Fill perm / blk_start for a validated partition; blk_start has nblk + 1 entries.
+void partition_fill(int T, int Hg, int Wg, const bsa_partition* part, int32_t* perm,
+                    int32_t* blk_start) {
+  const int64_t N = (int64_t)T * Hg * Wg;
+  if (part->kind == BSA_PART_FLAT) {
+    const int64_t nb = ceil_div(N, part->flat);
+    for (int64_t n = 0; n < N; ++n) perm[n] = (int32_t)n;
+    for (int64_t j = 0; j <= nb; ++j) blk_start[j] = (int32_t)std::min<int64_t>(j * part->flat, N);
+    return;
+  }
+  const int nbt = (int)ceil_div(T, part->bt), nbh = (int)ceil_div(Hg, part->bh),
+            nbw = (int)ceil_div(Wg, part->bw);
+  int64_t pos = 0, j = 0;
+  for (int a = 0; a < nbt; ++a)
+    for (int b = 0; b < nbh; ++b)
+      for (int c = 0; c < nbw; ++c, ++j) {
+        blk_start[j] = (int32_t)pos;
+        const int t1 = std::min(T, (a + 1) * part->bt), h1 = std::min(Hg, (b + 1) * part->bh),
+                  w1 = std::min(Wg, (c + 1) * part->bw);
+        for (int t = a * part->bt; t < t1; ++t)
+          for (int h = b * part->bh; h < h1; ++h)
+            for (int w = c * part->bw; w < w1; ++w) perm[pos++] = (t * Hg + h) * Wg + w;
+      }
+  blk_start[j] = (int32_t)pos;
+}
+
+int check_device(const bsa_plan* p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess)
+    return fail(BSA_EHIP, "hipGetDevice failed: no usable HIP device");
+  if (dev != p->device)
+    return fail(BSA_EINVAL, "current device %d differs from the plan's device %d", dev,
+                p->device);
+  return BSA_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BSA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool supported_attention(const bsa_problem& pr) {
+  return (pr.d == 64 || pr.d == 128) && (pr.dtype == BSA_BF16 || pr.dtype == BSA_FP32);
+}
+
+template <typename T>
+int upload(const std::vector<T>& h, T** d) {
+  if (hipMalloc((void**)d, std::max<size_t>(1, h.size()) * sizeof(T)) != hipSuccess) return -1;
+  if (!h.empty() &&
+      hipMemcpy(*d, h.data(), h.size() * sizeof(T), hipMemcpyHostToDevice) != hipSuccess)
+    return -1;
+  return 0;
+}
+
+void free_plan(bsa_plan* p) {
+  if (!p) return;
+  for (void* ptr : {(void*)p->qperm, (void*)p->qstart, (void*)p->kvperm, (void*)p->kvstart,
+                    (void*)p->items, (void*)p->scale})
+    if (ptr) (void)hipFree(ptr);
+  delete p;
+}
+
+}  // namespace
+
+SelectWs select_ws_layout(const bsa_plan& p) {
+  SelectWs w;
+  const size_t rows = (size_t)p.prob.B * p.prob.H * p.nq;
+  w.nwords = (p.nkv + 31) / 32;
+  w.bitmap = 0;
+  w.base_counts = align_up(rows * w.nwords * 4);
+  w.head_k = w.base_counts + align_up(rows * 4);
+  w.total = w.head_k + align_up((size_t)p.prob.B * p.prob.H * 4);
+  return w;
+}
+
+BwdWs bwd_ws_layout(const bsa_plan& p) {
+  BwdWs w;
+  const size_t BH = (size_t)p.prob.B * p.prob.H;
+  const size_t cols = BH * p.nkv, rows = BH * p.nq;
+  w.delta = 0;
+  w.col_ptr = align_up(BH * p.prob.N * 4);
+  w.col_fill = w.col_ptr + align_up((cols + 1) * 4);
+  w.row_of = w.col_fill + align_up(cols * 4);
+  w.total = w.row_of + align_up(rows * p.nkv * 4);
+  return w;
+}
+
+size_t calib_ws_bytes(const bsa_plan& p) {
+  return align_up((size_t)p.prob.B * p.prob.H * p.prob.N * 4);
+}
+
+extern "C" {
+
+const char* bsa_last_error(void) { return g_last_error.c_str(); }
+
+int bsa_partition_build(int32_t T, int32_t Hg, int32_t Wg, const bsa_partition* part,
+                        int32_t* perm, int32_t* blk_start, int32_t cap_blocks, int32_t* nblk) {
+  if (!part || !perm || !blk_start || !nblk)
+    return fail(BSA_EINVAL, "bsa_partition_build: NULL argument");
+  if (T < 1 || Hg < 1 || Wg < 1) return fail(BSA_EINVAL, "bsa_partition_build: empty grid");
+  if ((int64_t)T * Hg * Wg > INT32_MAX)
+    return fail(BSA_EUNSUPPORTED, "bsa_partition_build: grid exceeds 2^31 tokens");
+  int rc = check_partition(part, "bsa_partition_build");
+  if (rc) return rc;
+  const int64_t nb = partition_count(T, Hg, Wg, part);
+  *nblk = (int32_t)nb;
+  if (nb > cap_blocks)
+    return fail(BSA_ECAPACITY, "bsa_partition_build: %lld blocks exceed capacity %d",
+                (long long)nb, cap_blocks);
+  partition_fill(T, Hg, Wg, part, perm, blk_start);
+  return ok();
+}
+
+int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan** out) {
+  if (!prob || !out) return fail(BSA_EINVAL, "bsa_plan_create: NULL argument");
+  *out = nullptr;
+  const bsa_problem& pr = *prob;
+  if (pr.B < 1 || pr.H < 1 || pr.T < 1 || pr.Hg < 1 || pr.Wg < 1 || pr.d < 1)
+    return fail(BSA_EINVAL, "bsa_plan_create: B, H, d and the grid must be >= 1");
+  if ((int64_t)pr.T * pr.Hg * pr.Wg != (int64_t)pr.N)
+    return fail(BSA_EINVAL, "bsa_plan_create: N = %d but T*Hg*Wg = %lld", pr.N,
+                (long long)pr.T * pr.Hg * pr.Wg);
+  if (pr.dtype != BSA_BF16 && pr.dtype != BSA_FP32)
+    return fail(BSA_EINVAL, "bsa_plan_create: unknown dtype %d", pr.dtype);
+  if (pr.d != 64 && pr.d != 128)
+    return fail(BSA_EUNSUPPORTED, "bsa_plan_create: head dim %d (supported: 64, 128)", pr.d);
+  int rc = check_partition(&pr.qpart, "bsa_plan_create qpart");
+  if (rc) return rc;
+  rc = check_partition(&pr.kvpart, "bsa_plan_create kvpart");
+  if (rc) return rc;
+  if ((int64_t)pr.B * pr.H > (1 << 24))
+    return fail(BSA_EUNSUPPORTED, "bsa_plan_create: B*H too large");
+  if (head_scale)
+    for (int h = 0; h < pr.H; ++h)
+      if (!std::isfinite(head_scale[h]))
+        return fail(BSA_EINVAL, "bsa_plan_create: head_scale[%d] is not finite", h);
+
+  bsa_plan* p = new bsa_plan();
+  p->prob = pr;
+  p->nq = (int)partition_count(pr.T, pr.Hg, pr.Wg, &pr.qpart);
+  p->nkv = (int)partition_count(pr.T, pr.Hg, pr.Wg, &pr.kvpart);
+  p->h_qperm.resize(pr.N);
+  p->h_kvperm.resize(pr.N);
+  p->h_qstart.resize(p->nq + 1);
+  p->h_kvstart.resize(p->nkv + 1);
+  partition_fill(pr.T, pr.Hg, pr.Wg, &pr.qpart, p->h_qperm.data(), p->h_qstart.data());
+  partition_fill(pr.T, pr.Hg, pr.Wg, &pr.kvpart, p->h_kvperm.data(), p->h_kvstart.data());
+  for (int i = 0; i < p->nq; ++i) {
+    const int sz = p->h_qstart[i + 1] - p->h_qstart[i];
+    p->max_qblk = std::max(p->max_qblk, sz);
+    for (int off = 0; off < sz; off += kAttnRows) {
+      p->h_items.push_back(i);
+      p->h_items.push_back(off);
+    }
+  }
+  for (int j = 0; j < p->nkv; ++j)
+    p->max_kvblk = std::max(p->max_kvblk, p->h_kvstart[j + 1] - p->h_kvstart[j]);
+  p->n_items = (int)(p->h_items.size() / 2);
+  p->h_scale.resize(pr.H);
+  for (int h = 0; h < pr.H; ++h)
+    p->h_scale[h] = head_scale ? head_scale[h] : (float)(1.0 / std::sqrt((double)pr.d));
+
+  if (hipGetDevice(&p->device) != hipSuccess) {
+    free_plan(p);
+    return fail(BSA_EHIP, "bsa_plan_create: no usable HIP device");
+  }
+  if (upload(p->h_qperm, &p->qperm) || upload(p->h_qstart, &p->qstart) ||
+      upload(p->h_kvperm, &p->kvperm) || upload(p->h_kvstart, &p->kvstart) ||
+      upload(p->h_items, &p->items) || upload(p->h_scale, &p->scale)) {
+    free_plan(p);
+    return fail(BSA_EHIP, "bsa_plan_create: device allocation or upload failed");
+  }
+  *out = p;
+  return ok();
+}
+
+int bsa_plan_destroy(bsa_plan* plan) {
+  if (!plan) return fail(BSA_EINVAL, "bsa_plan_destroy: NULL plan");
+  free_plan(plan);
+  return ok();
+}
+
+int bsa_plan_info(const bsa_plan* plan, int32_t* nq, int32_t* nkv, size_t* ws_select,
+                  size_t* ws_calib, size_t* ws_bwd) {
+  if (!plan) return fail(BSA_EINVAL, "bsa_plan_info: NULL plan");
+  if (nq) *nq = plan->nq;
+  if (nkv) *nkv = plan->nkv;
+  if (ws_select) *ws_select = select_ws_layout(*plan).total;
+  if (ws_calib) *ws_calib = calib_ws_bytes(*plan);
+  if (ws_bwd) *ws_bwd = bwd_ws_layout(*plan).total;
+  return ok();
+}
+
+int bsa_plan_blocks(const bsa_plan* plan, int32_t which, int32_t* perm, int32_t* blk_start) {
+  if (!plan || !perm || !blk_start) return fail(BSA_EINVAL, "bsa_plan_blocks: NULL argument");
+  if (which != 0 && which != 1) return fail(BSA_EINVAL, "bsa_plan_blocks: which must be 0 or 1");
+  const auto& pv = which == 0 ? plan->h_qperm : plan->h_kvperm;
+  const auto& sv = which == 0 ? plan->h_qstart : plan->h_kvstart;
+  std::memcpy(perm, pv.data(), pv.size() * sizeof(int32_t));
+  std::memcpy(blk_start, sv.data(), sv.size() * sizeof(int32_t));
+  return ok();
+}
+
+int bsa_pool(const bsa_plan* plan, int32_t which, const void* X, float* Xbar, void* stream) {
+  if (!plan || !X || !Xbar) return fail(BSA_EINVAL, "bsa_pool: NULL argument");
+  if (which != 0 && which != 1) return fail(BSA_EINVAL, "bsa_pool: which must be 0 or 1");
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_pool(*plan, which, X, Xbar, (hipStream_t)stream), "bsa_pool");
+}
+
+int bsa_score(const bsa_plan* plan, const float* Qbar, const float* Kbar, int32_t norm, float* S,
+              void* stream) {
+  if (!plan || !Qbar || !Kbar || !S) return fail(BSA_EINVAL, "bsa_score: NULL argument");
+  if (norm != BSA_NORM_ROW && norm != BSA_NORM_HEAD)
+    return fail(BSA_EINVAL, "bsa_score: norm must be BSA_NORM_ROW or BSA_NORM_HEAD");
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_score(*plan, Qbar, Kbar, norm, S, (hipStream_t)stream),
+                       "bsa_score");
+}
+
+int bsa_calibrate_mass(const bsa_plan* plan, const void* Q, const void* K, float* M, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!plan || !Q || !K || !M) return fail(BSA_EINVAL, "bsa_calibrate_mass: NULL argument");
+  if (plan->prob.dtype != BSA_BF16 || plan->prob.d != 128)
+    return fail(BSA_EUNSUPPORTED, "bsa_calibrate_mass: bf16 with d = 128 only");
+  const size_t need = calib_ws_bytes(*plan);
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ECAPACITY, "bsa_calibrate_mass: workspace %zu < %zu bytes", ws_bytes, need);
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_calibrate(*plan, Q, K, M, ws, (hipStream_t)stream),
+                       "bsa_calibrate_mass");
+}
+
+int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* prm,
+               int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
+               int32_t* head_k, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || !S || !prm || !row_ptr || !col_idx)
+    return fail(BSA_EINVAL, "bsa_select: NULL argument");
+  if (!(prm->p > 0.0 && prm->p <= 1.0))
+    return fail(BSA_EINVAL, "bsa_select: p must lie in (0, 1]");
+  if (prm->pool != BSA_POOL_ROW && prm->pool != BSA_POOL_HEAD)
+    return fail(BSA_EINVAL, "bsa_select: unknown pool %d", prm->pool);
+  if (prm->min_k_mode < BSA_MINK_NONE || prm->min_k_mode > BSA_MINK_WEIGHTED_MEAN)
+    return fail(BSA_EINVAL, "bsa_select: unknown min_k_mode %d", prm->min_k_mode);
+  if (prm->min_k_mode == BSA_MINK_FIXED && prm->fixed_k < 0)
+    return fail(BSA_EINVAL, "bsa_select: fixed_k must be >= 0");
+  if (prm->pool == BSA_POOL_HEAD && prm->min_k_mode != BSA_MINK_NONE)
+    return fail(BSA_EUNSUPPORTED, "bsa_select: a minimum count applies to the ROW pool only");
+  if (plan->nkv > kMaxSelectBlocks)
+    return fail(BSA_EUNSUPPORTED, "bsa_select: %d kv blocks exceed the supported %d", plan->nkv,
+                kMaxSelectBlocks);
+  const int64_t need_cols = (int64_t)plan->prob.B * plan->prob.H * plan->nq * plan->nkv;
+  if (col_cap < need_cols)
+    return fail(BSA_ECAPACITY, "bsa_select: col_idx capacity %lld < %lld", (long long)col_cap,
+                (long long)need_cols);
+  const size_t need = select_ws_layout(*plan).total;
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ECAPACITY, "bsa_select: workspace %zu < %zu bytes", ws_bytes, need);
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_select(*plan, S, *prm, row_ptr, col_idx, counts, head_k, ws,
+                                     (hipStream_t)stream),
+                       "bsa_select");
+}
+
+int bsa_attn_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
+                 const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse,
+                 void* stream) {
+  if (!plan || !Q || !K || !V || !row_ptr || !col_idx || !O)
+    return fail(BSA_EINVAL, "bsa_attn_fwd: NULL argument");
+  if (!supported_attention(plan->prob))
+    return fail(BSA_EUNSUPPORTED, "bsa_attn_fwd: unsupported dtype/d combination");
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_attn_fwd(*plan, Q, K, V, row_ptr, col_idx, O, lse,
+                                       (hipStream_t)stream),
+                       "bsa_attn_fwd");
+}
+
+int bsa_attn_bwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* lse, const int32_t* row_ptr,
+                 const int32_t* col_idx, void* dQ, void* dK, void* dV, void* ws,
+                 size_t ws_bytes, void* stream) {
+  if (!plan || !Q || !K || !V || !O || !dO || !lse || !row_ptr || !col_idx || !dQ || !dK || !dV)
+    return fail(BSA_EINVAL, "bsa_attn_bwd: NULL argument");
+  if (plan->prob.dtype != BSA_BF16 || plan->prob.d != 128)
+    return fail(BSA_EUNSUPPORTED, "bsa_attn_bwd: bf16 with d = 128 only");
+  const size_t need = bwd_ws_layout(*plan).total;
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ECAPACITY, "bsa_attn_bwd: workspace %zu < %zu bytes", ws_bytes, need);
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_attn_bwd(*plan, Q, K, V, O, dO, lse, row_ptr, col_idx, dQ, dK, dV,
+                                       ws, (hipStream_t)stream),
+                       "bsa_attn_bwd");
+}
+
+}  // extern "C"

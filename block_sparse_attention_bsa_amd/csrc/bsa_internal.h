@@ -1,0 +1,66 @@
+// Internal declarations shared by the C-ABI host code and the HIP kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/bsa.h"
+
+// Largest kv-block count a row selection supports: one bitmap word per thread of a 256-thread
+// workgroup in the CSR emit pass.
+constexpr int kMaxSelectBlocks = 8192;
+// Query rows one attention workgroup owns (4 wavefronts x 32 rows).
+constexpr int kAttnRows = 128;
+
+struct bsa_plan {
+  bsa_problem prob;
+  int device = 0;
+  int nq = 0, nkv = 0;
+  int max_qblk = 0, max_kvblk = 0;
+  std::vector<int32_t> h_qperm, h_qstart, h_kvperm, h_kvstart, h_items;
+  // Device copies (owned by the plan).
+  int32_t* qperm = nullptr;
+  int32_t* qstart = nullptr;
+  int32_t* kvperm = nullptr;
+  int32_t* kvstart = nullptr;
+  int32_t* items = nullptr;   // attention work items: pairs (I, first row within block I)
+  int n_items = 0;
+  float* scale = nullptr;     // sigma_h, [H]
+  std::vector<float> h_scale;
+};
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+// Workspace layouts (byte offsets), derived from the plan.
+struct SelectWs {
+  size_t bitmap, base_counts, head_k, total;
+  int nwords;
+};
+SelectWs select_ws_layout(const bsa_plan& p);
+
+struct BwdWs {
+  size_t delta, col_ptr, col_fill, row_of, total;
+};
+BwdWs bwd_ws_layout(const bsa_plan& p);
+
+size_t calib_ws_bytes(const bsa_plan& p);
+
+// Kernel launchers (defined in the .hip files). Each returns the launch status.
+hipError_t launch_pool(const bsa_plan& p, int which, const void* X, float* Xbar, hipStream_t s);
+hipError_t launch_score(const bsa_plan& p, const float* Qbar, const float* Kbar, int norm,
+                        float* S, hipStream_t s);
+hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_params& prm,
+                         int32_t* row_ptr, int32_t* col_idx, int32_t* counts, int32_t* head_k,
+                         void* ws, hipStream_t s);
+hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
+                           const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse,
+                           hipStream_t s);
+hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, float* M, void* ws,
+                            hipStream_t s);
+hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
+                           const void* O, const void* dO, const float* lse,
+                           const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK,
+                           void* dV, void* ws, hipStream_t s);

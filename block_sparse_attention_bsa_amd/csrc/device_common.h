@@ -1,0 +1,80 @@
+// Device helpers for gfx950 kernels: vector types, bf16 packing, wave reductions, XCD mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to bf16 (nearest even, one v_cvt_pk_bf16_f32) and pack them, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Workgroup ids are dealt round-robin to the 8 XCDs (id % 8). Renumber them so that logical
+// ids [x * q + min(x, r), ...) all run on XCD x: consecutive logical work (one head's query
+// blocks) then shares one XCD's L2. A bijection on [0, total).
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int q = total >> 3, r = total & 7;
+  return xcd * q + (xcd < r ? xcd : r) + idx;
+}
+
+__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, int delta) {
+  uint32_t lo = __shfl_up((uint32_t)v, delta, 64);
+  uint32_t hi = __shfl_up((uint32_t)(v >> 32), delta, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    unsigned long long o = shfl_up_u64(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}

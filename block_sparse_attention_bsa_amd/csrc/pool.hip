@@ -1,0 +1,110 @@
+// Block means of Q or K (pith.science review of VMoBA, "What carries the argument" and the
+// Figure 2 caption: each block is represented by the mean of its token vectors).
+//
+// One workgroup of 256 threads per (block J, head bh). A token row of d elements is read as
+// 16-byte segments: SEGS threads cover one row and 256 / SEGS rows are in flight per pass, so a
+// wavefront reads whole rows (a 4x4x8 tile is 16 runs of 8 contiguous tokens, 2 KiB each for
+// bf16, d = 128). Each thread accumulates its segment over the rows it visits in fp32; the
+// partial sums are combined across row groups in LDS in a fixed order (deterministic).
+#include "bsa_internal.h"
+#include "device_common.h"
+
+namespace {
+
+template <typename T>
+struct Seg;
+
+template <>
+struct Seg<uint16_t> {  // bf16 words: 8 per 16 bytes
+  static constexpr int kVec = 8;
+  __device__ static void add(float* acc, uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_lo(w[i]);
+      acc[2 * i + 1] += bf16_hi(w[i]);
+    }
+  }
+};
+
+template <>
+struct Seg<float> {  // fp32: 4 per 16 bytes
+  static constexpr int kVec = 4;
+  __device__ static void add(float* acc, uint4 v) {
+    acc[0] += __uint_as_float(v.x);
+    acc[1] += __uint_as_float(v.y);
+    acc[2] += __uint_as_float(v.z);
+    acc[3] += __uint_as_float(v.w);
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
+                                                   float* __restrict__ Xbar,
+                                                   const int32_t* __restrict__ perm,
+                                                   const int32_t* __restrict__ start, int N,
+                                                   int nblk) {
+  constexpr int VEC = Seg<T>::kVec;
+  constexpr int SEGS = D / VEC;
+  constexpr int GROUPS = 256 / SEGS;
+  constexpr int UNROLL = 4;
+  __shared__ float red[GROUPS][D + 1];
+
+  const int J = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int seg = threadIdx.x % SEGS;
+  const int grp = threadIdx.x / SEGS;
+  const int s0 = start[J];
+  const int cnt = start[J + 1] - s0;
+  const T* __restrict__ Xh = X + (size_t)bh * N * D + seg * VEC;
+
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+
+  for (int k = grp; k < cnt; k += UNROLL * GROUPS) {
+    uint4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int kk = k + u * GROUPS;
+      if (kk < cnt) {
+        const int n = perm[s0 + kk];
+        v[u] = *reinterpret_cast<const uint4*>(Xh + (size_t)n * D);
+      } else {
+        v[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+      if (k + u * GROUPS < cnt) Seg<T>::add(acc, v[u]);
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) red[grp][seg * VEC + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < GROUPS; ++g) s += red[g][threadIdx.x];
+    Xbar[((size_t)bh * nblk + J) * D + threadIdx.x] = s / (float)cnt;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch(const bsa_plan& p, int which, const void* X, float* Xbar, hipStream_t s) {
+  const int nblk = which == 0 ? p.nq : p.nkv;
+  dim3 grid(nblk, p.prob.B * p.prob.H);
+  pool_kernel<T, D><<<grid, 256, 0, s>>>(static_cast<const T*>(X), Xbar,
+                                         which == 0 ? p.qperm : p.kvperm,
+                                         which == 0 ? p.qstart : p.kvstart, p.prob.N, nblk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pool(const bsa_plan& p, int which, const void* X, float* Xbar, hipStream_t s) {
+  if (p.prob.dtype == BSA_BF16)
+    return p.prob.d == 128 ? launch<uint16_t, 128>(p, which, X, Xbar, s)
+                           : launch<uint16_t, 64>(p, which, X, Xbar, s);
+  return p.prob.d == 128 ? launch<float, 128>(p, which, X, Xbar, s)
+                         : launch<float, 64>(p, which, X, Xbar, s);
+}

@@ -1,0 +1,91 @@
+"""One block-sparse attention layer call, built from the C-ABI entry points.
+
+Allocates the block-level buffers, CSR and workspaces with PyTorch on the current device and
+calls bsa_pool / bsa_score / bsa_select / bsa_attn_fwd (and bsa_calibrate_mass, bsa_attn_bwd) in
+order on one stream. No arithmetic happens here.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (BSA_MINK_NONE, BSA_NORM_HEAD, BSA_NORM_ROW, BSA_POOL_HEAD, BSA_POOL_ROW, Plan,
+               bsa_attn_bwd, bsa_attn_fwd, bsa_calibrate_mass, bsa_pool, bsa_score, bsa_select)
+
+
+class BlockSparseAttention:
+    def __init__(self, B, H, d, grid, qpart, kvpart, dtype="bf16", head_scale=None,
+                 device="cuda"):
+        self.plan = Plan(B, H, d, grid, qpart, kvpart, dtype=dtype, head_scale=head_scale)
+        p = self.plan
+        self.device = torch.device(device)
+        f32 = dict(dtype=torch.float32, device=self.device)
+        i32 = dict(dtype=torch.int32, device=self.device)
+        self.rows = B * H * p.nq
+        self.qbar = torch.empty((B, H, p.nq, d), **f32)
+        self.kbar = torch.empty((B, H, p.nkv, d), **f32)
+        self.S = torch.empty((B, H, p.nq, p.nkv), **f32)
+        self.row_ptr = torch.empty(self.rows + 1, **i32)
+        self.col_cap = self.rows * p.nkv
+        self.col_idx = torch.empty(self.col_cap, **i32)
+        self.counts = torch.empty(self.rows, **i32)
+        self.head_k = torch.empty(B * H, **i32)
+        self.ws_select = torch.empty(max(p.ws_select, 1), dtype=torch.uint8, device=self.device)
+        self._ws_calib = None
+        self._ws_bwd = None
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    # -- stages -----------------------------------------------------------------------------
+    def pool(self, q, k, stream=None):
+        bsa_pool(self.plan, 0, q, self.qbar, stream)
+        bsa_pool(self.plan, 1, k, self.kbar, stream)
+
+    def score(self, norm=BSA_NORM_ROW, stream=None):
+        bsa_score(self.plan, self.qbar, self.kbar, norm, self.S, stream)
+        return self.S
+
+    def calibrate(self, q, k, stream=None):
+        if self._ws_calib is None:
+            self._ws_calib = torch.empty(self.plan.ws_calib, dtype=torch.uint8, device=self.device)
+        bsa_calibrate_mass(self.plan, q, k, self.S, self._ws_calib, self.plan.ws_calib, stream)
+        return self.S
+
+    def select(self, p, pool=BSA_POOL_ROW, min_k_mode=BSA_MINK_NONE, fixed_k=0, stream=None,
+               scores=None):
+        bsa_select(self.plan, self.S if scores is None else scores, p, pool, min_k_mode, fixed_k,
+                   self.row_ptr, self.col_idx, self.col_cap, self.counts, self.head_k,
+                   self.ws_select, self.plan.ws_select, stream)
+        return self.row_ptr, self.col_idx
+
+    def attention(self, q, k, v, row_ptr=None, col_idx=None, out=None, lse=None, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=self.device)
+        bsa_attn_fwd(self.plan, q, k, v, self.row_ptr if row_ptr is None else row_ptr,
+                     self.col_idx if col_idx is None else col_idx, out, lse, stream)
+        return out, lse
+
+    def backward(self, q, k, v, o, do, lse, row_ptr=None, col_idx=None, stream=None):
+        if self._ws_bwd is None:
+            self._ws_bwd = torch.empty(self.plan.ws_bwd, dtype=torch.uint8, device=self.device)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bsa_attn_bwd(self.plan, q, k, v, o, do, lse, self.row_ptr if row_ptr is None else row_ptr,
+                     self.col_idx if col_idx is None else col_idx, dq, dk, dv, self._ws_bwd,
+                     self.plan.ws_bwd, stream)
+        return dq, dk, dv
+
+    # -- whole layer ---------------------------------------------------------------------------
+    def forward(self, q, k, v, p, mode="row", min_k_mode=BSA_MINK_NONE, out=None, lse=None,
+                stream=None):
+        """pool(Q), pool(K), score, select, sparse attention. mode: 'row' or 'head'."""
+        self.pool(q, k, stream)
+        self.score(BSA_NORM_HEAD if mode == "head" else BSA_NORM_ROW, stream)
+        self.select(p, BSA_POOL_HEAD if mode == "head" else BSA_POOL_ROW, min_k_mode,
+                    stream=stream)
+        return self.attention(q, k, v, out=out, lse=lse, stream=stream)
+
+    def csr_host(self):
+        rp = self.row_ptr.cpu().numpy()
+        return rp, self.col_idx[: int(rp[-1])].cpu().numpy()

@@ -1,0 +1,190 @@
+/*
+ * bsa.h - C ABI of a block-sparse attention library for long 3D (frame x height x width) video
+ * token sequences, written for AMD Instinct MI355X (gfx950).
+ *
+ * The path (each step cites the page that defines it):
+ *   1. bsa_pool           mean of Q (or K) over each block of a 1D/2D/3D partition of the token grid
+ *                         (pith.science review of VMoBA, "What carries the argument": every key
+ *                         block is represented by its mean key; Figure 2 caption).
+ *   2. bsa_score          query-block x key-block similarity of the block means, normalised per
+ *                         query block (row) or over the whole head (VMoBA review, referee report
+ *                         major comment 1: Eq. 3 global selection over the query-by-block matrix).
+ *      bsa_calibrate_mass exact per-(head, q-block, kv-block) softmax mass from one dense step
+ *                         (LoSA abstract, scholarbro author page).
+ *   3. bsa_select         per (head, q-block) the smallest kv-block set, in descending score
+ *                         order, whose cumulative score or mass reaches p (VMoBA review, major
+ *                         comment 1 on Sec. 3.4 Eq. 4; LoSA abstract), optionally raised to a
+ *                         per-head minimum count (SCOPE abstract, mlsift sparse-attention listing)
+ *                         or ranked over a head-global pool of (q-block, kv-block) pairs (VMoBA
+ *                         Eq. 3). The result is an int32 CSR list that callers may freeze and
+ *                         reuse across denoising steps (LoSA abstract).
+ *   4. bsa_attn_fwd       online-softmax attention of every query over the tokens of its selected
+ *                         kv blocks only (VMoBA review, Figure 2 caption), and bsa_attn_bwd, its
+ *                         gradient for training through the sparse attention (VMoBA review,
+ *                         "The reading").
+ *
+ * Conventions shared by every entry point
+ *   - Tensors Q, K, V, O, dO, dQ, dK, dV are [B, H, N, d], d contiguous, in device memory. Tokens
+ *     are in frame-major order n = (t * Hg + h) * Wg + w. dtype BSA_BF16 passes raw bf16 words
+ *     (uint16); BSA_FP32 passes float.
+ *   - Block-level tensors are fp32: Xbar [B, H, nblk, d]; S and M [B, H, nq, nkv].
+ *   - CSR row r = (b * H + h) * nq + I lists the kv blocks J selected for query block I of head
+ *     (b, h), ascending; row_ptr has B*H*nq + 1 entries, row_ptr[0] = 0.
+ *   - Every pointer argument is a device pointer unless it says "host". The caller owns every
+ *     tensor, CSR buffer and workspace; the plan owns only its own small device descriptors.
+ *   - Every call validates all arguments on the host before enqueuing anything; on an error it
+ *     writes nothing and returns a negative status, and bsa_last_error() (thread-local) describes
+ *     it. Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the null stream).
+ *     Results are deterministic: the same inputs give the same bits.
+ *   - NaN inputs propagate into scores and outputs; the selection made from NaN scores is
+ *     unspecified but always a valid CSR.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define BSA_OK 0
+#define BSA_EINVAL (-1)        /* a NULL pointer, a bad shape or parameter                       */
+#define BSA_EUNSUPPORTED (-2)  /* a valid request this build does not implement (d, dtype, size) */
+#define BSA_ECAPACITY (-3)     /* an output or workspace buffer is smaller than required          */
+#define BSA_EHIP (-4)          /* the HIP runtime reported an error (no device, launch failure)   */
+
+/* partitions */
+#define BSA_PART_FLAT 0        /* contiguous runs of `flat` tokens in frame-major order           */
+#define BSA_PART_TILE 1        /* bt x bh x bw tiles of the grid, clipped at the edge             */
+
+/* dtypes */
+#define BSA_BF16 0
+#define BSA_FP32 1
+
+/* normalisation (bsa_score) and selection pool (bsa_select) */
+#define BSA_NORM_ROW 0         /* softmax over kv blocks of each query block                      */
+#define BSA_NORM_HEAD 1        /* |I|-weighted softmax over all (I, J) pairs of a head            */
+#define BSA_POOL_ROW 0         /* select per (head, query block)                                  */
+#define BSA_POOL_HEAD 1        /* select over all (I, J) pairs of a head                          */
+
+/* per-head minimum count after top-p (bsa_select) */
+#define BSA_MINK_NONE 0
+#define BSA_MINK_FIXED 1       /* k = fixed_k for every head                                      */
+#define BSA_MINK_WEIGHTED_MEAN 2 /* k_h = ceil(sum_I |I| c_I / sum_I |I|), SCOPE abstract          */
+
+/*
+ * Block partition of the (T, Hg, Wg) token grid into non-overlapping blocks (VMoBA review,
+ * circularity check: Eq. 1-2 build the partition constructively; 1D temporal blocks are
+ * (bt, Hg, Wg) tiles, 2D spatial blocks (T, bh, bw), 3D blocks (bt, bh, bw)). Block (a, b, c) of
+ * a TILE partition is numbered (a * nbh + b) * nbw + c and holds its tokens in ascending n.
+ */
+typedef struct {
+  int32_t kind;          /* BSA_PART_FLAT or BSA_PART_TILE        */
+  int32_t flat;          /* FLAT: tokens per block (>= 1)         */
+  int32_t bt, bh, bw;    /* TILE: tile extents (each >= 1)        */
+} bsa_partition;
+
+typedef struct {
+  int32_t B, H, N, d;    /* batch, heads, tokens (= T * Hg * Wg), head dim (64 or 128)         */
+  int32_t dtype;         /* BSA_BF16 or BSA_FP32                                                */
+  int32_t T, Hg, Wg;     /* token grid                                                          */
+  bsa_partition qpart;   /* partition of the queries (pooled in step 1, one CSR row per block)  */
+  bsa_partition kvpart;  /* partition of the keys/values (the selectable blocks)                */
+} bsa_problem;
+
+typedef struct {
+  double p;              /* threshold in (0, 1]: top-p / retained mass (ROW) or tau (HEAD).
+                            Selection keeps the shortest prefix of the (score descending, index
+                            ascending) order whose cumulative sum is >= p; p >= 1, or a sum
+                            that never reaches p, keeps every block (pair).                     */
+  int32_t pool;          /* BSA_POOL_ROW or BSA_POOL_HEAD                                       */
+  int32_t min_k_mode;    /* BSA_MINK_*; ROW pool only                                           */
+  int32_t fixed_k;       /* BSA_MINK_FIXED: the per-head minimum (>= 0)                         */
+} bsa_select_params;
+
+typedef struct bsa_plan bsa_plan;
+
+/* Host only, no device call: fill perm[N] (block-major token order: block j's tokens are
+ * perm[blk_start[j] .. blk_start[j+1]), ascending) and blk_start[nblk + 1]; *nblk receives the
+ * block count. blk_start must hold cap_blocks + 1 entries; returns BSA_ECAPACITY (with *nblk set)
+ * when the partition has more than cap_blocks blocks. */
+int bsa_partition_build(int32_t T, int32_t Hg, int32_t Wg, const bsa_partition* part,
+                        int32_t* perm, int32_t* blk_start, int32_t cap_blocks, int32_t* nblk);
+
+/* Validate `prob`, build both partitions and upload them to the current device. head_scale is
+ * a host array of H softmax scales sigma_h (copied), or NULL for 1/sqrt(d). The plan is
+ * immutable afterwards and may be shared by calls on several streams. */
+int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan** out);
+int bsa_plan_destroy(bsa_plan* plan);
+
+/* Block counts and the workspace sizes (bytes) that bsa_select, bsa_calibrate_mass and
+ * bsa_attn_bwd require for this plan. Any output pointer may be NULL. */
+int bsa_plan_info(const bsa_plan* plan, int32_t* nq, int32_t* nkv, size_t* ws_select,
+                  size_t* ws_calib, size_t* ws_bwd);
+
+/* Host copies of a plan's partition (which = 0 queries, 1 keys/values): perm[N] and
+ * blk_start[nblk + 1], both host buffers. */
+int bsa_plan_blocks(const bsa_plan* plan, int32_t which, int32_t* perm, int32_t* blk_start);
+
+/* Step 1. Xbar[b, h, J, :] = (1/|J|) sum_{n in J} X[b, h, n, :] over the partition `which`
+ * (0 = qpart, 1 = kvpart), accumulated in fp32. X is [B, H, N, d] of the plan's dtype, Xbar fp32
+ * [B, H, nblk, d]. */
+int bsa_pool(const bsa_plan* plan, int32_t which, const void* X, float* Xbar, void* stream);
+
+/* Step 2. L[b, h, I, J] = sigma_h <Qbar_I, Kbar_J>, then
+ *   norm = BSA_NORM_ROW : S = softmax over J of each row;
+ *   norm = BSA_NORM_HEAD: S[I, J] = |I| exp(L[I, J]) / sum_{I', J'} |I'| exp(L[I', J']) per head.
+ * Qbar [B, H, nq, d], Kbar [B, H, nkv, d], S [B, H, nq, nkv], all fp32. */
+int bsa_score(const bsa_plan* plan, const float* Qbar, const float* Kbar, int32_t norm, float* S,
+              void* stream);
+
+/* Step 2'. Exact block masses of one dense step (LoSA abstract):
+ *   M[b, h, I, J] = (1/|I|) sum_{i in I} sum_{j in J} softmax_j(sigma_h q_i . k_j),
+ * the softmax taken over all N keys. Q, K [B, H, N, d] of the plan's dtype (bf16 only, d = 128);
+ * M fp32 [B, H, nq, nkv]. ws must hold the ws_calib bytes of bsa_plan_info. Rows of M sum to 1. */
+int bsa_calibrate_mass(const bsa_plan* plan, const void* Q, const void* K, float* M, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Step 3. Selection from S (scores from bsa_score, or masses from bsa_calibrate_mass), written
+ * as CSR: row_ptr [B*H*nq + 1], col_idx with capacity col_cap >= B*H*nq*nkv entries (the number
+ * used is row_ptr[B*H*nq], left on the device; nothing is synchronised). counts (nullable,
+ * [B*H*nq]) receives each row's final count; head_k (nullable, [B*H]) receives the per-head
+ * minimum used (0 when min_k_mode is NONE). ws must hold the ws_select bytes of bsa_plan_info.
+ * With BSA_POOL_HEAD a query block may receive no block at all (an empty row, as the VMoBA
+ * referee report points out); attention then returns O = 0 and LSE = -inf for its queries. */
+int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* params,
+               int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
+               int32_t* head_k, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 4. For every query i of block I: O_i = sum_j softmax_j(sigma_h q_i . k_j) v_j over the
+ * tokens j of the kv blocks listed in CSR row I, and lse_i = log sum_j exp(sigma_h q_i . k_j).
+ * Q, K, V, O [B, H, N, d] of the plan's dtype; lse fp32 [B, H, N] (nullable). bf16: products on
+ * bf16 matrix cores with fp32 accumulation and fp32 online softmax; P is rounded to bf16 before
+ * the PV product. The CSR must come from bsa_select for this plan (or be equivalent: indices
+ * in [0, nkv), no duplicates within a row). */
+int bsa_attn_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
+                 const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse,
+                 void* stream);
+
+/* Gradient of step 4 with the selection held fixed (a hard gate): given O and lse from
+ * bsa_attn_fwd and the upstream gradient dO, writes dQ, dK, dV ([B, H, N, d], plan dtype):
+ *   D_i = dO_i . O_i; P_ij = exp(sigma_h q_i . k_j - lse_i) on selected pairs;
+ *   dV = P^T dO; dS = P * (dO V^T - D); dQ = sigma_h dS K; dK = sigma_h dS^T Q.
+ * Tokens no selected pair touches get zero gradient. bf16, d = 128 only. ws must hold the
+ * ws_bwd bytes of bsa_plan_info. No atomics: results are deterministic. */
+int bsa_attn_bwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* lse, const int32_t* row_ptr,
+                 const int32_t* col_idx, void* dQ, void* dK, void* dV, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/* Thread-local description of the last error on this thread ("" if none). */
+const char* bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */
