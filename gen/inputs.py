@@ -40,10 +40,8 @@ def _streams(cid: int) -> dict:
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (nearest, ties to even) and return the raw 16-bit words."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -91,11 +89,9 @@ def _smooth_field(rng: np.random.Generator, grid, d: int) -> np.ndarray:
     taps = _gauss_taps()
     for axis in range(3):
         z = _smooth_axis(z, axis, taps)
-    f = z.numpy()
-    std = f.reshape(-1, d).astype(np.float64).std(axis=0)
-    f = (f / std.astype(np.float32)).astype(np.float32)
-    noise = rng.standard_normal((T, Hg, Wg, d), dtype=np.float32)
-    return f + np.float32(0.5) * noise
+    std = z.reshape(-1, d).to(torch.float64).std(dim=0, unbiased=False).to(torch.float32)
+    noise = torch.from_numpy(rng.standard_normal((T, Hg, Wg, d), dtype=np.float32))
+    return (z / std).add_(noise, alpha=0.5).numpy()
 
 
 def _rope_tables(grid, d: int):
@@ -123,12 +119,11 @@ def _rope_tables(grid, d: int):
 
 def _apply_rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
     """x: (N, d) fp32; rotates adjacent pairs (2k, 2k+1)."""
-    x0 = x[:, 0::2]
-    x1 = x[:, 1::2]
-    out = np.empty_like(x)
-    out[:, 0::2] = x0 * cos - x1 * sin
-    out[:, 1::2] = x0 * sin + x1 * cos
-    return out
+    xt = torch.from_numpy(np.ascontiguousarray(x)).view(x.shape[0], -1, 2)
+    c, s = torch.from_numpy(cos), torch.from_numpy(sin)
+    x0, x1 = xt[..., 0], xt[..., 1]
+    out = torch.stack((x0 * c - x1 * s, x0 * s + x1 * c), dim=-1)
+    return out.reshape(x.shape).numpy()
 
 
 # ---------------------------------------------------------------------------------------------

@@ -188,16 +188,22 @@ def head_min_k(counts: Sequence[int], qsizes: Sequence[int], nkv: int) -> int:
     return min(-(-num // den), int(nkv))
 
 
-def select_hybrid(S: np.ndarray, p: float, qsizes) -> Tuple[List[np.ndarray], np.ndarray]:
+def select_hybrid(S: np.ndarray, p: float, qsizes,
+                  fixed_k: Optional[int] = None) -> Tuple[List[np.ndarray], np.ndarray]:
     """[SCOPE] top-p, then rows whose retained count is below the head's k are extended with the
-    next blocks of the same (score desc, index asc) order up to k. Returns (rows, k per (b, h))."""
+    next blocks of the same (score desc, index asc) order up to k. k is the head's weighted mean
+    count (head_min_k), or, for the fixed top-k minimum that SCOPE builds on, min(fixed_k, nkv)
+    for every head. Returns (rows, k per (b, h))."""
     B, H, nq, nkv = S.shape
     rows: List[np.ndarray] = []
     head_k = np.zeros(B * H, np.int64)
     for b in range(B):
         for h in range(H):
             base = [select_topp(S[b, h, i], p) for i in range(nq)]
-            k = head_min_k([len(r) for r in base], qsizes, nkv)
+            if fixed_k is None:
+                k = head_min_k([len(r) for r in base], qsizes, nkv)
+            else:
+                k = min(int(fixed_k), nkv)
             head_k[b * H + h] = k
             for i in range(nq):
                 f = max(len(base[i]), k)

@@ -12,7 +12,8 @@ def test_bf16_rounding_matches_torch():
     x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
                         np.array([1.0, -2.5, 1e-30, 65504.0, 3.0e38], np.float32)])
     ours = f32_to_bf16_bits(x)
-    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    u = x.view(np.uint32).astype(np.uint64)
+    ref = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)  # nearest, ties to even
     np.testing.assert_array_equal(ours, ref)
     np.testing.assert_array_equal(bf16_bits_to_f32(ours),
                                   torch.from_numpy(x).to(torch.bfloat16).float().numpy())

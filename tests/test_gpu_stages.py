@@ -1,0 +1,217 @@
+"""GPU parity of the pooling, scoring and selection stages against the oracle.
+
+Tolerances: pooled means and scores within 1e-5 absolute (fp32 accumulation of bf16 inputs versus
+fp64); selections bit-exact, except near-ties whose cumulative score lies within 1e-5 of p (the
+tie-tolerant checker in helpers.py). Selection inputs are fp32 score tensors given identically to
+both sides, so the GPU's exact fixed-point sums and the oracle's fp64 cumulative sums agree up to
+fp64 rounding."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+from gen import CONFIGS, make_inputs
+from helpers import check_csr_rows, dev_to_f64, log, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(w, head_scale=None):
+    from block_sparse_attention_bsa_amd.layer import BlockSparseAttention
+    return BlockSparseAttention(w.B, w.H, w.d, w.grid, w.qpart, w.kvpart, dtype=w.dtype,
+                                head_scale=head_scale)
+
+
+# ----------------------------------------------------------------------------------- pooling
+
+@pytest.mark.parametrize("name,w", [
+    ("c1", CONFIGS[1]),
+    ("c2-small", replace(CONFIGS[2], grid=(6, 9, 20), H=2)),
+    ("c5-1d", replace(CONFIGS[5], grid=(6, 9, 20), H=2, kvpart=("tile", (3, 9, 20)))),
+    ("c2-full", CONFIGS[2]),
+])
+def test_pool_parity(name, w):
+    import torch
+    log(f"pool {name}")
+    x = make_inputs(w)
+    layer = _layer(w, x["head_scale"])
+    layer.pool(to_dev(x["q"]), to_dev(x["k"]))
+    torch.cuda.synchronize()
+    for which, X, part, got in ((0, x["q"], w.qpart, layer.qbar), (1, x["k"], w.kvpart,
+                                                                   layer.kbar)):
+        ref = oracle.pool(to_f64(X), oracle.partition(w.grid, part))
+        err = np.abs(dev_to_f64(got) - ref).max()
+        log(f"  which={which} max-abs {err:.2e}")
+        assert err <= 1e-5
+
+
+# ----------------------------------------------------------------------------------- scoring
+
+@pytest.mark.parametrize("mode", ["row", "head"])
+def test_score_parity(mode):
+    import torch
+    w = replace(CONFIGS[5], grid=(9, 12, 24), H=3, kvpart=("tile", (3, 4, 8)))
+    x = make_inputs(w)
+    qb, kb = oracle.partition(w.grid, w.qpart), oracle.partition(w.grid, w.kvpart)
+    # block means given identically to both sides (fp32)
+    Qb = oracle.pool(to_f64(x["q"]), qb).astype(np.float32)
+    Kb = oracle.pool(to_f64(x["k"]), kb).astype(np.float32)
+    hs = x["head_scale"]
+    layer = _layer(w, hs)
+    layer.qbar.copy_(torch.from_numpy(Qb))
+    layer.kbar.copy_(torch.from_numpy(Kb))
+    S = layer.score(0 if mode == "row" else 1)
+    torch.cuda.synchronize()
+    if mode == "row":
+        ref = oracle.score_row(Qb.astype(np.float64), Kb.astype(np.float64), hs.astype(np.float64))
+    else:
+        ref = oracle.score_head(Qb.astype(np.float64), Kb.astype(np.float64),
+                                hs.astype(np.float64), oracle.block_sizes(qb))
+    err = np.abs(dev_to_f64(S) - ref).max()
+    rel = (np.abs(dev_to_f64(S) - ref) / np.maximum(ref, 1e-30)).max()
+    log(f"score {mode}: max-abs {err:.2e} max-rel {rel:.2e}")
+    assert err <= 1e-5
+    assert rel <= 1e-4
+
+
+# ----------------------------------------------------------------------------------- selection
+
+def _synthetic_rows(shape, rng):
+    """fp32 score rows: Dirichlet rows of varied concentration, uniform rows (exact ties),
+    rows with repeated values, rows with zeros."""
+    B, H, nq, nkv = shape
+    S = np.empty(shape, np.float64)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nq):
+                kind = rng.integers(0, 6)
+                if kind == 0:
+                    row = np.full(nkv, 1.0 / nkv)
+                elif kind == 1:
+                    vals = rng.dirichlet(np.ones(4))
+                    row = vals[rng.integers(0, 4, size=nkv)]
+                    row /= row.sum()
+                elif kind == 2:
+                    row = rng.dirichlet(np.full(nkv, 0.5))
+                    row[rng.random(nkv) < 0.3] = 0.0
+                    row /= row.sum()
+                else:
+                    row = rng.dirichlet(np.full(nkv, [0.05, 0.3, 1.0, 5.0][kind - 2]))
+                S[b, h, i] = row
+    return S.astype(np.float32)
+
+
+def _gpu_select(layer, S32, p, pool=0, min_k_mode=0, fixed_k=0):
+    import torch
+    scores = torch.from_numpy(S32).cuda()
+    layer.select(p, pool, min_k_mode, fixed_k, scores=scores)
+    torch.cuda.synchronize()
+    rp, ci = layer.csr_host()
+    return oracle.csr_rows(rp, ci), layer.counts.cpu().numpy(), layer.head_k.cpu().numpy()
+
+
+@pytest.mark.parametrize("p", [0.9, 0.5, 0.99, 0.01, 1.0])
+def test_select_row_parity(p):
+    w = replace(CONFIGS[2], H=2)
+    layer = _layer(w)
+    rng = np.random.default_rng(int(p * 1000))
+    S32 = _synthetic_rows((1, 2, layer.plan.nq, layer.plan.nkv), rng)
+    rows, counts, _ = _gpu_select(layer, S32, p)
+    S64 = S32.astype(np.float64)
+    ref = oracle.select_row(S64, p)
+    flat = S64.reshape(-1, S64.shape[-1])
+    exact, tol, bad = check_csr_rows(rows, ref, flat, p)
+    log(f"select row p={p}: exact {exact} tolerated {tol} bad {len(bad)}")
+    assert not bad
+    assert exact >= len(ref) - 2
+    assert counts.tolist() == [len(r) for r in rows]
+
+
+@pytest.mark.parametrize("mode", ["weighted", "fixed"])
+def test_select_hybrid_parity(mode):
+    w = replace(CONFIGS[4], grid=(9, 13, 24), H=3)
+    layer = _layer(w)
+    qsizes = oracle.block_sizes(oracle.partition(w.grid, w.qpart))
+    rng = np.random.default_rng(11)
+    S32 = _synthetic_rows((1, 3, layer.plan.nq, layer.plan.nkv), rng)
+    S64 = S32.astype(np.float64)
+    if mode == "weighted":
+        rows, counts, head_k = _gpu_select(layer, S32, 0.8, min_k_mode=2)
+        ref, ref_k = oracle.select_hybrid(S64, 0.8, qsizes)
+    else:
+        rows, counts, head_k = _gpu_select(layer, S32, 0.8, min_k_mode=1, fixed_k=9)
+        ref, ref_k = oracle.select_hybrid(S64, 0.8, qsizes, fixed_k=9)
+    log(f"hybrid {mode}: head_k gpu {head_k.tolist()} oracle {ref_k.tolist()}")
+    assert head_k.tolist() == ref_k.tolist()
+    same = sum(np.array_equal(a, b) for a, b in zip(rows, ref))
+    log(f"  rows exact {same}/{len(ref)}")
+    assert same == len(ref)
+
+
+@pytest.mark.parametrize("tau", [0.25, 0.05, 0.9])
+def test_select_head_parity(tau):
+    w = replace(CONFIGS[5], H=2)  # 720 query blocks x 60 kv blocks per head
+    layer = _layer(w)
+    nq, nkv = layer.plan.nq, layer.plan.nkv
+    rng = np.random.default_rng(int(tau * 100))
+    W = np.empty((1, 2, nq, nkv))
+    W[0, 0] = rng.dirichlet(np.full(nq * nkv, 0.2)).reshape(nq, nkv)
+    base = rng.dirichlet(np.ones(50))
+    W[0, 1] = base[rng.integers(0, 50, size=(nq, nkv))]  # many exact ties
+    W[0, 1] /= W[0, 1].sum()
+    W32 = W.astype(np.float32)
+    rows, counts, _ = _gpu_select(layer, W32, tau, pool=1)
+    ref = oracle.select_head(W32.astype(np.float64), tau)
+    same = sum(np.array_equal(a, b) for a, b in zip(rows, ref))
+    empty = sum(len(r) == 0 for r in rows)
+    log(f"head tau={tau}: rows exact {same}/{len(ref)}, empty rows {empty}")
+    assert same == len(ref)
+    assert counts.tolist() == [len(r) for r in rows]
+
+
+def test_select_deterministic_and_p1_full():
+    w = replace(CONFIGS[2], H=2)
+    layer = _layer(w)
+    rng = np.random.default_rng(5)
+    S32 = _synthetic_rows((1, 2, layer.plan.nq, layer.plan.nkv), rng)
+    a, _, _ = _gpu_select(layer, S32, 0.9)
+    b, _, _ = _gpu_select(layer, S32, 0.9)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    full, _, _ = _gpu_select(layer, S32, 1.0)
+    assert all(len(r) == layer.plan.nkv for r in full)
+
+
+def test_select_validation_errors():
+    import torch
+    import block_sparse_attention_bsa_amd as bsa
+    w = replace(CONFIGS[2], grid=(4, 8, 8), H=1)
+    layer = _layer(w)
+    S = torch.zeros(layer.S.shape, device="cuda")
+    for kw in (dict(p=0.0), dict(p=1.5), dict(p=float("nan")), dict(p=0.9, pool=7),
+               dict(p=0.9, min_k_mode=5), dict(p=0.9, min_k_mode=1, fixed_k=-1)):
+        args = dict(p=0.9, pool=0, min_k_mode=0, fixed_k=0)
+        args.update(kw)
+        with pytest.raises(bsa.BsaError) as e:
+            bsa.bsa_select(layer.plan, S, args["p"], args["pool"], args["min_k_mode"],
+                           args["fixed_k"], layer.row_ptr, layer.col_idx, layer.col_cap,
+                           None, None, layer.ws_select, layer.plan.ws_select)
+        assert e.value.code == bsa.BSA_EINVAL
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_select(layer.plan, S, 0.9, 1, 2, 0, layer.row_ptr, layer.col_idx, layer.col_cap,
+                       None, None, layer.ws_select, layer.plan.ws_select)
+    assert e.value.code == bsa.BSA_EUNSUPPORTED
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_select(layer.plan, S, 0.9, 0, 0, 0, layer.row_ptr, layer.col_idx,
+                       layer.col_cap - 1, None, None, layer.ws_select, layer.plan.ws_select)
+    assert e.value.code == bsa.BSA_ECAPACITY
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_select(layer.plan, S, 0.9, 0, 0, 0, layer.row_ptr, layer.col_idx, layer.col_cap,
+                       None, None, layer.ws_select, layer.plan.ws_select - 1)
+    assert e.value.code == bsa.BSA_ECAPACITY
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_pool(layer.plan, 2, layer.qbar, layer.qbar)
+    assert e.value.code == bsa.BSA_EINVAL
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_score(layer.plan, layer.qbar, layer.kbar, 3, layer.S)
+    assert e.value.code == bsa.BSA_EINVAL

@@ -147,3 +147,13 @@ def test_csr_roundtrip():
     rp, ci = oracle.to_csr(rows)
     assert rp.tolist() == [0, 2, 2, 5] and ci.tolist() == [0, 3, 1, 2, 5]
     assert [r.tolist() for r in oracle.csr_rows(rp, ci)] == [[0, 3], [], [1, 2, 5]]
+
+
+def test_fixed_k_minimum():
+    # fixed minimum k: every row keeps max(top-p count, k) blocks of the same ranking
+    S = np.asarray([[[[0.7, 0.2, 0.05, 0.05], [0.3, 0.3, 0.2, 0.2]]]])
+    rows, head_k = oracle.select_hybrid(S, 0.6, [8, 8], fixed_k=2)
+    assert head_k.tolist() == [2]
+    assert [r.tolist() for r in rows] == [[0, 1], [0, 1]]
+    rows, _ = oracle.select_hybrid(S, 0.6, [8, 8], fixed_k=9)
+    assert all(r.tolist() == [0, 1, 2, 3] for r in rows)
