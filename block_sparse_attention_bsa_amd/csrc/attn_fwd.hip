@@ -9,13 +9,15 @@
 // needed; 3D tiles clipped at the grid edge (8..128 tokens) waste at most a few percent.
 //
 // bf16, d = 128 (MFMA path). One workgroup = 4 wavefronts = 128 query rows of one query block.
-// Per iteration it gathers a 64-token KV tile (two chunks) into LDS: K row-major with a 16-byte
-// row pad, V transposed (d-major) with an XOR swizzle of 8-byte units so that the MFMA operand
-// reads are bank-conflict free. Each wavefront computes S^T = K Q^T for its 32 queries with
+// Per iteration it gathers a 64-token KV tile (two chunks) into one of two LDS stages: K
+// row-major with a 16-byte row pad, V transposed (d-major, kv permuted within groups of 16,
+// 16-byte units XOR-swizzled by row) so that each MFMA operand is one conflict-free 16-byte read. Each wavefront computes S^T = K Q^T for its 32 queries with
 // v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B operand), so that each lane holds 16
 // scores of a single query: the row max needs one cross-half exchange, the row sum none. P^T is
-// converted to bf16 in registers and used directly as the B operand of O^T += V^T P^T. Token ids
-// of tile t+2 and the K/V data of tile t+1 are in flight while tile t is computed.
+// converted to bf16 in registers and used directly as the B operand of O^T += V^T P^T. While tile t
+// is computed from one LDS stage, tile t+1 is written to the other from registers, the K/V data
+// of tile t+2 and the token ids of tile t+3 are in flight; one barrier per tile. The running max
+// is raised lazily (only when it grows by more than 2^8), so the O rescale is rare.
 #include "bsa_internal.h"
 #include "device_common.h"
 
@@ -71,11 +73,24 @@ __device__ __forceinline__ Chunk take_chunk(Cursor& c, const int32_t* __restrict
 
 // ------------------------------------------------------------------------------- MFMA path
 
-constexpr int kKStride = 272;   // bytes per K row in LDS: 256 + 16 pad
-constexpr int kTileKV = 64;     // kv tokens per iteration (two chunks)
+constexpr int kTileKV = 64;                    // kv tokens per iteration (two chunks)
+constexpr int kRowBytes = 256;                 // one token row of d = 128 bf16
+constexpr int kTileBytes = kTileKV * kRowBytes;
+constexpr int kStage = 2 * kTileBytes;         // K tile then V tile
+// Lazy rescaling: the running max used for exp2 is only raised when a tile's max exceeds it by
+// more than this (log2 units), so P stays <= 2^8 and the O rescale is rare.
+constexpr float kRescaleSlack = 8.f;
 
-__device__ __forceinline__ int vt_offset(int d, int unit) {  // byte offset of a 4-kv unit
-  return d * 128 + ((unit ^ ((d >> 1) & 15)) << 3);
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// K and V tiles are row-major in LDS (one 256-byte row per kv token); the 16-byte units of a row
+// are XOR-swizzled by the row index so that the MFMA operand reads hit distinct banks.
+__device__ __forceinline__ int swz(int row, int unit) { return (unit ^ (row & 15)) << 4; }
+
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt left unconstrained
 }
 
 __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
@@ -87,8 +102,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
     const float* __restrict__ scale, int H, int N, int nq, uint16_t* __restrict__ O,
     float* __restrict__ lse) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(16))) char k_lds[kTileKV * kKStride];
-  __shared__ __attribute__((aligned(16))) char vt_lds[D * kTileKV * 2];
+  __shared__ __attribute__((aligned(1024))) char lds_a[kStage];
+  __shared__ __attribute__((aligned(1024))) char lds_b[kStage];
 
   const int total = n_items * (int)gridDim.y;
   const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
@@ -98,7 +113,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
   const int nrows = min(128, qstart[I + 1] - q0);
   const int64_t r = (int64_t)bh * nq + I;
   const size_t head_off = (size_t)bh * N * D;
-  const float c2 = scale[bh % H] * kLog2e;
+  const float c2 = scale[bh % H] * kLog2e;  // sigma_h > 0 (checked at plan creation)
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
@@ -124,8 +139,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Loader role: 4 consecutive kv rows (4*quad ..) x 8 d values (8*dseg ..).
-  const int dseg = t & 15, quad = t >> 4, half = quad >> 3, r0 = (4 * quad) & 31;
+  // Loader role: wave w fills tile rows 16w + 4i + lane/16 (i = 0..3), 16-byte unit lane%16 of
+  // the swizzled row, for K and for V, with direct global->LDS loads (no staging registers).
+  // Rows past a chunk's end repeat the chunk's first token: their scores are masked and their
+  // probabilities are exactly 0, so any finite row will do.
+  const int lrow0 = 16 * wave + (lane >> 4);
+  const int lchunk = wave >> 1;
 
   Cursor cur;
   cur.slot = row_ptr[r];
@@ -134,127 +153,149 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
   cursor_load(cur, col_idx, kvstart);
 
   auto tile_ids = [&](Chunk a, Chunk b, int* ids) {
-    const Chunk c = half ? b : a;
+    const Chunk c = lchunk ? b : a;
+    const Chunk c0 = a;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) ids[u] = (r0 + u < c.nv) ? kvperm[c.pos + r0 + u] : -1;
+    for (int i = 0; i < 4; ++i) {
+      const int rr = (lrow0 + 4 * i) & 31;
+      const int pos = c.nv > 0 ? c.pos + (rr < c.nv ? rr : 0) : c0.pos;
+      ids[i] = kvperm[pos];
+    }
   };
-  uint4 kreg[4], vreg[4];
-  auto tile_load = [&](const int* ids) {
+  auto tile_issue = [&](const int* ids, char* st) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (ids[u] >= 0) {
-        const size_t o = head_off + (size_t)ids[u] * D + 8 * dseg;
-        kreg[u] = *reinterpret_cast<const uint4*>(K + o);
-        vreg[u] = *reinterpret_cast<const uint4*>(V + o);
-      } else {
-        kreg[u] = make_uint4(0, 0, 0, 0);
-        vreg[u] = make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int lunit = (lane & 15) ^ ((lrow0 + 4 * i) & 15);  // logical unit at this position
+      const size_t o = head_off + (size_t)ids[i] * D + 8 * lunit;
+      char* dst = st + (16 * wave + 4 * i) * kRowBytes;
+      __builtin_amdgcn_global_load_lds(K + o, dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(V + o, dst + kTileBytes, 16, 0, 0);
     }
   };
 
+  // Pipeline: LDS stage buf holds tile t; tile t+1 is being loaded into the other stage; ids
+  // hold the token ids of tile t+2.
   Chunk a0 = take_chunk(cur, col_idx, kvstart), b0 = take_chunk(cur, col_idx, kvstart);
   int ids[4];
-  tile_ids(a0, b0, ids);
-  tile_load(ids);
+  if (a0.nv > 0) {
+    tile_ids(a0, b0, ids);
+    tile_issue(ids, lds_a);
+  }
   Chunk a1 = take_chunk(cur, col_idx, kvstart), b1 = take_chunk(cur, col_idx, kvstart);
-  tile_ids(a1, b1, ids);
+  if (a1.nv > 0) tile_ids(a1, b1, ids);
+  wait_vmem_all();
+  __syncthreads();
 
-  while (a0.nv > 0) {
-    __syncthreads();
-    // Stage tile t: K row-major, V transposed.
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *reinterpret_cast<uint4*>(k_lds + (4 * quad + u) * kKStride + 16 * dseg) = kreg[u];
-    {
-      const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-      const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-      const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int d = 8 * dseg + i;
-        uint2 pk;
-        if (i & 1) {
-          pk.x = (w0[i >> 1] >> 16) | (w1[i >> 1] & 0xffff0000u);
-          pk.y = (w2[i >> 1] >> 16) | (w3[i >> 1] & 0xffff0000u);
-        } else {
-          pk.x = (w0[i >> 1] & 0xffffu) | (w1[i >> 1] << 16);
-          pk.y = (w2[i >> 1] & 0xffffu) | (w3[i >> 1] << 16);
-        }
-        *reinterpret_cast<uint2*>(vt_lds + vt_offset(d, quad)) = pk;
-      }
-    }
-    __syncthreads();
+  // Per-lane read offsets (bytes within a stage).
+  const int krow0 = l32;                       // K row for M block mb: 32*mb + l32
+  // V transposed reads: row 16*kc + 8*sh + 4*hl + (lane%16)/4, column 32*dm + 16*((lane/16)&1)
+  // + 4*(lane&3): 16-byte unit 4*dm + 2*((lane/16)&1) + ((lane&3)>>1), 8-byte half (lane&1).
+  const int vrow_l = 4 * hl + ((lane & 15) >> 2);
+  const int vunit_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vhalf_l = 8 * (lane & 1);
 
-    // Tile t+1 data and tile t+2 ids in flight during the compute of tile t.
-    const int nvA = a0.nv, nvB = b0.nv;
-    tile_load(ids);
-    Chunk a2 = take_chunk(cur, col_idx, kvstart), b2 = take_chunk(cur, col_idx, kvstart);
-    tile_ids(a2, b2, ids);
+  // One tile: compute from stage `st` while the next tile streams into `nx`. The two stages
+  // are distinct arrays so that the compiler can tell the streamed writes never alias the reads.
+  auto step = [&](const char* st, char* nx) {
+    if (a1.nv > 0) tile_issue(ids, nx);
+    const Chunk a2 = take_chunk(cur, col_idx, kvstart), b2 = take_chunk(cur, col_idx, kvstart);
+    if (a2.nv > 0) tile_ids(a2, b2, ids);
 
-    // S^T for this wave's 32 queries: two 32-kv M blocks.
+    // S^T for this wave's 32 queries: two 32-kv M blocks (raw, unscaled scores).
     f32x16_t sacc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
+      const int row = 32 * mb + krow0;
+      const char* kp = st + row * kRowBytes;
+      bf16x8_t kf[8];
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        kf[kc] = *reinterpret_cast<const bf16x8_t*>(kp + swz(row, 2 * kc + hl));
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[mb][e] = 0.f;
-      const char* kp = k_lds + (32 * mb + l32) * kKStride + 16 * hl;
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kp + 32 * kc);
-        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kc], sacc[mb], 0, 0, 0);
+      for (int kc = 0; kc < 8; ++kc)
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], sacc[mb], 0, 0, 0);
+    }
+    if (a0.nv < 32 || b0.nv < 32) {  // partial chunk(s): mask padded kv rows
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int nv = mb ? b0.nv : a0.nv;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (8 * (e >> 2) + 4 * hl + (e & 3) >= nv) sacc[mb][e] = -INFINITY;
       }
     }
-    // Online softmax (base 2, scale folded in).
-    float mx = -INFINITY;
+    float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[1][0], sacc[1][1]);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int nv = mb ? nvB : nvA;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int i = 8 * (e >> 2) + 4 * hl + (e & 3);
-        const float s = i < nv ? sacc[mb][e] * c2 : -INFINITY;
-        sacc[mb][e] = s;
-        mx = fmaxf(mx, s);
-      }
+    for (int e = 2; e < 16; e += 2) {
+      mx0 = fmaxf(mx0, fmaxf(sacc[0][e], sacc[0][e + 1]));
+      mx1 = fmaxf(mx1, fmaxf(sacc[1][e], sacc[1][e + 1]));
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float lsum = 0.f;
+    float mx = fmaxf(mx0, mx1);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dm][e] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = -m_run;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
     bf16x8_t pb[4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sacc[mb][e] - m_new);
-        lsum += p;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nm));
+        ls[e & 3] += p;
         pb[2 * mb + (e >> 3)][e & 7] = (__bf16)p;
       }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int dm = 0; dm < 4; ++dm)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[dm][e] *= alpha;
-    // O^T += V^T P^T
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // O^T += V^T P^T; each V^T fragment is two transposing 8-byte LDS reads.
+    const char* vt = st + kTileBytes;
 #pragma unroll
     for (int dm = 0; dm < 4; ++dm) {
-      const int d = 32 * dm + l32;
+      bf16x8_t vf[4];
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vt_lds + vt_offset(d, 4 * kc + hl));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vt_lds + vt_offset(d, 4 * kc + 2 + hl));
-        const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                           pb[kc], oacc[dm], 0, 0, 0);
+        v4i16_t lo, hi;
+        {
+          const int row = 16 * kc + vrow_l;
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)((lds_char_t*)vt + row * kRowBytes + swz(row, 4 * dm + vunit_l) +
+                             vhalf_l));
+        }
+        {
+          const int row = 16 * kc + 8 + vrow_l;
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)((lds_char_t*)vt + row * kRowBytes + swz(row, 4 * dm + vunit_l) +
+                             vhalf_l));
+        }
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        vf[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
       }
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc], pb[kc], oacc[dm], 0, 0, 0);
     }
+    wait_vmem_all();
+    __syncthreads();
     a0 = a1;
     b0 = b1;
     a1 = a2;
     b1 = b2;
+    };
+  while (true) {
+    if (a0.nv <= 0) break;
+    step(lds_a, lds_b);
+    if (a0.nv <= 0) break;
+    step(lds_b, lds_a);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

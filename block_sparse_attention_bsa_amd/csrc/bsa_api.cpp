@@ -185,8 +185,8 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
     return fail(BSA_EUNSUPPORTED, "bsa_plan_create: B*H too large");
   if (head_scale)
     for (int h = 0; h < pr.H; ++h)
-      if (!std::isfinite(head_scale[h]))
-        return fail(BSA_EINVAL, "bsa_plan_create: head_scale[%d] is not finite", h);
+      if (!std::isfinite(head_scale[h]) || !(head_scale[h] > 0.f))
+        return fail(BSA_EINVAL, "bsa_plan_create: head_scale[%d] must be finite and > 0", h);
 
   bsa_plan* p = new bsa_plan();
   p->prob = pr;

@@ -115,7 +115,8 @@ int bsa_partition_build(int32_t T, int32_t Hg, int32_t Wg, const bsa_partition* 
                         int32_t* perm, int32_t* blk_start, int32_t cap_blocks, int32_t* nblk);
 
 /* Validate `prob`, build both partitions and upload them to the current device. head_scale is
- * a host array of H softmax scales sigma_h (copied), or NULL for 1/sqrt(d). The plan is
+ * a host array of H softmax scales sigma_h (copied; each finite and > 0), or NULL for
+ * 1/sqrt(d). The plan is
  * immutable afterwards and may be shared by calls on several streams. */
 int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan** out);
 int bsa_plan_destroy(bsa_plan* plan);

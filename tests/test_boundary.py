@@ -76,9 +76,10 @@ def test_bad_partitions_rejected(L):
     pr = _problem()
     pr.kvpart = bsa.Partition(5, 1, 1, 1, 1)
     assert L.bsa_plan_create(ctypes.byref(pr), None, ctypes.byref(h)) == bsa.BSA_EINVAL
-    hs = np.array([1.0, np.nan], np.float32)
-    assert L.bsa_plan_create(ctypes.byref(_problem()), hs.ctypes.data,
-                             ctypes.byref(h)) == bsa.BSA_EINVAL
+    for bad in (np.nan, 0.0, -0.5, np.inf):
+        hs = np.array([1.0, bad], np.float32)
+        assert L.bsa_plan_create(ctypes.byref(_problem()), hs.ctypes.data,
+                                 ctypes.byref(h)) == bsa.BSA_EINVAL
 
 
 def test_null_arguments_rejected(L):
