@@ -1,23 +1,29 @@
-// Sparse attention forward (step 4): every query of block I attends only to the tokens of the kv
-// blocks listed in CSR row I (pith.science review of VMoBA, Figure 2 caption: attention over the
-// selected blocks only; "What carries the argument": only the highest-scoring blocks contribute
-// their key-value pairs). Online softmax in the FlashAttention style.
+// Sparse attention forward (step 4) and the two dense passes of the exact block-mass calibration
+// (step 2'), on bf16 matrix cores for d = 128, plus a plain VALU path for fp32 and d = 64.
 //
-// KV stream. The selected blocks of a row are walked as a sequence of 32-token chunks: block J
-// contributes ceil(|J| / 32) chunks, the last one possibly partial. Chunks are padded per block,
-// not concatenated, so each chunk's token ids are perm[kvstart[J] + 32 * sub + r] and no search is
-// needed; 3D tiles clipped at the grid edge (8..128 tokens) waste at most a few percent.
+// Forward: every query of block I attends only to the tokens of the kv blocks listed in CSR row I
+// (pith.science review of VMoBA, Figure 2 caption: attention over the selected blocks only; "What
+// carries the argument": only the highest-scoring blocks contribute their key-value pairs), with
+// a FlashAttention-style online softmax. Calibration (LoSA abstract, scholarbro author page):
+// exact block attention masses from one dense step, computed as a dense log-sum-exp pass over all
+// N keys followed by a dense pass that sums exp(sigma q.k - lse) per (query block, kv block).
 //
-// bf16, d = 128 (MFMA path). One workgroup = 4 wavefronts = 128 query rows of one query block.
-// Per iteration it gathers a 64-token KV tile (two chunks) into one of two LDS stages: K
-// row-major with a 16-byte row pad, V transposed (d-major, kv permuted within groups of 16,
-// 16-byte units XOR-swizzled by row) so that each MFMA operand is one conflict-free 16-byte read. Each wavefront computes S^T = K Q^T for its 32 queries with
-// v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B operand), so that each lane holds 16
-// scores of a single query: the row max needs one cross-half exchange, the row sum none. P^T is
-// converted to bf16 in registers and used directly as the B operand of O^T += V^T P^T. While tile t
-// is computed from one LDS stage, tile t+1 is written to the other from registers, the K/V data
-// of tile t+2 and the token ids of tile t+3 are in flight; one barrier per tile. The running max
-// is raised lazily (only when it grows by more than 2^8), so the O rescale is rare.
+// KV stream. The kv blocks of a row (the CSR list, or all blocks for the dense passes) are walked
+// as a sequence of 32-token chunks: block J contributes ceil(|J| / 32) chunks, the last one
+// possibly partial. Chunks are padded per block, not concatenated, so a chunk's token ids are
+// perm[kvstart[J] + 32 * sub + r] and no search is needed; 3D tiles clipped at the grid edge
+// (8..128 tokens) waste at most a few percent.
+//
+// MFMA path. One workgroup = 4 wavefronts = 128 query rows of one query block. Per iteration a
+// 64-token tile (two chunks) of K (and V for the forward pass) is copied global -> LDS with direct
+// 16-byte loads (no staging registers) into one of two stages while the other stage is
+// computed; rows are 256 bytes with the 16-byte units XOR-swizzled by row, so that the MFMA
+// operand reads are conflict free. Each wavefront computes S^T = K Q^T for its 32 queries with
+// v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B operand), so each lane holds 16 scores
+// of a single query: the row max needs one cross-half exchange and the row sum none. P^T is
+// converted to bf16 in registers and is directly the B operand of O^T += V^T P^T, whose A operand
+// comes from two transposing 8-byte LDS reads (ds_read_b64_tr_b16) of the row-major V tile. The
+// running max is raised lazily (only when it grows by more than 2^8), so the O rescale is rare.
 #include "bsa_internal.h"
 #include "device_common.h"
 
@@ -26,57 +32,60 @@ namespace {
 // ------------------------------------------------------------------------------- KV cursor
 
 struct Cursor {
-  int slot, end, sub, base, size;  // position in col_idx, block token base and size
+  int slot, end, sub, base, size, J;  // position in the block list, current block and its tokens
 };
 
+template <bool kDense>
 __device__ __forceinline__ void cursor_load(Cursor& c, const int32_t* __restrict__ col_idx,
                                             const int32_t* __restrict__ kvstart) {
   if (c.slot < c.end) {
-    const int J = col_idx[c.slot];
-    c.base = kvstart[J];
-    c.size = kvstart[J + 1] - c.base;
+    c.J = kDense ? c.slot : col_idx[c.slot];
+    c.base = kvstart[c.J];
+    c.size = kvstart[c.J + 1] - c.base;
   } else {
+    c.J = 0;
     c.base = 0;
     c.size = 0;
   }
 }
 
-__device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* __restrict__ col_idx,
-                                            const int32_t* __restrict__ kvstart) {
-  if (c.slot >= c.end) return;
-  ++c.sub;
-  if (32 * c.sub >= c.size) {
-    ++c.slot;
-    c.sub = 0;
-    cursor_load(c, col_idx, kvstart);
-  }
-}
-
-// One chunk: first token position in perm and number of valid rows (0 = past the end).
+// One chunk: first token position in perm, number of valid rows (0 = past the end), its block,
+// and whether it is the block's last chunk.
 struct Chunk {
-  int pos, nv;
+  int pos, nv, J, last;
 };
 
+template <bool kDense>
 __device__ __forceinline__ Chunk take_chunk(Cursor& c, const int32_t* __restrict__ col_idx,
                                             const int32_t* __restrict__ kvstart) {
   Chunk k;
   if (c.slot < c.end) {
     k.pos = c.base + 32 * c.sub;
     k.nv = min(32, c.size - 32 * c.sub);
+    k.J = c.J;
+    k.last = 32 * (c.sub + 1) >= c.size;
+    ++c.sub;
+    if (k.last) {
+      ++c.slot;
+      c.sub = 0;
+      cursor_load<kDense>(c, col_idx, kvstart);
+    }
   } else {
     k.pos = 0;
     k.nv = 0;
+    k.J = 0;
+    k.last = 0;
   }
-  cursor_next(c, col_idx, kvstart);
   return k;
 }
 
 // ------------------------------------------------------------------------------- MFMA path
 
+enum Mode { kFwd = 0, kLse = 1, kMass = 2 };
+
 constexpr int kTileKV = 64;                    // kv tokens per iteration (two chunks)
 constexpr int kRowBytes = 256;                 // one token row of d = 128 bf16
 constexpr int kTileBytes = kTileKV * kRowBytes;
-constexpr int kStage = 2 * kTileBytes;         // K tile then V tile
 // Lazy rescaling: the running max used for exp2 is only raised when a tile's max exceeds it by
 // more than this (log2 units), so P stays <= 2^8 and the O rescale is rare.
 constexpr float kRescaleSlack = 8.f;
@@ -93,27 +102,44 @@ __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt left unconstrained
 }
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ qperm,
-    const int32_t* __restrict__ qstart, const int32_t* __restrict__ kvperm,
-    const int32_t* __restrict__ kvstart, const int32_t* __restrict__ items, int n_items,
-    const float* __restrict__ scale, int H, int N, int nq, uint16_t* __restrict__ O,
-    float* __restrict__ lse) {
+struct MfmaArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* qperm;
+  const int32_t* qstart;
+  const int32_t* kvperm;
+  const int32_t* kvstart;
+  const int32_t* items;
+  const float* scale;
+  const float* lse_in;  // kMass: per-token log-sum-exp from the kLse pass
+  uint16_t* O;          // kFwd
+  float* lse;           // kFwd (nullable) and kLse
+  float* part;          // kMass: [bh][item][wave][nkv] per-wave block sums
+  int n_items, H, N, nq, nkv;
+};
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void attn_mfma_d128(const MfmaArgs a) {
   constexpr int D = 128;
+  constexpr bool kDense = MODE != kFwd;
+  constexpr bool kNeedV = MODE == kFwd;
+  constexpr int kStage = kNeedV ? 2 * kTileBytes : kTileBytes;
   __shared__ __attribute__((aligned(1024))) char lds_a[kStage];
   __shared__ __attribute__((aligned(1024))) char lds_b[kStage];
 
+  const int n_items = a.n_items;
   const int total = n_items * (int)gridDim.y;
   const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
   const int bh = lin / n_items, item = lin % n_items;
-  const int I = items[2 * item], off = items[2 * item + 1];
-  const int q0 = qstart[I] + off;
-  const int nrows = min(128, qstart[I + 1] - q0);
-  const int64_t r = (int64_t)bh * nq + I;
-  const size_t head_off = (size_t)bh * N * D;
-  const float c2 = scale[bh % H] * kLog2e;  // sigma_h > 0 (checked at plan creation)
+  const int I = a.items[2 * item], off = a.items[2 * item + 1];
+  const int q0 = a.qstart[I] + off;
+  const int nrows = min(128, a.qstart[I + 1] - q0);
+  const int64_t r = (int64_t)bh * a.nq + I;
+  const size_t head_off = (size_t)bh * a.N * D;
+  const float c2 = a.scale[bh % a.H] * kLog2e;  // sigma_h > 0 (checked at plan creation)
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
@@ -121,10 +147,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
   // Q fragments (B operand of S^T = K Q^T): query row 32*wave + l32, d = 16*kc + 8*hl .. +8.
   const int qrow = 32 * wave + l32;
   const bool qvalid = qrow < nrows;
-  const int qtok = qvalid ? qperm[q0 + qrow] : 0;
+  const int qtok = qvalid ? a.qperm[q0 + qrow] : 0;
   bf16x8_t qf[8];
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(Q + head_off + (size_t)qtok * D + 8 * hl);
+    const uint4* qp =
+        reinterpret_cast<const uint4*>(a.Q + head_off + (size_t)qtok * D + 8 * hl);
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       uint4 v = qvalid ? qp[2 * kc] : make_uint4(0, 0, 0, 0);
@@ -133,33 +160,38 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
   }
 
   f32x16_t oacc[4];
+  if constexpr (MODE == kFwd) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+      for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+  }
+  float m_run = -INFINITY, l_run = 0.f, lb_run = 0.f;
+  // kMass: log2-domain lse of this lane's query (+inf for padding rows, so they add nothing)
+  float nlse2 = 0.f, blk_acc = 0.f;
+  if constexpr (MODE == kMass)
+    nlse2 = qvalid ? -a.lse_in[(size_t)bh * a.N + qtok] * kLog2e : -INFINITY;
 
   // Loader role: wave w fills tile rows 16w + 4i + lane/16 (i = 0..3), 16-byte unit lane%16 of
-  // the swizzled row, for K and for V, with direct global->LDS loads (no staging registers).
+  // the swizzled row, for K (and V), with direct global->LDS loads (no staging registers).
   // Rows past a chunk's end repeat the chunk's first token: their scores are masked and their
   // probabilities are exactly 0, so any finite row will do.
   const int lrow0 = 16 * wave + (lane >> 4);
   const int lchunk = wave >> 1;
 
   Cursor cur;
-  cur.slot = row_ptr[r];
-  cur.end = row_ptr[r + 1];
+  cur.slot = kDense ? 0 : a.row_ptr[r];
+  cur.end = kDense ? a.nkv : a.row_ptr[r + 1];
   cur.sub = 0;
-  cursor_load(cur, col_idx, kvstart);
+  cursor_load<kDense>(cur, a.col_idx, a.kvstart);
 
-  auto tile_ids = [&](Chunk a, Chunk b, int* ids) {
-    const Chunk c = lchunk ? b : a;
-    const Chunk c0 = a;
+  auto tile_ids = [&](Chunk ca, Chunk cb, int* ids) {
+    const Chunk c = lchunk ? cb : ca;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = (lrow0 + 4 * i) & 31;
-      const int pos = c.nv > 0 ? c.pos + (rr < c.nv ? rr : 0) : c0.pos;
-      ids[i] = kvperm[pos];
+      const int pos = c.nv > 0 ? c.pos + (rr < c.nv ? rr : 0) : ca.pos;
+      ids[i] = a.kvperm[pos];
     }
   };
   auto tile_issue = [&](const int* ids, char* st) {
@@ -168,44 +200,44 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
       const int lunit = (lane & 15) ^ ((lrow0 + 4 * i) & 15);  // logical unit at this position
       const size_t o = head_off + (size_t)ids[i] * D + 8 * lunit;
       char* dst = st + (16 * wave + 4 * i) * kRowBytes;
-      __builtin_amdgcn_global_load_lds(K + o, dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(V + o, dst + kTileBytes, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.K + o, dst, 16, 0, 0);
+      if constexpr (kNeedV) __builtin_amdgcn_global_load_lds(a.V + o, dst + kTileBytes, 16, 0, 0);
     }
   };
 
-  // Pipeline: LDS stage buf holds tile t; tile t+1 is being loaded into the other stage; ids
-  // hold the token ids of tile t+2.
-  Chunk a0 = take_chunk(cur, col_idx, kvstart), b0 = take_chunk(cur, col_idx, kvstart);
+  // Pipeline: one stage holds tile t, tile t+1 streams into the other, ids hold tile t+2.
+  Chunk a0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+  Chunk b0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
   int ids[4];
   if (a0.nv > 0) {
     tile_ids(a0, b0, ids);
     tile_issue(ids, lds_a);
   }
-  Chunk a1 = take_chunk(cur, col_idx, kvstart), b1 = take_chunk(cur, col_idx, kvstart);
+  Chunk a1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+  Chunk b1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
   if (a1.nv > 0) tile_ids(a1, b1, ids);
   wait_vmem_all();
   __syncthreads();
 
-  // Per-lane read offsets (bytes within a stage).
-  const int krow0 = l32;                       // K row for M block mb: 32*mb + l32
   // V transposed reads: row 16*kc + 8*sh + 4*hl + (lane%16)/4, column 32*dm + 16*((lane/16)&1)
   // + 4*(lane&3): 16-byte unit 4*dm + 2*((lane/16)&1) + ((lane&3)>>1), 8-byte half (lane&1).
   const int vrow_l = 4 * hl + ((lane & 15) >> 2);
   const int vunit_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int vhalf_l = 8 * (lane & 1);
 
-  // One tile: compute from stage `st` while the next tile streams into `nx`. The two stages
-  // are distinct arrays so that the compiler can tell the streamed writes never alias the reads.
+  // One tile: compute from stage `st` while the next tile streams into `nx`. The two stages are
+  // distinct arrays so that the compiler can tell the streamed writes never alias the reads.
   auto step = [&](const char* st, char* nx) {
     if (a1.nv > 0) tile_issue(ids, nx);
-    const Chunk a2 = take_chunk(cur, col_idx, kvstart), b2 = take_chunk(cur, col_idx, kvstart);
+    const Chunk a2 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+    const Chunk b2 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
     if (a2.nv > 0) tile_ids(a2, b2, ids);
 
     // S^T for this wave's 32 queries: two 32-kv M blocks (raw, unscaled scores).
     f32x16_t sacc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const int row = 32 * mb + krow0;
+      const int row = 32 * mb + l32;
       const char* kp = st + row * kRowBytes;
       bf16x8_t kf[8];
 #pragma unroll
@@ -226,63 +258,105 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
           if (8 * (e >> 2) + 4 * hl + (e & 3) >= nv) sacc[mb][e] = -INFINITY;
       }
     }
-    float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[1][0], sacc[1][1]);
+
+    if constexpr (MODE == kMass) {
+      // Block sums of exp(sigma q.k - lse): one chunk per M block, flushed at block ends.
 #pragma unroll
-    for (int e = 2; e < 16; e += 2) {
-      mx0 = fmaxf(mx0, fmaxf(sacc[0][e], sacc[0][e + 1]));
-      mx1 = fmaxf(mx1, fmaxf(sacc[1][e], sacc[1][e + 1]));
-    }
-    float mx = fmaxf(mx0, mx1);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-    const bool grow = mx > m_run + kRescaleSlack;
-    if (__ballot(grow) != 0) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+      for (int mb = 0; mb < 2; ++mb) {
+        const Chunk& c = mb ? b0 : a0;
+        if (c.nv > 0) {
+          float cs0 = 0.f, cs1 = 0.f;
 #pragma unroll
-      for (int dm = 0; dm < 4; ++dm)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[dm][e] *= alpha;
-      m_run = m_new;
-    }
-    const float nm = -m_run;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-    bf16x8_t pb[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nm));
-        ls[e & 3] += p;
-        pb[2 * mb + (e >> 3)][e & 7] = (__bf16)p;
-      }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    // O^T += V^T P^T; each V^T fragment is two transposing 8-byte LDS reads.
-    const char* vt = st + kTileBytes;
-#pragma unroll
-    for (int dm = 0; dm < 4; ++dm) {
-      bf16x8_t vf[4];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        v4i16_t lo, hi;
-        {
-          const int row = 16 * kc + vrow_l;
-          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)((lds_char_t*)vt + row * kRowBytes + swz(row, 4 * dm + vunit_l) +
-                             vhalf_l));
+          for (int e = 0; e < 16; e += 2) {
+            cs0 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nlse2));
+            cs1 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e + 1], c2, nlse2));
+          }
+          blk_acc += cs0 + cs1;
+          if (c.last) {
+            const float tot = wave_sum_f32(blk_acc);
+            if (lane == 0)
+              a.part[(((size_t)bh * n_items + item) * 4 + wave) * a.nkv + c.J] = tot;
+            blk_acc = 0.f;
+          }
         }
-        {
-          const int row = 16 * kc + 8 + vrow_l;
-          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)((lds_char_t*)vt + row * kRowBytes + swz(row, 4 * dm + vunit_l) +
-                             vhalf_l));
-        }
-        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        vf[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
       }
+    } else {
+      float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[1][0], sacc[1][1]);
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc], pb[kc], oacc[dm], 0, 0, 0);
+      for (int e = 2; e < 16; e += 2) {
+        mx0 = fmaxf(mx0, fmaxf(sacc[0][e], sacc[0][e + 1]));
+        mx1 = fmaxf(mx1, fmaxf(sacc[1][e], sacc[1][e + 1]));
+      }
+      float mx = fmaxf(mx0, mx1);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+      const bool grow = mx > m_run + kRescaleSlack;
+      if (__ballot(grow) != 0) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        lb_run *= alpha;
+        if constexpr (MODE == kFwd) {
+#pragma unroll
+          for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[dm][e] *= alpha;
+        }
+        m_run = m_new;
+      }
+      const float nm = -m_run;
+      float ls[4] = {0.f, 0.f, 0.f, 0.f}, lb[2] = {0.f, 0.f};
+      uint32_t pw[2][8];  // P rounded to bf16, two per word (the B operand of the PV product)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e + 1], c2, nm));
+          ls[e & 3] += p0;
+          ls[(e & 3) + 1] += p1;
+          if constexpr (MODE == kFwd) {
+            // O is normalised by the sum of the same bf16-rounded weights the PV product uses
+            // (an exactly normalised combination); the LSE keeps the fp32 sum.
+            const uint32_t w = pack_bf16x2(p0, p1);
+            pw[mb][e >> 1] = w;
+            lb[0] += bf16_lo(w);
+            lb[1] += bf16_hi(w);
+          }
+        }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      if constexpr (MODE == kFwd) lb_run += lb[0] + lb[1];
+      bf16x8_t pb[4];
+      if constexpr (MODE == kFwd) {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const uint32_t* src = &pw[kc >> 1][4 * (kc & 1)];
+          pb[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
+        }
+      }
+      if constexpr (MODE == kFwd) {
+        // O^T += V^T P^T; each V^T fragment is two transposing 8-byte LDS reads.
+        const char* vt = st + kTileBytes;
+#pragma unroll
+        for (int dm = 0; dm < 4; ++dm) {
+          bf16x8_t vf[4];
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
+            const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16_t*)((lds_char_t*)vt + row_lo * kRowBytes +
+                               swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
+            const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16_t*)((lds_char_t*)vt + row_hi * kRowBytes +
+                               swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            vf[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+          }
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc)
+            oacc[dm] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc], pb[kc], oacc[dm], 0, 0, 0);
+        }
+      }
     }
     wait_vmem_all();
     __syncthreads();
@@ -290,7 +364,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
     b0 = b1;
     a1 = a2;
     b1 = b2;
-    };
+  };
   while (true) {
     if (a0.nv <= 0) break;
     step(lds_a, lds_b);
@@ -298,21 +372,59 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma_d128(
     step(lds_b, lds_a);
   }
 
+  if constexpr (MODE == kMass) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* op = O + head_off + (size_t)qtok * D;
+  if constexpr (MODE == kFwd) {
+    const float lb_tot = lb_run + __shfl_xor(lb_run, 32, 64);
+    const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
+    uint16_t* op = a.O + head_off + (size_t)qtok * D;
 #pragma unroll
-  for (int dm = 0; dm < 4; ++dm)
+    for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint2 pk;
-      pk.x = pack_bf16x2(oacc[dm][4 * g] * inv, oacc[dm][4 * g + 1] * inv);
-      pk.y = pack_bf16x2(oacc[dm][4 * g + 2] * inv, oacc[dm][4 * g + 3] * inv);
-      *reinterpret_cast<uint2*>(op + 32 * dm + 8 * g + 4 * hl) = pk;
-    }
-  if (lse && hl == 0)
-    lse[(size_t)bh * N + qtok] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      for (int g = 0; g < 4; ++g) {
+        uint2 pk;
+        pk.x = pack_bf16x2(oacc[dm][4 * g] * inv, oacc[dm][4 * g + 1] * inv);
+        pk.y = pack_bf16x2(oacc[dm][4 * g + 2] * inv, oacc[dm][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(op + 32 * dm + 8 * g + 4 * hl) = pk;
+      }
+  }
+  if (a.lse && hl == 0)
+    a.lse[(size_t)bh * a.N + qtok] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+// M[bh, I, J] = (sum over I's work items and the 4 waves of the block sums) / |I|, in fp64 and in
+// a fixed order.
+__global__ __launch_bounds__(256) void mass_combine_kernel(const float* __restrict__ part,
+                                                           const int32_t* __restrict__ qstart,
+                                                           const int32_t* __restrict__ qitem0,
+                                                           int n_items, int nq, int nkv,
+                                                           float* __restrict__ M) {
+  const int I = blockIdx.x, bh = blockIdx.y;
+  const int i0 = qitem0[I], i1 = qitem0[I + 1];
+  const double inv = 1.0 / (double)(qstart[I + 1] - qstart[I]);
+  for (int J = threadIdx.x; J < nkv; J += 256) {
+    double s = 0.0;
+    for (int it = i0; it < i1; ++it)
+      for (int w = 0; w < 4; ++w) s += part[(((size_t)bh * n_items + it) * 4 + w) * nkv + J];
+    M[((size_t)bh * nq + I) * nkv + J] = (float)(s * inv);
+  }
+}
+
+MfmaArgs mfma_args(const bsa_plan& p) {
+  MfmaArgs a{};
+  a.qperm = p.qperm;
+  a.qstart = p.qstart;
+  a.kvperm = p.kvperm;
+  a.kvstart = p.kvstart;
+  a.items = p.items;
+  a.scale = p.scale;
+  a.n_items = p.n_items;
+  a.H = p.prob.H;
+  a.N = p.prob.N;
+  a.nq = p.nq;
+  a.nkv = p.nkv;
+  return a;
 }
 
 // ------------------------------------------------------------------------------- VALU path
@@ -371,9 +483,9 @@ __global__ __launch_bounds__(128) void attn_fwd_valu(
   cur.slot = row_ptr[r];
   cur.end = row_ptr[r + 1];
   cur.sub = 0;
-  cursor_load(cur, col_idx, kvstart);
+  cursor_load<false>(cur, col_idx, kvstart);
   while (true) {
-    const Chunk c = take_chunk(cur, col_idx, kvstart);
+    const Chunk c = take_chunk<false>(cur, col_idx, kvstart);
     if (c.nv == 0) break;
     __syncthreads();
     for (int e = t; e < 32 * D; e += 128) {
@@ -438,17 +550,44 @@ hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, cons
                            const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse,
                            hipStream_t s) {
   if (p.prob.dtype == BSA_BF16 && p.prob.d == 128) {
-    const int BH = p.prob.B * p.prob.H;
-    // Flattened (item, head) space; gridDim.x * gridDim.y must equal n_items * BH exactly.
-    dim3 grid(p.n_items, BH);
-    attn_fwd_mfma_d128<<<grid, 256, 0, s>>>(
-        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
-        static_cast<const uint16_t*>(V), row_ptr, col_idx, p.qperm, p.qstart, p.kvperm,
-        p.kvstart, p.items, p.n_items, p.scale, p.prob.H, p.prob.N, p.nq,
-        static_cast<uint16_t*>(O), lse);
+    MfmaArgs a = mfma_args(p);
+    a.Q = static_cast<const uint16_t*>(Q);
+    a.K = static_cast<const uint16_t*>(K);
+    a.V = static_cast<const uint16_t*>(V);
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.O = static_cast<uint16_t*>(O);
+    a.lse = lse;
+    // gridDim.x * gridDim.y is exactly n_items * B * H (the XCD remap is a bijection on it).
+    attn_mfma_d128<kFwd><<<dim3(p.n_items, p.prob.B * p.prob.H), 256, 0, s>>>(a);
     return hipGetLastError();
   }
-  if (p.prob.dtype == BSA_BF16) return launch_valu<uint16_t, 64>(p, Q, K, V, row_ptr, col_idx, O, lse, s);
+  if (p.prob.dtype == BSA_BF16)
+    return launch_valu<uint16_t, 64>(p, Q, K, V, row_ptr, col_idx, O, lse, s);
   if (p.prob.d == 128) return launch_valu<float, 128>(p, Q, K, V, row_ptr, col_idx, O, lse, s);
   return launch_valu<float, 64>(p, Q, K, V, row_ptr, col_idx, O, lse, s);
+}
+
+hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, float* M, void* ws,
+                            hipStream_t s) {
+  const CalibWs L = calib_ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  float* lse = reinterpret_cast<float*>(base + L.lse);
+  float* part = reinterpret_cast<float*>(base + L.part);
+  const dim3 grid(p.n_items, p.prob.B * p.prob.H);
+  MfmaArgs a = mfma_args(p);
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.lse = lse;
+  attn_mfma_d128<kLse><<<grid, 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.lse = nullptr;
+  a.lse_in = lse;
+  a.part = part;
+  attn_mfma_d128<kMass><<<grid, 256, 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  mass_combine_kernel<<<dim3(p.nq, p.prob.B * p.prob.H), 256, 0, s>>>(
+      part, p.qstart, p.qitem0, p.n_items, p.nq, p.nkv, M);
+  return hipGetLastError();
 }

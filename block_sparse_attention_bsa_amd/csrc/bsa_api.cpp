@@ -108,7 +108,7 @@ int upload(const std::vector<T>& h, T** d) {
 void free_plan(bsa_plan* p) {
   if (!p) return;
   for (void* ptr : {(void*)p->qperm, (void*)p->qstart, (void*)p->kvperm, (void*)p->kvstart,
-                    (void*)p->items, (void*)p->scale})
+                    (void*)p->items, (void*)p->qitem0, (void*)p->scale})
     if (ptr) (void)hipFree(ptr);
   delete p;
 }
@@ -138,8 +138,13 @@ BwdWs bwd_ws_layout(const bsa_plan& p) {
   return w;
 }
 
-size_t calib_ws_bytes(const bsa_plan& p) {
-  return align_up((size_t)p.prob.B * p.prob.H * p.prob.N * 4);
+CalibWs calib_ws_layout(const bsa_plan& p) {
+  CalibWs w;
+  const size_t BH = (size_t)p.prob.B * p.prob.H;
+  w.lse = 0;
+  w.part = align_up(BH * p.prob.N * 4);
+  w.total = w.part + align_up(BH * p.n_items * 4 * (size_t)p.nkv * 4);
+  return w;
 }
 
 extern "C" {
@@ -201,11 +206,13 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
   for (int i = 0; i < p->nq; ++i) {
     const int sz = p->h_qstart[i + 1] - p->h_qstart[i];
     p->max_qblk = std::max(p->max_qblk, sz);
+    p->h_qitem0.push_back((int32_t)(p->h_items.size() / 2));
     for (int off = 0; off < sz; off += kAttnRows) {
       p->h_items.push_back(i);
       p->h_items.push_back(off);
     }
   }
+  p->h_qitem0.push_back((int32_t)(p->h_items.size() / 2));
   for (int j = 0; j < p->nkv; ++j)
     p->max_kvblk = std::max(p->max_kvblk, p->h_kvstart[j + 1] - p->h_kvstart[j]);
   p->n_items = (int)(p->h_items.size() / 2);
@@ -219,7 +226,8 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
   }
   if (upload(p->h_qperm, &p->qperm) || upload(p->h_qstart, &p->qstart) ||
       upload(p->h_kvperm, &p->kvperm) || upload(p->h_kvstart, &p->kvstart) ||
-      upload(p->h_items, &p->items) || upload(p->h_scale, &p->scale)) {
+      upload(p->h_items, &p->items) || upload(p->h_qitem0, &p->qitem0) ||
+      upload(p->h_scale, &p->scale)) {
     free_plan(p);
     return fail(BSA_EHIP, "bsa_plan_create: device allocation or upload failed");
   }
@@ -239,7 +247,7 @@ int bsa_plan_info(const bsa_plan* plan, int32_t* nq, int32_t* nkv, size_t* ws_se
   if (nq) *nq = plan->nq;
   if (nkv) *nkv = plan->nkv;
   if (ws_select) *ws_select = select_ws_layout(*plan).total;
-  if (ws_calib) *ws_calib = calib_ws_bytes(*plan);
+  if (ws_calib) *ws_calib = calib_ws_layout(*plan).total;
   if (ws_bwd) *ws_bwd = bwd_ws_layout(*plan).total;
   return ok();
 }
@@ -278,7 +286,7 @@ int bsa_calibrate_mass(const bsa_plan* plan, const void* Q, const void* K, float
   if (!plan || !Q || !K || !M) return fail(BSA_EINVAL, "bsa_calibrate_mass: NULL argument");
   if (plan->prob.dtype != BSA_BF16 || plan->prob.d != 128)
     return fail(BSA_EUNSUPPORTED, "bsa_calibrate_mass: bf16 with d = 128 only");
-  const size_t need = calib_ws_bytes(*plan);
+  const size_t need = calib_ws_layout(*plan).total;
   if (!ws || ws_bytes < need)
     return fail(BSA_ECAPACITY, "bsa_calibrate_mass: workspace %zu < %zu bytes", ws_bytes, need);
   int rc = check_device(plan);

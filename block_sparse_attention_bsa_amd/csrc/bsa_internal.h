@@ -20,13 +20,14 @@ struct bsa_plan {
   int device = 0;
   int nq = 0, nkv = 0;
   int max_qblk = 0, max_kvblk = 0;
-  std::vector<int32_t> h_qperm, h_qstart, h_kvperm, h_kvstart, h_items;
+  std::vector<int32_t> h_qperm, h_qstart, h_kvperm, h_kvstart, h_items, h_qitem0;
   // Device copies (owned by the plan).
   int32_t* qperm = nullptr;
   int32_t* qstart = nullptr;
   int32_t* kvperm = nullptr;
   int32_t* kvstart = nullptr;
   int32_t* items = nullptr;   // attention work items: pairs (I, first row within block I)
+  int32_t* qitem0 = nullptr;  // [nq + 1]: first work item of each query block
   int n_items = 0;
   float* scale = nullptr;     // sigma_h, [H]
   std::vector<float> h_scale;
@@ -46,7 +47,10 @@ struct BwdWs {
 };
 BwdWs bwd_ws_layout(const bsa_plan& p);
 
-size_t calib_ws_bytes(const bsa_plan& p);
+struct CalibWs {
+  size_t lse, part, total;  // per-token log-sum-exp; per (item, wave, kv block) block sums
+};
+CalibWs calib_ws_layout(const bsa_plan& p);
 
 // Kernel launchers (defined in the .hip files). Each returns the launch status.
 hipError_t launch_pool(const bsa_plan& p, int which, const void* X, float* Xbar, hipStream_t s);

@@ -1,0 +1,106 @@
+"""GPU parity of the calibrate-then-reuse path (LoSA abstract): exact block masses from one dense
+step, the minimal block set reaching 99% of the mass, and sparse attention with those indices
+frozen over later steps whose inputs drift.
+
+Tolerances: masses within 1e-5 absolute (fp32 accumulation of exact bf16 products versus fp64);
+selections bit-exact except near-ties within 1e-5 of p; O within max-abs 1e-2 (bf16 inputs)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+from gen import CONFIGS, drift_step, make_inputs
+from helpers import check_csr_rows, dev_to_f64, log, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(w, x):
+    from block_sparse_attention_bsa_amd.layer import BlockSparseAttention
+    return BlockSparseAttention(w.B, w.H, w.d, w.grid, w.qpart, w.kvpart, dtype=w.dtype,
+                                head_scale=x["head_scale"])
+
+
+def _calibrate(w, x, rows=None):
+    import torch
+    layer = _layer(w, x)
+    M = layer.calibrate(to_dev(x["q"]), to_dev(x["k"]))
+    torch.cuda.synchronize()
+    qb, kb = oracle.partition(w.grid, w.qpart), oracle.partition(w.grid, w.kvpart)
+    M_ref = oracle.exact_mass(to_f64(x["q"]), to_f64(x["k"]), x["head_scale"].astype(np.float64),
+                              qb, kb, rows=rows)
+    return layer, dev_to_f64(M), M_ref, qb, kb
+
+
+def test_calibrate_masses_reduced():
+    w = replace(CONFIGS[3], grid=(9, 14, 26), H=3)
+    x = make_inputs(w)
+    layer, M, M_ref, qb, kb = _calibrate(w, x)
+    err = np.abs(M - M_ref).max()
+    log(f"calibrate reduced: max-abs {err:.2e}; row sums {M.sum(-1).min():.6f}..{M.sum(-1).max():.6f}")
+    assert err <= 1e-5
+    np.testing.assert_allclose(M.sum(-1), 1.0, atol=1e-5)
+
+
+def test_calibrate_big_blocks_multi_item():
+    # 1D temporal kv blocks of 540 tokens (17 chunks each) and 540-token query blocks split into
+    # 5 work items, whose partial sums the combine pass adds.
+    w = replace(CONFIGS[3], grid=(6, 9, 20), H=2, qpart=("tile", (3, 9, 20)),
+                kvpart=("tile", (3, 9, 20)))
+    x = make_inputs(w)
+    _, M, M_ref, _, _ = _calibrate(w, x)
+    err = np.abs(M - M_ref).max()
+    log(f"calibrate big blocks: max-abs {err:.2e}")
+    assert err <= 1e-5
+
+
+def test_calibrate_select_freeze_and_reuse_reduced():
+    import torch
+    w = replace(CONFIGS[3], grid=(9, 14, 26), H=3)
+    x = make_inputs(w)
+    layer, M, M_ref, qb, kb = _calibrate(w, x)
+    layer.select(w.p)
+    torch.cuda.synchronize()
+    rp, ci = layer.csr_host()
+    rows_gpu = oracle.csr_rows(rp, ci)
+    rows_ref = oracle.select_row(M_ref, w.p)
+    exact, tol, bad = check_csr_rows(rows_gpu, rows_ref, M_ref.reshape(-1, M_ref.shape[-1]), w.p)
+    dens = oracle.density(rows_ref, oracle.block_sizes(qb), oracle.block_sizes(kb), w.H)
+    log(f"select p={w.p}: exact {exact} tolerated {tol} bad {len(bad)}; density {dens:.3f}")
+    assert not bad
+    # Freeze: later steps reuse the step-0 CSR byte for byte on drifting inputs.
+    frozen_rp, frozen_ci = layer.row_ptr.clone(), layer.col_idx.clone()
+    masters = {k: x[k + "32"].copy() for k in ("q", "k", "v")}
+    hs = x["head_scale"].astype(np.float64)
+    same = [r for r in range(len(rows_ref)) if np.array_equal(rows_gpu[r], rows_ref[r])]
+    rp_ref, ci_ref = oracle.to_csr(rows_ref)
+    nq = len(qb)
+    sample = [(0, (r // nq) % w.H, r % nq) for r in same[:: max(1, len(same) // 24)]]
+    for step in (1, 2, 3):
+        xs = drift_step(w, masters, step)
+        q, k, v = (to_dev(xs[n]) for n in ("q", "k", "v"))
+        O, _ = layer.attention(q, k, v, row_ptr=frozen_rp, col_idx=frozen_ci)
+        torch.cuda.synchronize()
+        assert torch.equal(frozen_rp, layer.row_ptr)
+        O_ref, _ = oracle.attention_fwd(*(to_f64(xs[n]) for n in ("q", "k", "v")), hs, qb, kb,
+                                        rp_ref, ci_ref, rows=sample)
+        Og = dev_to_f64(O)
+        worst = max(float(np.abs(Og[b, h, qb[i]] - O_ref[b, h, qb[i]]).max())
+                    for b, h, i in sample)
+        log(f"  step {step}: O max-abs {worst:.2e} over {len(sample)} q-blocks")
+        assert worst <= 1e-2
+
+
+def test_calibrate_full_size_sampled():
+    w = CONFIGS[3]
+    x = make_inputs(w)
+    rng = np.random.default_rng(3)
+    nq = 336
+    rows = [(0, int(h), int(i)) for h, i in zip(rng.integers(0, w.H, 10), rng.integers(0, nq, 10))]
+    layer, M, M_ref, qb, kb = _calibrate(w, x, rows=rows)
+    err = max(float(np.abs(M[b, h, i] - M_ref[b, h, i]).max()) for b, h, i in rows)
+    log(f"calibrate full size: max-abs {err:.2e} over {len(rows)} sampled rows; "
+        f"all row sums within {np.abs(M.sum(-1) - 1).max():.1e} of 1")
+    assert err <= 1e-5
+    np.testing.assert_allclose(M.sum(-1), 1.0, atol=1e-4)
