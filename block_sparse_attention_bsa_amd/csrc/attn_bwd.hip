@@ -1,8 +1,456 @@
-// Sparse attention backward: placeholder until the dK/dV and dQ kernels land.
+// Backward of the block-sparse attention (training through the sparse attention: pith.science
+// review of VMoBA, "The reading"), with the selection held fixed as a hard gate. For every
+// selected pair (i, j): P = exp(sigma q_i.k_j - lse_i), dV_j += P dO_i, dP = dO_i.v_j,
+// dS = P (dP - D_i) with D_i = dO_i.O_i, dQ_i += sigma dS k_j, dK_j += sigma dS q_i.
+//
+// Passes, all deterministic (no atomics on floating point):
+//   1. delta_kernel   D = rowsum(dO * O), streaming both tensors once.
+//   2. CSR -> CSC      a per-row bitmap of the selection, then for every (head, kv block) the
+//                      ascending list of query blocks that selected it (column counts, a scan,
+//                      and a fill that walks the bitmap in query-block order).
+//   3. dkdv_kernel     kv-stationary: a workgroup owns 128 tokens of one kv block (4 wavefronts x
+//                      32 tokens, K and V held in registers as MFMA B operands) and streams the
+//                      64-query chunks of every query block in its CSC column through LDS (Q, dO,
+//                      lse, D; double-buffered direct loads). Per chunk and wave: S = Q K^T and
+//                      dP = dO V^T (lane = kv token), P and dS in registers, then
+//                      dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T from transposing reads.
+//   4. dQ              the forward kernel's kDq mode over the CSR (one workgroup per query block).
 #include "bsa_internal.h"
+#include "device_common.h"
 
-hipError_t launch_attn_bwd(const bsa_plan&, const void*, const void*, const void*, const void*,
-                           const void*, const float*, const int32_t*, const int32_t*, void*,
-                           void*, void*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+constexpr int kRowBytes = 256;
+constexpr int kChunkQ = 64;                     // queries per streamed chunk
+constexpr int kTileBytes = kChunkQ * kRowBytes;  // one of Q / dO
+constexpr int kStage = 2 * kTileBytes + 2 * kChunkQ * 4;  // Q, dO, lse2, D
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+__device__ __forceinline__ int swz(int row, int unit) { return (unit ^ (row & 15)) << 4; }
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// D[bh, n] = sum_d dO[bh, n, d] * O[bh, n, d]; 16 lanes per token row.
+__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ O,
+                                                    const uint16_t* __restrict__ dO,
+                                                    int64_t rows, float* __restrict__ D) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int seg = threadIdx.x & 15;
+  float s = 0.f;
+  if (row < rows) {
+    const uint4 o = *reinterpret_cast<const uint4*>(O + row * 128 + 8 * seg);
+    const uint4 g = *reinterpret_cast<const uint4*>(dO + row * 128 + 8 * seg);
+    const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s += bf16_lo(ow[i]) * bf16_lo(gw[i]) + bf16_hi(ow[i]) * bf16_hi(gw[i]);
+  }
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+  if (row < rows && seg == 0) D[row] = s;
+}
+
+// Selection bitmap of one CSR row (one workgroup per row, nwords <= 256).
+__global__ __launch_bounds__(256) void csr_bitmap_kernel(const int32_t* __restrict__ row_ptr,
+                                                         const int32_t* __restrict__ col_idx,
+                                                         int nwords, uint32_t* __restrict__ bm) {
+  __shared__ uint32_t w[256];
+  const int64_t r = blockIdx.x;
+  for (int i = threadIdx.x; i < nwords; i += 256) w[i] = 0u;
+  __syncthreads();
+  for (int s = row_ptr[r] + threadIdx.x; s < row_ptr[r + 1]; s += 256) {
+    const int J = col_idx[s];
+    atomicOr(&w[J >> 5], 1u << (J & 31));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nwords; i += 256) bm[r * nwords + i] = w[i];
+}
+
+// One thread per column (bh, J): count (fill == false) or write (fill == true) the query blocks
+// that selected J, in ascending order.
+__global__ __launch_bounds__(256) void csc_kernel(const uint32_t* __restrict__ bm, int nq,
+                                                  int nkv, int nwords, int64_t cols, bool fill,
+                                                  int32_t* __restrict__ col_cnt,
+                                                  const int32_t* __restrict__ col_ptr,
+                                                  int32_t* __restrict__ row_idx) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  const int64_t bh = c / nkv;
+  const int J = (int)(c % nkv);
+  const uint32_t* b = bm + bh * nq * (int64_t)nwords + (J >> 5);
+  const uint32_t bit = 1u << (J & 31);
+  int pos = fill ? col_ptr[c] : 0;
+  int n = 0;
+  for (int I = 0; I < nq; ++I) {
+    if (b[(int64_t)I * nwords] & bit) {
+      if (fill) row_idx[pos++] = I;
+      ++n;
+    }
+  }
+  if (!fill) col_cnt[c] = n;
+}
+
+// Exclusive scan of the column counts (one workgroup).
+__global__ __launch_bounds__(1024) void col_scan_kernel(const int32_t* __restrict__ cnt,
+                                                        int64_t cols,
+                                                        int32_t* __restrict__ col_ptr) {
+  __shared__ int wtot[16];
+  __shared__ int carry_s;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (t == 0) {
+    carry_s = 0;
+    col_ptr[0] = 0;
+  }
+  __syncthreads();
+  for (int64_t base = 0; base < cols; base += 1024) {
+    const int64_t c = base + t;
+    const int f = c < cols ? cnt[c] : 0;
+    const int incl = wave_incl_scan_i32(f);
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int before = carry_s;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
+    if (c < cols) col_ptr[c + 1] = before + incl;
+    __syncthreads();
+    if (t == 0) {
+      int tot = 0;
+      for (int w = 0; w < 16; ++w) tot += wtot[w];
+      carry_s += tot;
+    }
+    __syncthreads();
+  }
+}
+
+struct DkdvArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* dO;
+  const float* lse;
+  const float* delta;
+  const int32_t* col_ptr;
+  const int32_t* row_idx;
+  const int32_t* qperm;
+  const int32_t* qstart;
+  const int32_t* kvperm;
+  const int32_t* kvstart;
+  const int32_t* kvitems;
+  const float* scale;
+  uint16_t* dK;
+  uint16_t* dV;
+  int n_kvitems, H, N, nkv;
+};
+
+// Walks the query blocks of a CSC column as 64-query chunks.
+struct QCursor {
+  int slot, end, sub, base, size;
+};
+
+__device__ __forceinline__ void qcur_load(QCursor& c, const int32_t* __restrict__ row_idx,
+                                          const int32_t* __restrict__ qstart) {
+  if (c.slot < c.end) {
+    const int I = row_idx[c.slot];
+    c.base = qstart[I];
+    c.size = qstart[I + 1] - c.base;
+  } else {
+    c.base = 0;
+    c.size = 0;
+  }
+}
+
+struct QChunk {
+  int pos, nv;
+};
+
+__device__ __forceinline__ QChunk qcur_take(QCursor& c, const int32_t* __restrict__ row_idx,
+                                            const int32_t* __restrict__ qstart) {
+  QChunk k;
+  if (c.slot < c.end) {
+    k.pos = c.base + kChunkQ * c.sub;
+    k.nv = min(kChunkQ, c.size - kChunkQ * c.sub);
+    ++c.sub;
+    if (kChunkQ * c.sub >= c.size) {
+      ++c.slot;
+      c.sub = 0;
+      qcur_load(c, row_idx, qstart);
+    }
+  } else {
+    k.pos = 0;
+    k.nv = 0;
+  }
+  return k;
+}
+
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(1024))) char lds_a[kStage];
+  __shared__ __attribute__((aligned(1024))) char lds_b[kStage];
+
+  const int total = a.n_kvitems * (int)gridDim.y;
+  const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
+  const int bh = lin / a.n_kvitems, item = lin % a.n_kvitems;
+  const int J = a.kvitems[2 * item], off = a.kvitems[2 * item + 1];
+  const int k0 = a.kvstart[J] + off;
+  const int nkvrows = min(128, a.kvstart[J + 1] - k0);
+  const size_t head_off = (size_t)bh * a.N * D;
+  const float c2 = a.scale[bh % a.H] * kLog2e;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l32 = lane & 31, hl = lane >> 5;
+
+  // K and V fragments of this lane's kv token (B operands of S = Q K^T and dP = dO V^T).
+  const int kvrow = 32 * wave + l32;
+  const bool kvvalid = kvrow < nkvrows;
+  const int kvtok = kvvalid ? a.kvperm[k0 + kvrow] : 0;
+  bf16x8_t kf[8], vf[8];
+  {
+    const uint4* kp = reinterpret_cast<const uint4*>(a.K + head_off + (size_t)kvtok * D + 8 * hl);
+    const uint4* vp = reinterpret_cast<const uint4*>(a.V + head_off + (size_t)kvtok * D + 8 * hl);
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      kf[kc] = __builtin_bit_cast(bf16x8_t, kvvalid ? kp[2 * kc] : make_uint4(0, 0, 0, 0));
+      vf[kc] = __builtin_bit_cast(bf16x8_t, kvvalid ? vp[2 * kc] : make_uint4(0, 0, 0, 0));
+    }
+  }
+  f32x16_t dk[4], dv[4];  // dK^T, dV^T: lane = kv token, registers = d
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dk[i][e] = 0.f;
+      dv[i][e] = 0.f;
+    }
+
+  const int64_t col = (int64_t)bh * a.nkv + J;
+  QCursor cur;
+  cur.slot = a.col_ptr[col];
+  cur.end = a.col_ptr[col + 1];
+  cur.sub = 0;
+  qcur_load(cur, a.row_idx, a.qstart);
+
+  // Loader roles: rows 16w + 4i + lane/16 of the Q and dO tiles (direct loads, swizzled), and
+  // threads 0..63 stage lse2 / D of query row t (padding rows: lse2 = +inf, D = 0).
+  const int lrow0 = 16 * wave + (lane >> 4);
+  int ids[4];
+  float st_lse = 0.f, st_d = 0.f;
+  auto chunk_ids = [&](QChunk c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = lrow0 + 4 * i;
+      ids[i] = a.qperm[c.pos + (rr < c.nv ? rr : 0)];
+    }
+  };
+  auto chunk_issue = [&](QChunk c, char* st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lunit = (lane & 15) ^ ((lrow0 + 4 * i) & 15);
+      const size_t o = head_off + (size_t)ids[i] * D + 8 * lunit;
+      char* dst = st + (16 * wave + 4 * i) * kRowBytes;
+      __builtin_amdgcn_global_load_lds(a.Q + o, dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.dO + o, dst + kTileBytes, 16, 0, 0);
+    }
+    if (t < kChunkQ) {
+      if (t < c.nv) {
+        const size_t n = (size_t)bh * a.N + a.qperm[c.pos + t];
+        st_lse = a.lse[n] * kLog2e;
+        st_d = a.delta[n];
+      } else {
+        st_lse = INFINITY;
+        st_d = 0.f;
+      }
+    }
+  };
+  auto chunk_finish = [&](char* st) {
+    if (t < kChunkQ) {
+      reinterpret_cast<float*>(st + 2 * kTileBytes)[t] = st_lse;
+      reinterpret_cast<float*>(st + 2 * kTileBytes + kChunkQ * 4)[t] = st_d;
+    }
+  };
+
+  // Transposing-read offsets (as for V^T in the forward kernel).
+  const int vrow_l = 4 * hl + ((lane & 15) >> 2);
+  const int vunit_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vhalf_l = 8 * (lane & 1);
+
+  QChunk c0 = qcur_take(cur, a.row_idx, a.qstart);
+  if (c0.nv > 0) {
+    chunk_ids(c0);
+    chunk_issue(c0, lds_a);
+    chunk_finish(lds_a);
+  }
+  QChunk c1 = qcur_take(cur, a.row_idx, a.qstart);
+  if (c1.nv > 0) chunk_ids(c1);
+  wait_vmem_all();
+  __syncthreads();
+
+  auto step = [&](const char* st, char* nx) {
+    if (c1.nv > 0) chunk_issue(c1, nx);
+    const QChunk c2n = qcur_take(cur, a.row_idx, a.qstart);
+    if (c2n.nv > 0) chunk_ids(c2n);
+
+    const float* lse2 = reinterpret_cast<const float*>(st + 2 * kTileBytes);
+    const float* dd = reinterpret_cast<const float*>(st + 2 * kTileBytes + kChunkQ * 4);
+    // S = Q K^T and dP = dO V^T for two 32-query M blocks (lane = kv token, regs = query).
+    f32x16_t sacc[2], dpacc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int row = 32 * mb + l32;
+      const char* qp = st + row * kRowBytes;
+      const char* gp = st + kTileBytes + row * kRowBytes;
+      bf16x8_t qa[8], ga[8];
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        qa[kc] = *reinterpret_cast<const bf16x8_t*>(qp + swz(row, 2 * kc + hl));
+        ga[kc] = *reinterpret_cast<const bf16x8_t*>(gp + swz(row, 2 * kc + hl));
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sacc[mb][e] = 0.f;
+        dpacc[mb][e] = 0.f;
+      }
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kc], kf[kc], sacc[mb], 0, 0, 0);
+        dpacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[kc], vf[kc], dpacc[mb], 0, 0, 0);
+      }
+    }
+    // P = exp(sigma s - lse) and dS = P (dP - D), both rounded to bf16 (B operands below).
+    uint32_t pw[2][8], dw[2][8];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int q = 32 * mb + 8 * g + 4 * hl;
+        const float4 l4 = *reinterpret_cast<const float4*>(lse2 + q);
+        const float4 d4 = *reinterpret_cast<const float4*>(dd + q);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        float pr[4], dsr[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int e = 4 * g + rr;
+          pr[rr] = kvvalid ? __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, -lv[rr])) : 0.f;
+          dsr[rr] = pr[rr] * (dpacc[mb][e] - dv4[rr]);
+        }
+        pw[mb][2 * g] = pack_bf16x2(pr[0], pr[1]);
+        pw[mb][2 * g + 1] = pack_bf16x2(pr[2], pr[3]);
+        dw[mb][2 * g] = pack_bf16x2(dsr[0], dsr[1]);
+        dw[mb][2 * g + 1] = pack_bf16x2(dsr[2], dsr[3]);
+      }
+    // dV^T += dO^T P and dK^T += Q^T dS (A operands from transposing reads of dO / Q).
+#pragma unroll
+    for (int dm = 0; dm < 4; ++dm) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
+        const int olo = row_lo * kRowBytes + swz(row_lo, 4 * dm + vunit_l) + vhalf_l;
+        const int ohi = row_hi * kRowBytes + swz(row_hi, 4 * dm + vunit_l) + vhalf_l;
+        const v4i16_t glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((lds_char_t*)st + kTileBytes + olo));
+        const v4i16_t ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((lds_char_t*)st + kTileBytes + ohi));
+        const v4i16_t qlo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)((lds_char_t*)st + olo));
+        const v4i16_t qhi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)((lds_char_t*)st + ohi));
+        const uint2 g0 = __builtin_bit_cast(uint2, glo), g1 = __builtin_bit_cast(uint2, ghi);
+        const uint2 q0 = __builtin_bit_cast(uint2, qlo), q1 = __builtin_bit_cast(uint2, qhi);
+        const bf16x8_t gt = __builtin_bit_cast(bf16x8_t, make_uint4(g0.x, g0.y, g1.x, g1.y));
+        const bf16x8_t qt = __builtin_bit_cast(bf16x8_t, make_uint4(q0.x, q0.y, q1.x, q1.y));
+        const uint32_t* ps = &pw[kc >> 1][4 * (kc & 1)];
+        const uint32_t* ds = &dw[kc >> 1][4 * (kc & 1)];
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(ps[0], ps[1], ps[2], ps[3]));
+        const bf16x8_t db = __builtin_bit_cast(bf16x8_t, make_uint4(ds[0], ds[1], ds[2], ds[3]));
+        dv[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt, pb, dv[dm], 0, 0, 0);
+        dk[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, db, dk[dm], 0, 0, 0);
+      }
+    }
+    if (c1.nv > 0) chunk_finish(nx);
+    wait_vmem_all();
+    __syncthreads();
+    c0 = c1;
+    c1 = c2n;
+  };
+  while (true) {
+    if (c0.nv <= 0) break;
+    step(lds_a, lds_b);
+    if (c0.nv <= 0) break;
+    step(lds_b, lds_a);
+  }
+
+  if (!kvvalid) return;
+  const float sig = a.scale[bh % a.H];
+  uint16_t* kop = a.dK + head_off + (size_t)kvtok * D;
+  uint16_t* vop = a.dV + head_off + (size_t)kvtok * D;
+#pragma unroll
+  for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint2 pk, pv;
+      pk.x = pack_bf16x2(dk[dm][4 * g] * sig, dk[dm][4 * g + 1] * sig);
+      pk.y = pack_bf16x2(dk[dm][4 * g + 2] * sig, dk[dm][4 * g + 3] * sig);
+      pv.x = pack_bf16x2(dv[dm][4 * g], dv[dm][4 * g + 1]);
+      pv.y = pack_bf16x2(dv[dm][4 * g + 2], dv[dm][4 * g + 3]);
+      *reinterpret_cast<uint2*>(kop + 32 * dm + 8 * g + 4 * hl) = pk;
+      *reinterpret_cast<uint2*>(vop + 32 * dm + 8 * g + 4 * hl) = pv;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
+                           const void* O, const void* dO, const float* lse,
+                           const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK,
+                           void* dV, void* ws, hipStream_t s) {
+  const BwdWs L = bwd_ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  float* delta = reinterpret_cast<float*>(base + L.delta);
+  uint32_t* bm = reinterpret_cast<uint32_t*>(base + L.bitmap);
+  int32_t* col_cnt = reinterpret_cast<int32_t*>(base + L.col_cnt);
+  int32_t* col_ptr = reinterpret_cast<int32_t*>(base + L.col_ptr);
+  int32_t* row_idx = reinterpret_cast<int32_t*>(base + L.row_idx);
+  const int BH = p.prob.B * p.prob.H;
+  const int64_t tok_rows = (int64_t)BH * p.prob.N;
+  const int64_t rows = (int64_t)BH * p.nq, cols = (int64_t)BH * p.nkv;
+  hipError_t e;
+  delta_kernel<<<(unsigned)((tok_rows + 15) / 16), 256, 0, s>>>(
+      static_cast<const uint16_t*>(O), static_cast<const uint16_t*>(dO), tok_rows, delta);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  csr_bitmap_kernel<<<(unsigned)rows, 256, 0, s>>>(row_ptr, col_idx, L.nwords, bm);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned cblocks = (unsigned)((cols + 255) / 256);
+  csc_kernel<<<cblocks, 256, 0, s>>>(bm, p.nq, p.nkv, L.nwords, cols, false, col_cnt, nullptr,
+                                     nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  col_scan_kernel<<<1, 1024, 0, s>>>(col_cnt, cols, col_ptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  csc_kernel<<<cblocks, 256, 0, s>>>(bm, p.nq, p.nkv, L.nwords, cols, true, nullptr, col_ptr,
+                                     row_idx);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  DkdvArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.dO = static_cast<const uint16_t*>(dO);
+  a.lse = lse;
+  a.delta = delta;
+  a.col_ptr = col_ptr;
+  a.row_idx = row_idx;
+  a.qperm = p.qperm;
+  a.qstart = p.qstart;
+  a.kvperm = p.kvperm;
+  a.kvstart = p.kvstart;
+  a.kvitems = p.kvitems;
+  a.scale = p.scale;
+  a.dK = static_cast<uint16_t*>(dK);
+  a.dV = static_cast<uint16_t*>(dV);
+  a.n_kvitems = p.n_kvitems;
+  a.H = p.prob.H;
+  a.N = p.prob.N;
+  a.nkv = p.nkv;
+  dkdv_kernel<<<dim3(p.n_kvitems, BH), 256, 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_attn_dq(p, Q, K, V, dO, lse, delta, row_ptr, col_idx, dQ, s);
 }

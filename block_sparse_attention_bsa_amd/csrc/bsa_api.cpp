@@ -108,7 +108,7 @@ int upload(const std::vector<T>& h, T** d) {
 void free_plan(bsa_plan* p) {
   if (!p) return;
   for (void* ptr : {(void*)p->qperm, (void*)p->qstart, (void*)p->kvperm, (void*)p->kvstart,
-                    (void*)p->items, (void*)p->qitem0, (void*)p->scale})
+                    (void*)p->items, (void*)p->qitem0, (void*)p->kvitems, (void*)p->scale})
     if (ptr) (void)hipFree(ptr);
   delete p;
 }
@@ -130,11 +130,13 @@ BwdWs bwd_ws_layout(const bsa_plan& p) {
   BwdWs w;
   const size_t BH = (size_t)p.prob.B * p.prob.H;
   const size_t cols = BH * p.nkv, rows = BH * p.nq;
+  w.nwords = (p.nkv + 31) / 32;
   w.delta = 0;
-  w.col_ptr = align_up(BH * p.prob.N * 4);
-  w.col_fill = w.col_ptr + align_up((cols + 1) * 4);
-  w.row_of = w.col_fill + align_up(cols * 4);
-  w.total = w.row_of + align_up(rows * p.nkv * 4);
+  w.bitmap = align_up(BH * p.prob.N * 4);
+  w.col_cnt = w.bitmap + align_up(rows * w.nwords * 4);
+  w.col_ptr = w.col_cnt + align_up(cols * 4);
+  w.row_idx = w.col_ptr + align_up((cols + 1) * 4);
+  w.total = w.row_idx + align_up(rows * p.nkv * 4);
   return w;
 }
 
@@ -213,8 +215,15 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
     }
   }
   p->h_qitem0.push_back((int32_t)(p->h_items.size() / 2));
-  for (int j = 0; j < p->nkv; ++j)
-    p->max_kvblk = std::max(p->max_kvblk, p->h_kvstart[j + 1] - p->h_kvstart[j]);
+  for (int j = 0; j < p->nkv; ++j) {
+    const int sz = p->h_kvstart[j + 1] - p->h_kvstart[j];
+    p->max_kvblk = std::max(p->max_kvblk, sz);
+    for (int off = 0; off < sz; off += kAttnRows) {
+      p->h_kvitems.push_back(j);
+      p->h_kvitems.push_back(off);
+    }
+  }
+  p->n_kvitems = (int)(p->h_kvitems.size() / 2);
   p->n_items = (int)(p->h_items.size() / 2);
   p->h_scale.resize(pr.H);
   for (int h = 0; h < pr.H; ++h)
@@ -227,6 +236,7 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
   if (upload(p->h_qperm, &p->qperm) || upload(p->h_qstart, &p->qstart) ||
       upload(p->h_kvperm, &p->kvperm) || upload(p->h_kvstart, &p->kvstart) ||
       upload(p->h_items, &p->items) || upload(p->h_qitem0, &p->qitem0) ||
+      upload(p->h_kvitems, &p->kvitems) ||
       upload(p->h_scale, &p->scale)) {
     free_plan(p);
     return fail(BSA_EHIP, "bsa_plan_create: device allocation or upload failed");

@@ -20,7 +20,7 @@ struct bsa_plan {
   int device = 0;
   int nq = 0, nkv = 0;
   int max_qblk = 0, max_kvblk = 0;
-  std::vector<int32_t> h_qperm, h_qstart, h_kvperm, h_kvstart, h_items, h_qitem0;
+  std::vector<int32_t> h_qperm, h_qstart, h_kvperm, h_kvstart, h_items, h_qitem0, h_kvitems;
   // Device copies (owned by the plan).
   int32_t* qperm = nullptr;
   int32_t* qstart = nullptr;
@@ -29,6 +29,8 @@ struct bsa_plan {
   int32_t* items = nullptr;   // attention work items: pairs (I, first row within block I)
   int32_t* qitem0 = nullptr;  // [nq + 1]: first work item of each query block
   int n_items = 0;
+  int32_t* kvitems = nullptr;  // backward work items: pairs (J, first token within block J)
+  int n_kvitems = 0;
   float* scale = nullptr;     // sigma_h, [H]
   std::vector<float> h_scale;
 };
@@ -43,7 +45,10 @@ struct SelectWs {
 SelectWs select_ws_layout(const bsa_plan& p);
 
 struct BwdWs {
-  size_t delta, col_ptr, col_fill, row_of, total;
+  // D = rowsum(dO * O) per token; CSR row bitmap; CSC (per (head, kv block) ascending q-block
+  // lists): per-column counts, column pointers, row ids.
+  size_t delta, bitmap, col_cnt, col_ptr, row_idx, total;
+  int nwords;
 };
 BwdWs bwd_ws_layout(const bsa_plan& p);
 
@@ -64,6 +69,11 @@ hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, cons
                            hipStream_t s);
 hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, float* M, void* ws,
                             hipStream_t s);
+// dQ of the backward pass (a mode of the forward MFMA kernel), given D and the forward's LSE.
+hipError_t launch_attn_dq(const bsa_plan& p, const void* Q, const void* K, const void* V,
+                          const void* dO, const float* lse, const float* delta,
+                          const int32_t* row_ptr, const int32_t* col_idx, void* dQ,
+                          hipStream_t s);
 hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
                            const void* O, const void* dO, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK,
