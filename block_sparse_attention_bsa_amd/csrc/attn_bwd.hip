@@ -27,11 +27,9 @@ constexpr int kStage = 2 * kTileBytes + 2 * kChunkQ * 4;  // Q, dO, lse2, D
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-typedef __attribute__((address_space(3))) char lds_char_t;
 
 __device__ __forceinline__ int swz(int row, int unit) { return (unit ^ (row & 15)) << 4; }
 
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // D[bh, n] = sum_d dO[bh, n, d] * O[bh, n, d]; 16 lanes per token row.
 __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ O,
@@ -152,9 +150,9 @@ struct QCursor {
 __device__ __forceinline__ void qcur_load(QCursor& c, const int32_t* __restrict__ row_idx,
                                           const int32_t* __restrict__ qstart) {
   if (c.slot < c.end) {
-    const int I = row_idx[c.slot];
-    c.base = qstart[I];
-    c.size = qstart[I + 1] - c.base;
+    const int I = ld_ro(row_idx + c.slot);
+    c.base = ld_ro(qstart + I);
+    c.size = ld_ro(qstart + I + 1) - c.base;
   } else {
     c.base = 0;
     c.size = 0;
@@ -192,13 +190,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
   const int total = a.n_kvitems * (int)gridDim.y;
   const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
   const int bh = lin / a.n_kvitems, item = lin % a.n_kvitems;
-  const int J = a.kvitems[2 * item], off = a.kvitems[2 * item + 1];
-  const int k0 = a.kvstart[J] + off;
-  const int nkvrows = min(128, a.kvstart[J + 1] - k0);
+  const int J = ld_ro(a.kvitems + 2 * item), off = ld_ro(a.kvitems + 2 * item + 1);
+  const int k0 = ld_ro(a.kvstart + J) + off;
+  const int nkvrows = min(128, ld_ro(a.kvstart + J + 1) - k0);
   const size_t head_off = (size_t)bh * a.N * D;
-  const float c2 = a.scale[bh % a.H] * kLog2e;
+  const float c2 = ld_ro(a.scale + bh % a.H) * kLog2e;
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
 
   // K and V fragments of this lane's kv token (B operands of S = Q K^T and dP = dO V^T).
@@ -226,8 +225,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
 
   const int64_t col = (int64_t)bh * a.nkv + J;
   QCursor cur;
-  cur.slot = a.col_ptr[col];
-  cur.end = a.col_ptr[col + 1];
+  cur.slot = ld_ro(a.col_ptr + col);
+  cur.end = ld_ro(a.col_ptr + col + 1);
   cur.sub = 0;
   qcur_load(cur, a.row_idx, a.qstart);
 
@@ -249,8 +248,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
       const int lunit = (lane & 15) ^ ((lrow0 + 4 * i) & 15);
       const size_t o = head_off + (size_t)ids[i] * D + 8 * lunit;
       char* dst = st + (16 * wave + 4 * i) * kRowBytes;
-      __builtin_amdgcn_global_load_lds(a.Q + o, dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.dO + o, dst + kTileBytes, 16, 0, 0);
+      lds_dma16(a.Q + o, dst);
+      lds_dma16(a.dO + o, dst + kTileBytes);
     }
     if (t < kChunkQ) {
       if (t < c.nv) {
@@ -283,7 +282,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
   }
   QChunk c1 = qcur_take(cur, a.row_idx, a.qstart);
   if (c1.nv > 0) chunk_ids(c1);
-  wait_vmem_all();
+  vmem_wait_all();
   __syncthreads();
 
   auto step = [&](const char* st, char* nx) {
@@ -293,34 +292,28 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
 
     const float* lse2 = reinterpret_cast<const float*>(st + 2 * kTileBytes);
     const float* dd = reinterpret_cast<const float*>(st + 2 * kTileBytes + kChunkQ * 4);
-    // S = Q K^T and dP = dO V^T for two 32-query M blocks (lane = kv token, regs = query).
-    f32x16_t sacc[2], dpacc[2];
-#pragma unroll
+    // One 32-query half (M block) at a time, to keep few registers live.
+#pragma unroll 1
     for (int mb = 0; mb < 2; ++mb) {
+      // S = Q K^T and dP = dO V^T (lane = kv token, registers = query).
       const int row = 32 * mb + l32;
       const char* qp = st + row * kRowBytes;
       const char* gp = st + kTileBytes + row * kRowBytes;
-      bf16x8_t qa[8], ga[8];
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        qa[kc] = *reinterpret_cast<const bf16x8_t*>(qp + swz(row, 2 * kc + hl));
-        ga[kc] = *reinterpret_cast<const bf16x8_t*>(gp + swz(row, 2 * kc + hl));
-      }
+      f32x16_t sacc, dpacc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        sacc[mb][e] = 0.f;
-        dpacc[mb][e] = 0.f;
+        sacc[e] = 0.f;
+        dpacc[e] = 0.f;
       }
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
-        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kc], kf[kc], sacc[mb], 0, 0, 0);
-        dpacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[kc], vf[kc], dpacc[mb], 0, 0, 0);
+        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qp + swz(row, 2 * kc + hl));
+        const bf16x8_t ga = *reinterpret_cast<const bf16x8_t*>(gp + swz(row, 2 * kc + hl));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kc], sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kc], dpacc, 0, 0, 0);
       }
-    }
-    // P = exp(sigma s - lse) and dS = P (dP - D), both rounded to bf16 (B operands below).
-    uint32_t pw[2][8], dw[2][8];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      // P = exp(sigma s - lse) and dS = P (dP - D), rounded to bf16 (B operands below).
+      uint32_t pw[8], dw[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int q = 32 * mb + 8 * g + 4 * hl;
@@ -331,44 +324,47 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int e = 4 * g + rr;
-          pr[rr] = kvvalid ? __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, -lv[rr])) : 0.f;
-          dsr[rr] = pr[rr] * (dpacc[mb][e] - dv4[rr]);
+          pr[rr] = kvvalid ? __builtin_amdgcn_exp2f(fmaf(sacc[e], c2, -lv[rr])) : 0.f;
+          dsr[rr] = pr[rr] * (dpacc[e] - dv4[rr]);
         }
-        pw[mb][2 * g] = pack_bf16x2(pr[0], pr[1]);
-        pw[mb][2 * g + 1] = pack_bf16x2(pr[2], pr[3]);
-        dw[mb][2 * g] = pack_bf16x2(dsr[0], dsr[1]);
-        dw[mb][2 * g + 1] = pack_bf16x2(dsr[2], dsr[3]);
+        pw[2 * g] = pack_bf16x2(pr[0], pr[1]);
+        pw[2 * g + 1] = pack_bf16x2(pr[2], pr[3]);
+        dw[2 * g] = pack_bf16x2(dsr[0], dsr[1]);
+        dw[2 * g + 1] = pack_bf16x2(dsr[2], dsr[3]);
       }
-    // dV^T += dO^T P and dK^T += Q^T dS (A operands from transposing reads of dO / Q).
+      // dV^T += dO^T P and dK^T += Q^T dS over this half's 32 queries (two 16-query k-steps);
+      // A operands from transposing reads of the dO / Q tiles.
 #pragma unroll
-    for (int dm = 0; dm < 4; ++dm) {
+      for (int dm = 0; dm < 4; ++dm) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
-        const int olo = row_lo * kRowBytes + swz(row_lo, 4 * dm + vunit_l) + vhalf_l;
-        const int ohi = row_hi * kRowBytes + swz(row_hi, 4 * dm + vunit_l) + vhalf_l;
-        const v4i16_t glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)((lds_char_t*)st + kTileBytes + olo));
-        const v4i16_t ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)((lds_char_t*)st + kTileBytes + ohi));
-        const v4i16_t qlo =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)((lds_char_t*)st + olo));
-        const v4i16_t qhi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)((lds_char_t*)st + ohi));
-        const uint2 g0 = __builtin_bit_cast(uint2, glo), g1 = __builtin_bit_cast(uint2, ghi);
-        const uint2 q0 = __builtin_bit_cast(uint2, qlo), q1 = __builtin_bit_cast(uint2, qhi);
-        const bf16x8_t gt = __builtin_bit_cast(bf16x8_t, make_uint4(g0.x, g0.y, g1.x, g1.y));
-        const bf16x8_t qt = __builtin_bit_cast(bf16x8_t, make_uint4(q0.x, q0.y, q1.x, q1.y));
-        const uint32_t* ps = &pw[kc >> 1][4 * (kc & 1)];
-        const uint32_t* ds = &dw[kc >> 1][4 * (kc & 1)];
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(ps[0], ps[1], ps[2], ps[3]));
-        const bf16x8_t db = __builtin_bit_cast(bf16x8_t, make_uint4(ds[0], ds[1], ds[2], ds[3]));
-        dv[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt, pb, dv[dm], 0, 0, 0);
-        dk[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, db, dk[dm], 0, 0, 0);
+        for (int kk = 0; kk < 2; ++kk) {
+          const int kc = 2 * mb + kk;
+          const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
+          const int olo = row_lo * kRowBytes + swz(row_lo, 4 * dm + vunit_l) + vhalf_l;
+          const int ohi = row_hi * kRowBytes + swz(row_hi, 4 * dm + vunit_l) + vhalf_l;
+          const v4i16_t glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)((lds_char_t*)st + kTileBytes + olo));
+          const v4i16_t ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)((lds_char_t*)st + kTileBytes + ohi));
+          const v4i16_t qlo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)((lds_char_t*)st + olo));
+          const v4i16_t qhi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)((lds_char_t*)st + ohi));
+          const uint2 g0 = __builtin_bit_cast(uint2, glo), g1 = __builtin_bit_cast(uint2, ghi);
+          const uint2 q0 = __builtin_bit_cast(uint2, qlo), q1 = __builtin_bit_cast(uint2, qhi);
+          const bf16x8_t gt = __builtin_bit_cast(bf16x8_t, make_uint4(g0.x, g0.y, g1.x, g1.y));
+          const bf16x8_t qt = __builtin_bit_cast(bf16x8_t, make_uint4(q0.x, q0.y, q1.x, q1.y));
+          const bf16x8_t pb = __builtin_bit_cast(
+              bf16x8_t, make_uint4(pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]));
+          const bf16x8_t db = __builtin_bit_cast(
+              bf16x8_t, make_uint4(dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]));
+          dv[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt, pb, dv[dm], 0, 0, 0);
+          dk[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, db, dk[dm], 0, 0, 0);
+        }
       }
     }
     if (c1.nv > 0) chunk_finish(nx);
-    wait_vmem_all();
+    vmem_wait_all();
     __syncthreads();
     c0 = c1;
     c1 = c2n;

@@ -39,9 +39,9 @@ template <bool kDense>
 __device__ __forceinline__ void cursor_load(Cursor& c, const int32_t* __restrict__ col_idx,
                                             const int32_t* __restrict__ kvstart) {
   if (c.slot < c.end) {
-    c.J = kDense ? c.slot : col_idx[c.slot];
-    c.base = kvstart[c.J];
-    c.size = kvstart[c.J + 1] - c.base;
+    c.J = kDense ? c.slot : ld_ro(col_idx + c.slot);
+    c.base = ld_ro(kvstart + c.J);
+    c.size = ld_ro(kvstart + c.J + 1) - c.base;
   } else {
     c.J = 0;
     c.base = 0;
@@ -94,15 +94,11 @@ constexpr float kRescaleSlack = 8.f;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-typedef __attribute__((address_space(3))) char lds_char_t;
 
 // K and V tiles are row-major in LDS (one 256-byte row per kv token); the 16-byte units of a row
 // are XOR-swizzled by the row index so that the MFMA operand reads hit distinct banks.
 __device__ __forceinline__ int swz(int row, int unit) { return (unit ^ (row & 15)) << 4; }
 
-__device__ __forceinline__ void wait_vmem_all() {
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt left unconstrained
-}
 
 struct MfmaArgs {
   const uint16_t* Q;
@@ -138,14 +134,15 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   const int total = n_items * (int)gridDim.y;
   const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
   const int bh = lin / n_items, item = lin % n_items;
-  const int I = a.items[2 * item], off = a.items[2 * item + 1];
-  const int q0 = a.qstart[I] + off;
-  const int nrows = min(128, a.qstart[I + 1] - q0);
+  const int I = ld_ro(a.items + 2 * item), off = ld_ro(a.items + 2 * item + 1);
+  const int q0 = ld_ro(a.qstart + I) + off;
+  const int nrows = min(128, ld_ro(a.qstart + I + 1) - q0);
   const int64_t r = (int64_t)bh * a.nq + I;
   const size_t head_off = (size_t)bh * a.N * D;
-  const float c2 = a.scale[bh % a.H] * kLog2e;  // sigma_h > 0 (checked at plan creation)
+  const float c2 = ld_ro(a.scale + bh % a.H) * kLog2e;  // sigma_h > 0 (checked at plan creation)
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
 
   // Q fragments (B operand of S^T = K Q^T): query row 32*wave + l32, d = 16*kc + 8*hl .. +8.
@@ -198,18 +195,20 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   const int lchunk = wave >> 1;
 
   Cursor cur;
-  cur.slot = kDense ? 0 : a.row_ptr[r];
-  cur.end = kDense ? a.nkv : a.row_ptr[r + 1];
+  cur.slot = kDense ? 0 : ld_ro(a.row_ptr + r);
+  cur.end = kDense ? a.nkv : ld_ro(a.row_ptr + r + 1);
   cur.sub = 0;
   cursor_load<kDense>(cur, a.col_idx, a.kvstart);
 
   auto tile_ids = [&](Chunk ca, Chunk cb, int* ids) {
-    const Chunk c = lchunk ? cb : ca;
+    // Branch-free: an empty second chunk repeats the first chunk's first token.
+    const int nvc = lchunk ? cb.nv : ca.nv;
+    const int base = nvc > 0 ? (lchunk ? cb.pos : ca.pos) : ca.pos;
+    const int lim = nvc > 0 ? nvc : 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = (lrow0 + 4 * i) & 31;
-      const int pos = c.nv > 0 ? c.pos + (rr < c.nv ? rr : 0) : ca.pos;
-      ids[i] = a.kvperm[pos];
+      ids[i] = a.kvperm[base + (rr < lim ? rr : 0)];
     }
   };
   auto tile_issue = [&](const int* ids, char* st) {
@@ -218,8 +217,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
       const int lunit = (lane & 15) ^ ((lrow0 + 4 * i) & 15);  // logical unit at this position
       const size_t o = head_off + (size_t)ids[i] * D + 8 * lunit;
       char* dst = st + (16 * wave + 4 * i) * kRowBytes;
-      __builtin_amdgcn_global_load_lds(a.K + o, dst, 16, 0, 0);
-      if constexpr (kNeedV) __builtin_amdgcn_global_load_lds(a.V + o, dst + kTileBytes, 16, 0, 0);
+      lds_dma16(a.K + o, dst);
+      if constexpr (kNeedV) lds_dma16(a.V + o, dst + kTileBytes);
     }
   };
 
@@ -234,7 +233,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   Chunk a1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
   Chunk b1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
   if (a1.nv > 0) tile_ids(a1, b1, ids);
-  wait_vmem_all();
+  vmem_wait_all();
   __syncthreads();
 
   // V transposed reads: row 16*kc + 8*sh + 4*hl + (lane%16)/4, column 32*dm + 16*((lane/16)&1)
@@ -427,7 +426,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         }
       }
     }
-    wait_vmem_all();
+    vmem_wait_all();
     __syncthreads();
     a0 = a1;
     b0 = b1;

@@ -78,3 +78,30 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
   return v;
 }
+
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane i of the
+// wavefront writes LDS bytes [lds_base + 16 i, +16). lds_base must be wave-uniform. Issued from
+// inline assembly so that the compiler does not order later LDS reads of *other* buffers behind
+// it; the caller waits for it explicitly (vmem_wait_all) and then synchronises the workgroup
+// before any wavefront reads the destination.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, char* lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((lds_char_t*)lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(m0v)
+               : "m0");
+}
+
+// Wait until every vector memory operation of this wavefront has completed (vmcnt(0); the
+// other counters unconstrained).
+__device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Load from memory that no kernel writes while it runs (plan descriptors, CSR, scales) through
+// the constant address space, so that wave-uniform indices become scalar loads.
+template <typename T>
+__device__ __forceinline__ T ld_ro(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
