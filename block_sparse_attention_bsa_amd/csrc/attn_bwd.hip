@@ -28,7 +28,6 @@ constexpr int kStage = 2 * kTileBytes + 2 * kChunkQ * 4;  // Q, dO, lse2, D
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-__device__ __forceinline__ int swz(int row, int unit) { return (unit ^ (row & 15)) << 4; }
 
 
 // D[bh, n] = sum_d dO[bh, n, d] * O[bh, n, d]; 16 lanes per token row.
@@ -245,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
   auto chunk_issue = [&](QChunk c, char* st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int lunit = (lane & 15) ^ ((lrow0 + 4 * i) & 15);
+      const int lunit = (lane & 15) ^ lds_key(lrow0 + 4 * i);
       const size_t o = head_off + (size_t)ids[i] * D + 8 * lunit;
       char* dst = st + (16 * wave + 4 * i) * kRowBytes;
       lds_dma16(a.Q + o, dst);
@@ -307,8 +306,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
       }
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
-        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qp + swz(row, 2 * kc + hl));
-        const bf16x8_t ga = *reinterpret_cast<const bf16x8_t*>(gp + swz(row, 2 * kc + hl));
+        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qp + lds_swz(row, 2 * kc + hl));
+        const bf16x8_t ga = *reinterpret_cast<const bf16x8_t*>(gp + lds_swz(row, 2 * kc + hl));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kc], sacc, 0, 0, 0);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kc], dpacc, 0, 0, 0);
       }
@@ -340,8 +339,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
         for (int kk = 0; kk < 2; ++kk) {
           const int kc = 2 * mb + kk;
           const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
-          const int olo = row_lo * kRowBytes + swz(row_lo, 4 * dm + vunit_l) + vhalf_l;
-          const int ohi = row_hi * kRowBytes + swz(row_hi, 4 * dm + vunit_l) + vhalf_l;
+          const int olo = row_lo * kRowBytes + lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l;
+          const int ohi = row_hi * kRowBytes + lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l;
           const v4i16_t glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_v4i16_t*)((lds_char_t*)st + kTileBytes + olo));
           const v4i16_t ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(

@@ -16,9 +16,9 @@
 //
 // MFMA path. One workgroup = 4 wavefronts = 128 query rows of one query block. Per iteration a
 // 64-token tile (two chunks) of K (and V for the forward pass) is copied global -> LDS with direct
-// 16-byte loads (no staging registers) into one of two stages while the other stage is
-// computed; rows are 256 bytes with the 16-byte units XOR-swizzled by row, so that the MFMA
-// operand reads are conflict free. Each wavefront computes S^T = K Q^T for its 32 queries with
+// 16-byte loads (no staging registers) into one stage while another stage is computed; rows are
+// 256 bytes with the 16-byte units XOR-swizzled by a per-row key, so that the MFMA operand reads
+// (straight 16-byte and transposing 8-byte) are conflict free. Each wavefront computes S^T = K Q^T for its 32 queries with
 // v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B operand), so each lane holds 16 scores
 // of a single query: the row max needs one cross-half exchange and the row sum none. P^T is
 // converted to bf16 in registers and is directly the B operand of O^T += V^T P^T, whose A operand
@@ -85,6 +85,11 @@ __device__ __forceinline__ Chunk take_chunk(Cursor& c, const int32_t* __restrict
 // backward pass over the same CSR (S and dP recomputed per tile).
 enum Mode { kFwd = 0, kLse = 1, kMass = 2, kDq = 3 };
 
+#ifndef BSA_FWD_STAGES
+#define BSA_FWD_STAGES 2
+#endif
+constexpr int kFwdStages = BSA_FWD_STAGES;
+
 constexpr int kTileKV = 64;                    // kv tokens per iteration (two chunks)
 constexpr int kRowBytes = 256;                 // one token row of d = 128 bf16
 constexpr int kTileBytes = kTileKV * kRowBytes;
@@ -96,9 +101,7 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 // K and V tiles are row-major in LDS (one 256-byte row per kv token); the 16-byte units of a row
-// are XOR-swizzled by the row index so that the MFMA operand reads hit distinct banks.
-__device__ __forceinline__ int swz(int row, int unit) { return (unit ^ (row & 15)) << 4; }
-
+// are XOR-swizzled with lds_key(row) so that the MFMA operand reads hit distinct banks.
 
 struct MfmaArgs {
   const uint16_t* Q;
@@ -121,14 +124,19 @@ struct MfmaArgs {
   int n_items, H, N, nq, nkv;
 };
 
-template <int MODE>
+// NST LDS stages: tile t is computed while tiles t+1 .. t+NST-1 stream in.
+template <int MODE, int NST>
 __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
+  static_assert(NST == 2 || NST == 3, "two or three stages");
   constexpr int D = 128;
   constexpr bool kDense = MODE == kLse || MODE == kMass;  // all kv blocks, not a CSR row
   constexpr bool kNeedV = MODE == kFwd || MODE == kDq;
   constexpr int kStage = kNeedV ? 2 * kTileBytes : kTileBytes;
-  __shared__ __attribute__((aligned(1024))) char lds_a[kStage];
-  __shared__ __attribute__((aligned(1024))) char lds_b[kStage];
+  constexpr int kCopiesPerTile = kNeedV ? 8 : 4;  // direct copies one wavefront issues per tile
+  __shared__ __attribute__((aligned(1024))) char lds[NST * kStage];
+  char* const lds_a = lds;
+  char* const lds_b = lds + kStage;
+  char* const lds_c = lds + (NST - 1) * kStage;
 
   const int n_items = a.n_items;
   const int total = n_items * (int)gridDim.y;
@@ -180,6 +188,9 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
       for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f, lb_run = 0.f;
+  bf16x8_t ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
   // kMass: log2-domain lse of this lane's query (+inf for padding rows, so they add nothing)
   float nlse2 = 0.f, blk_acc = 0.f;
   float dq_d = 0.f;  // kDq: this lane's D
@@ -188,11 +199,12 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   if constexpr (MODE == kDq) dq_d = qvalid ? a.delta[(size_t)bh * a.N + qtok] : 0.f;
 
   // Loader role: wave w fills tile rows 16w + 4i + lane/16 (i = 0..3), 16-byte unit lane%16 of
-  // the swizzled row, for K (and V), with direct global->LDS loads (no staging registers).
-  // Rows past a chunk's end repeat the chunk's first token: their scores are masked and their
-  // probabilities are exactly 0, so any finite row will do.
-  const int lrow0 = 16 * wave + (lane >> 4);
-  const int lchunk = wave >> 1;
+  // the swizzled row, for K (and V), with direct global->LDS copies (no staging registers).
+  // The 16 token ids of a wavefront's rows are read with one scalar load (perm is padded by 32
+  // entries); rows past a chunk's end repeat the chunk's first token: their scores are masked
+  // and their probabilities are exactly 0, so any finite row will do. With scalar ids the
+  // copies are the only vector memory operations in the loop, so their waits are exact.
+  const int lchunk = wave >> 1, loff = 16 * (wave & 1), lgrp = lane >> 4;
 
   Cursor cur;
   cur.slot = kDense ? 0 : ld_ro(a.row_ptr + r);
@@ -200,39 +212,56 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   cur.sub = 0;
   cursor_load<kDense>(cur, a.col_idx, a.kvstart);
 
-  auto tile_ids = [&](Chunk ca, Chunk cb, int* ids) {
-    // Branch-free: an empty second chunk repeats the first chunk's first token.
+  // This lane's token for each of its 4 tile rows.
+  auto tile_ids = [&](Chunk ca, Chunk cb) {
     const int nvc = lchunk ? cb.nv : ca.nv;
     const int base = nvc > 0 ? (lchunk ? cb.pos : ca.pos) : ca.pos;
     const int lim = nvc > 0 ? nvc : 1;
+    const int first = ld_ro(a.kvperm + base);
+    int4 d;
+    int* dv = &d.x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = (lrow0 + 4 * i) & 31;
-      ids[i] = a.kvperm[base + (rr < lim ? rr : 0)];
+      int v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int jj = loff + 4 * i + j;
+        const int id = ld_ro(a.kvperm + base + jj);  // in bounds: perm is padded
+        v[j] = jj < lim ? id : first;
+      }
+      int tok = v[0];
+      tok = lgrp == 1 ? v[1] : tok;
+      tok = lgrp == 2 ? v[2] : tok;
+      tok = lgrp == 3 ? v[3] : tok;
+      dv[i] = tok;
     }
+    return d;
   };
-  auto tile_issue = [&](const int* ids, char* st) {
+  auto tile_issue = [&](int4 d, char* st) {
+    const int toks[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int lunit = (lane & 15) ^ ((lrow0 + 4 * i) & 15);  // logical unit at this position
-      const size_t o = head_off + (size_t)ids[i] * D + 8 * lunit;
+      const int row = 16 * wave + 4 * i + lgrp;
+      const int lunit = (lane & 15) ^ lds_key(row);  // logical unit at this position
+      const size_t o = head_off + (size_t)toks[i] * D + 8 * lunit;
       char* dst = st + (16 * wave + 4 * i) * kRowBytes;
       lds_dma16(a.K + o, dst);
       if constexpr (kNeedV) lds_dma16(a.V + o, dst + kTileBytes);
     }
   };
 
-  // Pipeline: one stage holds tile t, tile t+1 streams into the other, ids hold tile t+2.
-  Chunk a0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-  Chunk b0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-  int ids[4];
-  if (a0.nv > 0) {
-    tile_ids(a0, b0, ids);
-    tile_issue(ids, lds_a);
+  // Pipeline: tiles t .. t+NST-2 are in LDS or in flight; `ids` holds tile t+NST-1's token ids.
+  Chunk ca[NST], cb[NST];
+  int4 ids = make_int4(0, 0, 0, 0);
+#pragma unroll
+  for (int k = 0; k < NST - 1; ++k) {
+    ca[k] = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+    cb[k] = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+    if (ca[k].nv > 0) tile_issue(tile_ids(ca[k], cb[k]), k == 0 ? lds_a : lds_b);
   }
-  Chunk a1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-  Chunk b1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-  if (a1.nv > 0) tile_ids(a1, b1, ids);
+  ca[NST - 1] = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+  cb[NST - 1] = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+  if (ca[NST - 1].nv > 0) ids = tile_ids(ca[NST - 1], cb[NST - 1]);
   vmem_wait_all();
   __syncthreads();
 
@@ -242,13 +271,17 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   const int vunit_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int vhalf_l = 8 * (lane & 1);
 
-  // One tile: compute from stage `st` while the next tile streams into `nx`. The two stages are
-  // distinct arrays so that the compiler can tell the streamed writes never alias the reads.
+  // One tile: compute tile t from stage `st` while tile t+NST-1 is issued into `nx` (the stage
+  // tile t-1 used). The stages are distinct arrays.
   auto step = [&](const char* st, char* nx) {
-    if (a1.nv > 0) tile_issue(ids, nx);
-    const Chunk a2 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-    const Chunk b2 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-    if (a2.nv > 0) tile_ids(a2, b2, ids);
+    const Chunk a0 = ca[0], b0 = cb[0];
+    const Chunk an = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+    const Chunk bn = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+    int4 nids = make_int4(0, 0, 0, 0);
+    if (an.nv > 0) nids = tile_ids(an, bn);
+    const bool issued = ca[NST - 1].nv > 0;
+    if (issued) tile_issue(ids, nx);
+    ids = nids;
 
     // S^T for this wave's 32 queries: two 32-kv M blocks (raw, unscaled scores).
     f32x16_t sacc[2];
@@ -259,7 +292,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
       bf16x8_t kf[8];
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc)
-        kf[kc] = *reinterpret_cast<const bf16x8_t*>(kp + swz(row, 2 * kc + hl));
+        kf[kc] = *reinterpret_cast<const bf16x8_t*>(kp + lds_swz(row, 2 * kc + hl));
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[mb][e] = 0.f;
 #pragma unroll
@@ -286,7 +319,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         bf16x8_t vfr[8];
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc)
-          vfr[kc] = *reinterpret_cast<const bf16x8_t*>(vp + swz(row, 2 * kc + hl));
+          vfr[kc] = *reinterpret_cast<const bf16x8_t*>(vp + lds_swz(row, 2 * kc + hl));
 #pragma unroll
         for (int e = 0; e < 16; ++e) dpacc[mb][e] = 0.f;
 #pragma unroll
@@ -312,10 +345,10 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
           const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
           const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_v4i16_t*)((lds_char_t*)st + row_lo * kRowBytes +
-                             swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
+                             lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
           const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_v4i16_t*)((lds_char_t*)st + row_hi * kRowBytes +
-                             swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
+                             lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
           const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
           kt[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
         }
@@ -349,17 +382,28 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         }
       }
     } else {
-      float mx0 = fmaxf(sacc[0][0], sacc[0][1]), mx1 = fmaxf(sacc[1][0], sacc[1][1]);
+      // tt = c2 * s - m_run is the base-2 exponent of this tile's weights. The running max is
+      // raised (and O, l rescaled) only when max tt exceeds the slack: on the first tile (m_run
+      // = -inf makes tt +inf or NaN, and the test below is written to catch both) and rarely
+      // after. Taking the max over tt (outputs of an fma) rather than the raw matrix-core
+      // results lets the compiler skip NaN canonicalisation of every score.
+      float tt[2][16];
 #pragma unroll
-      for (int e = 2; e < 16; e += 2) {
-        mx0 = fmaxf(mx0, fmaxf(sacc[0][e], sacc[0][e + 1]));
-        mx1 = fmaxf(mx1, fmaxf(sacc[1][e], sacc[1][e + 1]));
-      }
-      float mx = fmaxf(mx0, mx1);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-      const bool grow = mx > m_run + kRescaleSlack;
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tt[mb][e] = fmaf(sacc[mb][e], c2, -m_run);
+      float mx = fmaxf(tt[0][0], tt[0][1]);
+#pragma unroll
+      for (int i = 2; i < 32; i += 2) mx = fmaxf(mx, fmaxf(tt[i >> 4][i & 15], tt[i >> 4][(i & 15) + 1]));
+      mx = pair_max(mx);
+      const bool grow = !(mx <= kRescaleSlack);
       if (__ballot(grow) != 0) {
-        const float m_new = grow ? mx : m_run;
+        // exact tile max of c2 * s (every tile has at least one unmasked kv row)
+        float sm = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+        for (int e = 1; e < 16; ++e) sm = fmaxf(sm, fmaxf(sacc[0][e], sacc[1][e]));
+        sm = pair_max(sm) * c2;
+        const float m_new = grow ? sm : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
         lb_run *= alpha;
@@ -370,29 +414,29 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
             for (int e = 0; e < 16; ++e) oacc[dm][e] *= alpha;
         }
         m_run = m_new;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) tt[mb][e] = fmaf(sacc[mb][e], c2, -m_run);
       }
-      const float nm = -m_run;
-      float ls[4] = {0.f, 0.f, 0.f, 0.f}, lb[2] = {0.f, 0.f};
+      float ls[4];
       uint32_t pw[2][8];  // P rounded to bf16, two per word (the B operand of the PV product)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nm));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e + 1], c2, nm));
-          ls[e & 3] += p0;
-          ls[(e & 3) + 1] += p1;
-          if constexpr (MODE == kFwd) {
-            // O is normalised by the sum of the same bf16-rounded weights the PV product uses
-            // (an exactly normalised combination); the LSE keeps the fp32 sum.
-            const uint32_t w = pack_bf16x2(p0, p1);
-            pw[mb][e >> 1] = w;
-            lb[0] += bf16_lo(w);
-            lb[1] += bf16_hi(w);
+          const float p0 = __builtin_amdgcn_exp2f(tt[mb][e]);
+          const float p1 = __builtin_amdgcn_exp2f(tt[mb][e + 1]);
+          if (mb == 0 && e < 4) {
+            ls[e] = p0;
+            ls[e + 1] = p1;
+          } else {
+            ls[e & 3] += p0;
+            ls[(e & 3) + 1] += p1;
           }
+          if constexpr (MODE == kFwd) pw[mb][e >> 1] = pack_bf16x2(p0, p1);
         }
       l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      if constexpr (MODE == kFwd) lb_run += lb[0] + lb[1];
       bf16x8_t pb[4];
       if constexpr (MODE == kFwd) {
 #pragma unroll
@@ -400,6 +444,17 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
           const uint32_t* src = &pw[kc >> 1][4 * (kc & 1)];
           pb[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
         }
+        // O is normalised by the sum of the same bf16-rounded weights the PV product uses (an
+        // exactly normalised combination); the LSE keeps the fp32 sum. The bf16 row sums come
+        // from the matrix cores: (all-ones 32 x 16) x P^T gives every row the column sums, so
+        // each lane receives the full 64-key sum of its query.
+        f32x16_t rs;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) rs[e] = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          rs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kc], rs, 0, 0, 0);
+        lb_run += rs[0];
       }
       if constexpr (MODE == kFwd) {
         // O^T += V^T P^T; each V^T fragment is two transposing 8-byte LDS reads.
@@ -412,10 +467,10 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
             const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
             const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_v4i16_t*)((lds_char_t*)vt + row_lo * kRowBytes +
-                               swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
+                               lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
             const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_v4i16_t*)((lds_char_t*)vt + row_hi * kRowBytes +
-                               swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
+                               lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
             const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
             vf[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
           }
@@ -426,18 +481,38 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         }
       }
     }
-    vmem_wait_all();
+    // Tile t+1 must be in LDS before the barrier; with three stages tile t+2's copies (the most
+    // recent ones) may stay in flight. kMass issues global stores after the copies, so it
+    // waits for everything.
+    if (NST == 3 && MODE != kMass && issued)
+      vmem_wait_keep<kCopiesPerTile>();
+    else
+      vmem_wait_all();
     __syncthreads();
-    a0 = a1;
-    b0 = b1;
-    a1 = a2;
-    b1 = b2;
+#pragma unroll
+    for (int k = 0; k < NST - 1; ++k) {
+      ca[k] = ca[k + 1];
+      cb[k] = cb[k + 1];
+    }
+    ca[NST - 1] = an;
+    cb[NST - 1] = bn;
   };
-  while (true) {
-    if (a0.nv <= 0) break;
-    step(lds_a, lds_b);
-    if (a0.nv <= 0) break;
-    step(lds_b, lds_a);
+  if constexpr (NST == 2) {
+    while (true) {
+      if (ca[0].nv <= 0) break;
+      step(lds_a, lds_b);
+      if (ca[0].nv <= 0) break;
+      step(lds_b, lds_a);
+    }
+  } else {
+    while (true) {
+      if (ca[0].nv <= 0) break;
+      step(lds_a, lds_c);
+      if (ca[0].nv <= 0) break;
+      step(lds_b, lds_a);
+      if (ca[0].nv <= 0) break;
+      step(lds_c, lds_b);
+    }
   }
 
   if constexpr (MODE == kMass) return;
@@ -459,8 +534,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
   if constexpr (MODE == kFwd) {
-    const float lb_tot = lb_run + __shfl_xor(lb_run, 32, 64);
-    const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
+    const float inv = lb_run > 0.f ? 1.f / lb_run : 0.f;  // full sum in both halves
     uint16_t* op = a.O + head_off + (size_t)qtok * D;
 #pragma unroll
     for (int dm = 0; dm < 4; ++dm)
@@ -480,11 +554,11 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
 // fragments as well and runs at one wave per SIMD with the full register file.
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void attn_mfma_d128(const MfmaArgs a) {
-  attn_mfma_body<MODE>(a);
+  attn_mfma_body<MODE, kFwdStages>(a);
 }
 
 __global__ __launch_bounds__(256, 1) void attn_dq_d128(const MfmaArgs a) {
-  attn_mfma_body<kDq>(a);
+  attn_mfma_body<kDq, kFwdStages>(a);
 }
 
 // M[bh, I, J] = (sum over I's work items and the 4 waves of the block sums) / |I|, in fp64 and in

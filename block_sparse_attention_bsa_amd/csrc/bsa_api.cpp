@@ -233,8 +233,13 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
     free_plan(p);
     return fail(BSA_EHIP, "bsa_plan_create: no usable HIP device");
   }
-  if (upload(p->h_qperm, &p->qperm) || upload(p->h_qstart, &p->qstart) ||
-      upload(p->h_kvperm, &p->kvperm) || upload(p->h_kvstart, &p->kvstart) ||
+  // perm arrays carry 32 padding entries (token 0) so that fixed-size scalar reads of a chunk's
+  // token ids never leave the allocation.
+  std::vector<int32_t> qperm_pad(p->h_qperm), kvperm_pad(p->h_kvperm);
+  qperm_pad.resize(qperm_pad.size() + 32, 0);
+  kvperm_pad.resize(kvperm_pad.size() + 32, 0);
+  if (upload(qperm_pad, &p->qperm) || upload(p->h_qstart, &p->qstart) ||
+      upload(kvperm_pad, &p->kvperm) || upload(p->h_kvstart, &p->kvstart) ||
       upload(p->h_items, &p->items) || upload(p->h_qitem0, &p->qitem0) ||
       upload(p->h_kvitems, &p->kvitems) ||
       upload(p->h_scale, &p->scale)) {

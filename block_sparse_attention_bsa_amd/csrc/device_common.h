@@ -61,6 +61,21 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
   return v;
 }
 
+// max / sum of the values held by lanes l and l ^ 32 (gfx950 v_permlane32_swap exchanges the
+// two 32-lane halves between two registers; combining both outputs does not depend on which
+// output holds which half).
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
@@ -81,6 +96,18 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 typedef __attribute__((address_space(3))) char lds_char_t;
 
+// LDS tiles of bf16 rows with d = 128 (256 bytes, sixteen 16-byte units): logical unit u of row r
+// is stored at unit u ^ lds_key(r). The key (a bijection on units for every row) makes both read
+// patterns of the matrix-core kernels bank-conflict free, for 32 or 64 four-byte banks:
+//   16-byte reads of one unit from 8 (16) consecutive aligned rows need key mod 8 (16) distinct;
+//   transposing 8-byte reads of units {4m, 4m+1} (4m .. 4m+3) from 4 consecutive aligned rows
+//   need bits 1-2 (2-3) of the key distinct over those rows.
+// Rows 0..3 take keys 0, 10, 6, 12; bit 2 of the row flips key bit 0 and bit 3 flips key bit 3.
+__device__ __forceinline__ int lds_key(int row) {
+  return ((0xC6A0 >> (4 * (row & 3))) & 15) ^ ((row >> 2) & 1) ^ (row & 8);
+}
+__device__ __forceinline__ int lds_swz(int row, int unit) { return (unit ^ lds_key(row)) << 4; }
+
 // Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane i of the
 // wavefront writes LDS bytes [lds_base + 16 i, +16). lds_base must be wave-uniform. Issued from
 // inline assembly so that the compiler does not order later LDS reads of *other* buffers behind
@@ -92,12 +119,20 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, char* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gsrc), "s"(m0v)
-               : "m0");
+               : "m0", "memory");
 }
 
 // Wait until every vector memory operation of this wavefront has completed (vmcnt(0); the
 // other counters unconstrained).
 __device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Wait until at most N vector memory operations of this wavefront are outstanding (they
+// complete in issue order, so everything older than the N most recent has completed).
+template <int N>
+__device__ __forceinline__ void vmem_wait_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Load from memory that no kernel writes while it runs (plan descriptors, CSR, scales) through
 // the constant address space, so that wave-uniform indices become scalar loads.
