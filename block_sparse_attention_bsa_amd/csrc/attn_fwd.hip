@@ -151,6 +151,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const bool active = 32 * wave < nrows;  // wave-uniform
   const int l32 = lane & 31, hl = lane >> 5;
 
   // Q fragments (B operand of S^T = K Q^T): query row 32*wave + l32, d = 16*kc + 8*hl .. +8.
@@ -283,201 +284,206 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     if (issued) tile_issue(ids, nx);
     ids = nids;
 
-    // S^T for this wave's 32 queries: two 32-kv M blocks (raw, unscaled scores).
-    f32x16_t sacc[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int row = 32 * mb + l32;
-      const char* kp = st + row * kRowBytes;
-      bf16x8_t kf[8];
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        kf[kc] = *reinterpret_cast<const bf16x8_t*>(kp + lds_swz(row, 2 * kc + hl));
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[mb][e] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], sacc[mb], 0, 0, 0);
-    }
-    if (a0.nv < 32 || b0.nv < 32) {  // partial chunk(s): mask padded kv rows
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int nv = mb ? b0.nv : a0.nv;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (8 * (e >> 2) + 4 * hl + (e & 3) >= nv) sacc[mb][e] = -INFINITY;
-      }
-    }
-
-    if constexpr (MODE == kDq) {
-      // dP^T = V dO^T (A: V rows from LDS, like K), then dS^T = P^T * (dP^T - D) in bf16.
-      f32x16_t dpacc[2];
+    // A wavefront whose 32 query rows all lie past the end of the query block (ragged blocks at
+    // the grid edge) only takes part in the copies and barriers, leaving its SIMD to the other
+    // resident workgroup.
+    if (active) {
+      // S^T for this wave's 32 queries: two 32-kv M blocks (raw, unscaled scores).
+      f32x16_t sacc[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int row = 32 * mb + l32;
-        const char* vp = st + kTileBytes + row * kRowBytes;
-        bf16x8_t vfr[8];
+        const char* kp = st + row * kRowBytes;
+        bf16x8_t kf[8];
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc)
-          vfr[kc] = *reinterpret_cast<const bf16x8_t*>(vp + lds_swz(row, 2 * kc + hl));
+          kf[kc] = *reinterpret_cast<const bf16x8_t*>(kp + lds_swz(row, 2 * kc + hl));
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dpacc[mb][e] = 0.f;
+        for (int e = 0; e < 16; ++e) sacc[mb][e] = 0.f;
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc)
-          dpacc[mb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[kc], dof[kc], dpacc[mb], 0, 0, 0);
+          sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], sacc[mb], 0, 0, 0);
       }
-      uint32_t dw[2][8];
+      if (a0.nv < 32 || b0.nv < 32) {  // partial chunk(s): mask padded kv rows
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb) {
+          const int nv = mb ? b0.nv : a0.nv;
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nlse2));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e + 1], c2, nlse2));
-          dw[mb][e >> 1] = pack_bf16x2(p0 * (dpacc[mb][e] - dq_d), p1 * (dpacc[mb][e + 1] - dq_d));
-        }
-      // dQ^T += K^T dS^T; each K^T fragment is two transposing 8-byte reads of the K tile.
-#pragma unroll
-      for (int dm = 0; dm < 4; ++dm) {
-        bf16x8_t kt[4];
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
-          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)((lds_char_t*)st + row_lo * kRowBytes +
-                             lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
-          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)((lds_char_t*)st + row_hi * kRowBytes +
-                             lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
-          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-          kt[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
-        }
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const uint32_t* src = &dw[kc >> 1][4 * (kc & 1)];
-          const bf16x8_t dsb =
-              __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
-          oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[kc], dsb, oacc[dm], 0, 0, 0);
+          for (int e = 0; e < 16; ++e)
+            if (8 * (e >> 2) + 4 * hl + (e & 3) >= nv) sacc[mb][e] = -INFINITY;
         }
       }
-    } else if constexpr (MODE == kMass) {
-      // Block sums of exp(sigma q.k - lse): one chunk per M block, flushed at block ends.
+
+      if constexpr (MODE == kDq) {
+        // dP^T = V dO^T (A: V rows from LDS, like K), then dS^T = P^T * (dP^T - D) in bf16.
+        f32x16_t dpacc[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const Chunk& c = mb ? b0 : a0;
-        if (c.nv > 0) {
-          float cs0 = 0.f, cs1 = 0.f;
+        for (int mb = 0; mb < 2; ++mb) {
+          const int row = 32 * mb + l32;
+          const char* vp = st + kTileBytes + row * kRowBytes;
+          bf16x8_t vfr[8];
 #pragma unroll
-          for (int e = 0; e < 16; e += 2) {
-            cs0 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nlse2));
-            cs1 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e + 1], c2, nlse2));
-          }
-          blk_acc += cs0 + cs1;
-          if (c.last) {
-            const float tot = wave_sum_f32(blk_acc);
-            if (lane == 0)
-              a.part[(((size_t)bh * n_items + item) * 4 + wave) * a.nkv + c.J] = tot;
-            blk_acc = 0.f;
-          }
+          for (int kc = 0; kc < 8; ++kc)
+            vfr[kc] = *reinterpret_cast<const bf16x8_t*>(vp + lds_swz(row, 2 * kc + hl));
+#pragma unroll
+          for (int e = 0; e < 16; ++e) dpacc[mb][e] = 0.f;
+#pragma unroll
+          for (int kc = 0; kc < 8; ++kc)
+            dpacc[mb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[kc], dof[kc], dpacc[mb], 0, 0, 0);
         }
-      }
-    } else {
-      // tt = c2 * s - m_run is the base-2 exponent of this tile's weights. The running max is
-      // raised (and O, l rescaled) only when max tt exceeds the slack: on the first tile (m_run
-      // = -inf makes tt +inf or NaN, and the test below is written to catch both) and rarely
-      // after. Taking the max over tt (outputs of an fma) rather than the raw matrix-core
-      // results lets the compiler skip NaN canonicalisation of every score.
-      float tt[2][16];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) tt[mb][e] = fmaf(sacc[mb][e], c2, -m_run);
-      float mx = fmaxf(tt[0][0], tt[0][1]);
-#pragma unroll
-      for (int i = 2; i < 32; i += 2) mx = fmaxf(mx, fmaxf(tt[i >> 4][i & 15], tt[i >> 4][(i & 15) + 1]));
-      mx = pair_max(mx);
-      const bool grow = !(mx <= kRescaleSlack);
-      if (__ballot(grow) != 0) {
-        // exact tile max of c2 * s (every tile has at least one unmasked kv row)
-        float sm = fmaxf(sacc[0][0], sacc[1][0]);
-#pragma unroll
-        for (int e = 1; e < 16; ++e) sm = fmaxf(sm, fmaxf(sacc[0][e], sacc[1][e]));
-        sm = pair_max(sm) * c2;
-        const float m_new = grow ? sm : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        lb_run *= alpha;
-        if constexpr (MODE == kFwd) {
-#pragma unroll
-          for (int dm = 0; dm < 4; ++dm)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[dm][e] *= alpha;
-        }
-        m_run = m_new;
+        uint32_t dw[2][8];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) tt[mb][e] = fmaf(sacc[mb][e], c2, -m_run);
-      }
-      float ls[4];
-      uint32_t pw[2][8];  // P rounded to bf16, two per word (the B operand of the PV product)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(tt[mb][e]);
-          const float p1 = __builtin_amdgcn_exp2f(tt[mb][e + 1]);
-          if (mb == 0 && e < 4) {
-            ls[e] = p0;
-            ls[e + 1] = p1;
-          } else {
-            ls[e & 3] += p0;
-            ls[(e & 3) + 1] += p1;
+          for (int e = 0; e < 16; e += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nlse2));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e + 1], c2, nlse2));
+            dw[mb][e >> 1] = pack_bf16x2(p0 * (dpacc[mb][e] - dq_d), p1 * (dpacc[mb][e + 1] - dq_d));
           }
-          if constexpr (MODE == kFwd) pw[mb][e >> 1] = pack_bf16x2(p0, p1);
-        }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      bf16x8_t pb[4];
-      if constexpr (MODE == kFwd) {
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const uint32_t* src = &pw[kc >> 1][4 * (kc & 1)];
-          pb[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
-        }
-        // O is normalised by the sum of the same bf16-rounded weights the PV product uses (an
-        // exactly normalised combination); the LSE keeps the fp32 sum. The bf16 row sums come
-        // from the matrix cores: (all-ones 32 x 16) x P^T gives every row the column sums, so
-        // each lane receives the full 64-key sum of its query.
-        f32x16_t rs;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) rs[e] = 0.f;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          rs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kc], rs, 0, 0, 0);
-        lb_run += rs[0];
-      }
-      if constexpr (MODE == kFwd) {
-        // O^T += V^T P^T; each V^T fragment is two transposing 8-byte LDS reads.
-        const char* vt = st + kTileBytes;
+        // dQ^T += K^T dS^T; each K^T fragment is two transposing 8-byte reads of the K tile.
 #pragma unroll
         for (int dm = 0; dm < 4; ++dm) {
-          bf16x8_t vf[4];
+          bf16x8_t kt[4];
 #pragma unroll
           for (int kc = 0; kc < 4; ++kc) {
             const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
             const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16_t*)((lds_char_t*)vt + row_lo * kRowBytes +
+                (lds_v4i16_t*)((lds_char_t*)st + row_lo * kRowBytes +
                                lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
             const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16_t*)((lds_char_t*)vt + row_hi * kRowBytes +
+                (lds_v4i16_t*)((lds_char_t*)st + row_hi * kRowBytes +
                                lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
             const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-            vf[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+            kt[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
           }
 #pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            const uint32_t* src = &dw[kc >> 1][4 * (kc & 1)];
+            const bf16x8_t dsb =
+                __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
+            oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[kc], dsb, oacc[dm], 0, 0, 0);
+          }
+        }
+      } else if constexpr (MODE == kMass) {
+        // Block sums of exp(sigma q.k - lse): one chunk per M block, flushed at block ends.
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const Chunk& c = mb ? b0 : a0;
+          if (c.nv > 0) {
+            float cs0 = 0.f, cs1 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+              cs0 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nlse2));
+              cs1 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e + 1], c2, nlse2));
+            }
+            blk_acc += cs0 + cs1;
+            if (c.last) {
+              const float tot = wave_sum_f32(blk_acc);
+              if (lane == 0)
+                a.part[(((size_t)bh * n_items + item) * 4 + wave) * a.nkv + c.J] = tot;
+              blk_acc = 0.f;
+            }
+          }
+        }
+      } else {
+        // tt = c2 * s - m_run is the base-2 exponent of this tile's weights. The running max is
+        // raised (and O, l rescaled) only when max tt exceeds the slack: on the first tile (m_run
+        // = -inf makes tt +inf or NaN, and the test below is written to catch both) and rarely
+        // after. Taking the max over tt (outputs of an fma) rather than the raw matrix-core
+        // results lets the compiler skip NaN canonicalisation of every score.
+        float tt[2][16];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) tt[mb][e] = fmaf(sacc[mb][e], c2, -m_run);
+        float mx = fmaxf(tt[0][0], tt[0][1]);
+#pragma unroll
+        for (int i = 2; i < 32; i += 2) mx = fmaxf(mx, fmaxf(tt[i >> 4][i & 15], tt[i >> 4][(i & 15) + 1]));
+        mx = pair_max(mx);
+        const bool grow = !(mx <= kRescaleSlack);
+        if (__ballot(grow) != 0) {
+          // exact tile max of c2 * s (every tile has at least one unmasked kv row)
+          float sm = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+          for (int e = 1; e < 16; ++e) sm = fmaxf(sm, fmaxf(sacc[0][e], sacc[1][e]));
+          sm = pair_max(sm) * c2;
+          const float m_new = grow ? sm : m_run;
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+          lb_run *= alpha;
+          if constexpr (MODE == kFwd) {
+#pragma unroll
+            for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) oacc[dm][e] *= alpha;
+          }
+          m_run = m_new;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) tt[mb][e] = fmaf(sacc[mb][e], c2, -m_run);
+        }
+        float ls[4];
+        uint32_t pw[2][8];  // P rounded to bf16, two per word (the B operand of the PV product)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(tt[mb][e]);
+            const float p1 = __builtin_amdgcn_exp2f(tt[mb][e + 1]);
+            if (mb == 0 && e < 4) {
+              ls[e] = p0;
+              ls[e + 1] = p1;
+            } else {
+              ls[e & 3] += p0;
+              ls[(e & 3) + 1] += p1;
+            }
+            if constexpr (MODE == kFwd) pw[mb][e >> 1] = pack_bf16x2(p0, p1);
+          }
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        bf16x8_t pb[4];
+        if constexpr (MODE == kFwd) {
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            const uint32_t* src = &pw[kc >> 1][4 * (kc & 1)];
+            pb[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
+          }
+          // O is normalised by the sum of the same bf16-rounded weights the PV product uses (an
+          // exactly normalised combination); the LSE keeps the fp32 sum. The bf16 row sums come
+          // from the matrix cores: (all-ones 32 x 16) x P^T gives every row the column sums, so
+          // each lane receives the full 64-key sum of its query.
+          f32x16_t rs;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) rs[e] = 0.f;
+#pragma unroll
           for (int kc = 0; kc < 4; ++kc)
-            oacc[dm] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc], pb[kc], oacc[dm], 0, 0, 0);
+            rs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kc], rs, 0, 0, 0);
+          lb_run += rs[0];
+        }
+        if constexpr (MODE == kFwd) {
+          // O^T += V^T P^T; each V^T fragment is two transposing 8-byte LDS reads.
+          const char* vt = st + kTileBytes;
+#pragma unroll
+          for (int dm = 0; dm < 4; ++dm) {
+            bf16x8_t vf[4];
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+              const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
+              const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_v4i16_t*)((lds_char_t*)vt + row_lo * kRowBytes +
+                                 lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
+              const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_v4i16_t*)((lds_char_t*)vt + row_hi * kRowBytes +
+                                 lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
+              const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+              vf[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+            }
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+              oacc[dm] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc], pb[kc], oacc[dm], 0, 0, 0);
+          }
         }
       }
     }
@@ -561,20 +567,25 @@ __global__ __launch_bounds__(256, 1) void attn_dq_d128(const MfmaArgs a) {
   attn_mfma_body<kDq, kFwdStages>(a);
 }
 
-// M[bh, I, J] = (sum over I's work items and the 4 waves of the block sums) / |I|, in fp64 and in
-// a fixed order.
+// M[bh, I, J] = (sum over I's work items and their active waves of the block sums) / |I|, in fp64
+// and in a fixed order. Wave w of an item is active iff it holds a valid query row (32 w < rows).
 __global__ __launch_bounds__(256) void mass_combine_kernel(const float* __restrict__ part,
                                                            const int32_t* __restrict__ qstart,
                                                            const int32_t* __restrict__ qitem0,
+                                                           const int32_t* __restrict__ items,
                                                            int n_items, int nq, int nkv,
                                                            float* __restrict__ M) {
   const int I = blockIdx.x, bh = blockIdx.y;
   const int i0 = qitem0[I], i1 = qitem0[I + 1];
-  const double inv = 1.0 / (double)(qstart[I + 1] - qstart[I]);
+  const int size = qstart[I + 1] - qstart[I];
+  const double inv = 1.0 / (double)size;
   for (int J = threadIdx.x; J < nkv; J += 256) {
     double s = 0.0;
-    for (int it = i0; it < i1; ++it)
-      for (int w = 0; w < 4; ++w) s += part[(((size_t)bh * n_items + it) * 4 + w) * nkv + J];
+    for (int it = i0; it < i1; ++it) {
+      const int rows = min(128, size - items[2 * it + 1]);
+      for (int w = 0; 32 * w < rows; ++w)
+        s += part[(((size_t)bh * n_items + it) * 4 + w) * nkv + J];
+    }
     M[((size_t)bh * nq + I) * nkv + J] = (float)(s * inv);
   }
 }
@@ -756,7 +767,7 @@ hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, flo
   attn_mfma_d128<kMass><<<grid, 256, 0, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mass_combine_kernel<<<dim3(p.nq, p.prob.B * p.prob.H), 256, 0, s>>>(
-      part, p.qstart, p.qitem0, p.n_items, p.nq, p.nkv, M);
+      part, p.qstart, p.qitem0, p.items, p.n_items, p.nq, p.nkv, M);
   return hipGetLastError();
 }
 
