@@ -85,10 +85,6 @@ __device__ __forceinline__ Chunk take_chunk(Cursor& c, const int32_t* __restrict
 // backward pass over the same CSR (S and dP recomputed per tile).
 enum Mode { kFwd = 0, kLse = 1, kMass = 2, kDq = 3 };
 
-#ifndef BSA_FWD_STAGES
-#define BSA_FWD_STAGES 2
-#endif
-constexpr int kFwdStages = BSA_FWD_STAGES;
 
 constexpr int kTileKV = 64;                    // kv tokens per iteration (two chunks)
 constexpr int kRowBytes = 256;                 // one token row of d = 128 bf16
@@ -124,19 +120,16 @@ struct MfmaArgs {
   int n_items, H, N, nq, nkv;
 };
 
-// NST LDS stages: tile t is computed while tiles t+1 .. t+NST-1 stream in.
-template <int MODE, int NST>
+// Two LDS stages: tile t is computed while tile t+1 streams in.
+template <int MODE>
 __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
-  static_assert(NST == 2 || NST == 3, "two or three stages");
   constexpr int D = 128;
   constexpr bool kDense = MODE == kLse || MODE == kMass;  // all kv blocks, not a CSR row
   constexpr bool kNeedV = MODE == kFwd || MODE == kDq;
   constexpr int kStage = kNeedV ? 2 * kTileBytes : kTileBytes;
-  constexpr int kCopiesPerTile = kNeedV ? 8 : 4;  // direct copies one wavefront issues per tile
-  __shared__ __attribute__((aligned(1024))) char lds[NST * kStage];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kStage];
   char* const lds_a = lds;
   char* const lds_b = lds + kStage;
-  char* const lds_c = lds + (NST - 1) * kStage;
 
   const int n_items = a.n_items;
   const int total = n_items * (int)gridDim.y;
@@ -238,31 +231,37 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     }
     return d;
   };
-  auto tile_issue = [&](int4 d, char* st) {
-    const int toks[4] = {d.x, d.y, d.z, d.w};
+  // Copies of this wave's row group i (rows 16w + 4i .. +4) of a tile's K (and V) into the stage
+  // whose LDS address is st_m0: lane l fetches the logical 16-byte unit that the row's swizzle
+  // places at position l % 16. Byte offsets within the head fit 32 bits (N * 256 < 2^31).
+  const uint16_t* const kbase = a.K + head_off;
+  const uint16_t* const vbase = kNeedV ? a.V + head_off : a.K;
+  uint32_t unit_off[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * wave + 4 * i + lgrp;
-      const int lunit = (lane & 15) ^ lds_key(row);  // logical unit at this position
-      const size_t o = head_off + (size_t)toks[i] * D + 8 * lunit;
-      char* dst = st + (16 * wave + 4 * i) * kRowBytes;
-      lds_dma16(a.K + o, dst);
-      if constexpr (kNeedV) lds_dma16(a.V + o, dst + kTileBytes);
-    }
+  for (int i = 0; i < 4; ++i)
+    unit_off[i] = 16u * (uint32_t)((lane & 15) ^ lds_key(16 * wave + 4 * i + lgrp));
+  auto tile_issue_part = [&](int4 d, uint32_t st_m0, int i) {
+    const int tok = i == 0 ? d.x : i == 1 ? d.y : i == 2 ? d.z : d.w;
+    const uint32_t voff = (uint32_t)tok * (uint32_t)kRowBytes + unit_off[i];
+    const uint32_t m0v = st_m0 + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
+    lds_dma16_so(kbase, voff, m0v);
+    if constexpr (kNeedV) lds_dma16_so(vbase, voff, m0v + kTileBytes);
+  };
+  auto tile_issue = [&](int4 d, uint32_t st_m0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tile_issue_part(d, st_m0, i);
   };
 
-  // Pipeline: tiles t .. t+NST-2 are in LDS or in flight; `ids` holds tile t+NST-1's token ids.
-  Chunk ca[NST], cb[NST];
+  // Pipeline: tile t (chunks a0, b0) is in LDS and tile t+1 (a1, b1, token ids `ids`) is copied
+  // into the other stage while tile t is computed.
+  const uint32_t m0_a = lds_addr(lds_a), m0_b = lds_addr(lds_b);
+  Chunk a0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+  Chunk b0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+  if (a0.nv > 0) tile_issue(tile_ids(a0, b0), m0_a);
+  Chunk a1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+  Chunk b1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
   int4 ids = make_int4(0, 0, 0, 0);
-#pragma unroll
-  for (int k = 0; k < NST - 1; ++k) {
-    ca[k] = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-    cb[k] = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-    if (ca[k].nv > 0) tile_issue(tile_ids(ca[k], cb[k]), k == 0 ? lds_a : lds_b);
-  }
-  ca[NST - 1] = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-  cb[NST - 1] = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-  if (ca[NST - 1].nv > 0) ids = tile_ids(ca[NST - 1], cb[NST - 1]);
+  if (a1.nv > 0) ids = tile_ids(a1, b1);
   vmem_wait_all();
   __syncthreads();
 
@@ -272,38 +271,55 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   const int vunit_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int vhalf_l = 8 * (lane & 1);
 
-  // One tile: compute tile t from stage `st` while tile t+NST-1 is issued into `nx` (the stage
-  // tile t-1 used). The stages are distinct arrays.
-  auto step = [&](const char* st, char* nx) {
-    const Chunk a0 = ca[0], b0 = cb[0];
+  // One tile: compute tile t from stage `st` while tile t+1 is copied into the other stage (LDS
+  // address nx_m0), which tile t-1 used.
+  auto step = [&](const char* st, uint32_t nx_m0) {
+    // A wavefront whose 32 query rows all lie past the end of the query block (ragged blocks at
+    // the grid edge) only takes part in the copies and barriers, leaving its SIMD to the other
+    // resident workgroup.
+    // S^T for this wave's 32 queries: two 32-kv M blocks (raw, unscaled scores).
+    f32x16_t sacc[2];
+    if (active) {
+      {
+        bf16x8_t kf[2][8];
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const int row = 32 * mb + l32;
+            kf[mb][kc] = *reinterpret_cast<const bf16x8_t*>(st + row * kRowBytes +
+                                                            lds_swz(row, 2 * kc + hl));
+          }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sacc[mb][e] = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            sacc[mb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mb][kc], qf[kc], sacc[mb], 0, 0, 0);
+        // Keep eight K reads in flight ahead of the MFMAs that consume them (LDS latency exceeds
+        // an MFMA's duration): 8 reads, then alternate one MFMA and one read, then the last 8.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+    }
+    // The next tile's copies are issued while the score MFMAs execute.
     const Chunk an = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
     const Chunk bn = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
     int4 nids = make_int4(0, 0, 0, 0);
     if (an.nv > 0) nids = tile_ids(an, bn);
-    const bool issued = ca[NST - 1].nv > 0;
-    if (issued) tile_issue(ids, nx);
+    if (a1.nv > 0) tile_issue(ids, nx_m0);
     ids = nids;
 
-    // A wavefront whose 32 query rows all lie past the end of the query block (ragged blocks at
-    // the grid edge) only takes part in the copies and barriers, leaving its SIMD to the other
-    // resident workgroup.
     if (active) {
-      // S^T for this wave's 32 queries: two 32-kv M blocks (raw, unscaled scores).
-      f32x16_t sacc[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int row = 32 * mb + l32;
-        const char* kp = st + row * kRowBytes;
-        bf16x8_t kf[8];
-#pragma unroll
-        for (int kc = 0; kc < 8; ++kc)
-          kf[kc] = *reinterpret_cast<const bf16x8_t*>(kp + lds_swz(row, 2 * kc + hl));
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[mb][e] = 0.f;
-#pragma unroll
-        for (int kc = 0; kc < 8; ++kc)
-          sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], sacc[mb], 0, 0, 0);
-      }
       if (a0.nv < 32 || b0.nv < 32) {  // partial chunk(s): mask padded kv rows
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -424,6 +440,27 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) tt[mb][e] = fmaf(sacc[mb][e], c2, -m_run);
         }
+        // V^T fragment (d block dm, kv rows 16 kc .. +16) of this tile: two transposing 8-byte
+        // LDS reads. The first d block's fragments are read before the weights are formed, so
+        // their latency hides behind that VALU work.
+        const char* vt = st + kTileBytes;
+        auto vfrag = [&](int dm, int kc) {
+          const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)((lds_char_t*)vt + row_lo * kRowBytes +
+                             lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)((lds_char_t*)vt + row_hi * kRowBytes +
+                             lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+        };
+        bf16x8_t vf0[4];
+        if constexpr (MODE == kFwd) {
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) vf0[kc] = vfrag(0, kc);
+          __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the VALU work below
+        }
         float ls[4];
         uint32_t pw[2][8];  // P rounded to bf16, two per word (the B operand of the PV product)
 #pragma unroll
@@ -462,63 +499,42 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
           lb_run += rs[0];
         }
         if constexpr (MODE == kFwd) {
-          // O^T += V^T P^T; each V^T fragment is two transposing 8-byte LDS reads.
-          const char* vt = st + kTileBytes;
+          // O^T += V^T P^T.
 #pragma unroll
           for (int dm = 0; dm < 4; ++dm) {
             bf16x8_t vf[4];
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-              const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
-              const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_v4i16_t*)((lds_char_t*)vt + row_lo * kRowBytes +
-                                 lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
-              const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_v4i16_t*)((lds_char_t*)vt + row_hi * kRowBytes +
-                                 lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
-              const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-              vf[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
-            }
+            for (int kc = 0; kc < 4; ++kc) vf[kc] = dm == 0 ? vf0[kc] : vfrag(dm, kc);
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc)
               oacc[dm] =
                   __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc], pb[kc], oacc[dm], 0, 0, 0);
           }
+          // Weights first (their VALU work covers the first reads' latency), then the MFMAs
+          // with the remaining V reads interleaved, two per MFMA.
+          __builtin_amdgcn_sched_group_barrier(0x002, 100, 0);
+#pragma unroll
+          for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
       }
     }
-    // Tile t+1 must be in LDS before the barrier; with three stages tile t+2's copies (the most
-    // recent ones) may stay in flight. kMass issues global stores after the copies, so it
-    // waits for everything.
-    if (NST == 3 && MODE != kMass && issued)
-      vmem_wait_keep<kCopiesPerTile>();
-    else
-      vmem_wait_all();
+    // Tile t+1 must be in LDS before the barrier that opens step t+1.
+    vmem_wait_all();
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < NST - 1; ++k) {
-      ca[k] = ca[k + 1];
-      cb[k] = cb[k + 1];
-    }
-    ca[NST - 1] = an;
-    cb[NST - 1] = bn;
+    a0 = a1;
+    b0 = b1;
+    a1 = an;
+    b1 = bn;
   };
-  if constexpr (NST == 2) {
-    while (true) {
-      if (ca[0].nv <= 0) break;
-      step(lds_a, lds_b);
-      if (ca[0].nv <= 0) break;
-      step(lds_b, lds_a);
-    }
-  } else {
-    while (true) {
-      if (ca[0].nv <= 0) break;
-      step(lds_a, lds_c);
-      if (ca[0].nv <= 0) break;
-      step(lds_b, lds_a);
-      if (ca[0].nv <= 0) break;
-      step(lds_c, lds_b);
-    }
+  while (true) {
+    if (a0.nv <= 0) break;
+    step(lds_a, m0_b);
+    if (a0.nv <= 0) break;
+    step(lds_b, m0_a);
   }
 
   if constexpr (MODE == kMass) return;
@@ -560,11 +576,11 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
 // fragments as well and runs at one wave per SIMD with the full register file.
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void attn_mfma_d128(const MfmaArgs a) {
-  attn_mfma_body<MODE, kFwdStages>(a);
+  attn_mfma_body<MODE>(a);
 }
 
 __global__ __launch_bounds__(256, 1) void attn_dq_d128(const MfmaArgs a) {
-  attn_mfma_body<kDq, kFwdStages>(a);
+  attn_mfma_body<kDq>(a);
 }
 
 // M[bh, I, J] = (sum over I's work items and their active waves of the block sums) / |I|, in fp64

@@ -122,6 +122,21 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, char* lds_base) {
                : "m0", "memory");
 }
 
+// The same copy with the global address split into a wave-uniform 64-bit base (held in SGPRs,
+// the instruction's saddr form) and a per-lane 32-bit byte offset, and the LDS destination given
+// as a precomputed M0 value: no 64-bit address arithmetic per copy.
+__device__ __forceinline__ void lds_dma16_so(const void* sbase, uint32_t voff, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0v)
+               : "m0", "memory");
+}
+
+// LDS byte address of a __shared__ location, as a wave-uniform value (for M0).
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_char_t*)p));
+}
+
 // Wait until every vector memory operation of this wavefront has completed (vmcnt(0); the
 // other counters unconstrained).
 __device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
