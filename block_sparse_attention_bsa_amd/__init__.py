@@ -74,13 +74,13 @@ def lib():
         "bsa_plan_create": [ctypes.POINTER(Problem), P, ctypes.POINTER(P)],
         "bsa_plan_destroy": [P],
         "bsa_plan_info": [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(SZ),
-                          ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
+                          ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
         "bsa_plan_blocks": [P, I32, P, P],
         "bsa_pool": [P, I32, P, P, P],
         "bsa_score": [P, P, P, I32, P, P],
         "bsa_calibrate_mass": [P, P, P, P, P, SZ, P],
         "bsa_select": [P, P, ctypes.POINTER(SelectParams), P, P, I64, P, P, P, SZ, P],
-        "bsa_attn_fwd": [P, P, P, P, P, P, P, P, P],
+        "bsa_attn_fwd": [P, P, P, P, P, P, P, P, P, SZ, P],
         "bsa_attn_bwd": [P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
@@ -165,11 +165,12 @@ class Plan:
                                      ctypes.byref(handle)))
         self.handle = handle
         nq, nkv = ctypes.c_int32(0), ctypes.c_int32(0)
-        wss, wsc, wsb = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+        wss, wsc, wsb, wsf = (ctypes.c_size_t(0) for _ in range(4))
         _check(lib().bsa_plan_info(handle, ctypes.byref(nq), ctypes.byref(nkv), ctypes.byref(wss),
-                                   ctypes.byref(wsc), ctypes.byref(wsb)))
+                                   ctypes.byref(wsc), ctypes.byref(wsb), ctypes.byref(wsf)))
         self.nq, self.nkv = nq.value, nkv.value
         self.ws_select, self.ws_calib, self.ws_bwd = wss.value, wsc.value, wsb.value
+        self.ws_fwd = wsf.value
 
     def blocks(self, which: int) -> Tuple[np.ndarray, np.ndarray]:
         nb = self.nq if which == 0 else self.nkv
@@ -211,9 +212,10 @@ def bsa_select(plan: Plan, S, p: float, pool: int, min_k_mode: int, fixed_k: int
                             ws_bytes, _stream(stream)))
 
 
-def bsa_attn_fwd(plan: Plan, Q, K, V, row_ptr, col_idx, O, lse, stream=None):
+def bsa_attn_fwd(plan: Plan, Q, K, V, row_ptr, col_idx, O, lse, ws, ws_bytes: int, stream=None):
     _check(lib().bsa_attn_fwd(plan.handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(row_ptr),
-                              _ptr(col_idx), _ptr(O), _ptr(lse), _stream(stream)))
+                              _ptr(col_idx), _ptr(O), _ptr(lse), _ptr(ws), ws_bytes,
+                              _stream(stream)))
 
 
 def bsa_attn_bwd(plan: Plan, Q, K, V, O, dO, lse, row_ptr, col_idx, dQ, dK, dV, ws,

@@ -447,5 +447,7 @@ hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, cons
   a.nkv = p.nkv;
   dkdv_kernel<<<dim3(p.n_kvitems, BH), 256, 0, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_attn_dq(p, Q, K, V, dO, lse, delta, row_ptr, col_idx, dQ, s);
+  if ((e = launch_permute_rows(p, K, base + L.kp, s)) != hipSuccess) return e;
+  if ((e = launch_permute_rows(p, V, base + L.vp, s)) != hipSuccess) return e;
+  return launch_attn_dq(p, Q, base + L.kp, base + L.vp, dO, lse, delta, row_ptr, col_idx, dQ, s);
 }

@@ -118,6 +118,7 @@ struct MfmaArgs {
   float* lse;           // kFwd (nullable) and kLse
   float* part;          // kMass: [bh][item][wave][nkv] per-wave block sums
   int n_items, H, N, nq, nkv;
+  int Npad;  // K and V are permuted into block order: [B*H][Npad][d], Npad = N + 32
 };
 
 // Two LDS stages: tile t is computed while tile t+1 streams in.
@@ -193,11 +194,12 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   if constexpr (MODE == kDq) dq_d = qvalid ? a.delta[(size_t)bh * a.N + qtok] : 0.f;
 
   // Loader role: wave w fills tile rows 16w + 4i + lane/16 (i = 0..3), 16-byte unit lane%16 of
-  // the swizzled row, for K (and V), with direct global->LDS copies (no staging registers).
-  // The 16 token ids of a wavefront's rows are read with one scalar load (perm is padded by 32
-  // entries); rows past a chunk's end repeat the chunk's first token: their scores are masked
-  // and their probabilities are exactly 0, so any finite row will do. With scalar ids the
-  // copies are the only vector memory operations in the loop, so their waits are exact.
+  // the swizzled row, for K (and V), with direct global->LDS copies (no staging registers). K and
+  // V arrive permuted into block order ([B*H][Npad][d], see permute_rows_kernel), so a chunk is
+  // 32 consecutive rows starting at its position: the per-lane byte offset of each copy is fixed
+  // and the chunk's position goes into the scalar base address. Rows past a chunk's end are the
+  // next rows of the permuted array (other tokens, or the zero padding after the last block):
+  // their scores are masked and their weights are exactly 0.
   const int lchunk = wave >> 1, loff = 16 * (wave & 1), lgrp = lane >> 4;
 
   Cursor cur;
@@ -206,62 +208,35 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   cur.sub = 0;
   cursor_load<kDense>(cur, a.col_idx, a.kvstart);
 
-  // This lane's token for each of its 4 tile rows.
-  auto tile_ids = [&](Chunk ca, Chunk cb) {
-    const int nvc = lchunk ? cb.nv : ca.nv;
-    const int base = nvc > 0 ? (lchunk ? cb.pos : ca.pos) : ca.pos;
-    const int lim = nvc > 0 ? nvc : 1;
-    const int first = ld_ro(a.kvperm + base);
-    int4 d;
-    int* dv = &d.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int jj = loff + 4 * i + j;
-        const int id = ld_ro(a.kvperm + base + jj);  // in bounds: perm is padded
-        v[j] = jj < lim ? id : first;
-      }
-      int tok = v[0];
-      tok = lgrp == 1 ? v[1] : tok;
-      tok = lgrp == 2 ? v[2] : tok;
-      tok = lgrp == 3 ? v[3] : tok;
-      dv[i] = tok;
-    }
-    return d;
-  };
-  // Copies of this wave's row group i (rows 16w + 4i .. +4) of a tile's K (and V) into the stage
-  // whose LDS address is st_m0: lane l fetches the logical 16-byte unit that the row's swizzle
-  // places at position l % 16. Byte offsets within the head fit 32 bits (N * 256 < 2^31).
-  const uint16_t* const kbase = a.K + head_off;
-  const uint16_t* const vbase = kNeedV ? a.V + head_off : a.K;
-  uint32_t unit_off[4];
+  const size_t kv_off = (size_t)bh * a.Npad * D;
+  const uint16_t* const kbase = a.K + kv_off;
+  const uint16_t* const vbase = kNeedV ? a.V + kv_off : a.K;
+  uint32_t voff[4];  // byte offset of this lane's copy i within its chunk
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    unit_off[i] = 16u * (uint32_t)((lane & 15) ^ lds_key(16 * wave + 4 * i + lgrp));
-  auto tile_issue_part = [&](int4 d, uint32_t st_m0, int i) {
-    const int tok = i == 0 ? d.x : i == 1 ? d.y : i == 2 ? d.z : d.w;
-    const uint32_t voff = (uint32_t)tok * (uint32_t)kRowBytes + unit_off[i];
-    const uint32_t m0v = st_m0 + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
-    lds_dma16_so(kbase, voff, m0v);
-    if constexpr (kNeedV) lds_dma16_so(vbase, voff, m0v + kTileBytes);
-  };
-  auto tile_issue = [&](int4 d, uint32_t st_m0) {
+    voff[i] = (uint32_t)((loff + 4 * i + lgrp) * kRowBytes) +
+              16u * (uint32_t)((lane & 15) ^ lds_key(16 * wave + 4 * i + lgrp));
+  // Copies of this wave's 16 rows of the tile (chunks ca, cb) into the stage at LDS address st_m0.
+  auto tile_issue = [&](Chunk ca, Chunk cb, uint32_t st_m0) {
+    const int pos = (lchunk && cb.nv > 0) ? cb.pos : ca.pos;
+    const uint16_t* kb = kbase + (size_t)pos * D;
+    const uint16_t* vb = vbase + (size_t)pos * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tile_issue_part(d, st_m0, i);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m0v = st_m0 + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
+      lds_dma16_so(kb, voff[i], m0v);
+      if constexpr (kNeedV) lds_dma16_so(vb, voff[i], m0v + kTileBytes);
+    }
   };
 
-  // Pipeline: tile t (chunks a0, b0) is in LDS and tile t+1 (a1, b1, token ids `ids`) is copied
-  // into the other stage while tile t is computed.
+  // Pipeline: tile t (chunks a0, b0) is in LDS and tile t+1 (a1, b1) is copied into the other
+  // stage while tile t is computed.
   const uint32_t m0_a = lds_addr(lds_a), m0_b = lds_addr(lds_b);
   Chunk a0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
   Chunk b0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-  if (a0.nv > 0) tile_issue(tile_ids(a0, b0), m0_a);
+  if (a0.nv > 0) tile_issue(a0, b0, m0_a);
   Chunk a1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
   Chunk b1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-  int4 ids = make_int4(0, 0, 0, 0);
-  if (a1.nv > 0) ids = tile_ids(a1, b1);
   vmem_wait_all();
   __syncthreads();
 
@@ -314,10 +289,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     // The next tile's copies are issued while the score MFMAs execute.
     const Chunk an = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
     const Chunk bn = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-    int4 nids = make_int4(0, 0, 0, 0);
-    if (an.nv > 0) nids = tile_ids(an, bn);
-    if (a1.nv > 0) tile_issue(ids, nx_m0);
-    ids = nids;
+    if (a1.nv > 0) tile_issue(a1, b1, nx_m0);
 
     if (active) {
       if (a0.nv < 32 || b0.nv < 32) {  // partial chunk(s): mask padded kv rows
@@ -606,6 +578,22 @@ __global__ __launch_bounds__(256) void mass_combine_kernel(const float* __restri
   }
 }
 
+// dst[bh][pos] = src[bh][perm[pos]] for pos < N (256-byte rows of d = 128 bf16) and zero rows for
+// N <= pos < Npad: K or V in block order, so that the 32 rows of a chunk are contiguous and the
+// rows past any chunk's end exist. One 16-byte unit per thread, 16 rows per workgroup.
+__global__ __launch_bounds__(256) void permute_rows_kernel(const uint16_t* __restrict__ src,
+                                                           const int32_t* __restrict__ perm,
+                                                           int N, int Npad,
+                                                           uint16_t* __restrict__ dst) {
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4), unit = threadIdx.x & 15;
+  if (row >= Npad) return;
+  const size_t bh = blockIdx.y;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (row < N)
+    v = *reinterpret_cast<const uint4*>(src + (bh * N + (size_t)perm[row]) * 128 + 8 * unit);
+  *reinterpret_cast<uint4*>(dst + (bh * Npad + (size_t)row) * 128 + 8 * unit) = v;
+}
+
 MfmaArgs mfma_args(const bsa_plan& p) {
   MfmaArgs a{};
   a.qperm = p.qperm;
@@ -619,6 +607,7 @@ MfmaArgs mfma_args(const bsa_plan& p) {
   a.N = p.prob.N;
   a.nq = p.nq;
   a.nkv = p.nkv;
+  a.Npad = p.prob.N + kPermPad;
   return a;
 }
 
@@ -741,14 +730,26 @@ hipError_t launch_valu(const bsa_plan& p, const void* Q, const void* K, const vo
 
 }  // namespace
 
+hipError_t launch_permute_rows(const bsa_plan& p, const void* src, void* dst, hipStream_t s) {
+  const int N = p.prob.N, Npad = N + kPermPad;
+  permute_rows_kernel<<<dim3((Npad + 15) / 16, p.prob.B * p.prob.H), 256, 0, s>>>(
+      static_cast<const uint16_t*>(src), p.kvperm, N, Npad, static_cast<uint16_t*>(dst));
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
                            const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse,
-                           hipStream_t s) {
+                           void* ws, hipStream_t s) {
   if (p.prob.dtype == BSA_BF16 && p.prob.d == 128) {
+    const FwdWs L = fwd_ws_layout(p);
+    char* base = static_cast<char*>(ws);
+    hipError_t e = launch_permute_rows(p, K, base + L.kp, s);
+    if (e == hipSuccess) e = launch_permute_rows(p, V, base + L.vp, s);
+    if (e != hipSuccess) return e;
     MfmaArgs a = mfma_args(p);
     a.Q = static_cast<const uint16_t*>(Q);
-    a.K = static_cast<const uint16_t*>(K);
-    a.V = static_cast<const uint16_t*>(V);
+    a.K = reinterpret_cast<const uint16_t*>(base + L.kp);
+    a.V = reinterpret_cast<const uint16_t*>(base + L.vp);
     a.row_ptr = row_ptr;
     a.col_idx = col_idx;
     a.O = static_cast<uint16_t*>(O);
@@ -769,14 +770,15 @@ hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, flo
   char* base = static_cast<char*>(ws);
   float* lse = reinterpret_cast<float*>(base + L.lse);
   float* part = reinterpret_cast<float*>(base + L.part);
+  hipError_t e = launch_permute_rows(p, K, base + L.kp, s);
+  if (e != hipSuccess) return e;
   const dim3 grid(p.n_items, p.prob.B * p.prob.H);
   MfmaArgs a = mfma_args(p);
   a.Q = static_cast<const uint16_t*>(Q);
-  a.K = static_cast<const uint16_t*>(K);
+  a.K = reinterpret_cast<const uint16_t*>(base + L.kp);
   a.lse = lse;
   attn_mfma_d128<kLse><<<grid, 256, 0, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   a.lse = nullptr;
   a.lse_in = lse;
   a.part = part;
@@ -787,14 +789,14 @@ hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, flo
   return hipGetLastError();
 }
 
-hipError_t launch_attn_dq(const bsa_plan& p, const void* Q, const void* K, const void* V,
+hipError_t launch_attn_dq(const bsa_plan& p, const void* Q, const void* Kp, const void* Vp,
                           const void* dO, const float* lse, const float* delta,
                           const int32_t* row_ptr, const int32_t* col_idx, void* dQ,
                           hipStream_t s) {
   MfmaArgs a = mfma_args(p);
   a.Q = static_cast<const uint16_t*>(Q);
-  a.K = static_cast<const uint16_t*>(K);
-  a.V = static_cast<const uint16_t*>(V);
+  a.K = static_cast<const uint16_t*>(Kp);
+  a.V = static_cast<const uint16_t*>(Vp);
   a.dO = static_cast<const uint16_t*>(dO);
   a.lse_in = lse;
   a.delta = delta;

@@ -136,7 +136,21 @@ BwdWs bwd_ws_layout(const bsa_plan& p) {
   w.col_cnt = w.bitmap + align_up(rows * w.nwords * 4);
   w.col_ptr = w.col_cnt + align_up(cols * 4);
   w.row_idx = w.col_ptr + align_up((cols + 1) * 4);
-  w.total = w.row_idx + align_up(rows * p.nkv * 4);
+  const size_t perm_bytes = BH * (size_t)(p.prob.N + kPermPad) * p.prob.d * 2;
+  w.kp = w.row_idx + align_up(rows * p.nkv * 4);
+  w.vp = w.kp + align_up(perm_bytes);
+  w.total = w.vp + align_up(perm_bytes);
+  return w;
+}
+
+FwdWs fwd_ws_layout(const bsa_plan& p) {
+  FwdWs w{0, 0, 0};
+  if (p.prob.dtype != BSA_BF16 || p.prob.d != 128) return w;  // the VALU paths need none
+  const size_t perm_bytes =
+      (size_t)p.prob.B * p.prob.H * (size_t)(p.prob.N + kPermPad) * p.prob.d * 2;
+  w.kp = 0;
+  w.vp = align_up(perm_bytes);
+  w.total = w.vp + align_up(perm_bytes);
   return w;
 }
 
@@ -145,7 +159,8 @@ CalibWs calib_ws_layout(const bsa_plan& p) {
   const size_t BH = (size_t)p.prob.B * p.prob.H;
   w.lse = 0;
   w.part = align_up(BH * p.prob.N * 4);
-  w.total = w.part + align_up(BH * p.n_items * 4 * (size_t)p.nkv * 4);
+  w.kp = w.part + align_up(BH * p.n_items * 4 * (size_t)p.nkv * 4);
+  w.total = w.kp + align_up(BH * (size_t)(p.prob.N + kPermPad) * p.prob.d * 2);
   return w;
 }
 
@@ -257,13 +272,14 @@ int bsa_plan_destroy(bsa_plan* plan) {
 }
 
 int bsa_plan_info(const bsa_plan* plan, int32_t* nq, int32_t* nkv, size_t* ws_select,
-                  size_t* ws_calib, size_t* ws_bwd) {
+                  size_t* ws_calib, size_t* ws_bwd, size_t* ws_fwd) {
   if (!plan) return fail(BSA_EINVAL, "bsa_plan_info: NULL plan");
   if (nq) *nq = plan->nq;
   if (nkv) *nkv = plan->nkv;
   if (ws_select) *ws_select = select_ws_layout(*plan).total;
   if (ws_calib) *ws_calib = calib_ws_layout(*plan).total;
   if (ws_bwd) *ws_bwd = bwd_ws_layout(*plan).total;
+  if (ws_fwd) *ws_fwd = fwd_ws_layout(*plan).total;
   return ok();
 }
 
@@ -343,15 +359,18 @@ int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* pr
 }
 
 int bsa_attn_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
-                 const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse,
-                 void* stream) {
+                 const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse, void* ws,
+                 size_t ws_bytes, void* stream) {
   if (!plan || !Q || !K || !V || !row_ptr || !col_idx || !O)
     return fail(BSA_EINVAL, "bsa_attn_fwd: NULL argument");
   if (!supported_attention(plan->prob))
     return fail(BSA_EUNSUPPORTED, "bsa_attn_fwd: unsupported dtype/d combination");
+  const size_t need = fwd_ws_layout(*plan).total;
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(BSA_ECAPACITY, "bsa_attn_fwd: workspace %zu < %zu bytes", ws_bytes, need);
   int rc = check_device(plan);
   if (rc) return rc;
-  return launch_status(launch_attn_fwd(*plan, Q, K, V, row_ptr, col_idx, O, lse,
+  return launch_status(launch_attn_fwd(*plan, Q, K, V, row_ptr, col_idx, O, lse, ws,
                                        (hipStream_t)stream),
                        "bsa_attn_fwd");
 }

@@ -47,15 +47,26 @@ SelectWs select_ws_layout(const bsa_plan& p);
 struct BwdWs {
   // D = rowsum(dO * O) per token; CSR row bitmap; CSC (per (head, kv block) ascending q-block
   // lists): per-column counts, column pointers, row ids.
-  size_t delta, bitmap, col_cnt, col_ptr, row_idx, total;
+  // K and V in block order for the dQ pass.
+  size_t delta, bitmap, col_cnt, col_ptr, row_idx, kp, vp, total;
   int nwords;
 };
 BwdWs bwd_ws_layout(const bsa_plan& p);
 
 struct CalibWs {
-  size_t lse, part, total;  // per-token log-sum-exp; per (item, wave, kv block) block sums
+  // per-token log-sum-exp; per (item, wave, kv block) block sums; K in block order
+  size_t lse, part, kp, total;
 };
 CalibWs calib_ws_layout(const bsa_plan& p);
+
+// Rows appended to each head of a block-ordered K or V copy, so that the 32 rows read for any
+// chunk exist.
+constexpr int kPermPad = 32;
+
+struct FwdWs {
+  size_t kp, vp, total;  // K and V in block order, [B*H][N + kPermPad][d] (bf16, d = 128 path)
+};
+FwdWs fwd_ws_layout(const bsa_plan& p);
 
 // Kernel launchers (defined in the .hip files). Each returns the launch status.
 hipError_t launch_pool(const bsa_plan& p, int which, const void* X, float* Xbar, hipStream_t s);
@@ -66,11 +77,15 @@ hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_par
                          void* ws, hipStream_t s);
 hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
                            const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse,
-                           hipStream_t s);
+                           void* ws, hipStream_t s);
+// dst = src ([B, H, N, 128] bf16) with rows in block order (plan kvperm) and kPermPad zero rows
+// per head.
+hipError_t launch_permute_rows(const bsa_plan& p, const void* src, void* dst, hipStream_t s);
 hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, float* M, void* ws,
                             hipStream_t s);
-// dQ of the backward pass (a mode of the forward MFMA kernel), given D and the forward's LSE.
-hipError_t launch_attn_dq(const bsa_plan& p, const void* Q, const void* K, const void* V,
+// dQ of the backward pass (a mode of the forward MFMA kernel), given D and the forward's LSE;
+// Kp, Vp are K and V in block order (launch_permute_rows).
+hipError_t launch_attn_dq(const bsa_plan& p, const void* Q, const void* Kp, const void* Vp,
                           const void* dO, const float* lse, const float* delta,
                           const int32_t* row_ptr, const int32_t* col_idx, void* dQ,
                           hipStream_t s);

@@ -34,6 +34,7 @@ class BlockSparseAttention:
         self.ws_select = torch.empty(max(p.ws_select, 1), dtype=torch.uint8, device=self.device)
         self._ws_calib = None
         self._ws_bwd = None
+        self._ws_fwd = None
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
 
     # -- stages -----------------------------------------------------------------------------
@@ -63,8 +64,11 @@ class BlockSparseAttention:
             out = torch.empty_like(q)
         if lse is None:
             lse = torch.empty(q.shape[:3], dtype=torch.float32, device=self.device)
+        if self._ws_fwd is None and self.plan.ws_fwd > 0:
+            self._ws_fwd = torch.empty(self.plan.ws_fwd, dtype=torch.uint8, device=self.device)
         bsa_attn_fwd(self.plan, q, k, v, self.row_ptr if row_ptr is None else row_ptr,
-                     self.col_idx if col_idx is None else col_idx, out, lse, stream)
+                     self.col_idx if col_idx is None else col_idx, out, lse, self._ws_fwd,
+                     self.plan.ws_fwd, stream)
         return out, lse
 
     def backward(self, q, k, v, o, do, lse, row_ptr=None, col_idx=None, stream=None):

@@ -121,10 +121,12 @@ int bsa_partition_build(int32_t T, int32_t Hg, int32_t Wg, const bsa_partition* 
 int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan** out);
 int bsa_plan_destroy(bsa_plan* plan);
 
-/* Block counts and the workspace sizes (bytes) that bsa_select, bsa_calibrate_mass and
- * bsa_attn_bwd require for this plan. Any output pointer may be NULL. */
+/* Block counts and the workspace sizes (bytes) that bsa_select, bsa_calibrate_mass,
+ * bsa_attn_bwd and bsa_attn_fwd require for this plan (ws_fwd is 0 for the fp32 and d = 64
+ * paths). Any output pointer may be NULL. Workspaces are caller-owned device memory; their
+ * contents need no initialisation and are scratch between calls. */
 int bsa_plan_info(const bsa_plan* plan, int32_t* nq, int32_t* nkv, size_t* ws_select,
-                  size_t* ws_calib, size_t* ws_bwd);
+                  size_t* ws_calib, size_t* ws_bwd, size_t* ws_fwd);
 
 /* Host copies of a plan's partition (which = 0 queries, 1 keys/values): perm[N] and
  * blk_start[nblk + 1], both host buffers. */
@@ -165,10 +167,12 @@ int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* pa
  * Q, K, V, O [B, H, N, d] of the plan's dtype; lse fp32 [B, H, N] (nullable). bf16: products on
  * bf16 matrix cores with fp32 accumulation and fp32 online softmax; P is rounded to bf16 before
  * the PV product. The CSR must come from bsa_select for this plan (or be equivalent: indices
- * in [0, nkv), no duplicates within a row). */
+ * in [0, nkv), no duplicates within a row). ws (device, ws_bytes >= ws_fwd of bsa_plan_info;
+ * may be NULL when ws_fwd is 0) receives K and V copied into block order; BSA_ECAPACITY if it
+ * is too small. */
 int bsa_attn_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
-                 const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse,
-                 void* stream);
+                 const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse, void* ws,
+                 size_t ws_bytes, void* stream);
 
 /* Gradient of step 4 with the selection held fixed (a hard gate): given O and lse from
  * bsa_attn_fwd and the upstream gradient dO, writes dQ, dK, dV ([B, H, N, d], plan dtype):

@@ -90,10 +90,11 @@ def test_null_arguments_rejected(L):
     prm = bsa.SelectParams(0.9, 0, 0, 0)
     assert L.bsa_select(P, None, ctypes.byref(prm), None, None, 0, None, None, None, 0,
                         None) == bsa.BSA_EINVAL
-    assert L.bsa_attn_fwd(P, None, None, None, None, None, None, None, None) == bsa.BSA_EINVAL
+    assert L.bsa_attn_fwd(P, None, None, None, None, None, None, None, None, 0,
+                          None) == bsa.BSA_EINVAL
     assert L.bsa_attn_bwd(P, *([None] * 12), 0, None) == bsa.BSA_EINVAL
     assert L.bsa_plan_destroy(None) == bsa.BSA_EINVAL
-    assert L.bsa_plan_info(None, None, None, None, None, None) == bsa.BSA_EINVAL
+    assert L.bsa_plan_info(None, None, None, None, None, None, None) == bsa.BSA_EINVAL
     assert L.bsa_plan_blocks(None, 0, None, None) == bsa.BSA_EINVAL
 
 

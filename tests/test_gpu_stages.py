@@ -215,3 +215,33 @@ def test_select_validation_errors():
     with pytest.raises(bsa.BsaError) as e:
         bsa.bsa_score(layer.plan, layer.qbar, layer.kbar, 3, layer.S)
     assert e.value.code == bsa.BSA_EINVAL
+
+
+def test_workspace_capacity_errors():
+    """Attention forward, calibration and backward reject a workspace below the plan's size
+    (nothing is launched), and the forward's workspace holds block-ordered K and V."""
+    import torch
+    import block_sparse_attention_bsa_amd as bsa
+    w = replace(CONFIGS[2], grid=(4, 8, 8), H=1)
+    layer = _layer(w)
+    p = layer.plan
+    per = w.B * w.H * (p.N + 32) * w.d * 2
+    assert p.ws_fwd >= 2 * per
+    q = torch.zeros((w.B, w.H, p.N, w.d), dtype=torch.bfloat16, device="cuda")
+    out, lse = torch.empty_like(q), torch.empty(q.shape[:3], device="cuda")
+    ws = torch.empty(p.ws_fwd, dtype=torch.uint8, device="cuda")
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_attn_fwd(p, q, q, q, layer.row_ptr, layer.col_idx, out, lse, ws, p.ws_fwd - 1)
+    assert e.value.code == bsa.BSA_ECAPACITY
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_attn_fwd(p, q, q, q, layer.row_ptr, layer.col_idx, out, lse, None, 0)
+    assert e.value.code == bsa.BSA_ECAPACITY
+    wsc = torch.empty(p.ws_calib, dtype=torch.uint8, device="cuda")
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_calibrate_mass(p, q, q, layer.S, wsc, p.ws_calib - 1)
+    assert e.value.code == bsa.BSA_ECAPACITY
+    wsb = torch.empty(p.ws_bwd, dtype=torch.uint8, device="cuda")
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_attn_bwd(p, q, q, q, q, q, lse, layer.row_ptr, layer.col_idx, q, q, q, wsb,
+                         p.ws_bwd - 1)
+    assert e.value.code == bsa.BSA_ECAPACITY
