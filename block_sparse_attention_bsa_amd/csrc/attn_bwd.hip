@@ -4,14 +4,15 @@
 // dS = P (dP - D_i) with D_i = dO_i.O_i, dQ_i += sigma dS k_j, dK_j += sigma dS q_i.
 //
 // Passes, all deterministic (no atomics on floating point):
-//   1. delta_kernel   D = rowsum(dO * O), streaming both tensors once.
+//   1. bwd_prep_kernel D = rowsum(dO * O) (token order, for the dQ pass), and Q, dO, LSE and D
+//                      copied into query block order for the dK/dV pass (one read of Q, O, dO).
 //   2. CSR -> CSC      a per-row bitmap of the selection, then for every (head, kv block) the
 //                      ascending list of query blocks that selected it (column counts, a scan,
 //                      and a fill that walks the bitmap in query-block order).
 //   3. dkdv_kernel     kv-stationary: a workgroup owns 128 tokens of one kv block (4 wavefronts x
 //                      32 tokens, K and V held in registers as MFMA B operands) and streams the
 //                      64-query chunks of every query block in its CSC column through LDS (Q, dO,
-//                      lse, D; double-buffered direct loads). Per chunk and wave: S = Q K^T and
+//                      lse, D; double-buffered direct copies of consecutive block-order rows). Per chunk and wave: S = Q K^T and
 //                      dP = dO V^T (lane = kv token), P and dS in registers, then
 //                      dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T from transposing reads.
 //   4. dQ              the forward kernel's kDq mode over the CSR (one workgroup per query block).
@@ -30,16 +31,27 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 
 
-// D[bh, n] = sum_d dO[bh, n, d] * O[bh, n, d]; 16 lanes per token row.
-__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ O,
-                                                    const uint16_t* __restrict__ dO,
-                                                    int64_t rows, float* __restrict__ D) {
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int seg = threadIdx.x & 15;
+// Per query position pos of the block order (token n = qperm[pos]): D = dO_n . O_n, written in
+// token order (for the dQ pass) and in block order; Q_n and dO_n copied to block order; LSE
+// (times log2 e) in block order. Rows N <= pos < Npad are zero. 16 lanes per row, 16 rows per
+// workgroup.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ O,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+    const int32_t* __restrict__ qperm, int N, int Npad, uint16_t* __restrict__ Qp,
+    uint16_t* __restrict__ dOp, float* __restrict__ lsep, float* __restrict__ Dp,
+    float* __restrict__ Dnat) {
+  const int pos = blockIdx.x * 16 + (threadIdx.x >> 4), seg = threadIdx.x & 15;
+  const size_t bh = blockIdx.y;
+  const bool valid = pos < N;
+  const int tok = valid ? qperm[pos] : 0;
+  uint4 q = make_uint4(0, 0, 0, 0), g = q;
   float s = 0.f;
-  if (row < rows) {
-    const uint4 o = *reinterpret_cast<const uint4*>(O + row * 128 + 8 * seg);
-    const uint4 g = *reinterpret_cast<const uint4*>(dO + row * 128 + 8 * seg);
+  if (valid) {
+    const size_t src = (bh * N + (size_t)tok) * 128 + 8 * seg;
+    q = *reinterpret_cast<const uint4*>(Q + src);
+    g = *reinterpret_cast<const uint4*>(dO + src);
+    const uint4 o = *reinterpret_cast<const uint4*>(O + src);
     const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -47,7 +59,15 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
   }
 #pragma unroll
   for (int d = 8; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
-  if (row < rows && seg == 0) D[row] = s;
+  if (pos >= Npad) return;
+  const size_t dst = (bh * Npad + (size_t)pos) * 128 + 8 * seg;
+  *reinterpret_cast<uint4*>(Qp + dst) = q;
+  *reinterpret_cast<uint4*>(dOp + dst) = g;
+  if (seg == 0) {
+    Dp[bh * Npad + pos] = s;
+    lsep[bh * Npad + pos] = valid ? lse[bh * N + tok] * kLog2e : 0.f;
+    if (valid) Dnat[bh * N + tok] = s;
+  }
 }
 
 // Selection bitmap of one CSR row (one workgroup per row, nwords <= 256).
@@ -122,15 +142,14 @@ __global__ __launch_bounds__(1024) void col_scan_kernel(const int32_t* __restric
 }
 
 struct DkdvArgs {
-  const uint16_t* Q;
+  const uint16_t* Qp;   // Q, dO, LSE * log2 e and D in query block order ([B*H][Npad])
   const uint16_t* K;
   const uint16_t* V;
-  const uint16_t* dO;
-  const float* lse;
-  const float* delta;
+  const uint16_t* dOp;
+  const float* lsep;
+  const float* Dp;
   const int32_t* col_ptr;
   const int32_t* row_idx;
-  const int32_t* qperm;
   const int32_t* qstart;
   const int32_t* kvperm;
   const int32_t* kvstart;
@@ -138,7 +157,7 @@ struct DkdvArgs {
   const float* scale;
   uint16_t* dK;
   uint16_t* dV;
-  int n_kvitems, H, N, nkv;
+  int n_kvitems, H, N, nkv, Npad;
 };
 
 // Walks the query blocks of a CSC column as 64-query chunks.
@@ -229,43 +248,37 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
   cur.sub = 0;
   qcur_load(cur, a.row_idx, a.qstart);
 
-  // Loader roles: rows 16w + 4i + lane/16 of the Q and dO tiles (direct loads, swizzled), and
-  // threads 0..63 stage lse2 / D of query row t (padding rows: lse2 = +inf, D = 0).
-  const int lrow0 = 16 * wave + (lane >> 4);
-  int ids[4];
-  float st_lse = 0.f, st_d = 0.f;
-  auto chunk_ids = [&](QChunk c) {
+  // Loader roles: wave w copies rows 16w + 4i + lane/16 of a chunk's Q and dO tiles (direct
+  // global->LDS copies into swizzled rows); wave 0 copies the chunk's 64 LSE values and wave 1
+  // its 64 D values. Everything is read in query block order, so a chunk is consecutive rows
+  // starting at its position and the copies need no token ids. Rows past a chunk's end (the next
+  // block's queries, or zero padding) get LSE = +inf once their copy has landed, so their P and
+  // dS are exactly 0.
+  const int lgrp = lane >> 4;
+  const size_t qoff = (size_t)bh * a.Npad;
+  const uint16_t* const qbase = a.Qp + qoff * D;
+  const uint16_t* const gbase = a.dOp + qoff * D;
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    voff[i] = (uint32_t)((16 * wave + 4 * i + lgrp) * kRowBytes) +
+              16u * (uint32_t)((lane & 15) ^ lds_key(16 * wave + 4 * i + lgrp));
+  auto chunk_issue = [&](QChunk c, uint32_t st_m0) {
+    const uint16_t* qb = qbase + (size_t)c.pos * D;
+    const uint16_t* gb = gbase + (size_t)c.pos * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = lrow0 + 4 * i;
-      ids[i] = a.qperm[c.pos + (rr < c.nv ? rr : 0)];
+      const uint32_t m0v = st_m0 + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
+      lds_dma16_so(qb, voff[i], m0v);
+      lds_dma16_so(gb, voff[i], m0v + kTileBytes);
     }
+    if (wave == 0) lds_dma4_so(a.lsep + qoff + c.pos, 4u * lane, st_m0 + 2 * kTileBytes);
+    if (wave == 1)
+      lds_dma4_so(a.Dp + qoff + c.pos, 4u * lane, st_m0 + 2 * kTileBytes + kChunkQ * 4);
   };
-  auto chunk_issue = [&](QChunk c, char* st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lunit = (lane & 15) ^ lds_key(lrow0 + 4 * i);
-      const size_t o = head_off + (size_t)ids[i] * D + 8 * lunit;
-      char* dst = st + (16 * wave + 4 * i) * kRowBytes;
-      lds_dma16(a.Q + o, dst);
-      lds_dma16(a.dO + o, dst + kTileBytes);
-    }
-    if (t < kChunkQ) {
-      if (t < c.nv) {
-        const size_t n = (size_t)bh * a.N + a.qperm[c.pos + t];
-        st_lse = a.lse[n] * kLog2e;
-        st_d = a.delta[n];
-      } else {
-        st_lse = INFINITY;
-        st_d = 0.f;
-      }
-    }
-  };
-  auto chunk_finish = [&](char* st) {
-    if (t < kChunkQ) {
-      reinterpret_cast<float*>(st + 2 * kTileBytes)[t] = st_lse;
-      reinterpret_cast<float*>(st + 2 * kTileBytes + kChunkQ * 4)[t] = st_d;
-    }
+  // After this wave's copies have landed: padding rows of a partial chunk get LSE = +inf.
+  auto chunk_finish = [&](QChunk c, char* st) {
+    if (wave == 0 && lane >= c.nv) reinterpret_cast<float*>(st + 2 * kTileBytes)[lane] = INFINITY;
   };
 
   // Transposing-read offsets (as for V^T in the forward kernel).
@@ -273,21 +286,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
   const int vunit_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int vhalf_l = 8 * (lane & 1);
 
+  const uint32_t m0_a = lds_addr(lds_a), m0_b = lds_addr(lds_b);
   QChunk c0 = qcur_take(cur, a.row_idx, a.qstart);
-  if (c0.nv > 0) {
-    chunk_ids(c0);
-    chunk_issue(c0, lds_a);
-    chunk_finish(lds_a);
-  }
+  if (c0.nv > 0) chunk_issue(c0, m0_a);
   QChunk c1 = qcur_take(cur, a.row_idx, a.qstart);
-  if (c1.nv > 0) chunk_ids(c1);
   vmem_wait_all();
+  if (c0.nv > 0) chunk_finish(c0, lds_a);
   __syncthreads();
 
-  auto step = [&](const char* st, char* nx) {
-    if (c1.nv > 0) chunk_issue(c1, nx);
+  auto step = [&](const char* st, char* nx, uint32_t nx_m0) {
+    if (c1.nv > 0) chunk_issue(c1, nx_m0);
     const QChunk c2n = qcur_take(cur, a.row_idx, a.qstart);
-    if (c2n.nv > 0) chunk_ids(c2n);
 
     const float* lse2 = reinterpret_cast<const float*>(st + 2 * kTileBytes);
     const float* dd = reinterpret_cast<const float*>(st + 2 * kTileBytes + kChunkQ * 4);
@@ -362,17 +371,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
         }
       }
     }
-    if (c1.nv > 0) chunk_finish(nx);
     vmem_wait_all();
+    if (c1.nv > 0) chunk_finish(c1, nx);
     __syncthreads();
     c0 = c1;
     c1 = c2n;
   };
   while (true) {
     if (c0.nv <= 0) break;
-    step(lds_a, lds_b);
+    step(lds_a, lds_b, m0_b);
     if (c0.nv <= 0) break;
-    step(lds_b, lds_a);
+    step(lds_b, lds_a, m0_a);
   }
 
   if (!kvvalid) return;
@@ -402,16 +411,21 @@ hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, cons
   const BwdWs L = bwd_ws_layout(p);
   char* base = static_cast<char*>(ws);
   float* delta = reinterpret_cast<float*>(base + L.delta);
+  uint16_t* Qp = reinterpret_cast<uint16_t*>(base + L.qp);
+  uint16_t* dOp = reinterpret_cast<uint16_t*>(base + L.gp);
+  float* lsep = reinterpret_cast<float*>(base + L.lsep);
+  float* Dp = reinterpret_cast<float*>(base + L.dp);
+  const int Npad = p.prob.N + kPermPad;
   uint32_t* bm = reinterpret_cast<uint32_t*>(base + L.bitmap);
   int32_t* col_cnt = reinterpret_cast<int32_t*>(base + L.col_cnt);
   int32_t* col_ptr = reinterpret_cast<int32_t*>(base + L.col_ptr);
   int32_t* row_idx = reinterpret_cast<int32_t*>(base + L.row_idx);
   const int BH = p.prob.B * p.prob.H;
-  const int64_t tok_rows = (int64_t)BH * p.prob.N;
   const int64_t rows = (int64_t)BH * p.nq, cols = (int64_t)BH * p.nkv;
   hipError_t e;
-  delta_kernel<<<(unsigned)((tok_rows + 15) / 16), 256, 0, s>>>(
-      static_cast<const uint16_t*>(O), static_cast<const uint16_t*>(dO), tok_rows, delta);
+  bwd_prep_kernel<<<dim3((Npad + 15) / 16, BH), 256, 0, s>>>(
+      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(O),
+      static_cast<const uint16_t*>(dO), lse, p.qperm, p.prob.N, Npad, Qp, dOp, lsep, Dp, delta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   csr_bitmap_kernel<<<(unsigned)rows, 256, 0, s>>>(row_ptr, col_idx, L.nwords, bm);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -425,15 +439,15 @@ hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, cons
                                      row_idx);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   DkdvArgs a{};
-  a.Q = static_cast<const uint16_t*>(Q);
+  a.Qp = Qp;
   a.K = static_cast<const uint16_t*>(K);
   a.V = static_cast<const uint16_t*>(V);
-  a.dO = static_cast<const uint16_t*>(dO);
-  a.lse = lse;
-  a.delta = delta;
+  a.dOp = dOp;
+  a.lsep = lsep;
+  a.Dp = Dp;
+  a.Npad = Npad;
   a.col_ptr = col_ptr;
   a.row_idx = row_idx;
-  a.qperm = p.qperm;
   a.qstart = p.qstart;
   a.kvperm = p.kvperm;
   a.kvstart = p.kvstart;

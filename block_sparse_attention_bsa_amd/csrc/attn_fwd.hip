@@ -118,7 +118,7 @@ struct MfmaArgs {
   float* lse;           // kFwd (nullable) and kLse
   float* part;          // kMass: [bh][item][wave][nkv] per-wave block sums
   int n_items, H, N, nq, nkv;
-  int Npad;  // K and V are permuted into block order: [B*H][Npad][d], Npad = N + 32
+  int Npad;  // K and V are permuted into block order: [B*H][Npad][d], Npad = N + kPermPad
 };
 
 // Two LDS stages: tile t is computed while tile t+1 streams in.

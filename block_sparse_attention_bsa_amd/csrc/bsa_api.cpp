@@ -139,7 +139,11 @@ BwdWs bwd_ws_layout(const bsa_plan& p) {
   const size_t perm_bytes = BH * (size_t)(p.prob.N + kPermPad) * p.prob.d * 2;
   w.kp = w.row_idx + align_up(rows * p.nkv * 4);
   w.vp = w.kp + align_up(perm_bytes);
-  w.total = w.vp + align_up(perm_bytes);
+  w.qp = w.vp + align_up(perm_bytes);
+  w.gp = w.qp + align_up(perm_bytes);
+  w.lsep = w.gp + align_up(perm_bytes);
+  w.dp = w.lsep + align_up(BH * (size_t)(p.prob.N + kPermPad) * 4);
+  w.total = w.dp + align_up(BH * (size_t)(p.prob.N + kPermPad) * 4);
   return w;
 }
 

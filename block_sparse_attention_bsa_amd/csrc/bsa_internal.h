@@ -47,8 +47,9 @@ SelectWs select_ws_layout(const bsa_plan& p);
 struct BwdWs {
   // D = rowsum(dO * O) per token; CSR row bitmap; CSC (per (head, kv block) ascending q-block
   // lists): per-column counts, column pointers, row ids.
-  // K and V in block order for the dQ pass.
-  size_t delta, bitmap, col_cnt, col_ptr, row_idx, kp, vp, total;
+  // K and V in block order for the dQ pass; Q, dO, LSE * log2 e and D in query block order
+  // for the dK/dV pass.
+  size_t delta, bitmap, col_cnt, col_ptr, row_idx, kp, vp, qp, gp, lsep, dp, total;
   int nwords;
 };
 BwdWs bwd_ws_layout(const bsa_plan& p);
@@ -59,9 +60,10 @@ struct CalibWs {
 };
 CalibWs calib_ws_layout(const bsa_plan& p);
 
-// Rows appended to each head of a block-ordered K or V copy, so that the 32 rows read for any
-// chunk exist.
-constexpr int kPermPad = 32;
+// Zero rows appended to each head of a block-ordered copy (K, V; Q, dO, LSE, D), so that the
+// rows read for any chunk exist and are finite: 32 for a forward chunk, 64 for a backward
+// query chunk.
+constexpr int kPermPad = 64;
 
 struct FwdWs {
   size_t kp, vp, total;  // K and V in block order, [B*H][N + kPermPad][d] (bf16, d = 128 path)

@@ -132,6 +132,14 @@ __device__ __forceinline__ void lds_dma16_so(const void* sbase, uint32_t voff, u
                : "m0", "memory");
 }
 
+// 4 bytes per lane (global_load_lds_dword): lane i writes LDS bytes [m0v + 4 i, +4).
+__device__ __forceinline__ void lds_dma4_so(const void* sbase, uint32_t voff, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0v)
+               : "m0", "memory");
+}
+
 // LDS byte address of a __shared__ location, as a wave-uniform value (for M0).
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_char_t*)p));

@@ -225,7 +225,7 @@ def test_workspace_capacity_errors():
     w = replace(CONFIGS[2], grid=(4, 8, 8), H=1)
     layer = _layer(w)
     p = layer.plan
-    per = w.B * w.H * (p.N + 32) * w.d * 2
+    per = w.B * w.H * (p.N + 64) * w.d * 2
     assert p.ws_fwd >= 2 * per
     q = torch.zeros((w.B, w.H, p.N, w.d), dtype=torch.bfloat16, device="cuda")
     out, lse = torch.empty_like(q), torch.empty(q.shape[:3], device="cuda")
