@@ -25,6 +25,7 @@ constexpr int kRowBytes = 256;
 constexpr int kChunkQ = 64;                     // queries per streamed chunk
 constexpr int kTileBytes = kChunkQ * kRowBytes;  // one of Q / dO
 constexpr int kStage = 2 * kTileBytes + 2 * kChunkQ * 4;  // Q, dO, lse2, D
+constexpr int kKvTileBytes = 2 * 128 * kRowBytes;          // an item's K and V rows
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(1024) void col_scan_kernel(const int32_t* __restric
 
 struct DkdvArgs {
   const uint16_t* Qp;   // Q, dO, LSE * log2 e and D in query block order ([B*H][Npad])
-  const uint16_t* K;
-  const uint16_t* V;
+  const uint16_t* Kp;   // K and V in kv block order ([B*H][Npad][d])
+  const uint16_t* Vp;
   const uint16_t* dOp;
   const float* lsep;
   const float* Dp;
@@ -200,10 +201,16 @@ __device__ __forceinline__ QChunk qcur_take(QCursor& c, const int32_t* __restric
   return k;
 }
 
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
+// Eight wavefronts: wave w owns kv tokens 32 (w % 4) .. +32 of the 128-token item and query half
+// w / 4 (32 queries) of every 64-query chunk, so two wavefronts share each SIMD; the two halves'
+// partial dK and dV are summed through LDS at the end (a fixed order: deterministic).
+__global__ __launch_bounds__(512, 2) void dkdv_kernel(const DkdvArgs a) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(1024))) char lds_a[kStage];
-  __shared__ __attribute__((aligned(1024))) char lds_b[kStage];
+  // Two Q/dO stages, then this item's K and V tiles (128 rows each, swizzled like the stages).
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kStage + kKvTileBytes];
+  char* const lds_a = lds;
+  char* const lds_b = lds + kStage;
+  char* const kv_lds = lds + 2 * kStage;
 
   const int total = a.n_kvitems * (int)gridDim.y;
   const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
@@ -216,20 +223,29 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int kvg = wave & 3, mb = wave >> 2;  // kv group, query half
   const int l32 = lane & 31, hl = lane >> 5;
 
-  // K and V fragments of this lane's kv token (B operands of S = Q K^T and dP = dO V^T).
-  const int kvrow = 32 * wave + l32;
+  // This lane's kv token. The item's 128 rows of K and V (block order, so consecutive rows from
+  // k0; rows past the item's end are other tokens or zero padding, all finite) are copied into
+  // LDS once; the S and dP MFMAs read their B operands (K and V fragments) from there, which
+  // keeps the register budget within two wavefronts per SIMD.
+  const int kvrow = 32 * kvg + l32;
   const bool kvvalid = kvrow < nkvrows;
+  const bool active = 32 * kvg < nkvrows;  // wave-uniform
   const int kvtok = kvvalid ? a.kvperm[k0 + kvrow] : 0;
-  bf16x8_t kf[8], vf[8];
   {
-    const uint4* kp = reinterpret_cast<const uint4*>(a.K + head_off + (size_t)kvtok * D + 8 * hl);
-    const uint4* vp = reinterpret_cast<const uint4*>(a.V + head_off + (size_t)kvtok * D + 8 * hl);
+    const uint16_t* kb = a.Kp + ((size_t)bh * a.Npad + k0) * D;
+    const uint16_t* vb = a.Vp + ((size_t)bh * a.Npad + k0) * D;
+    const uint32_t kv_m0 = lds_addr(kv_lds);
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      kf[kc] = __builtin_bit_cast(bf16x8_t, kvvalid ? kp[2 * kc] : make_uint4(0, 0, 0, 0));
-      vf[kc] = __builtin_bit_cast(bf16x8_t, kvvalid ? vp[2 * kc] : make_uint4(0, 0, 0, 0));
+    for (int i = 0; i < 4; ++i) {  // wave w: rows 16w + 4i + lane/16
+      const int row = 16 * wave + 4 * i + (lane >> 4);
+      const uint32_t vo =
+          (uint32_t)(row * kRowBytes) + 16u * (uint32_t)((lane & 15) ^ lds_key(row));
+      const uint32_t m0v = kv_m0 + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
+      lds_dma16_so(kb, vo, m0v);
+      lds_dma16_so(vb, vo, m0v + kKvTileBytes / 2);
     }
   }
   f32x16_t dk[4], dv[4];  // dK^T, dV^T: lane = kv token, registers = d
@@ -248,9 +264,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
   cur.sub = 0;
   qcur_load(cur, a.row_idx, a.qstart);
 
-  // Loader roles: wave w copies rows 16w + 4i + lane/16 of a chunk's Q and dO tiles (direct
-  // global->LDS copies into swizzled rows); wave 0 copies the chunk's 64 LSE values and wave 1
-  // its 64 D values. Everything is read in query block order, so a chunk is consecutive rows
+  // Loader roles: wave w copies rows 8w + 4i + lane/16 (i = 0, 1) of a chunk's Q and dO tiles
+  // (direct global->LDS copies into swizzled rows); wave 0 copies the chunk's 64 LSE values and
+  // wave 1 its 64 D values. Everything is read in query block order, so a chunk is consecutive rows
   // starting at its position and the copies need no token ids. Rows past a chunk's end (the next
   // block's queries, or zero padding) get LSE = +inf once their copy has landed, so their P and
   // dS are exactly 0.
@@ -258,17 +274,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
   const size_t qoff = (size_t)bh * a.Npad;
   const uint16_t* const qbase = a.Qp + qoff * D;
   const uint16_t* const gbase = a.dOp + qoff * D;
-  uint32_t voff[4];
+  uint32_t voff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    voff[i] = (uint32_t)((16 * wave + 4 * i + lgrp) * kRowBytes) +
-              16u * (uint32_t)((lane & 15) ^ lds_key(16 * wave + 4 * i + lgrp));
+  for (int i = 0; i < 2; ++i)
+    voff[i] = (uint32_t)((8 * wave + 4 * i + lgrp) * kRowBytes) +
+              16u * (uint32_t)((lane & 15) ^ lds_key(8 * wave + 4 * i + lgrp));
   auto chunk_issue = [&](QChunk c, uint32_t st_m0) {
     const uint16_t* qb = qbase + (size_t)c.pos * D;
     const uint16_t* gb = gbase + (size_t)c.pos * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t m0v = st_m0 + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t m0v = st_m0 + (uint32_t)((8 * wave + 4 * i) * kRowBytes);
       lds_dma16_so(qb, voff[i], m0v);
       lds_dma16_so(gb, voff[i], m0v + kTileBytes);
     }
@@ -300,9 +316,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
 
     const float* lse2 = reinterpret_cast<const float*>(st + 2 * kTileBytes);
     const float* dd = reinterpret_cast<const float*>(st + 2 * kTileBytes + kChunkQ * 4);
-    // One 32-query half (M block) at a time, to keep few registers live.
-#pragma unroll 1
-    for (int mb = 0; mb < 2; ++mb) {
+    // This wave's 32-query half (M block) of the chunk; kv groups past a ragged item's end skip.
+    if (active) {
       // S = Q K^T and dP = dO V^T (lane = kv token, registers = query).
       const int row = 32 * mb + l32;
       const char* qp = st + row * kRowBytes;
@@ -313,12 +328,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
         sacc[e] = 0.f;
         dpacc[e] = 0.f;
       }
+      const char* kr = kv_lds + kvrow * kRowBytes;
+      const char* vr = kr + kKvTileBytes / 2;
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc) {
         const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qp + lds_swz(row, 2 * kc + hl));
         const bf16x8_t ga = *reinterpret_cast<const bf16x8_t*>(gp + lds_swz(row, 2 * kc + hl));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kc], sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[kc], dpacc, 0, 0, 0);
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(kr + lds_swz(kvrow, 2 * kc + hl));
+        const bf16x8_t vf =
+            *reinterpret_cast<const bf16x8_t*>(vr + lds_swz(kvrow, 2 * kc + hl));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf, sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf, dpacc, 0, 0, 0);
       }
       // P = exp(sigma s - lse) and dS = P (dP - D), rounded to bf16 (B operands below).
       uint32_t pw[8], dw[8];
@@ -384,7 +405,30 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const DkdvArgs a) {
     step(lds_b, lds_a, m0_a);
   }
 
-  if (!kvvalid) return;
+  // Sum the two query halves' partial dK^T and dV^T in a fixed order: the half-1 waves store
+  // theirs ([kv group][register][lane] floats, 64 KB, in the now idle stages), the half-0 waves
+  // add them; dK first, then dV.
+  static_assert(4 * 64 * 64 * 4 <= 2 * kStage, "reduction buffer");
+  float* red = reinterpret_cast<float*>(lds) + kvg * 64 * 64 + lane;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    f32x16_t* acc = pass == 0 ? dk : dv;
+    if (mb == 1) {
+#pragma unroll
+      for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[(16 * dm + e) * 64] = acc[dm][e];
+    }
+    __syncthreads();
+    if (mb == 0) {
+#pragma unroll
+      for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[dm][e] += red[(16 * dm + e) * 64];
+    }
+    __syncthreads();
+  }
+  if (mb != 0 || !kvvalid) return;
   const float sig = a.scale[bh % a.H];
   uint16_t* kop = a.dK + head_off + (size_t)kvtok * D;
   uint16_t* vop = a.dV + head_off + (size_t)kvtok * D;
@@ -427,6 +471,8 @@ hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, cons
       static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(O),
       static_cast<const uint16_t*>(dO), lse, p.qperm, p.prob.N, Npad, Qp, dOp, lsep, Dp, delta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_permute_rows(p, K, base + L.kp, s)) != hipSuccess) return e;
+  if ((e = launch_permute_rows(p, V, base + L.vp, s)) != hipSuccess) return e;
   csr_bitmap_kernel<<<(unsigned)rows, 256, 0, s>>>(row_ptr, col_idx, L.nwords, bm);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned cblocks = (unsigned)((cols + 255) / 256);
@@ -440,8 +486,8 @@ hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, cons
   if ((e = hipGetLastError()) != hipSuccess) return e;
   DkdvArgs a{};
   a.Qp = Qp;
-  a.K = static_cast<const uint16_t*>(K);
-  a.V = static_cast<const uint16_t*>(V);
+  a.Kp = reinterpret_cast<const uint16_t*>(base + L.kp);
+  a.Vp = reinterpret_cast<const uint16_t*>(base + L.vp);
   a.dOp = dOp;
   a.lsep = lsep;
   a.Dp = Dp;
@@ -459,9 +505,7 @@ hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, cons
   a.H = p.prob.H;
   a.N = p.prob.N;
   a.nkv = p.nkv;
-  dkdv_kernel<<<dim3(p.n_kvitems, BH), 256, 0, s>>>(a);
+  dkdv_kernel<<<dim3(p.n_kvitems, BH), 512, 0, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_permute_rows(p, K, base + L.kp, s)) != hipSuccess) return e;
-  if ((e = launch_permute_rows(p, V, base + L.vp, s)) != hipSuccess) return e;
   return launch_attn_dq(p, Q, base + L.kp, base + L.vp, dO, lse, delta, row_ptr, col_idx, dQ, s);
 }

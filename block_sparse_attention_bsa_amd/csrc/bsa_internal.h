@@ -62,8 +62,8 @@ CalibWs calib_ws_layout(const bsa_plan& p);
 
 // Zero rows appended to each head of a block-ordered copy (K, V; Q, dO, LSE, D), so that the
 // rows read for any chunk exist and are finite: 32 for a forward chunk, 64 for a backward
-// query chunk.
-constexpr int kPermPad = 64;
+// query chunk, 128 for the K/V rows of a backward kv item.
+constexpr int kPermPad = 128;
 
 struct FwdWs {
   size_t kp, vp, total;  // K and V in block order, [B*H][N + kPermPad][d] (bf16, d = 128 path)
