@@ -15,9 +15,11 @@
 //                      lse, D; double-buffered direct copies of consecutive block-order rows). Per chunk and wave: S = Q K^T and
 //                      dP = dO V^T (lane = kv token), P and dS in registers, then
 //                      dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T from transposing reads.
-//   4. dQ              the forward kernel's kDq mode over the CSR (one workgroup per query block).
+//   4. dq_kernel       query-stationary over the CSR (one workgroup per 128 queries), K and V
+//                      tiles from block-ordered copies, S and dP recomputed per tile.
 #include "bsa_internal.h"
 #include "device_common.h"
+#include "kv_cursor.h"
 
 namespace {
 
@@ -446,6 +448,224 @@ __global__ __launch_bounds__(512, 2) void dkdv_kernel(const DkdvArgs a) {
     }
 }
 
+// ------------------------------------------------------------------------------- dQ pass
+
+struct DqArgs {
+  const uint16_t* Q;
+  const uint16_t* dO;
+  const uint16_t* Kp;  // K and V in kv block order ([B*H][Npad][d])
+  const uint16_t* Vp;
+  const float* lse;    // forward LSE per token
+  const float* delta;  // D per token
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* qperm;
+  const int32_t* qstart;
+  const int32_t* kvstart;
+  const int32_t* items;
+  const float* scale;
+  uint16_t* dQ;
+  int n_items, H, N, nq, nkv, Npad;
+};
+
+// dQ_i = sigma sum_j dS_ij k_j over the CSR row of i's query block, dS = P (dP - D) with
+// P = exp(sigma q.k - lse) and dP = dO.v recomputed per tile. Query-stationary: a workgroup owns
+// 128 queries of one query block and streams the selected K/V as 64-token tiles (two 32-token
+// chunks) through two LDS stages, as the forward pass does. Eight wavefronts, two per SIMD:
+// wave w owns queries 32 (w % 4) .. +32 and chunk w / 4 of every tile; the two chunks' partial
+// dQ are summed through LDS at the end in a fixed order.
+__global__ __launch_bounds__(512, 2) void dq_kernel(const DqArgs a) {
+  constexpr int D = 128;
+  constexpr int kTile = 64 * kRowBytes;  // one of K / V
+  constexpr int kDqStage = 2 * kTile;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kDqStage];
+  char* const lds_a = lds;
+  char* const lds_b = lds + kDqStage;
+
+  const int n_items = a.n_items;
+  const int total = n_items * (int)gridDim.y;
+  const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
+  const int bh = lin / n_items, item = lin % n_items;
+  const int I = ld_ro(a.items + 2 * item), off = ld_ro(a.items + 2 * item + 1);
+  const int q0 = ld_ro(a.qstart + I) + off;
+  const int nrows = min(128, ld_ro(a.qstart + I + 1) - q0);
+  const int64_t r = (int64_t)bh * a.nq + I;
+  const size_t head_off = (size_t)bh * a.N * D;
+  const float c2 = ld_ro(a.scale + bh % a.H) * kLog2e;
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int qg = wave & 3, kh = wave >> 2;  // query group, chunk of the tile
+  const int l32 = lane & 31, hl = lane >> 5;
+  const bool active = 32 * qg < nrows;  // wave-uniform
+
+  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T): query 32 qg + l32.
+  const int qrow = 32 * qg + l32;
+  const bool qvalid = qrow < nrows;
+  const int qtok = qvalid ? a.qperm[q0 + qrow] : 0;
+  bf16x8_t qf[8], dof[8];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.Q + head_off + (size_t)qtok * D + 8 * hl);
+    const uint4* gp = reinterpret_cast<const uint4*>(a.dO + head_off + (size_t)qtok * D + 8 * hl);
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      qf[kc] = __builtin_bit_cast(bf16x8_t, qvalid ? qp[2 * kc] : make_uint4(0, 0, 0, 0));
+      dof[kc] = __builtin_bit_cast(bf16x8_t, qvalid ? gp[2 * kc] : make_uint4(0, 0, 0, 0));
+    }
+  }
+  // log2-domain -lse (-inf for padding queries, so their P is 0) and D of this lane's query.
+  const float nlse2 = qvalid ? -a.lse[(size_t)bh * a.N + qtok] * kLog2e : -INFINITY;
+  const float dq_d = qvalid ? a.delta[(size_t)bh * a.N + qtok] : 0.f;
+  f32x16_t acc[4];  // dQ^T: lane = query, registers = d
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+
+  Cursor cur;
+  cur.slot = ld_ro(a.row_ptr + r);
+  cur.end = ld_ro(a.row_ptr + r + 1);
+  cur.sub = 0;
+  cursor_load<false>(cur, a.col_idx, a.kvstart);
+
+  // Loader: wave w copies rows 8 (w % 4) + 4i + lane/16 (i = 0, 1) of chunk w / 4 of a tile, for
+  // K and V, from the block-ordered copies (a chunk is consecutive rows at its position).
+  const int lgrp = lane >> 4;
+  const size_t kv_off = (size_t)bh * a.Npad * D;
+  uint32_t voff[2], roff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int crow = 8 * qg + 4 * i + lgrp;  // row within the chunk
+    const int trow = 32 * kh + crow;         // row within the tile
+    voff[i] = (uint32_t)(crow * kRowBytes) + 16u * (uint32_t)((lane & 15) ^ lds_key(trow));
+    roff[i] = (uint32_t)((32 * kh + 8 * qg + 4 * i) * kRowBytes);
+  }
+  auto tile_issue = [&](Chunk ca, Chunk cb, uint32_t st_m0) {
+    const int pos = (kh && cb.nv > 0) ? cb.pos : ca.pos;
+    const uint16_t* kb = a.Kp + kv_off + (size_t)pos * D;
+    const uint16_t* vb = a.Vp + kv_off + (size_t)pos * D;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lds_dma16_so(kb, voff[i], st_m0 + roff[i]);
+      lds_dma16_so(vb, voff[i], st_m0 + roff[i] + kTile);
+    }
+  };
+
+  // Transposing-read offsets for K^T (as for V^T in the forward kernel).
+  const int vrow_l = 4 * hl + ((lane & 15) >> 2);
+  const int vunit_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vhalf_l = 8 * (lane & 1);
+
+  const uint32_t m0_a = lds_addr(lds_a), m0_b = lds_addr(lds_b);
+  Chunk a0 = take_chunk<false>(cur, a.col_idx, a.kvstart);
+  Chunk b0 = take_chunk<false>(cur, a.col_idx, a.kvstart);
+  if (a0.nv > 0) tile_issue(a0, b0, m0_a);
+  Chunk a1 = take_chunk<false>(cur, a.col_idx, a.kvstart);
+  Chunk b1 = take_chunk<false>(cur, a.col_idx, a.kvstart);
+  vmem_wait_all();
+  __syncthreads();
+
+  auto step = [&](const char* st, uint32_t nx_m0) {
+    const Chunk mine = kh ? b0 : a0;
+    if (active && mine.nv > 0) {
+      // S^T and dP^T for this wave's chunk (32 kv rows) and 32 queries.
+      const int row = 32 * kh + l32;
+      const char* kp = st + row * kRowBytes;
+      const char* vp = st + kTile + row * kRowBytes;
+      f32x16_t sacc, dpacc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sacc[e] = 0.f;
+        dpacc[e] = 0.f;
+      }
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kp + lds_swz(row, 2 * kc + hl));
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vp + lds_swz(row, 2 * kc + hl));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[kc], dpacc, 0, 0, 0);
+      }
+      if (mine.nv < 32) {  // partial chunk: padded kv rows get P = 0
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (8 * (e >> 2) + 4 * hl + (e & 3) >= mine.nv) sacc[e] = -INFINITY;
+      }
+      // dS^T = P^T * (dP^T - D), rounded to bf16 (the B operand of dQ^T += K^T dS^T).
+      uint32_t dw[8];
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e], c2, nlse2));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[e + 1], c2, nlse2));
+        dw[e >> 1] = pack_bf16x2(p0 * (dpacc[e] - dq_d), p1 * (dpacc[e + 1] - dq_d));
+      }
+      // dQ^T += K^T dS^T over the chunk's 32 kv rows (two 16-row k-steps); each K^T fragment is
+      // two transposing 8-byte reads of the K tile.
+#pragma unroll
+      for (int dm = 0; dm < 4; ++dm) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int row_lo = 32 * kh + 16 * kk + vrow_l, row_hi = row_lo + 8;
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)((lds_char_t*)st + row_lo * kRowBytes +
+                             lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_t*)((lds_char_t*)st + row_hi * kRowBytes +
+                             lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          const bf16x8_t kt = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+          const bf16x8_t dsb = __builtin_bit_cast(
+              bf16x8_t, make_uint4(dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]));
+          acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb, acc[dm], 0, 0, 0);
+        }
+      }
+    }
+    // The next tile's copies (issued after this tile's MFMAs have been issued).
+    const Chunk an = take_chunk<false>(cur, a.col_idx, a.kvstart);
+    const Chunk bn = take_chunk<false>(cur, a.col_idx, a.kvstart);
+    if (a1.nv > 0) tile_issue(a1, b1, nx_m0);
+    vmem_wait_all();
+    __syncthreads();
+    a0 = a1;
+    b0 = b1;
+    a1 = an;
+    b1 = bn;
+  };
+  while (true) {
+    if (a0.nv <= 0) break;
+    step(lds_a, m0_b);
+    if (a0.nv <= 0) break;
+    step(lds_b, m0_a);
+  }
+
+  // Sum the two chunks' partial dQ^T in a fixed order: chunk-1 waves store theirs
+  // ([query group][register][lane] floats, 64 KB, in the idle stages), chunk-0 waves add them.
+  static_assert(4 * 64 * 64 * 4 <= 2 * kDqStage, "reduction buffer");
+  float* red = reinterpret_cast<float*>(lds) + qg * 64 * 64 + lane;
+  if (kh == 1) {
+#pragma unroll
+    for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[(16 * dm + e) * 64] = acc[dm][e];
+  }
+  __syncthreads();
+  if (kh == 1 || !qvalid) return;
+#pragma unroll
+  for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dm][e] += red[(16 * dm + e) * 64];
+  const float sig = a.scale[bh % a.H];  // dQ = sigma_h dS K
+  uint16_t* op = a.dQ + head_off + (size_t)qtok * D;
+#pragma unroll
+  for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[dm][4 * g] * sig, acc[dm][4 * g + 1] * sig);
+      pk.y = pack_bf16x2(acc[dm][4 * g + 2] * sig, acc[dm][4 * g + 3] * sig);
+      *reinterpret_cast<uint2*>(op + 32 * dm + 8 * g + 4 * hl) = pk;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
@@ -507,5 +727,27 @@ hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, cons
   a.nkv = p.nkv;
   dkdv_kernel<<<dim3(p.n_kvitems, BH), 512, 0, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_attn_dq(p, Q, base + L.kp, base + L.vp, dO, lse, delta, row_ptr, col_idx, dQ, s);
+  DqArgs q{};
+  q.Q = static_cast<const uint16_t*>(Q);
+  q.dO = static_cast<const uint16_t*>(dO);
+  q.Kp = a.Kp;
+  q.Vp = a.Vp;
+  q.lse = lse;
+  q.delta = delta;
+  q.row_ptr = row_ptr;
+  q.col_idx = col_idx;
+  q.qperm = p.qperm;
+  q.qstart = p.qstart;
+  q.kvstart = p.kvstart;
+  q.items = p.items;
+  q.scale = p.scale;
+  q.dQ = static_cast<uint16_t*>(dQ);
+  q.n_items = p.n_items;
+  q.H = p.prob.H;
+  q.N = p.prob.N;
+  q.nq = p.nq;
+  q.nkv = p.nkv;
+  q.Npad = Npad;
+  dq_kernel<<<dim3(p.n_items, BH), 512, 0, s>>>(q);
+  return hipGetLastError();
 }

@@ -10,15 +10,17 @@
 //
 // KV stream. The kv blocks of a row (the CSR list, or all blocks for the dense passes) are walked
 // as a sequence of 32-token chunks: block J contributes ceil(|J| / 32) chunks, the last one
-// possibly partial. Chunks are padded per block, not concatenated, so a chunk's token ids are
-// perm[kvstart[J] + 32 * sub + r] and no search is needed; 3D tiles clipped at the grid edge
-// (8..128 tokens) waste at most a few percent.
+// possibly partial. Chunks are padded per block, not concatenated; K and V are first copied into
+// block order (permute_rows_kernel), so a chunk is rows kvstart[J] + 32 * sub .. +32 of that copy
+// and no search is needed; 3D tiles clipped at the grid edge (8..128 tokens) waste at most a few
+// percent.
 //
 // MFMA path. One workgroup = 4 wavefronts = 128 query rows of one query block. Per iteration a
 // 64-token tile (two chunks) of K (and V for the forward pass) is copied global -> LDS with direct
 // 16-byte loads (no staging registers) into one stage while another stage is computed; rows are
 // 256 bytes with the 16-byte units XOR-swizzled by a per-row key, so that the MFMA operand reads
-// (straight 16-byte and transposing 8-byte) are conflict free. Each wavefront computes S^T = K Q^T for its 32 queries with
+// (straight 16-byte and transposing 8-byte) are conflict free. Each wavefront computes
+// S^T = K Q^T for its 32 queries with
 // v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B operand), so each lane holds 16 scores
 // of a single query: the row max needs one cross-half exchange and the row sum none. P^T is
 // converted to bf16 in registers and is directly the B operand of O^T += V^T P^T, whose A operand
@@ -26,64 +28,14 @@
 // running max is raised lazily (only when it grows by more than 2^8), so the O rescale is rare.
 #include "bsa_internal.h"
 #include "device_common.h"
+#include "kv_cursor.h"
 
 namespace {
 
-// ------------------------------------------------------------------------------- KV cursor
-
-struct Cursor {
-  int slot, end, sub, base, size, J;  // position in the block list, current block and its tokens
-};
-
-template <bool kDense>
-__device__ __forceinline__ void cursor_load(Cursor& c, const int32_t* __restrict__ col_idx,
-                                            const int32_t* __restrict__ kvstart) {
-  if (c.slot < c.end) {
-    c.J = kDense ? c.slot : ld_ro(col_idx + c.slot);
-    c.base = ld_ro(kvstart + c.J);
-    c.size = ld_ro(kvstart + c.J + 1) - c.base;
-  } else {
-    c.J = 0;
-    c.base = 0;
-    c.size = 0;
-  }
-}
-
-// One chunk: first token position in perm, number of valid rows (0 = past the end), its block,
-// and whether it is the block's last chunk.
-struct Chunk {
-  int pos, nv, J, last;
-};
-
-template <bool kDense>
-__device__ __forceinline__ Chunk take_chunk(Cursor& c, const int32_t* __restrict__ col_idx,
-                                            const int32_t* __restrict__ kvstart) {
-  Chunk k;
-  if (c.slot < c.end) {
-    k.pos = c.base + 32 * c.sub;
-    k.nv = min(32, c.size - 32 * c.sub);
-    k.J = c.J;
-    k.last = 32 * (c.sub + 1) >= c.size;
-    ++c.sub;
-    if (k.last) {
-      ++c.slot;
-      c.sub = 0;
-      cursor_load<kDense>(c, col_idx, kvstart);
-    }
-  } else {
-    k.pos = 0;
-    k.nv = 0;
-    k.J = 0;
-    k.last = 0;
-  }
-  return k;
-}
-
 // ------------------------------------------------------------------------------- MFMA path
 
-// kFwd: sparse attention; kLse / kMass: the two dense calibration passes; kDq: dQ of the
-// backward pass over the same CSR (S and dP recomputed per tile).
-enum Mode { kFwd = 0, kLse = 1, kMass = 2, kDq = 3 };
+// kFwd: sparse attention; kLse / kMass: the two dense calibration passes.
+enum Mode { kFwd = 0, kLse = 1, kMass = 2 };
 
 
 constexpr int kTileKV = 64;                    // kv tokens per iteration (two chunks)
@@ -111,10 +63,8 @@ struct MfmaArgs {
   const int32_t* kvstart;
   const int32_t* items;
   const float* scale;
-  const float* lse_in;  // kMass, kDq: per-token log-sum-exp (kLse pass / forward)
-  const uint16_t* dO;   // kDq
-  const float* delta;   // kDq: D = rowsum(dO * O) per token
-  uint16_t* O;          // kFwd: O; kDq: dQ
+  const float* lse_in;  // kMass: per-token log-sum-exp (from the kLse pass)
+  uint16_t* O;          // kFwd
   float* lse;           // kFwd (nullable) and kLse
   float* part;          // kMass: [bh][item][wave][nkv] per-wave block sums
   int n_items, H, N, nq, nkv;
@@ -126,7 +76,7 @@ template <int MODE>
 __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   constexpr int D = 128;
   constexpr bool kDense = MODE == kLse || MODE == kMass;  // all kv blocks, not a CSR row
-  constexpr bool kNeedV = MODE == kFwd || MODE == kDq;
+  constexpr bool kNeedV = MODE == kFwd;
   constexpr int kStage = kNeedV ? 2 * kTileBytes : kTileBytes;
   __shared__ __attribute__((aligned(1024))) char lds[2 * kStage];
   char* const lds_a = lds;
@@ -163,20 +113,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     }
   }
 
-  // kDq: dO fragments, the B operand of dP^T = V dO^T, laid out like Q's.
-  bf16x8_t dof[8];
-  if constexpr (MODE == kDq) {
-    const uint4* dp =
-        reinterpret_cast<const uint4*>(a.dO + head_off + (size_t)qtok * D + 8 * hl);
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      uint4 v = qvalid ? dp[2 * kc] : make_uint4(0, 0, 0, 0);
-      dof[kc] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
-
-  f32x16_t oacc[4];  // kFwd: O^T; kDq: dQ^T (lane = query, registers = d)
-  if constexpr (MODE == kFwd || MODE == kDq) {
+  f32x16_t oacc[4];  // kFwd: O^T (lane = query, registers = d)
+  if constexpr (MODE == kFwd) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -188,10 +126,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
   // kMass: log2-domain lse of this lane's query (+inf for padding rows, so they add nothing)
   float nlse2 = 0.f, blk_acc = 0.f;
-  float dq_d = 0.f;  // kDq: this lane's D
-  if constexpr (MODE == kMass || MODE == kDq)
+  if constexpr (MODE == kMass)
     nlse2 = qvalid ? -a.lse_in[(size_t)bh * a.N + qtok] * kLog2e : -INFINITY;
-  if constexpr (MODE == kDq) dq_d = qvalid ? a.delta[(size_t)bh * a.N + qtok] : 0.f;
 
   // Loader role: wave w fills tile rows 16w + 4i + lane/16 (i = 0..3), 16-byte unit lane%16 of
   // the swizzled row, for K (and V), with direct global->LDS copies (no staging registers). K and
@@ -302,58 +238,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         }
       }
 
-      if constexpr (MODE == kDq) {
-        // dP^T = V dO^T (A: V rows from LDS, like K), then dS^T = P^T * (dP^T - D) in bf16.
-        f32x16_t dpacc[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const int row = 32 * mb + l32;
-          const char* vp = st + kTileBytes + row * kRowBytes;
-          bf16x8_t vfr[8];
-#pragma unroll
-          for (int kc = 0; kc < 8; ++kc)
-            vfr[kc] = *reinterpret_cast<const bf16x8_t*>(vp + lds_swz(row, 2 * kc + hl));
-#pragma unroll
-          for (int e = 0; e < 16; ++e) dpacc[mb][e] = 0.f;
-#pragma unroll
-          for (int kc = 0; kc < 8; ++kc)
-            dpacc[mb] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[kc], dof[kc], dpacc[mb], 0, 0, 0);
-        }
-        uint32_t dw[2][8];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; e += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nlse2));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e + 1], c2, nlse2));
-            dw[mb][e >> 1] = pack_bf16x2(p0 * (dpacc[mb][e] - dq_d), p1 * (dpacc[mb][e + 1] - dq_d));
-          }
-        // dQ^T += K^T dS^T; each K^T fragment is two transposing 8-byte reads of the K tile.
-#pragma unroll
-        for (int dm = 0; dm < 4; ++dm) {
-          bf16x8_t kt[4];
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) {
-            const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
-            const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16_t*)((lds_char_t*)st + row_lo * kRowBytes +
-                               lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
-            const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16_t*)((lds_char_t*)st + row_hi * kRowBytes +
-                               lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
-            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-            kt[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
-          }
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) {
-            const uint32_t* src = &dw[kc >> 1][4 * (kc & 1)];
-            const bf16x8_t dsb =
-                __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
-            oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[kc], dsb, oacc[dm], 0, 0, 0);
-          }
-        }
-      } else if constexpr (MODE == kMass) {
+      if constexpr (MODE == kMass) {
         // Block sums of exp(sigma q.k - lse): one chunk per M block, flushed at block ends.
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -510,21 +395,6 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   }
 
   if constexpr (MODE == kMass) return;
-  if constexpr (MODE == kDq) {
-    if (!qvalid) return;
-    const float sig = a.scale[bh % a.H];  // dQ = sigma_h dS K
-    uint16_t* op = a.O + head_off + (size_t)qtok * D;
-#pragma unroll
-    for (int dm = 0; dm < 4; ++dm)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 pk;
-        pk.x = pack_bf16x2(oacc[dm][4 * g] * sig, oacc[dm][4 * g + 1] * sig);
-        pk.y = pack_bf16x2(oacc[dm][4 * g + 2] * sig, oacc[dm][4 * g + 3] * sig);
-        *reinterpret_cast<uint2*>(op + 32 * dm + 8 * g + 4 * hl) = pk;
-      }
-    return;
-  }
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
   if constexpr (MODE == kFwd) {
@@ -544,15 +414,10 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     a.lse[(size_t)bh * a.N + qtok] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-// Two waves per SIMD for the forward and calibration passes; the dQ pass holds dO, dP and dQ
-// fragments as well and runs at one wave per SIMD with the full register file.
+// Two waves per SIMD: two workgroups share a CU.
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void attn_mfma_d128(const MfmaArgs a) {
   attn_mfma_body<MODE>(a);
-}
-
-__global__ __launch_bounds__(256, 1) void attn_dq_d128(const MfmaArgs a) {
-  attn_mfma_body<kDq>(a);
 }
 
 // M[bh, I, J] = (sum over I's work items and their active waves of the block sums) / |I|, in fp64
@@ -789,20 +654,3 @@ hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, flo
   return hipGetLastError();
 }
 
-hipError_t launch_attn_dq(const bsa_plan& p, const void* Q, const void* Kp, const void* Vp,
-                          const void* dO, const float* lse, const float* delta,
-                          const int32_t* row_ptr, const int32_t* col_idx, void* dQ,
-                          hipStream_t s) {
-  MfmaArgs a = mfma_args(p);
-  a.Q = static_cast<const uint16_t*>(Q);
-  a.K = static_cast<const uint16_t*>(Kp);
-  a.V = static_cast<const uint16_t*>(Vp);
-  a.dO = static_cast<const uint16_t*>(dO);
-  a.lse_in = lse;
-  a.delta = delta;
-  a.row_ptr = row_ptr;
-  a.col_idx = col_idx;
-  a.O = static_cast<uint16_t*>(dQ);
-  attn_dq_d128<<<dim3(p.n_items, p.prob.B * p.prob.H), 256, 0, s>>>(a);
-  return hipGetLastError();
-}

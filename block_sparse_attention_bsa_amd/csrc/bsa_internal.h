@@ -85,12 +85,6 @@ hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, cons
 hipError_t launch_permute_rows(const bsa_plan& p, const void* src, void* dst, hipStream_t s);
 hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, float* M, void* ws,
                             hipStream_t s);
-// dQ of the backward pass (a mode of the forward MFMA kernel), given D and the forward's LSE;
-// Kp, Vp are K and V in block order (launch_permute_rows).
-hipError_t launch_attn_dq(const bsa_plan& p, const void* Q, const void* Kp, const void* Vp,
-                          const void* dO, const float* lse, const float* delta,
-                          const int32_t* row_ptr, const int32_t* col_idx, void* dQ,
-                          hipStream_t s);
 hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
                            const void* O, const void* dO, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK,
