@@ -191,6 +191,9 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     // S^T for this wave's 32 queries: two 32-kv M blocks (raw, unscaled scores).
     f32x16_t sacc[2];
     if (active) {
+      // Raised wave priority while the matrix phases issue: the co-resident wavefront (the other
+      // workgroup) then fills the gaps with its VALU work instead of competing for issue.
+      __builtin_amdgcn_s_setprio(2);
       {
         bf16x8_t kf[2][8];
 #pragma unroll
@@ -221,6 +224,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     // The next tile's copies are issued while the score MFMAs execute.
     const Chunk an = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
@@ -357,6 +361,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         }
         if constexpr (MODE == kFwd) {
           // O^T += V^T P^T.
+          __builtin_amdgcn_s_setprio(2);
 #pragma unroll
           for (int dm = 0; dm < 4; ++dm) {
             bf16x8_t vf[4];
@@ -376,6 +381,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_s_setprio(0);
         }
       }
     }
