@@ -369,6 +369,207 @@ __global__ __launch_bounds__(256) void emit_kernel(const uint32_t* __restrict__ 
   }
 }
 
+
+// ------------------------------------------------------------------ one wavefront per row
+
+// ROW-pool selection for rows of at most 64 * VPL candidates (VPL = 16 or 32): one wavefront per
+// row (four rows per workgroup), the row held in registers (value j = lane + 64 i), a wave-private
+// LDS histogram per radix pass, and no workgroup barrier at all. Same rule, same exact 2^-56 sums
+// and the same tie order as radix_select: results are identical.
+constexpr int kWaveRowMax = 2048;
+
+struct WaveHist {
+  unsigned int cnt[256];
+  unsigned long long sum[256];
+};
+
+// by_count: target is a count (top-k); else a 2^-56 fixed-point sum. Returns the chosen flags in
+// `sel` (value i of this lane) and the selected count.
+template <int kVpl>
+__device__ uint32_t wave_select(const float (&v)[kVpl], int n, unsigned long long target,
+                                bool by_count, bool all, WaveHist& h, bool (&sel)[kVpl]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[kVpl];
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) key[i] = (lane + 64 * i < n) ? sel_key(v[i]) : 0u;
+  if (all) {
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i) sel[i] = lane + 64 * i < n;
+    return (uint32_t)n;
+  }
+  uint32_t prefix = 0, mask = 0, eq_cnt = 0;
+  unsigned long long above_sum = 0;
+  uint32_t above_cnt = 0;
+  bool every = false;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      h.cnt[4 * lane + k] = 0u;
+      h.sum[4 * lane + k] = 0ull;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i) {
+      if (lane + 64 * i < n && (key[i] & mask) == prefix) {
+        const uint32_t b = (key[i] >> shift) & 255u;
+        atomicAdd(&h.cnt[b], 1u);
+        if (!by_count) atomicAdd(&h.sum[b], sel_fix(v[i]));
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // Bins in descending order: lane l holds bins 255 - 4l - k (k = 0..3).
+    unsigned long long lsum = 0, lcnt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lsum += h.sum[255 - 4 * lane - k];
+      lcnt += h.cnt[255 - 4 * lane - k];
+    }
+    const unsigned long long isum = wave_incl_scan_u64(lsum);
+    const unsigned long long icnt = wave_incl_scan_u64(lcnt);
+    unsigned long long asum = above_sum + (isum - lsum);
+    unsigned long long acnt = above_cnt + (icnt - lcnt);
+    int my_bin = -1;
+    unsigned long long my_asum = 0, my_acnt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int b = 255 - 4 * lane - k;
+      const unsigned long long cur = by_count ? acnt : asum;
+      const unsigned long long mb = by_count ? (unsigned long long)h.cnt[b] : h.sum[b];
+      if (my_bin < 0 && cur < target && cur + mb >= target) {
+        my_bin = b;
+        my_asum = asum;
+        my_acnt = acnt;
+      }
+      asum += h.sum[b];
+      acnt += h.cnt[b];
+    }
+    const unsigned long long found = __ballot(my_bin >= 0);
+    if (found == 0) {  // the target is never reached: keep every candidate
+      every = true;
+      break;
+    }
+    const int src = __ffsll((long long)found) - 1;
+    const int b = __shfl(my_bin, src, 64);
+    above_sum = ((unsigned long long)(uint32_t)__shfl((int)(my_asum >> 32), src, 64) << 32) |
+                (uint32_t)__shfl((int)(uint32_t)my_asum, src, 64);
+    above_cnt = (uint32_t)__shfl((int)my_acnt, src, 64);
+    prefix |= (uint32_t)b << shift;
+    mask |= 255u << shift;
+    eq_cnt = h.cnt[b];
+    __builtin_amdgcn_wave_barrier();
+    if (eq_cnt == 1) break;
+  }
+  if (every) {
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i) sel[i] = lane + 64 * i < n;
+    return (uint32_t)n;
+  }
+  uint32_t m;
+  if (by_count) {
+    m = (uint32_t)(target - above_cnt);
+  } else if (eq_cnt == 1) {
+    m = 1;
+  } else {
+    const unsigned long long vfix = sel_fix(__uint_as_float(prefix));
+    m = (uint32_t)((target - above_sum + vfix - 1) / vfix);
+  }
+  if (m > eq_cnt) m = eq_cnt;
+  // Everything strictly above the boundary class, plus its m lowest-index members.
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) {
+    const bool valid = lane + 64 * i < n;
+    const uint32_t k = key[i] & mask;
+    const bool eq = valid && k == prefix;
+    const unsigned long long bal = __ballot(eq);
+    const uint32_t rank = taken + __popcll(bal & ((1ull << lane) - 1ull));
+    sel[i] = valid && (k > prefix || (eq && rank < m));
+    taken += __popcll(bal);
+  }
+  return above_cnt + m;
+}
+
+// Bitmap words of one row from per-value flags (value j = lane + 64 i): words 2i and 2i + 1.
+template <int kVpl>
+__device__ __forceinline__ void write_row_bits(const bool (&sel)[kVpl], int nwords,
+                                               uint32_t* __restrict__ words) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) {
+    const unsigned long long bal = __ballot(sel[i]);
+    const int w = 2 * i + lane;
+    if (lane < 2 && w < nwords) words[w] = (uint32_t)(bal >> (32 * lane));
+  }
+}
+
+template <int kVpl>
+__global__ __launch_bounds__(256) void mark_row_wave_kernel(const float* __restrict__ S,
+                                                            int64_t rows, int nkv, int nwords,
+                                                            unsigned long long target,
+                                                            bool select_all,
+                                                            uint32_t* __restrict__ bitmap,
+                                                            int32_t* __restrict__ base_counts) {
+  __shared__ WaveHist hist[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+  if (r >= rows) return;  // whole wavefronts
+  const float* row = S + r * nkv;
+  float v[kVpl];
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) v[i] = lane + 64 * i < nkv ? row[lane + 64 * i] : 0.f;
+  bool sel[kVpl];
+  const uint32_t count = wave_select(v, nkv, target, false, select_all, hist[wave], sel);
+  write_row_bits(sel, nwords, bitmap + r * nwords);
+  if (lane == 0) base_counts[r] = (int32_t)count;
+}
+
+template <int kVpl>
+__global__ __launch_bounds__(256) void topup_wave_kernel(const float* __restrict__ S, int64_t rows,
+                                                         int nq, int nkv, int nwords,
+                                                         const int32_t* __restrict__ base_counts,
+                                                         const int32_t* __restrict__ head_k,
+                                                         uint32_t* __restrict__ bitmap) {
+  __shared__ WaveHist hist[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+  if (r >= rows) return;
+  const int k = head_k[r / nq];
+  if (base_counts[r] >= k) return;
+  const float* row = S + r * nkv;
+  float v[kVpl];
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) v[i] = lane + 64 * i < nkv ? row[lane + 64 * i] : 0.f;
+  bool sel[kVpl];
+  wave_select(v, nkv, (unsigned long long)k, true, false, hist[wave], sel);
+  write_row_bits(sel, nwords, bitmap + r * nwords);
+}
+
+// CSR columns of one row from its bitmap (at most 64 words), one wavefront per row: each 64-bit
+// word pair is a mask over 64 consecutive candidates; every set lane writes its column at the
+// running position plus its rank, so the stores of a wavefront are consecutive.
+__global__ __launch_bounds__(256) void emit_wave_kernel(const uint32_t* __restrict__ bitmap,
+                                                        int nwords, int64_t rows,
+                                                        const int32_t* __restrict__ row_ptr,
+                                                        int32_t* __restrict__ col_idx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const uint32_t word = lane < nwords ? bitmap[r * nwords + lane] : 0u;
+  int pos = row_ptr[r];
+  const int end = row_ptr[r + 1];
+  for (int g = 0; 2 * g < nwords; ++g) {
+    const uint32_t lo = (uint32_t)__shfl((int)word, 2 * g, 64);
+    const uint32_t hi = (uint32_t)__shfl((int)word, 2 * g + 1, 64);  // 0 past nwords
+    const unsigned long long m = ((unsigned long long)hi << 32) | lo;
+    const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
+    if ((m >> lane) & 1ull && at < end) col_idx[at] = 64 * g + lane;
+    pos += __popcll(m);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_params& prm,
@@ -385,7 +586,15 @@ hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_par
   const unsigned long long target = all ? 0ull : (unsigned long long)ceil(prm.p * kFix);
   if (rows == 0) return hipSuccess;
 
-  if (prm.pool == BSA_POOL_ROW)
+  const bool wave_rows = p.nkv <= kWaveRowMax;
+  const unsigned wgrid = (unsigned)((rows + 3) / 4);
+  if (prm.pool == BSA_POOL_ROW && p.nkv <= 1024)
+    mark_row_wave_kernel<16><<<wgrid, 256, 0, s>>>(S, rows, p.nkv, L.nwords, target, all, bitmap,
+                                                   base_counts);
+  else if (prm.pool == BSA_POOL_ROW && wave_rows)
+    mark_row_wave_kernel<32><<<wgrid, 256, 0, s>>>(S, rows, p.nkv, L.nwords, target, all, bitmap,
+                                                   base_counts);
+  else if (prm.pool == BSA_POOL_ROW)
     mark_row_kernel<<<(unsigned)rows, 256, 0, s>>>(S, p.nkv, L.nwords, target, all, bitmap,
                                                    base_counts);
   else
@@ -399,13 +608,25 @@ hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_par
                                      prm.fixed_k, head_k_ws, head_k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (use_min_k) {
+  if (use_min_k && wave_rows) {
+    if (p.nkv <= 1024)
+      topup_wave_kernel<16><<<wgrid, 256, 0, s>>>(S, rows, p.nq, p.nkv, L.nwords, base_counts,
+                                                  head_k_ws, bitmap);
+    else
+      topup_wave_kernel<32><<<wgrid, 256, 0, s>>>(S, rows, p.nq, p.nkv, L.nwords, base_counts,
+                                                  head_k_ws, bitmap);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else if (use_min_k) {
     topup_kernel<<<(unsigned)rows, 256, 0, s>>>(S, p.nq, p.nkv, L.nwords, base_counts,
                                                 head_k_ws, bitmap);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   scan_kernel<<<1, 1024, 0, s>>>(base_counts, head_k_ws, use_min_k, rows, p.nq, row_ptr, counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  emit_kernel<<<(unsigned)rows, 256, 0, s>>>(bitmap, L.nwords, row_ptr, col_idx);
+  if (L.nwords <= 64)
+    emit_wave_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(bitmap, L.nwords, rows, row_ptr,
+                                                                col_idx);
+  else
+    emit_kernel<<<(unsigned)rows, 256, 0, s>>>(bitmap, L.nwords, row_ptr, col_idx);
   return hipGetLastError();
 }
