@@ -67,13 +67,15 @@ def _run(w, kvpart, rows=None, tau=None):
     for r, sel in enumerate(rows):
         if len(sel) == 0:
             bh, I = divmod(r, nq)
-            assert np.all(g["dQ"][0, bh, qb[I]] == 0)
-    for bh in range(w.H):
+            b, h = divmod(bh, w.H)
+            assert np.all(g["dQ"][b, h, qb[I]] == 0)
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
         used = set()
         for I in range(nq):
             used.update(rows[bh * nq + I].tolist())
         for J in set(range(len(kb))) - used:
-            assert np.all(g["dK"][0, bh, kb[J]] == 0) and np.all(g["dV"][0, bh, kb[J]] == 0)
+            assert np.all(g["dK"][b, h, kb[J]] == 0) and np.all(g["dV"][b, h, kb[J]] == 0)
     return g
 
 
@@ -92,6 +94,19 @@ def test_bwd_random_rows_with_empty_rows_and_ragged_blocks():
     rng = np.random.default_rng(21)
     rows = []
     for r in range(w.H * len(qb)):
+        k = int(rng.integers(0, len(kb) + 1))
+        rows.append(np.sort(rng.choice(len(kb), size=k, replace=False)))
+    _run(w, kvpart, rows=rows)
+
+
+def test_bwd_batch2_random_rows():
+    w = replace(CONFIGS[5], B=2, grid=(5, 9, 20), H=2)
+    kvpart = ("tile", (4, 4, 8))
+    qb = oracle.partition(w.grid, w.qpart)
+    kb = oracle.partition(w.grid, kvpart)
+    rng = np.random.default_rng(23)
+    rows = []
+    for r in range(w.B * w.H * len(qb)):
         k = int(rng.integers(0, len(kb) + 1))
         rows.append(np.sort(rng.choice(len(kb), size=k, replace=False)))
     _run(w, kvpart, rows=rows)

@@ -104,3 +104,13 @@ def test_calibrate_full_size_sampled():
         f"all row sums within {np.abs(M.sum(-1) - 1).max():.1e} of 1")
     assert err <= 1e-5
     np.testing.assert_allclose(M.sum(-1), 1.0, atol=1e-4)
+
+
+def test_calibrate_masses_batch2():
+    w = replace(CONFIGS[3], B=2, grid=(5, 8, 16), H=2)
+    x = make_inputs(w)
+    _, M, M_ref, _, _ = _calibrate(w, x)
+    err = np.abs(M - M_ref).max()
+    log(f"calibrate B=2: max-abs {err:.2e}")
+    assert err <= 1e-5
+    np.testing.assert_allclose(M.sum(-1), 1.0, atol=1e-5)

@@ -78,3 +78,12 @@ def test_pipeline_c2_reduced():
 
 def test_pipeline_c2_full_size_sampled():
     _run(CONFIGS[2], tol_o=1e-2, tol_lse=1e-3, sample=36)
+
+
+def test_pipeline_batch2_bf16():
+    # B = 2: every kernel indexes (batch, head) pairs as b * H + h; the scales are per head.
+    _run(replace(CONFIGS[2], B=2, grid=(5, 8, 16), H=2), 1e-2, 1e-3)
+
+
+def test_pipeline_batch2_fp32():
+    _run(replace(CONFIGS[1], B=2), 1e-5, 1e-5)
