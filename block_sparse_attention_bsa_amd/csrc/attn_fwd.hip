@@ -25,7 +25,9 @@
 // of a single query: the row max needs one cross-half exchange and the row sum none. P^T is
 // converted to bf16 in registers and is directly the B operand of O^T += V^T P^T, whose A operand
 // comes from two transposing 8-byte LDS reads (ds_read_b64_tr_b16) of the row-major V tile. The
-// running max is raised lazily (only when it grows by more than 2^8), so the O rescale is rare.
+// running max is raised lazily: only when a tile's weights against the current max would sum past
+// 2^32, which is detected from the row sum the softmax needs anyway, so no per-tile max is formed
+// and the O rescale is rare.
 #include "bsa_internal.h"
 #include "device_common.h"
 #include "kv_cursor.h"
@@ -41,9 +43,10 @@ enum Mode { kFwd = 0, kLse = 1, kMass = 2 };
 constexpr int kTileKV = 64;                    // kv tokens per iteration (two chunks)
 constexpr int kRowBytes = 256;                 // one token row of d = 128 bf16
 constexpr int kTileBytes = kTileKV * kRowBytes;
-// Lazy rescaling: the running max used for exp2 is only raised when a tile's max exceeds it by
-// more than this (log2 units), so P stays <= 2^8 and the O rescale is rare.
-constexpr float kRescaleSlack = 8.f;
+// Lazy rescaling: the running max used for exp2 is only raised when a lane's sum of one tile's
+// weights exceeds this, so every weight stays <= 2^32 (bf16 and fp32 hold it, and the fp32 sums
+// over any row stay far from overflow) and the O rescale is rare.
+constexpr float kSumMax = 4294967296.f;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -120,10 +123,9 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   }
+  // l_run: fp32 sum of the weights (for the LSE); lb_run: sum of the same weights rounded to bf16
+  // as the PV product uses them (O is normalised by it, an exactly normalised combination)
   float m_run = -INFINITY, l_run = 0.f, lb_run = 0.f;
-  bf16x8_t ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
   // kMass: log2-domain lse of this lane's query (+inf for padding rows, so they add nothing)
   float nlse2 = 0.f, blk_acc = 0.f;
   if constexpr (MODE == kMass)
@@ -264,43 +266,6 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
           }
         }
       } else {
-        // tt = c2 * s - m_run is the base-2 exponent of this tile's weights. The running max is
-        // raised (and O, l rescaled) only when max tt exceeds the slack: on the first tile (m_run
-        // = -inf makes tt +inf or NaN, and the test below is written to catch both) and rarely
-        // after. Taking the max over tt (outputs of an fma) rather than the raw matrix-core
-        // results lets the compiler skip NaN canonicalisation of every score.
-        float tt[2][16];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) tt[mb][e] = fmaf(sacc[mb][e], c2, -m_run);
-        float mx = fmaxf(tt[0][0], tt[0][1]);
-#pragma unroll
-        for (int i = 2; i < 32; i += 2) mx = fmaxf(mx, fmaxf(tt[i >> 4][i & 15], tt[i >> 4][(i & 15) + 1]));
-        mx = pair_max(mx);
-        const bool grow = !(mx <= kRescaleSlack);
-        if (__ballot(grow) != 0) {
-          // exact tile max of c2 * s (every tile has at least one unmasked kv row)
-          float sm = fmaxf(sacc[0][0], sacc[1][0]);
-#pragma unroll
-          for (int e = 1; e < 16; ++e) sm = fmaxf(sm, fmaxf(sacc[0][e], sacc[1][e]));
-          sm = pair_max(sm) * c2;
-          const float m_new = grow ? sm : m_run;
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          l_run *= alpha;
-          lb_run *= alpha;
-          if constexpr (MODE == kFwd) {
-#pragma unroll
-            for (int dm = 0; dm < 4; ++dm)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) oacc[dm][e] *= alpha;
-          }
-          m_run = m_new;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) tt[mb][e] = fmaf(sacc[mb][e], c2, -m_run);
-        }
         // V^T fragment (d block dm, kv rows 16 kc .. +16) of this tile: two transposing 8-byte
         // LDS reads. The first d block's fragments are read before the weights are formed, so
         // their latency hides behind that VALU work.
@@ -322,24 +287,62 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
           for (int kc = 0; kc < 4; ++kc) vf0[kc] = vfrag(0, kc);
           __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the VALU work below
         }
-        float ls[4];
-        uint32_t pw[2][8];  // P rounded to bf16, two per word (the B operand of the PV product)
+        // Weights p = exp2(c2 * s - m_run) against the running max as it stands, and this
+        // lane's partial sum. No tile max is formed on this path: the sum bounds every weight,
+        // and while it stays <= kSumMax the weights (bf16 for the PV product) and the fp32 sums
+        // cannot overflow. Otherwise (the first tile, where m_run = -inf gives +inf weights, or
+        // a tile far above the running max) the running max is raised to the exact max of
+        // c2 * s so far and the tile's weights are formed again.
+        float pv[2][16];
+        auto weights = [&]() {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int e = 0; e < 16; e += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(tt[mb][e]);
-            const float p1 = __builtin_amdgcn_exp2f(tt[mb][e + 1]);
-            if (mb == 0 && e < 4) {
-              ls[e] = p0;
-              ls[e + 1] = p1;
-            } else {
-              ls[e & 3] += p0;
-              ls[(e & 3) + 1] += p1;
-            }
-            if constexpr (MODE == kFwd) pw[mb][e >> 1] = pack_bf16x2(p0, p1);
+            for (int e = 0; e < 16; ++e)
+              pv[mb][e] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, -m_run));
+          float ls[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ls[i] = pv[0][i];
+#pragma unroll
+          for (int i = 4; i < 32; ++i) ls[i & 3] += pv[i >> 4][i & 15];
+          return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        };
+        float lsum = weights();
+        if (__ballot(!(lsum <= kSumMax)) != 0) {
+          asm volatile("");  // keep this a branch: the compiler would otherwise form both paths
+          // exact tile max of c2 * s (every tile has an unmasked kv row in one of the halves)
+          float sm = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+          for (int e = 1; e < 16; ++e) sm = fmaxf(sm, fmaxf(sacc[0][e], sacc[1][e]));
+          const float m_new = fmaxf(m_run, pair_max(sm) * c2);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+          l_run *= alpha;
+          lb_run *= alpha;
+          if constexpr (MODE == kFwd) {
+#pragma unroll
+            for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) oacc[dm][e] *= alpha;
           }
-        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+          m_run = m_new;
+          lsum = weights();
+        }
+        l_run += lsum;
+        uint32_t pw[2][8];  // P rounded to bf16, two per word (the B operand of the PV product)
+        if constexpr (MODE == kFwd) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) pw[mb][e >> 1] = pack_bf16x2(pv[mb][e], pv[mb][e + 1]);
+          // sum of the rounded weights: one bf16 dot product with (1, 1) per packed word
+          const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+          float lb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            lb[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2_t, pw[i >> 3][i & 7]), one2, lb[i & 3], false);
+          lb_run += (lb[0] + lb[1]) + (lb[2] + lb[3]);
+        }
         bf16x8_t pb[4];
         if constexpr (MODE == kFwd) {
 #pragma unroll
@@ -347,17 +350,6 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
             const uint32_t* src = &pw[kc >> 1][4 * (kc & 1)];
             pb[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
           }
-          // O is normalised by the sum of the same bf16-rounded weights the PV product uses (an
-          // exactly normalised combination); the LSE keeps the fp32 sum. The bf16 row sums come
-          // from the matrix cores: (all-ones 32 x 16) x P^T gives every row the column sums, so
-          // each lane receives the full 64-key sum of its query.
-          f32x16_t rs;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) rs[e] = 0.f;
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc)
-            rs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[kc], rs, 0, 0, 0);
-          lb_run += rs[0];
         }
         if constexpr (MODE == kFwd) {
           // O^T += V^T P^T.
@@ -404,7 +396,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
   if constexpr (MODE == kFwd) {
-    const float inv = lb_run > 0.f ? 1.f / lb_run : 0.f;  // full sum in both halves
+    const float lb_tot = lb_run + __shfl_xor(lb_run, 32, 64);  // both halves of the wave
+    const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
     uint16_t* op = a.O + head_off + (size_t)qtok * D;
 #pragma unroll
     for (int dm = 0; dm < 4; ++dm)

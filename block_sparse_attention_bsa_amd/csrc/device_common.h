@@ -17,8 +17,8 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Round two floats to bf16 (nearest even, one v_cvt_pk_bf16_f32) and pack them, a in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x2_t v;
   v[0] = (__bf16)a;
   v[1] = (__bf16)b;
