@@ -17,6 +17,7 @@ events on the stream it runs on. `cpu_baseline` times the fp64 CPU oracle on a b
 the same layer (one GPU only).
 """
 import argparse
+from contextlib import nullcontext
 import hashlib
 import json
 import os
@@ -101,25 +102,67 @@ class Timer:
         ev = self.marks.get(name, [])
         return sum(a.elapsed_time(b) for a, b in ev) / max(len(ev), 1)
 
+    def stats_ms(self, name):
+        """Median, p10 and p90 of the individual calls."""
+        import numpy as np
+        t = np.array([a.elapsed_time(b) for a, b in self.marks.get(name, [])])
+        if not len(t):
+            return None
+        return {"median": round(float(np.median(t)), 4),
+                "p10": round(float(np.percentile(t, 10)), 4),
+                "p90": round(float(np.percentile(t, 90)), 4), "calls": int(len(t))}
+
     def reset(self):
         self.marks = {}
 
 
-def cpu_baseline(w, x, rows, total_flops, target_s):
+def host_info():
+    """CPU model and the BLAS numpy is built on (reported with the oracle's timing)."""
+    import numpy as np
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        blas = np.__config__.CONFIG["Build Dependencies"]["blas"]
+        blas = f"{blas.get('name')} {blas.get('version')}"
+    except Exception:  # older numpy: no structured config
+        blas = "unknown"
+    return model, blas
+
+
+def cpu_baseline(w, x, rows, total_flops, target_s, threads=None):
     """Time the oracle: pool + score + select over the whole layer, attention over a sample of
-    query blocks, extrapolated to the layer's selected FLOPs."""
+    query blocks, extrapolated to the layer's selected FLOPs. threads=1 limits BLAS to one
+    thread (otherwise it uses every core this process may run on)."""
     import numpy as np
     import oracle
     from gen import bf16_bits_to_f64
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=threads):
+            r = cpu_baseline(w, x, rows, total_flops, target_s)
+        r["cores"] = threads
+        return r
     cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     Q, K, V = (bf16_bits_to_f64(x[n]) if x[n].dtype == np.uint16 else x[n].astype(np.float64)
                for n in ("q", "k", "v"))
     qb, kb = oracle.partition(w.grid, w.qpart), oracle.partition(w.grid, w.kvpart)
     hs = x["head_scale"].astype(np.float64)
-    S = oracle.score_row(oracle.pool(Q, qb), oracle.pool(K, kb), hs)
+    ta = time.perf_counter()
+    Qb, Kb = oracle.pool(Q, qb), oracle.pool(K, kb)
+    tb = time.perf_counter()
+    S = oracle.score_row(Qb, Kb, hs)
+    tc = time.perf_counter()
     rows_o = oracle.select_row(S, w.p)
-    t_pss = time.perf_counter() - t0
+    td = time.perf_counter()
+    t_pss = td - t0
     rp, ci = oracle.to_csr(rows_o)
     qs, ks = oracle.block_sizes(qb), oracle.block_sizes(kb)
     nq = len(qb)
@@ -135,13 +178,41 @@ def cpu_baseline(w, x, rows, total_flops, target_s):
             break
     t_att = time.perf_counter() - t1
     est = t_pss + t_att * (total_flops / max(done_flops, 1))
+    model, blas = host_info()
     return {"value": total_flops / est / 1e12, "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "blas": blas,
+            "stage_s": {"pool": round(tb - ta, 4), "score": round(tc - tb, 4),
+                        "select": round(td - tc, 4),
+                        "attn_extrapolated": round(t_att * total_flops / max(done_flops, 1), 3)},
             "sample": (f"fp64 numpy oracle: pool+score+select over the whole layer "
                        f"({t_pss:.1f} s) plus attention for {n} of {len(rows_o)} query blocks "
                        f"({t_att:.1f} s), extrapolated by selected FLOPs to one layer call "
                        f"({est:.1f} s)"),
             "ms_per_layer": est * 1e3}
+
+
+def retained_mass(w, x, L, dev):
+    """Calibrate-then-reuse quality: the exact attention mass the frozen block set keeps on each
+    of the drifted steps. Exact block masses of step s come from the calibration kernel run on
+    that step's inputs; the retained mass of a row is the sum of its masses over the blocks frozen
+    at step 0. Reported as the mean and minimum over rows, per step."""
+    import numpy as np
+    from gen import drift_step
+    rp, ci = L.csr_host()
+    nq, nkv = L.plan.nq, L.plan.nkv
+    sel = np.zeros((len(rp) - 1, nkv), dtype=bool)
+    for r in range(len(rp) - 1):
+        sel[r, ci[rp[r]:rp[r + 1]]] = True
+    def kept_stats(M, s):
+        kept = (M.reshape(-1, nkv) * sel).sum(axis=1)
+        return {"step": s, "mean": round(float(kept.mean()), 5), "min": round(float(kept.min()), 5)}
+    out = [kept_stats(L.S.cpu().numpy(), 0)]  # the calibration step itself (>= p by construction)
+    masters = {n: x[n + "32"].copy() for n in ("q", "k", "v")}
+    for s in range(1, w.drift_steps + 1):
+        d = drift_step(w, masters, s)
+        out.append(kept_stats(L.calibrate(dev(d["q"]), dev(d["k"])).cpu().numpy(), s))
+    return {"threshold": w.p, "source": "exact block masses of each drifted step (calibration "
+            "kernel); blocks frozen at step 0", "retained_mass": out}
 
 
 def main():
@@ -165,6 +236,8 @@ def main():
     stream = torch.cuda.current_stream()
     tm = Timer(stream)
     kvparts = [kv_partition_for_layer(w, l) for l in range(3)] if w.kv_cycle else [w.kvpart]
+    # per-layer stage names for the 1D / 2D / 3D cycle (temporal, spatial, spatio-temporal)
+    tags = ["@1D", "@2D", "@3D"] if w.kv_cycle else [""]
     layers = [BlockSparseAttention(w.B, w.H, w.d, w.grid, w.qpart, kp, dtype=w.dtype,
                                    head_scale=x["head_scale"]) for kp in kvparts]
     out = torch.empty_like(q)
@@ -190,23 +263,23 @@ def main():
                 with tm("attn"):
                     L.attention(qd, kd, vd, out=out, lse=lse)
             return
-        for L in layers:
+        for L, tag in zip(layers, tags):
             with tm("pool"):
                 L.pool(q, k)
             with tm("score"):
                 L.score(1 if head else 0)
             with tm("select"):
                 L.select(w.p, 1 if head else 0, mink)
-            with tm("attn"):
+            with tm("attn"), (tm("attn" + tag) if tag else nullcontext()):
                 L.attention(q, k, v, out=out, lse=lse)
             if w.backward:
-                with tm("bwd"):
+                with tm("bwd"), (tm("bwd" + tag) if tag else nullcontext()):
                     L.backward(q, k, v, out, do, lse)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    fwd_flops, dens = [], []
+    fwd_flops, dens, empty = [], [], []
     for L in layers:
         rp, ci = L.csr_host()
         rows = oracle.csr_rows(rp, ci)
@@ -214,17 +287,20 @@ def main():
         f = attention_flops(rows, qs, ks, w.d)
         fwd_flops.append(f)
         dens.append(f / (4.0 * w.B * w.H * w.N * w.N * w.d))
+        empty.append(float(np.mean(np.diff(rp) == 0)))
     tm.reset()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(args.steps):
-        step()
+        with tm("step"):
+            step()
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1) / args.steps
     n_layers = len(layers)
-    stages = {s: tm.mean_ms(s) for s in tm.marks}
+    stages = {s: tm.mean_ms(s) for s in tm.marks if s != "step"}
+    stage_stats = {s: tm.stats_ms(s) for s in tm.marks}
     if w.mode == "calib":
         per_call = total_ms / (1 + w.drift_steps)            # (calibration + 10 steps) / 11
         step_flops = fwd_flops[0] * w.drift_steps / (1 + w.drift_steps)
@@ -250,6 +326,8 @@ def main():
                    "p": w.p, "mode": w.mode, "density": [round(d_, 4) for d_ in dens],
                    "selected_tflop_fwd": [f / 1e12 for f in fwd_flops]},
         "stage_ms": {s: round(v_, 4) for s, v_ in stages.items()},
+        "call_stats_ms": stage_stats,
+        "empty_row_fraction": [round(e, 4) for e in empty],
         "attn_tflops": achieved,
         "pct_bf16_peak_step": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
@@ -258,6 +336,26 @@ def main():
     }
     if w.backward:
         res["bwd_tflops"] = 2 * attn_flops / (stages["bwd"] * 1e-3) / 1e12
+        # per member of the 1D / 2D / 3D cycle: forward, backward and their sum
+        res["per_partition_ms"] = {
+            (t[1:] or "single"): {"fwd": round(stages["attn" + t], 4),
+                                  "bwd": round(stages["bwd" + t], 4),
+                                  "fwd+bwd": round(stages["attn" + t] + stages["bwd" + t], 4)}
+            for t in tags}
+    if "pool" in stages:
+        elt = 2 if w.dtype == "bf16" else 4
+        L = layers[0]
+        pool_bytes = (2 * w.B * w.H * w.N * w.d * elt
+                      + (L.plan.nq + L.plan.nkv) * w.B * w.H * w.d * 4)
+        gbs = pool_bytes / (stages["pool"] * 1e-3) / 1e9
+        res["pool"] = {"GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+                       "bytes": pool_bytes}
+    if w.mode == "hybrid":
+        hk = layers[0].head_k.cpu().numpy()
+        res["head_k"] = {"min": int(hk.min()), "median": float(np.median(hk)),
+                         "max": int(hk.max()), "nkv": layers[0].plan.nkv}
+    if w.mode == "calib":
+        res["calibrate_then_reuse"] = retained_mass(w, x, layers[0], dev)
     if args.copy_ref_mib:
         n = args.copy_ref_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -270,6 +368,9 @@ def main():
         rp, ci = L.csr_host()
         res["cpu_baseline"] = cpu_baseline(w, x, oracle.csr_rows(rp, ci), fwd_flops[0],
                                            args.cpu_seconds)
+        if args.config == 1:
+            res["cpu_baseline_1thread"] = cpu_baseline(w, x, oracle.csr_rows(rp, ci),
+                                                       fwd_flops[0], args.cpu_seconds, threads=1)
     print(json.dumps(res), flush=True)
 
 

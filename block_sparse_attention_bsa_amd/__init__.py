@@ -19,6 +19,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libbsa.so")
+_DEFAULT_LIB = LIB_PATH
 
 BSA_OK, BSA_EINVAL, BSA_EUNSUPPORTED, BSA_ECAPACITY, BSA_EHIP = 0, -1, -2, -3, -4
 BSA_PART_FLAT, BSA_PART_TILE = 0, 1
@@ -65,6 +66,14 @@ def lib():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libbsa.so not built at {LIB_PATH}; run __graft_entry__.build()")
+    if LIB_PATH == _DEFAULT_LIB:
+        # the in-tree library must have been built from the sources as they are now
+        from . import build as _build
+        stamp = _build.STAMP
+        built = open(stamp).read().strip() if os.path.exists(stamp) else None
+        if built != _build.source_hash():
+            raise ImportError(f"{LIB_PATH} was built from other sources than csrc/ and include/ "
+                              f"hold now; run __graft_entry__.build()")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ, D = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                           ctypes.c_double)

@@ -3,6 +3,7 @@
 Every source under csrc/ is compiled by hipcc in one invocation. Packed-fp32 instruction
 selection is disabled for device code (the compiler's own v_pk_*_f32 forms are avoided).
 """
+import hashlib
 import os
 import subprocess
 import sys
@@ -14,9 +15,25 @@ LIB = os.path.join(LIBDIR, "libbsa.so")
 ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
 
 
+INCLUDE = os.path.join(HERE, "..", "include")
+STAMP = LIB + ".srchash"
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
+
+
+def source_hash():
+    """sha256 over every file the library is built from (csrc/ and include/), with names."""
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in os.listdir(CSRC)]
+    files += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
+    for path in sorted(f for f in files if f.endswith((".hip", ".cpp", ".h"))):
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def build(verbose: bool = False) -> str:
@@ -38,6 +55,8 @@ def build(verbose: bool = False) -> str:
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, LIB)
+    with open(STAMP, "w") as f:  # which sources this library was built from (checked at load)
+        f.write(source_hash() + "\n")
     return LIB
 
 

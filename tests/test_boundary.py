@@ -109,3 +109,15 @@ def test_partition_build_capacity_and_errors(L):
     bad = bsa.make_partition(("flat", 0))
     assert L.bsa_partition_build(2, 2, 2, ctypes.byref(bad), perm.ctypes.data,
                                  start.ctypes.data, 10, ctypes.byref(n)) == bsa.BSA_EINVAL
+
+
+def test_stale_library_is_refused(monkeypatch, L):
+    """The in-tree library records the hash of the sources it was built from; a library built
+    from other sources fails to load instead of running old kernels."""
+    from block_sparse_attention_bsa_amd import build
+    monkeypatch.setattr(bsa, "_lib", None)
+    monkeypatch.setattr(build, "source_hash", lambda: "0" * 64)
+    with pytest.raises(ImportError, match="other sources"):
+        bsa.lib()
+    monkeypatch.undo()
+    assert bsa.lib() is not None
