@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
   constexpr int VEC = Seg<T>::kVec;
   constexpr int SEGS = D / VEC;
   constexpr int GROUPS = 256 / SEGS;
-  constexpr int UNROLL = 4;
+  constexpr int UNROLL = 8;  // one pass covers a 128-token block: all its rows in flight
   __shared__ float red[GROUPS][D + 1];
 
   const int J = blockIdx.x;
