@@ -4,8 +4,9 @@ Default workload: the Wan2.1-1.3B 480p attention call -- B=1, H=12, d=128, bf16,
 21 x 30 x 52 = 32760, 4x4x8 blocks (336 x 336), block-mean scoring, top-p 0.9. A step is one
 pass of the whole path over resident inputs: pool(Q), pool(K), score, select, sparse attention.
 
-Other workloads (--config): 1 tiny fp32; 3 calibrate-then-reuse (one exact-mass calibration and
-selection, then ten sparse steps; a step is their mean); 4 HunyuanVideo 720p with the per-head
+Other workloads (--config): 1 tiny fp32; 3 calibrate-then-reuse (one dense step that returns the
+exact block masses with its attention output, the selection, then ten sparse steps; a step is
+their mean); 4 HunyuanVideo 720p with the per-head
 minimum count; 5 Wan2.1-14B training (per layer: pool, head-global score and selection, forward
 and backward; a step is the mean over the 1D/2D/3D layer cycle).
 
@@ -254,9 +255,10 @@ def main():
 
     def step():
         if w.mode == "calib":
+            # the dense step: exact block masses and that step's dense attention output together
             L = layers[0]
-            with tm("calibrate"):
-                L.calibrate(q, k)
+            with tm("dense_step"):
+                L.calibrate_attention(q, k, v, out=out, lse=lse)
             with tm("select"):
                 L.select(w.p)
             for _ in range(w.drift_steps):
@@ -355,6 +357,11 @@ def main():
         res["head_k"] = {"min": int(hk.min()), "median": float(np.median(hk)),
                          "max": int(hk.max()), "nkv": layers[0].plan.nkv}
     if w.mode == "calib":
+        for _ in range(3):  # the masses alone (no dense output), for comparison
+            with tm("calibrate_masses_only"):
+                layers[0].calibrate(q, k)
+        torch.cuda.synchronize()
+        res["stage_ms"]["calibrate_masses_only"] = round(tm.mean_ms("calibrate_masses_only"), 4)
         res["calibrate_then_reuse"] = retained_mass(w, x, layers[0], dev)
     if args.copy_ref_mib:
         n = args.copy_ref_mib * (1 << 20) // 4

@@ -5,7 +5,7 @@ declared in include/bsa.h, and every step of the computation runs in the library
 PyTorch is used for device memory and streams. There is no CPU fallback: if the library is missing
 or a call fails, an exception is raised.
 
-Names follow the C ABI: bsa_pool, bsa_score, bsa_calibrate_mass, bsa_select, bsa_attn_fwd,
+Names follow the C ABI: bsa_pool, bsa_score, bsa_calibrate_mass(_fwd), bsa_select, bsa_attn_fwd,
 bsa_attn_bwd, bsa_partition_build; a Plan wraps bsa_plan_create / bsa_plan_info /
 bsa_plan_blocks / bsa_plan_destroy.
 """
@@ -29,8 +29,9 @@ BSA_POOL_ROW, BSA_POOL_HEAD = 0, 1
 BSA_MINK_NONE, BSA_MINK_FIXED, BSA_MINK_WEIGHTED_MEAN = 0, 1, 2
 
 EXPORTED = ("bsa_partition_build", "bsa_plan_create", "bsa_plan_destroy", "bsa_plan_info",
-            "bsa_plan_blocks", "bsa_pool", "bsa_score", "bsa_calibrate_mass", "bsa_select",
-            "bsa_attn_fwd", "bsa_attn_bwd", "bsa_last_error")
+            "bsa_plan_blocks", "bsa_pool", "bsa_score", "bsa_calibrate_mass",
+            "bsa_calibrate_mass_fwd", "bsa_select", "bsa_attn_fwd", "bsa_attn_bwd",
+            "bsa_last_error")
 
 
 class BsaError(RuntimeError):
@@ -88,6 +89,7 @@ def lib():
         "bsa_pool": [P, I32, P, P, P],
         "bsa_score": [P, P, P, I32, P, P],
         "bsa_calibrate_mass": [P, P, P, P, P, SZ, P],
+        "bsa_calibrate_mass_fwd": [P, P, P, P, P, P, P, P, SZ, P],
         "bsa_select": [P, P, ctypes.POINTER(SelectParams), P, P, I64, P, P, P, SZ, P],
         "bsa_attn_fwd": [P, P, P, P, P, P, P, P, P, SZ, P],
         "bsa_attn_bwd": [P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -211,6 +213,11 @@ def bsa_score(plan: Plan, Qbar, Kbar, norm: int, S, stream=None):
 def bsa_calibrate_mass(plan: Plan, Q, K, M, ws, ws_bytes: int, stream=None):
     _check(lib().bsa_calibrate_mass(plan.handle, _ptr(Q), _ptr(K), _ptr(M), _ptr(ws), ws_bytes,
                                     _stream(stream)))
+
+
+def bsa_calibrate_mass_fwd(plan: Plan, Q, K, V, M, O, lse, ws, ws_bytes: int, stream=None):
+    _check(lib().bsa_calibrate_mass_fwd(plan.handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(M), _ptr(O),
+                                        _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def bsa_select(plan: Plan, S, p: float, pool: int, min_k_mode: int, fixed_k: int, row_ptr,

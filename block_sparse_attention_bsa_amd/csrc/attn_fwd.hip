@@ -36,8 +36,9 @@ namespace {
 
 // ------------------------------------------------------------------------------- MFMA path
 
-// kFwd: sparse attention; kLse / kMass: the two dense calibration passes.
-enum Mode { kFwd = 0, kLse = 1, kMass = 2 };
+// kFwd: sparse attention; kLse / kMass: the two dense calibration passes; kMassO: the second
+// calibration pass that also forms the dense attention output from the same exact weights.
+enum Mode { kFwd = 0, kLse = 1, kMass = 2, kMassO = 3 };
 
 
 constexpr int kTileKV = 64;                    // kv tokens per iteration (two chunks)
@@ -66,9 +67,9 @@ struct MfmaArgs {
   const int32_t* kvstart;
   const int32_t* items;
   const float* scale;
-  const float* lse_in;  // kMass: per-token log-sum-exp (from the kLse pass)
-  uint16_t* O;          // kFwd
-  float* lse;           // kFwd (nullable) and kLse
+  const float* lse_in;  // kMass, kMassO: per-token log-sum-exp (from the kLse pass)
+  uint16_t* O;          // kFwd, kMassO
+  float* lse;           // kFwd and kMassO (nullable outputs), kLse
   float* part;          // kMass: [bh][item][wave][nkv] per-wave block sums
   int n_items, H, N, nq, nkv;
   int Npad;  // K and V are permuted into block order: [B*H][Npad][d], Npad = N + kPermPad
@@ -78,8 +79,9 @@ struct MfmaArgs {
 template <int MODE>
 __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   constexpr int D = 128;
-  constexpr bool kDense = MODE == kLse || MODE == kMass;  // all kv blocks, not a CSR row
-  constexpr bool kNeedV = MODE == kFwd;
+  constexpr bool kDense = MODE != kFwd;  // all kv blocks, not a CSR row
+  constexpr bool kPV = MODE == kFwd || MODE == kMassO;  // O = P V is formed
+  constexpr bool kNeedV = kPV;
   constexpr int kStage = kNeedV ? 2 * kTileBytes : kTileBytes;
   __shared__ __attribute__((aligned(1024))) char lds[2 * kStage];
   char* const lds_a = lds;
@@ -117,7 +119,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   }
 
   f32x16_t oacc[4];  // kFwd: O^T (lane = query, registers = d)
-  if constexpr (MODE == kFwd) {
+  if constexpr (kPV) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -128,7 +130,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   float m_run = -INFINITY, l_run = 0.f, lb_run = 0.f;
   // kMass: log2-domain lse of this lane's query (+inf for padding rows, so they add nothing)
   float nlse2 = 0.f, blk_acc = 0.f;
-  if constexpr (MODE == kMass)
+  if constexpr (MODE == kMass || MODE == kMassO)
     nlse2 = qvalid ? -a.lse_in[(size_t)bh * a.N + qtok] * kLog2e : -INFINITY;
 
   // Loader role: wave w fills tile rows 16w + 4i + lane/16 (i = 0..3), 16-byte unit lane%16 of
@@ -244,8 +246,81 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         }
       }
 
-      if constexpr (MODE == kMass) {
-        // Block sums of exp(sigma q.k - lse): one chunk per M block, flushed at block ends.
+      // V^T fragment (d block dm, kv rows 16 kc .. +16) of this tile: two transposing 8-byte LDS
+      // reads. The first d block's fragments are read before the weights are formed, so their
+      // latency hides behind that VALU work.
+      const char* vt = st + kTileBytes;
+      auto vfrag = [&](int dm, int kc) {
+        const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((lds_char_t*)vt + row_lo * kRowBytes +
+                           lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((lds_char_t*)vt + row_hi * kRowBytes +
+                           lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+      };
+      bf16x8_t vf0[4];
+      if constexpr (kPV) {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) vf0[kc] = vfrag(0, kc);
+        __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the VALU work below
+      }
+      // P rounded to bf16 (the B operand of the PV product), with the sum of the rounded weights
+      // (one bf16 dot product with (1, 1) per packed word) added to lb_run.
+      auto pack_weights = [&](const float (&pv)[2][16], bf16x8_t (&pb)[4]) {
+        uint32_t pw[2][8];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) pw[mb][e >> 1] = pack_bf16x2(pv[mb][e], pv[mb][e + 1]);
+        const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+        float lb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          lb[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(
+              __builtin_bit_cast(bf16x2_t, pw[i >> 3][i & 7]), one2, lb[i & 3], false);
+        lb_run += (lb[0] + lb[1]) + (lb[2] + lb[3]);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const uint32_t* src = &pw[kc >> 1][4 * (kc & 1)];
+          pb[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
+        }
+      };
+      // O^T += V^T P^T.
+      auto pv_product = [&](const bf16x8_t (&pb)[4]) {
+        __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+        for (int dm = 0; dm < 4; ++dm) {
+          bf16x8_t vf[4];
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) vf[kc] = dm == 0 ? vf0[kc] : vfrag(dm, kc);
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc)
+            oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc], pb[kc], oacc[dm], 0, 0, 0);
+        }
+        // Weights first (their VALU work covers the first reads' latency), then the MFMAs with
+        // the remaining V reads interleaved, two per MFMA.
+        __builtin_amdgcn_sched_group_barrier(0x002, 100, 0);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_s_setprio(0);
+      };
+
+      if constexpr (MODE == kMass || MODE == kMassO) {
+        // Exact weights exp(sigma q.k - lse) (the LSE over all N keys is known from the kLse
+        // pass). Block sums: one chunk per M block, flushed at block ends; kMassO also forms
+        // the dense output O from the same weights.
+        float pv[2][16];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) pv[mb][e] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nlse2));
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           const Chunk& c = mb ? b0 : a0;
@@ -253,8 +328,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
             float cs0 = 0.f, cs1 = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-              cs0 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nlse2));
-              cs1 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e + 1], c2, nlse2));
+              cs0 += pv[mb][e];
+              cs1 += pv[mb][e + 1];
             }
             blk_acc += cs0 + cs1;
             if (c.last) {
@@ -265,28 +340,12 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
             }
           }
         }
-      } else {
-        // V^T fragment (d block dm, kv rows 16 kc .. +16) of this tile: two transposing 8-byte
-        // LDS reads. The first d block's fragments are read before the weights are formed, so
-        // their latency hides behind that VALU work.
-        const char* vt = st + kTileBytes;
-        auto vfrag = [&](int dm, int kc) {
-          const int row_lo = 16 * kc + vrow_l, row_hi = row_lo + 8;
-          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)((lds_char_t*)vt + row_lo * kRowBytes +
-                             lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
-          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)((lds_char_t*)vt + row_hi * kRowBytes +
-                             lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
-          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-          return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
-        };
-        bf16x8_t vf0[4];
-        if constexpr (MODE == kFwd) {
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) vf0[kc] = vfrag(0, kc);
-          __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the VALU work below
+        if constexpr (MODE == kMassO) {
+          bf16x8_t pb[4];
+          pack_weights(pv, pb);
+          pv_product(pb);
         }
+      } else {
         // Weights p = exp2(c2 * s - m_run) against the running max as it stands, and this
         // lane's partial sum. No tile max is formed on this path: the sum bounds every weight,
         // and while it stays <= kSumMax the weights (bf16 for the PV product) and the fp32 sums
@@ -328,52 +387,10 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
           lsum = weights();
         }
         l_run += lsum;
-        uint32_t pw[2][8];  // P rounded to bf16, two per word (the B operand of the PV product)
         if constexpr (MODE == kFwd) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int e = 0; e < 16; e += 2) pw[mb][e >> 1] = pack_bf16x2(pv[mb][e], pv[mb][e + 1]);
-          // sum of the rounded weights: one bf16 dot product with (1, 1) per packed word
-          const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
-          float lb[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            lb[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(
-                __builtin_bit_cast(bf16x2_t, pw[i >> 3][i & 7]), one2, lb[i & 3], false);
-          lb_run += (lb[0] + lb[1]) + (lb[2] + lb[3]);
-        }
-        bf16x8_t pb[4];
-        if constexpr (MODE == kFwd) {
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) {
-            const uint32_t* src = &pw[kc >> 1][4 * (kc & 1)];
-            pb[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
-          }
-        }
-        if constexpr (MODE == kFwd) {
-          // O^T += V^T P^T.
-          __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-          for (int dm = 0; dm < 4; ++dm) {
-            bf16x8_t vf[4];
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) vf[kc] = dm == 0 ? vf0[kc] : vfrag(dm, kc);
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-              oacc[dm] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kc], pb[kc], oacc[dm], 0, 0, 0);
-          }
-          // Weights first (their VALU work covers the first reads' latency), then the MFMAs
-          // with the remaining V reads interleaved, two per MFMA.
-          __builtin_amdgcn_sched_group_barrier(0x002, 100, 0);
-#pragma unroll
-          for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-          __builtin_amdgcn_s_setprio(0);
+          bf16x8_t pb[4];
+          pack_weights(pv, pb);
+          pv_product(pb);
         }
       }
     }
@@ -395,7 +412,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   if constexpr (MODE == kMass) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
-  if constexpr (MODE == kFwd) {
+  if constexpr (kPV) {
     const float lb_tot = lb_run + __shfl_xor(lb_run, 32, 64);  // both halves of the wave
     const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
     uint16_t* op = a.O + head_off + (size_t)qtok * D;
@@ -408,6 +425,11 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         pk.y = pack_bf16x2(oacc[dm][4 * g + 2] * inv, oacc[dm][4 * g + 3] * inv);
         *reinterpret_cast<uint2*>(op + 32 * dm + 8 * g + 4 * hl) = pk;
       }
+  }
+  if constexpr (MODE == kMassO) {
+    // the dense step's LSE is the kLse pass's (the weights above are normalised by it)
+    if (a.lse && hl == 0) a.lse[(size_t)bh * a.N + qtok] = a.lse_in[(size_t)bh * a.N + qtok];
+    return;
   }
   if (a.lse && hl == 0)
     a.lse[(size_t)bh * a.N + qtok] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
@@ -628,13 +650,14 @@ hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, cons
   return launch_valu<float, 64>(p, Q, K, V, row_ptr, col_idx, O, lse, s);
 }
 
-hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, float* M, void* ws,
-                            hipStream_t s) {
+hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, const void* V,
+                            float* M, void* O, float* lse_out, void* ws, hipStream_t s) {
   const CalibWs L = calib_ws_layout(p);
   char* base = static_cast<char*>(ws);
   float* lse = reinterpret_cast<float*>(base + L.lse);
   float* part = reinterpret_cast<float*>(base + L.part);
   hipError_t e = launch_permute_rows(p, K, base + L.kp, s);
+  if (e == hipSuccess && V) e = launch_permute_rows(p, V, base + L.vp, s);
   if (e != hipSuccess) return e;
   const dim3 grid(p.n_items, p.prob.B * p.prob.H);
   MfmaArgs a = mfma_args(p);
@@ -646,7 +669,14 @@ hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, flo
   a.lse = nullptr;
   a.lse_in = lse;
   a.part = part;
-  attn_mfma_d128<kMass><<<grid, 256, 0, s>>>(a);
+  if (V) {  // the masses and the dense output from the same weights
+    a.V = reinterpret_cast<const uint16_t*>(base + L.vp);
+    a.O = static_cast<uint16_t*>(O);
+    a.lse = lse_out;
+    attn_mfma_d128<kMassO><<<grid, 256, 0, s>>>(a);
+  } else {
+    attn_mfma_d128<kMass><<<grid, 256, 0, s>>>(a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mass_combine_kernel<<<dim3(p.nq, p.prob.B * p.prob.H), 256, 0, s>>>(
       part, p.qstart, p.qitem0, p.items, p.n_items, p.nq, p.nkv, M);

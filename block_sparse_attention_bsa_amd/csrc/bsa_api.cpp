@@ -164,7 +164,8 @@ CalibWs calib_ws_layout(const bsa_plan& p) {
   w.lse = 0;
   w.part = align_up(BH * p.prob.N * 4);
   w.kp = w.part + align_up(BH * p.n_items * 4 * (size_t)p.nkv * 4);
-  w.total = w.kp + align_up(BH * (size_t)(p.prob.N + kPermPad) * p.prob.d * 2);
+  w.vp = w.kp + align_up(BH * (size_t)(p.prob.N + kPermPad) * p.prob.d * 2);
+  w.total = w.vp + align_up(BH * (size_t)(p.prob.N + kPermPad) * p.prob.d * 2);
   return w;
 }
 
@@ -326,8 +327,26 @@ int bsa_calibrate_mass(const bsa_plan* plan, const void* Q, const void* K, float
     return fail(BSA_ECAPACITY, "bsa_calibrate_mass: workspace %zu < %zu bytes", ws_bytes, need);
   int rc = check_device(plan);
   if (rc) return rc;
-  return launch_status(launch_calibrate(*plan, Q, K, M, ws, (hipStream_t)stream),
-                       "bsa_calibrate_mass");
+  return launch_status(
+      launch_calibrate(*plan, Q, K, nullptr, M, nullptr, nullptr, ws, (hipStream_t)stream),
+      "bsa_calibrate_mass");
+}
+
+int bsa_calibrate_mass_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
+                           float* M, void* O, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!plan || !Q || !K || !V || !M || !O)
+    return fail(BSA_EINVAL, "bsa_calibrate_mass_fwd: NULL argument");
+  if (plan->prob.dtype != BSA_BF16 || plan->prob.d != 128)
+    return fail(BSA_EUNSUPPORTED, "bsa_calibrate_mass_fwd: bf16 with d = 128 only");
+  const size_t need = calib_ws_layout(*plan).total;
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ECAPACITY, "bsa_calibrate_mass_fwd: workspace %zu < %zu bytes", ws_bytes,
+                need);
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_calibrate(*plan, Q, K, V, M, O, lse, ws, (hipStream_t)stream),
+                       "bsa_calibrate_mass_fwd");
 }
 
 int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* prm,

@@ -55,8 +55,9 @@ struct BwdWs {
 BwdWs bwd_ws_layout(const bsa_plan& p);
 
 struct CalibWs {
-  // per-token log-sum-exp; per (item, wave, kv block) block sums; K in block order
-  size_t lse, part, kp, total;
+  // per-token log-sum-exp; per (item, wave, kv block) block sums; K and V in block order (V for
+  // the variant that also forms the dense output)
+  size_t lse, part, kp, vp, total;
 };
 CalibWs calib_ws_layout(const bsa_plan& p);
 
@@ -83,8 +84,9 @@ hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, cons
 // dst = src ([B, H, N, 128] bf16) with rows in block order (plan kvperm) and kPermPad zero rows
 // per head.
 hipError_t launch_permute_rows(const bsa_plan& p, const void* src, void* dst, hipStream_t s);
-hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, float* M, void* ws,
-                            hipStream_t s);
+// V, O, lse_out: NULL for the masses alone; else the dense output O (and its LSE, nullable) too.
+hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, const void* V,
+                            float* M, void* O, float* lse_out, void* ws, hipStream_t s);
 hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
                            const void* O, const void* dO, const float* lse,
                            const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK,

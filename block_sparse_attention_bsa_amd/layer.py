@@ -11,7 +11,8 @@ from typing import Optional
 import torch
 
 from . import (BSA_MINK_NONE, BSA_NORM_HEAD, BSA_NORM_ROW, BSA_POOL_HEAD, BSA_POOL_ROW, Plan,
-               bsa_attn_bwd, bsa_attn_fwd, bsa_calibrate_mass, bsa_pool, bsa_score, bsa_select)
+               bsa_attn_bwd, bsa_attn_fwd, bsa_calibrate_mass, bsa_calibrate_mass_fwd, bsa_pool,
+               bsa_score, bsa_select)
 
 
 class BlockSparseAttention:
@@ -51,6 +52,16 @@ class BlockSparseAttention:
             self._ws_calib = torch.empty(self.plan.ws_calib, dtype=torch.uint8, device=self.device)
         bsa_calibrate_mass(self.plan, q, k, self.S, self._ws_calib, self.plan.ws_calib, stream)
         return self.S
+
+    def calibrate_attention(self, q, k, v, out=None, lse=None, stream=None):
+        """The dense step: exact block masses into self.S and the dense attention output."""
+        if self._ws_calib is None:
+            self._ws_calib = torch.empty(self.plan.ws_calib, dtype=torch.uint8, device=self.device)
+        if out is None:
+            out = torch.empty_like(q)
+        bsa_calibrate_mass_fwd(self.plan, q, k, v, self.S, out, lse, self._ws_calib,
+                               self.plan.ws_calib, stream)
+        return self.S, out
 
     def select(self, p, pool=BSA_POOL_ROW, min_k_mode=BSA_MINK_NONE, fixed_k=0, stream=None,
                scores=None):

@@ -10,7 +10,8 @@
  *                         query block (row) or over the whole head (VMoBA review, referee report
  *                         major comment 1: Eq. 3 global selection over the query-by-block matrix).
  *      bsa_calibrate_mass exact per-(head, q-block, kv-block) softmax mass from one dense step
- *                         (LoSA abstract, scholarbro author page).
+ *                         (LoSA abstract, scholarbro author page); bsa_calibrate_mass_fwd also
+ *                         returns that dense step's attention output.
  *   3. bsa_select         per (head, q-block) the smallest kv-block set, in descending score
  *                         order, whose cumulative score or mass reaches p (VMoBA review, major
  *                         comment 1 on Sec. 3.4 Eq. 4; LoSA abstract), optionally raised to a
@@ -150,6 +151,17 @@ int bsa_score(const bsa_plan* plan, const float* Qbar, const float* Kbar, int32_
  * M fp32 [B, H, nq, nkv]. ws must hold the ws_calib bytes of bsa_plan_info. Rows of M sum to 1. */
 int bsa_calibrate_mass(const bsa_plan* plan, const void* Q, const void* K, float* M, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* Step 2' as the dense step itself: the same masses M, plus the dense attention output of that
+ * step, O[b, h, i, :] = sum_j softmax_j(sigma_h q_i . k_j) v_j over all N keys, and its LSE
+ * (natural log, fp32 [B, H, N]; nullable). The LoSA abstract measures the masses at one early
+ * step that runs dense attention; both come from one pass over the same exact weights (the
+ * second calibration pass also multiplies them with V). Q, K, V, O [B, H, N, d] bf16 (d = 128),
+ * M fp32 [B, H, nq, nkv]; ws as for bsa_calibrate_mass (the ws_calib bytes). O is normalised by
+ * the sum of the same bf16-rounded weights that multiply V. Errors as bsa_calibrate_mass. */
+int bsa_calibrate_mass_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
+                           float* M, void* O, float* lse, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* Step 3. Selection from S (scores from bsa_score, or masses from bsa_calibrate_mass), written
  * as CSR: row_ptr [B*H*nq + 1], col_idx with capacity col_cap >= B*H*nq*nkv entries (the number

@@ -87,6 +87,7 @@ def test_null_arguments_rejected(L):
     assert L.bsa_pool(P, 0, None, None, None) == bsa.BSA_EINVAL
     assert L.bsa_score(P, None, None, 0, None, None) == bsa.BSA_EINVAL
     assert L.bsa_calibrate_mass(P, None, None, None, None, 0, None) == bsa.BSA_EINVAL
+    assert L.bsa_calibrate_mass_fwd(P, *([None] * 7), 0, None) == bsa.BSA_EINVAL
     prm = bsa.SelectParams(0.9, 0, 0, 0)
     assert L.bsa_select(P, None, ctypes.byref(prm), None, None, 0, None, None, None, 0,
                         None) == bsa.BSA_EINVAL

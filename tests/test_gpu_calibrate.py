@@ -114,3 +114,59 @@ def test_calibrate_masses_batch2():
     log(f"calibrate B=2: max-abs {err:.2e}")
     assert err <= 1e-5
     np.testing.assert_allclose(M.sum(-1), 1.0, atol=1e-5)
+
+
+def _dense_step(w, x, rows=None):
+    """The fused dense step against the masses-only call and the oracle's dense attention."""
+    import torch
+    layer = _layer(w, x)
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    M_only = dev_to_f64(layer.calibrate(q, k).clone())
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    M, O = layer.calibrate_attention(q, k, v, lse=lse)
+    torch.cuda.synchronize()
+    qb, kb = oracle.partition(w.grid, w.qpart), oracle.partition(w.grid, w.kvpart)
+    nq, nkv = len(qb), len(kb)
+    rp, ci = oracle.to_csr([np.arange(nkv) for _ in range(w.B * w.H * nq)])
+    O_ref, L_ref = oracle.attention_fwd(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]),
+                                        x["head_scale"].astype(np.float64), qb, kb, rp, ci,
+                                        rows=rows)
+    return M_only, dev_to_f64(M), dev_to_f64(O), lse.cpu().numpy().astype(np.float64), O_ref, L_ref
+
+
+def test_calibrate_dense_output_reduced():
+    # The dense step (LoSA abstract: masses measured at a step that runs dense attention): one
+    # pass gives the same masses as the masses-only call, bit for bit, and the dense output.
+    w = replace(CONFIGS[3], grid=(9, 14, 26), H=3)
+    x = make_inputs(w)
+    M_only, M, O, L, O_ref, L_ref = _dense_step(w, x)
+    assert np.array_equal(M, M_only)
+    err_o, err_l = np.abs(O - O_ref).max(), np.abs(L - L_ref).max()
+    log(f"dense step reduced: O max-abs {err_o:.2e}, LSE max-abs {err_l:.2e}")
+    assert err_o <= 1e-2 and err_l <= 1e-3
+
+
+def test_calibrate_dense_output_batch2_ragged():
+    w = replace(CONFIGS[3], B=2, grid=(5, 7, 13), H=2)  # ragged blocks at every grid edge
+    x = make_inputs(w)
+    M_only, M, O, L, O_ref, L_ref = _dense_step(w, x)
+    assert np.array_equal(M, M_only)
+    err_o, err_l = np.abs(O - O_ref).max(), np.abs(L - L_ref).max()
+    log(f"dense step B=2 ragged: O max-abs {err_o:.2e}, LSE max-abs {err_l:.2e}")
+    assert err_o <= 1e-2 and err_l <= 1e-3
+
+
+def test_calibrate_dense_output_full_size_sampled():
+    w = CONFIGS[3]
+    x = make_inputs(w)
+    rng = np.random.default_rng(5)
+    rows = [(0, int(h), int(i)) for h, i in zip(rng.integers(0, w.H, 6), rng.integers(0, 336, 6))]
+    M_only, M, O, L, O_ref, L_ref = _dense_step(w, x, rows=rows)
+    assert np.array_equal(M, M_only)
+    qb = oracle.partition(w.grid, w.qpart)
+    toks = [(b, h, qb[i]) for b, h, i in rows]
+    err_o = max(float(np.abs(O[b, h, t] - O_ref[b, h, t]).max()) for b, h, t in toks)
+    err_l = max(float(np.abs(L[b, h, t] - L_ref[b, h, t]).max()) for b, h, t in toks)
+    log(f"dense step full size: O max-abs {err_o:.2e}, LSE max-abs {err_l:.2e} over "
+        f"{len(rows)} sampled query blocks")
+    assert err_o <= 1e-2 and err_l <= 1e-3
