@@ -15,8 +15,9 @@
 //                      lse, D; double-buffered direct copies of consecutive block-order rows). Per chunk and wave: S = Q K^T and
 //                      dP = dO V^T (lane = kv token), P and dS in registers, then
 //                      dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T from transposing reads.
-//   4. dq_kernel       query-stationary over the CSR (one workgroup per 128 queries), K and V
-//                      tiles from block-ordered copies, S and dP recomputed per tile.
+//   4. dq_kernel       query-stationary over the CSR (one workgroup of four wavefronts per 128
+//                      queries, two workgroups per CU), K and V tiles from block-ordered copies,
+//                      S and dP recomputed per tile.
 #include "bsa_internal.h"
 #include "device_common.h"
 #include "kv_cursor.h"
@@ -474,7 +475,13 @@ struct DqArgs {
 // chunks) through two LDS stages, as the forward pass does. Eight wavefronts, two per SIMD:
 // wave w owns queries 32 (w % 4) .. +32 and chunk w / 4 of every tile; the two chunks' partial
 // dQ are summed through LDS at the end in a fixed order.
-__global__ __launch_bounds__(512, 2) void dq_kernel(const DqArgs a) {
+// dQ with four wavefronts per workgroup (two workgroups per CU): wave w owns queries 32w .. +32
+// of the item and computes both 32-row chunks of every 64-token tile itself, so no partial sums
+// are combined at the end, and the two co-resident workgroups run out of phase with each other
+// (as in the forward kernel) instead of two wavefronts of one workgroup sharing a SIMD in lock
+// step. Per chunk: S^T = K Q^T and dP^T = V dO^T (8 + 8 MFMAs), dS^T = P^T (dP^T - D) in bf16,
+// dQ^T += K^T dS^T (8 MFMAs); chunk 1's matrix work is independent of chunk 0's vector work.
+__global__ __launch_bounds__(256, 2) void dq_kernel(const DqArgs a) {
   constexpr int D = 128;
   constexpr int kTile = 64 * kRowBytes;  // one of K / V
   constexpr int kDqStage = 2 * kTile;
@@ -495,12 +502,11 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(const DqArgs a) {
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int qg = wave & 3, kh = wave >> 2;  // query group, chunk of the tile
   const int l32 = lane & 31, hl = lane >> 5;
-  const bool active = 32 * qg < nrows;  // wave-uniform
+  const bool active = 32 * wave < nrows;  // wave-uniform
 
-  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T): query 32 qg + l32.
-  const int qrow = 32 * qg + l32;
+  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T): query 32 wave + l32.
+  const int qrow = 32 * wave + l32;
   const bool qvalid = qrow < nrows;
   const int qtok = qvalid ? a.qperm[q0 + qrow] : 0;
   bf16x8_t qf[8], dof[8];
@@ -528,26 +534,24 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(const DqArgs a) {
   cur.sub = 0;
   cursor_load<false>(cur, a.col_idx, a.kvstart);
 
-  // Loader: wave w copies rows 8 (w % 4) + 4i + lane/16 (i = 0, 1) of chunk w / 4 of a tile, for
-  // K and V, from the block-ordered copies (a chunk is consecutive rows at its position).
-  const int lgrp = lane >> 4;
+  // Loader: wave w copies rows 16 w + 4 i + lane / 16 (i = 0..3) of the 64-row K and V tiles
+  // (chunk w / 2, rows 16 (w % 2) + 4 i + lane / 16 of it), from the block-ordered copies.
+  const int lchunk = wave >> 1, loff = 16 * (wave & 1), lgrp = lane >> 4;
   const size_t kv_off = (size_t)bh * a.Npad * D;
-  uint32_t voff[2], roff[2];
+  uint32_t voff[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int crow = 8 * qg + 4 * i + lgrp;  // row within the chunk
-    const int trow = 32 * kh + crow;         // row within the tile
-    voff[i] = (uint32_t)(crow * kRowBytes) + 16u * (uint32_t)((lane & 15) ^ lds_key(trow));
-    roff[i] = (uint32_t)((32 * kh + 8 * qg + 4 * i) * kRowBytes);
-  }
+  for (int i = 0; i < 4; ++i)
+    voff[i] = (uint32_t)((loff + 4 * i + lgrp) * kRowBytes) +
+              16u * (uint32_t)((lane & 15) ^ lds_key(16 * wave + 4 * i + lgrp));
   auto tile_issue = [&](Chunk ca, Chunk cb, uint32_t st_m0) {
-    const int pos = (kh && cb.nv > 0) ? cb.pos : ca.pos;
+    const int pos = (lchunk && cb.nv > 0) ? cb.pos : ca.pos;
     const uint16_t* kb = a.Kp + kv_off + (size_t)pos * D;
     const uint16_t* vb = a.Vp + kv_off + (size_t)pos * D;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      lds_dma16_so(kb, voff[i], st_m0 + roff[i]);
-      lds_dma16_so(vb, voff[i], st_m0 + roff[i] + kTile);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m0v = st_m0 + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
+      lds_dma16_so(kb, voff[i], m0v);
+      lds_dma16_so(vb, voff[i], m0v + kTile);
     }
   };
 
@@ -565,61 +569,65 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(const DqArgs a) {
   vmem_wait_all();
   __syncthreads();
 
-  auto step = [&](const char* st, uint32_t nx_m0) {
-    const Chunk mine = kh ? b0 : a0;
-    if (active && mine.nv > 0) {
-      // S^T and dP^T for this wave's chunk (32 kv rows) and 32 queries.
-      const int row = 32 * kh + l32;
-      const char* kp = st + row * kRowBytes;
-      const char* vp = st + kTile + row * kRowBytes;
-      f32x16_t sacc, dpacc;
+  // One chunk (kv rows 32 ch .. +32 of the tile at st).
+  auto chunk = [&](const char* st, int ch, int nv) {
+    const int row = 32 * ch + l32;
+    const char* kp = st + row * kRowBytes;
+    const char* vp = st + kTile + row * kRowBytes;
+    f32x16_t sacc, dpacc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sacc[e] = 0.f;
-        dpacc[e] = 0.f;
-      }
+    for (int e = 0; e < 16; ++e) {
+      sacc[e] = 0.f;
+      dpacc[e] = 0.f;
+    }
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kp + lds_swz(row, 2 * kc + hl));
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vp + lds_swz(row, 2 * kc + hl));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[kc], dpacc, 0, 0, 0);
-      }
-      if (mine.nv < 32) {  // partial chunk: padded kv rows get P = 0
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kp + lds_swz(row, 2 * kc + hl));
+      const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vp + lds_swz(row, 2 * kc + hl));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], sacc, 0, 0, 0);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[kc], dpacc, 0, 0, 0);
+    }
+    if (nv < 32) {  // partial chunk: padded kv rows get P = 0
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (8 * (e >> 2) + 4 * hl + (e & 3) >= mine.nv) sacc[e] = -INFINITY;
-      }
-      // dS^T = P^T * (dP^T - D), rounded to bf16 (the B operand of dQ^T += K^T dS^T).
-      uint32_t dw[8];
+      for (int e = 0; e < 16; ++e)
+        if (8 * (e >> 2) + 4 * hl + (e & 3) >= nv) sacc[e] = -INFINITY;
+    }
+    // dS^T = P^T * (dP^T - D), rounded to bf16 (the B operand of dQ^T += K^T dS^T).
+    uint32_t dw[8];
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e], c2, nlse2));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[e + 1], c2, nlse2));
-        dw[e >> 1] = pack_bf16x2(p0 * (dpacc[e] - dq_d), p1 * (dpacc[e + 1] - dq_d));
-      }
-      // dQ^T += K^T dS^T over the chunk's 32 kv rows (two 16-row k-steps); each K^T fragment is
-      // two transposing 8-byte reads of the K tile.
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e], c2, nlse2));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[e + 1], c2, nlse2));
+      dw[e >> 1] = pack_bf16x2(p0 * (dpacc[e] - dq_d), p1 * (dpacc[e + 1] - dq_d));
+    }
+    // dQ^T += K^T dS^T over the chunk's 32 kv rows (two 16-row k-steps); each K^T fragment is
+    // two transposing 8-byte reads of the K tile.
 #pragma unroll
-      for (int dm = 0; dm < 4; ++dm) {
+    for (int dm = 0; dm < 4; ++dm) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int row_lo = 32 * kh + 16 * kk + vrow_l, row_hi = row_lo + 8;
-          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)((lds_char_t*)st + row_lo * kRowBytes +
-                             lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
-          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_t*)((lds_char_t*)st + row_hi * kRowBytes +
-                             lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
-          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-          const bf16x8_t kt = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
-          const bf16x8_t dsb = __builtin_bit_cast(
-              bf16x8_t, make_uint4(dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]));
-          acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb, acc[dm], 0, 0, 0);
-        }
+      for (int kk = 0; kk < 2; ++kk) {
+        const int row_lo = 32 * ch + 16 * kk + vrow_l, row_hi = row_lo + 8;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((lds_char_t*)st + row_lo * kRowBytes +
+                           lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((lds_char_t*)st + row_hi * kRowBytes +
+                           lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        const bf16x8_t kt = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+        const bf16x8_t dsb = __builtin_bit_cast(
+            bf16x8_t, make_uint4(dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]));
+        acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb, acc[dm], 0, 0, 0);
       }
     }
-    // The next tile's copies (issued after this tile's MFMAs have been issued).
+  };
+
+  auto step = [&](const char* st, uint32_t nx_m0) {
+    if (active) {
+      chunk(st, 0, a0.nv);
+      if (b0.nv > 0) chunk(st, 1, b0.nv);
+    }
+    // The next tile's copies (issued after this tile's matrix work has been issued).
     const Chunk an = take_chunk<false>(cur, a.col_idx, a.kvstart);
     const Chunk bn = take_chunk<false>(cur, a.col_idx, a.kvstart);
     if (a1.nv > 0) tile_issue(a1, b1, nx_m0);
@@ -637,22 +645,7 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(const DqArgs a) {
     step(lds_b, m0_a);
   }
 
-  // Sum the two chunks' partial dQ^T in a fixed order: chunk-1 waves store theirs
-  // ([query group][register][lane] floats, 64 KB, in the idle stages), chunk-0 waves add them.
-  static_assert(4 * 64 * 64 * 4 <= 2 * kDqStage, "reduction buffer");
-  float* red = reinterpret_cast<float*>(lds) + qg * 64 * 64 + lane;
-  if (kh == 1) {
-#pragma unroll
-    for (int dm = 0; dm < 4; ++dm)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) red[(16 * dm + e) * 64] = acc[dm][e];
-  }
-  __syncthreads();
-  if (kh == 1 || !qvalid) return;
-#pragma unroll
-  for (int dm = 0; dm < 4; ++dm)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[dm][e] += red[(16 * dm + e) * 64];
+  if (!qvalid) return;
   const float sig = a.scale[bh % a.H];  // dQ = sigma_h dS K
   uint16_t* op = a.dQ + head_off + (size_t)qtok * D;
 #pragma unroll
@@ -665,6 +658,7 @@ __global__ __launch_bounds__(512, 2) void dq_kernel(const DqArgs a) {
       *reinterpret_cast<uint2*>(op + 32 * dm + 8 * g + 4 * hl) = pk;
     }
 }
+
 
 }  // namespace
 
@@ -748,6 +742,6 @@ hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, cons
   q.nq = p.nq;
   q.nkv = p.nkv;
   q.Npad = Npad;
-  dq_kernel<<<dim3(p.n_items, BH), 512, 0, s>>>(q);
+  dq_kernel<<<dim3(p.n_items, BH), 256, 0, s>>>(q);
   return hipGetLastError();
 }
