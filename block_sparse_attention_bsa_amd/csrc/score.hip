@@ -2,8 +2,8 @@
 // carries the argument": queries score the block means; referee report major comment 1:
 // Eq. 3 ranks entries of the whole query-by-block matrix of a head).
 //
-//   logits_kernel   L[bh, I, J] = sigma_h * <Qbar_I, Kbar_J> in fp32, 32 x 64 output tiles,
-//                   each thread a 2 x 4 micro-tile, operands staged in padded LDS.
+//   logits_kernel   L[bh, I, J] = sigma_h * <Qbar_I, Kbar_J> in fp32 on the matrix cores
+//                   (v_mfma_f32_32x32x2_f32), one wavefront per 32 x 32 tile.
 //   row_softmax     one wavefront per row: S = exp(L - max) / sum, fp32, fixed reduction order.
 //   head_softmax    one 1024-thread workgroup per head: W = |I| exp(L - M) / Z with the head max
 //                   M and Z = sum |I| exp(L - M) accumulated in fp64 (fixed order).
@@ -12,51 +12,51 @@
 
 namespace {
 
-constexpr int kTI = 32, kTJ = 64;
+constexpr int kTI = 32, kTJ = 32;
 
+// One wavefront per 32 x 32 tile of L. In each k-step of the MFMA the two 32-lane halves supply
+// the two k-indices; half h takes d = (D/2) h + s at step s, so that every lane streams one
+// contiguous half row of Qbar (A operand, row I0 + lane % 32) and of Kbar (B operand, column
+// J0 + lane % 32) with 16-byte loads. The products and sums are fp32; the summation order over d
+// is the matrix core's.
 template <int D>
-__global__ __launch_bounds__(256) void logits_kernel(const float* __restrict__ Qbar,
-                                                     const float* __restrict__ Kbar,
-                                                     const float* __restrict__ scale, int H,
-                                                     int nq, int nkv, float* __restrict__ S) {
-  __shared__ float qs[kTI][D + 1];
-  __shared__ float ks[kTJ][D + 1];
+__global__ __launch_bounds__(64) void logits_kernel(const float* __restrict__ Qbar,
+                                                    const float* __restrict__ Kbar,
+                                                    const float* __restrict__ scale, int H,
+                                                    int nq, int nkv, float* __restrict__ S) {
+  constexpr int kHalf = D / 2, kVec = kHalf / 4;
   const int bh = blockIdx.z;
   const int I0 = blockIdx.y * kTI, J0 = blockIdx.x * kTJ;
-  const int t = threadIdx.x;
-  const float* Qh = Qbar + (size_t)bh * nq * D;
-  const float* Kh = Kbar + (size_t)bh * nkv * D;
-  for (int e = t; e < kTI * D; e += 256) {
-    const int r = e / D, c = e % D;
-    qs[r][c] = (I0 + r < nq) ? Qh[(size_t)(I0 + r) * D + c] : 0.f;
-  }
-  for (int e = t; e < kTJ * D; e += 256) {
-    const int r = e / D, c = e % D;
-    ks[r][c] = (J0 + r < nkv) ? Kh[(size_t)(J0 + r) * D + c] : 0.f;
-  }
-  __syncthreads();
-  const int ty = t / 16, tx = t % 16;
-  float acc[2][4] = {};
-#pragma unroll 8
-  for (int k = 0; k < D; ++k) {
-    const float a0 = qs[2 * ty][k], a1 = qs[2 * ty + 1][k];
+  const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
+  // rows and columns past the matrix edge read the last row (in bounds); they are not stored
+  const float4* qp = reinterpret_cast<const float4*>(
+      Qbar + ((size_t)bh * nq + min(I0 + l32, nq - 1)) * D + kHalf * h);
+  const float4* kp = reinterpret_cast<const float4*>(
+      Kbar + ((size_t)bh * nkv + min(J0 + l32, nkv - 1)) * D + kHalf * h);
+  float4 qa[kVec], kb[kVec];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float b = ks[tx + 16 * c][k];
-      acc[0][c] = fmaf(a0, b, acc[0][c]);
-      acc[1][c] = fmaf(a1, b, acc[1][c]);
-    }
+  for (int i = 0; i < kVec; ++i) {
+    qa[i] = qp[i];
+    kb[i] = kp[i];
   }
+  f32x16_t acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i].x, kb[i].x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i].y, kb[i].y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i].z, kb[i].z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i].w, kb[i].w, acc, 0, 0, 0);
+  }
+  // lane holds column J0 + lane % 32 and rows I0 + 8 (e / 4) + 4 h + e % 4
   const float sig = scale[bh % H];
+  const int J = J0 + l32;
+  if (J >= nkv) return;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int I = I0 + 2 * ty + r;
-    if (I >= nq) continue;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int J = J0 + tx + 16 * c;
-      if (J < nkv) S[((size_t)bh * nq + I) * nkv + J] = sig * acc[r][c];
-    }
+  for (int e = 0; e < 16; ++e) {
+    const int I = I0 + 8 * (e >> 2) + 4 * h + (e & 3);
+    if (I < nq) S[((size_t)bh * nq + I) * nkv + J] = sig * acc[e];
   }
 }
 
@@ -119,9 +119,9 @@ hipError_t launch_score(const bsa_plan& p, const float* Qbar, const float* Kbar,
   const int BH = p.prob.B * p.prob.H;
   dim3 grid((p.nkv + kTJ - 1) / kTJ, (p.nq + kTI - 1) / kTI, BH);
   if (p.prob.d == 128)
-    logits_kernel<128><<<grid, 256, 0, s>>>(Qbar, Kbar, p.scale, p.prob.H, p.nq, p.nkv, S);
+    logits_kernel<128><<<grid, 64, 0, s>>>(Qbar, Kbar, p.scale, p.prob.H, p.nq, p.nkv, S);
   else
-    logits_kernel<64><<<grid, 256, 0, s>>>(Qbar, Kbar, p.scale, p.prob.H, p.nq, p.nkv, S);
+    logits_kernel<64><<<grid, 64, 0, s>>>(Qbar, Kbar, p.scale, p.prob.H, p.nq, p.nkv, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (norm == BSA_NORM_ROW) {
