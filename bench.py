@@ -242,7 +242,9 @@ def main():
     layers = [BlockSparseAttention(w.B, w.H, w.d, w.grid, w.qpart, kp, dtype=w.dtype,
                                    head_scale=x["head_scale"]) for kp in kvparts]
     out = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    # The LSE is an output of the training layer (the backward consumes it); an inference layer
+    # requests O only, which runs the output-only attention kernel.
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda") if w.backward else None
     do = dev(x["do"]) if w.backward else None
     head = w.mode == "head"
     mink = 2 if w.mode == "hybrid" else 0
@@ -263,7 +265,7 @@ def main():
                 L.select(w.p)
             for _ in range(w.drift_steps):
                 with tm("attn"):
-                    L.attention(qd, kd, vd, out=out, lse=lse)
+                    L.attention(qd, kd, vd, out=out, lse=lse, with_lse=w.backward)
             return
         for L, tag in zip(layers, tags):
             with tm("pool"):
@@ -273,7 +275,7 @@ def main():
             with tm("select"):
                 L.select(w.p, 1 if head else 0, mink)
             with tm("attn"), (tm("attn" + tag) if tag else nullcontext()):
-                L.attention(q, k, v, out=out, lse=lse)
+                L.attention(q, k, v, out=out, lse=lse, with_lse=w.backward)
             if w.backward:
                 with tm("bwd"), (tm("bwd" + tag) if tag else nullcontext()):
                     L.backward(q, k, v, out, do, lse)
@@ -363,6 +365,18 @@ def main():
         torch.cuda.synchronize()
         res["stage_ms"]["calibrate_masses_only"] = round(tm.mean_ms("calibrate_masses_only"), 4)
         res["calibrate_then_reuse"] = retained_mass(w, x, layers[0], dev)
+    if not w.backward:
+        # the same attention call with the LSE requested as well (the training kernel), untimed
+        # in the step
+        lse_x = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        qa, ka, va = (qd, kd, vd) if w.mode == "calib" else (q, k, v)
+        for _ in range(5):
+            with tm("attn_with_lse"):
+                layers[0].attention(qa, ka, va, out=out, lse=lse_x)
+        torch.cuda.synchronize()
+        res["attn_with_lse"] = {"ms": round(tm.mean_ms("attn_with_lse"), 4),
+                                "tflops": attn_flops / (tm.mean_ms("attn_with_lse") * 1e-3)
+                                / 1e12}
     if args.copy_ref_mib:
         n = args.copy_ref_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")

@@ -27,7 +27,8 @@
 // comes from two transposing 8-byte LDS reads (ds_read_b64_tr_b16) of the row-major V tile. The
 // running max is raised lazily: only when a tile's weights against the current max would sum past
 // 2^32, which is detected from the row sum the softmax needs anyway, so no per-tile max is formed
-// and the O rescale is rare.
+// and the O rescale is rare. When no LSE is requested (an inference call) the fp32 row sum is not
+// formed: the sum of the bf16-rounded weights, which O is normalised by, serves as the bound.
 #include "bsa_internal.h"
 #include "device_common.h"
 #include "kv_cursor.h"
@@ -36,9 +37,10 @@ namespace {
 
 // ------------------------------------------------------------------------------- MFMA path
 
-// kFwd: sparse attention; kLse / kMass: the two dense calibration passes; kMassO: the second
-// calibration pass that also forms the dense attention output from the same exact weights.
-enum Mode { kFwd = 0, kLse = 1, kMass = 2, kMassO = 3 };
+// kFwd: sparse attention with its LSE; kFwdO: sparse attention, output only; kLse / kMass: the
+// two dense calibration passes; kMassO: the second calibration pass that also forms the dense
+// attention output from the same exact weights.
+enum Mode { kFwd = 0, kLse = 1, kMass = 2, kMassO = 3, kFwdO = 4 };
 
 
 constexpr int kTileKV = 64;                    // kv tokens per iteration (two chunks)
@@ -68,8 +70,8 @@ struct MfmaArgs {
   const int32_t* items;
   const float* scale;
   const float* lse_in;  // kMass, kMassO: per-token log-sum-exp (from the kLse pass)
-  uint16_t* O;          // kFwd, kMassO
-  float* lse;           // kFwd and kMassO (nullable outputs), kLse
+  uint16_t* O;          // kFwd, kFwdO, kMassO
+  float* lse;           // kFwd (required), kMassO (nullable), kLse
   float* part;          // kMass: [bh][item][wave][nkv] per-wave block sums
   int n_items, H, N, nq, nkv;
   int Npad;  // K and V are permuted into block order: [B*H][Npad][d], Npad = N + kPermPad
@@ -79,8 +81,8 @@ struct MfmaArgs {
 template <int MODE>
 __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   constexpr int D = 128;
-  constexpr bool kDense = MODE != kFwd;  // all kv blocks, not a CSR row
-  constexpr bool kPV = MODE == kFwd || MODE == kMassO;  // O = P V is formed
+  constexpr bool kDense = MODE == kLse || MODE == kMass || MODE == kMassO;  // all kv blocks
+  constexpr bool kPV = MODE == kFwd || MODE == kFwdO || MODE == kMassO;  // O = P V is formed
   constexpr bool kNeedV = kPV;
   constexpr int kStage = kNeedV ? 2 * kTileBytes : kTileBytes;
   __shared__ __attribute__((aligned(1024))) char lds[2 * kStage];
@@ -267,9 +269,9 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         for (int kc = 0; kc < 4; ++kc) vf0[kc] = vfrag(0, kc);
         __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the VALU work below
       }
-      // P rounded to bf16 (the B operand of the PV product), with the sum of the rounded weights
-      // (one bf16 dot product with (1, 1) per packed word) added to lb_run.
-      auto pack_weights = [&](const float (&pv)[2][16], bf16x8_t (&pb)[4]) {
+      // P rounded to bf16 (the B operand of the PV product); returns the sum of the rounded
+      // weights (one bf16 dot product with (1, 1) per packed word).
+      auto pack_weights = [&](const float (&pv)[2][16], bf16x8_t (&pb)[4]) -> float {
         uint32_t pw[2][8];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -281,12 +283,12 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         for (int i = 0; i < 16; ++i)
           lb[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(
               __builtin_bit_cast(bf16x2_t, pw[i >> 3][i & 7]), one2, lb[i & 3], false);
-        lb_run += (lb[0] + lb[1]) + (lb[2] + lb[3]);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
           const uint32_t* src = &pw[kc >> 1][4 * (kc & 1)];
           pb[kc] = __builtin_bit_cast(bf16x8_t, make_uint4(src[0], src[1], src[2], src[3]));
         }
+        return (lb[0] + lb[1]) + (lb[2] + lb[3]);
       };
       // O^T += V^T P^T.
       auto pv_product = [&](const bf16x8_t (&pb)[4]) {
@@ -342,9 +344,40 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         }
         if constexpr (MODE == kMassO) {
           bf16x8_t pb[4];
-          pack_weights(pv, pb);
+          lb_run += pack_weights(pv, pb);
           pv_product(pb);
         }
+      } else if constexpr (MODE == kFwdO) {
+        // As the path below, with the bf16-rounded weights' sum (which O is normalised by) as
+        // the only sum: it bounds every weight as well, and no LSE is formed.
+        float pv[2][16];
+        bf16x8_t pb[4];
+        auto weights = [&]() {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              pv[mb][e] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, -m_run));
+          return pack_weights(pv, pb);
+        };
+        float lsum = weights();
+        if (__ballot(!(lsum <= kSumMax)) != 0) {
+          asm volatile("");  // keep this a branch
+          float sm = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+          for (int e = 1; e < 16; ++e) sm = fmaxf(sm, fmaxf(sacc[0][e], sacc[1][e]));
+          const float m_new = fmaxf(m_run, pair_max(sm) * c2);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          lb_run *= alpha;
+#pragma unroll
+          for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[dm][e] *= alpha;
+          m_run = m_new;
+          lsum = weights();
+        }
+        lb_run += lsum;
+        pv_product(pb);
       } else {
         // Weights p = exp2(c2 * s - m_run) against the running max as it stands, and this
         // lane's partial sum. No tile max is formed on this path: the sum bounds every weight,
@@ -389,7 +422,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         l_run += lsum;
         if constexpr (MODE == kFwd) {
           bf16x8_t pb[4];
-          pack_weights(pv, pb);
+          lb_run += pack_weights(pv, pb);
           pv_product(pb);
         }
       }
@@ -431,7 +464,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     if (a.lse && hl == 0) a.lse[(size_t)bh * a.N + qtok] = a.lse_in[(size_t)bh * a.N + qtok];
     return;
   }
-  if (a.lse && hl == 0)
+  if constexpr (MODE == kFwdO) return;
+  if (hl == 0)
     a.lse[(size_t)bh * a.N + qtok] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
@@ -641,7 +675,11 @@ hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, cons
     a.O = static_cast<uint16_t*>(O);
     a.lse = lse;
     // gridDim.x * gridDim.y is exactly n_items * B * H (the XCD remap is a bijection on it).
-    attn_mfma_d128<kFwd><<<dim3(p.n_items, p.prob.B * p.prob.H), 256, 0, s>>>(a);
+    const dim3 grid(p.n_items, p.prob.B * p.prob.H);
+    if (lse)
+      attn_mfma_d128<kFwd><<<grid, 256, 0, s>>>(a);
+    else
+      attn_mfma_d128<kFwdO><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
   }
   if (p.prob.dtype == BSA_BF16)

@@ -70,10 +70,13 @@ class BlockSparseAttention:
                    self.ws_select, self.plan.ws_select, stream)
         return self.row_ptr, self.col_idx
 
-    def attention(self, q, k, v, row_ptr=None, col_idx=None, out=None, lse=None, stream=None):
+    def attention(self, q, k, v, row_ptr=None, col_idx=None, out=None, lse=None, stream=None,
+                  with_lse=True):
+        """O (and the LSE, unless with_lse is False: then the output-only kernel runs and the
+        returned lse is None)."""
         if out is None:
             out = torch.empty_like(q)
-        if lse is None:
+        if lse is None and with_lse:
             lse = torch.empty(q.shape[:3], dtype=torch.float32, device=self.device)
         if self._ws_fwd is None and self.plan.ws_fwd > 0:
             self._ws_fwd = torch.empty(self.plan.ws_fwd, dtype=torch.uint8, device=self.device)
@@ -93,13 +96,13 @@ class BlockSparseAttention:
 
     # -- whole layer ---------------------------------------------------------------------------
     def forward(self, q, k, v, p, mode="row", min_k_mode=BSA_MINK_NONE, out=None, lse=None,
-                stream=None):
+                stream=None, with_lse=True):
         """pool(Q), pool(K), score, select, sparse attention. mode: 'row' or 'head'."""
         self.pool(q, k, stream)
         self.score(BSA_NORM_HEAD if mode == "head" else BSA_NORM_ROW, stream)
         self.select(p, BSA_POOL_HEAD if mode == "head" else BSA_POOL_ROW, min_k_mode,
                     stream=stream)
-        return self.attention(q, k, v, out=out, lse=lse, stream=stream)
+        return self.attention(q, k, v, out=out, lse=lse, stream=stream, with_lse=with_lse)
 
     def csr_host(self):
         rp = self.row_ptr.cpu().numpy()

@@ -22,7 +22,9 @@ import sqlite3
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-ATTN = "attn_mfma_d128<0>"
+# The attention kernel of the call measured: the output-only kernel (an inference layer) when
+# the run has it, else the one that also writes the LSE.
+ATTN_KERNELS = ("attn_mfma_d128<4>", "attn_mfma_d128<0>")
 PERM = "permute_rows_kernel"
 COPY = "__amd_rocclr_copyBuffer"
 
@@ -69,6 +71,7 @@ def counters(fetch_csv, write_csv, workload, cmd_f, cmd_w, copy_mib=1024):
     f_scale = ref_kib / max(fe[COPY])       # the largest copy dispatch is the reference copy
     w_scale = ref_kib / max(wr[COPY])
     mean = lambda v: sum(v) / len(v)
+    ATTN = next(k for k in ATTN_KERNELS if fe.get(k) and wr.get(k))
     f_attn, w_attn = mean(fe[ATTN]) * f_scale, mean(wr[ATTN]) * w_scale
     f_perm, w_perm = mean(fe[PERM]) * f_scale, mean(wr[PERM]) * w_scale
     per_call_kib = f_attn + w_attn + 2 * (f_perm + w_perm)

@@ -178,7 +178,10 @@ int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* pa
  * tokens j of the kv blocks listed in CSR row I, and lse_i = log sum_j exp(sigma_h q_i . k_j).
  * Q, K, V, O [B, H, N, d] of the plan's dtype; lse fp32 [B, H, N] (nullable). bf16: products on
  * bf16 matrix cores with fp32 accumulation and fp32 online softmax; P is rounded to bf16 before
- * the PV product. The CSR must come from bsa_select for this plan (or be equivalent: indices
+ * the PV product, and O is normalised by the sum of those rounded weights. With lse NULL the
+ * fp32 row sums that only the LSE needs are not formed (the same O; a faster kernel for bf16,
+ * d = 128).
+ * The CSR must come from bsa_select for this plan (or be equivalent: indices
  * in [0, nkv), no duplicates within a row). ws (device, ws_bytes >= ws_fwd of bsa_plan_info;
  * may be NULL when ws_fwd is 0) receives K and V copied into block order; BSA_ECAPACITY if it
  * is too small. */

@@ -67,6 +67,18 @@ def _run_case(w, seed, tol_o, tol_lse, grid=None, H=None, kvpart=None, qpart=Non
         if len(sel) == 0:
             bh, I = divmod(r, len(qblocks))
             assert np.all(O_gpu[bh // w.H, bh % w.H, qblocks[I]] == 0)
+    # the output-only kernel (no LSE requested) on the same inputs
+    O2, L2 = layer.attention(q, k, v, row_ptr=rp_d, col_idx=ci_d, with_lse=False)
+    torch.cuda.synchronize()
+    assert L2 is None
+    O2_gpu = dev_to_f64(O2)
+    err2 = np.abs(O2_gpu - O_ref).max()
+    log(f"  output-only O max-abs {err2:.3e}")
+    assert err2 <= tol_o
+    for r, sel in enumerate(rows):
+        if len(sel) == 0:
+            bh, I = divmod(r, len(qblocks))
+            assert np.all(O2_gpu[bh // w.H, bh % w.H, qblocks[I]] == 0)
 
 
 def test_attn_fwd_fp32_tiny():

@@ -67,6 +67,16 @@ def _run(w, tol_o, tol_lse, sample=None, seed=0):
     assert torch.equal(O2.view(torch.int16) if O2.dtype == torch.bfloat16 else O2,
                        O1.view(torch.int16) if O1.dtype == torch.bfloat16 else O1)
 
+    # the output-only kernel (no LSE requested, as an inference layer calls it)
+    O3, L3 = layer.forward(q, k, v, w.p, with_lse=False)
+    torch.cuda.synchronize()
+    assert L3 is None and torch.equal(layer.row_ptr, rp1)
+    O3_gpu = dev_to_f64(O3)
+    worst3 = max(float(np.abs(O3_gpu[b, h, qb[i]] - O_ref[b, h, qb[i]]).max())
+                 for b, h, i in sel_rows)
+    log(f"  output-only O max-abs {worst3:.3e}")
+    assert worst3 <= tol_o
+
 
 def test_pipeline_c1_tiny_fp32():
     _run(CONFIGS[1], tol_o=1e-5, tol_lse=1e-5)
