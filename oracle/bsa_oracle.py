@@ -6,6 +6,10 @@ Sources (page title, then the section on it):
   [LoSA]   scholarbro author page (Changming Sun), LoSA abstract: exact block attention masses at one
            early dense step; per head and query block the smallest key/value block set meeting a
            99% retained-mass threshold; the frozen indices are reused for the remaining steps.
+  [EG]     readsearch page "Competition Domains Matter: Selective Head Globalization for
+           Training-Free Sparse Attention in Video Diffusion Transformers", abstract (EG-Sparse):
+           low-entropy heads compete in a grouped cross-head pool, high-entropy heads keep per-row
+           selection, using only the scores the pipeline already has.
   [SCOPE]  mlsift "sparse attention" listing, SCOPE abstract: hybrid top-p / fixed top-k; a
            head-specific k from the initial retained counts averaged with query-cluster-size
            weights; extra keys only for clusters whose initial count falls below it.
@@ -30,7 +34,15 @@ reasoning in the design notes):
   * indices within a row are returned ascending;
   * SCOPE's head k is the integer ceiling of the |I|-weighted mean count, capped at the block count;
   * a query block with no selected block outputs O = 0 and LSE = -inf, with zero gradients;
-  * the selection is a hard, stop-gradient gate in the backward pass.
+  * the selection is a hard, stop-gradient gate in the backward pass;
+  * [EG] (the abstract fixes none of these): a head's entropy is the |I|-weighted mean over its
+    query blocks of the Shannon entropy of the row-normalised scores, divided by ln(nkv); a
+    head is low-entropy when that is below a caller threshold theta; groups are runs of
+    group_size consecutive heads; the pool of a group holds every (h, I, J) of its low-entropy
+    heads with weight S[h, I, J] * |I| / (N * m) (m pooled heads, so the pool sums to 1) and
+    keeps the shortest prefix, in (weight desc, pool index asc) order, reaching p; pool index
+    runs over (pooled head in head order, I, J). High-entropy heads select per row with the
+    same p.
 """
 from __future__ import annotations
 
@@ -42,7 +54,8 @@ import numpy as np
 __all__ = [
     "partition", "block_sizes", "pool", "block_logits", "score_row", "score_head",
     "exact_mass", "exact_mass_row", "select_topp", "select_row", "head_min_k",
-    "select_hybrid", "select_head", "to_csr", "csr_rows", "attention_rows", "attention_fwd",
+    "select_hybrid", "select_head", "head_entropy", "select_group", "select_eg", "to_csr",
+    "csr_rows", "attention_rows", "attention_fwd",
     "attention_bwd", "row_backward", "density",
 ]
 
@@ -230,6 +243,67 @@ def select_head(W: np.ndarray, tau: float) -> List[np.ndarray]:
             for i in range(nq):
                 rows.append(np.sort(J[I == i]))
     return rows
+
+
+def head_entropy(S: np.ndarray, qsizes) -> np.ndarray:
+    """[EG] per-head score entropy [B, H]: sum_I |I| * H_I / (N * ln nkv), with
+    H_I = -sum_J S[b, h, I, J] ln S[b, h, I, J] (0 ln 0 = 0) of the row-normalised scores.
+    A uniform head gives 1, a head whose rows are one-hot gives 0; with one kv block, 0."""
+    B, H, nq, nkv = S.shape
+    w = np.asarray(qsizes, np.float64)
+    out = np.zeros((B, H))
+    if nkv <= 1:
+        return out
+    for b in range(B):
+        for h in range(H):
+            tot = 0.0
+            for i in range(nq):
+                row = np.asarray(S[b, h, i], np.float64)
+                pos = row[row > 0]
+                tot += w[i] * float(-(pos * np.log(pos)).sum())
+            out[b, h] = tot / (w.sum() * math.log(nkv))
+    return out
+
+
+def select_group(S: np.ndarray, p: float, qsizes, pooled: np.ndarray,
+                 group_size: int) -> List[np.ndarray]:
+    """[EG] competition domains: heads not flagged in `pooled` [B, H] select per row (top-p of
+    their row); each run of group_size consecutive heads pools the (h, I, J) of its flagged
+    heads, weighted S * |I| / (N * m) for m flagged heads, and keeps the shortest prefix in
+    (weight desc, pool index asc) order reaching p. A pooled query block may keep no block."""
+    B, H, nq, nkv = S.shape
+    qs = np.asarray(qsizes, np.float64)
+    N = qs.sum()
+    rows: Dict[int, np.ndarray] = {}
+    for b in range(B):
+        for g0 in range(0, H, group_size):
+            heads = list(range(g0, min(g0 + group_size, H)))
+            members = [h for h in heads if pooled[b, h]]
+            for h in heads:
+                if not pooled[b, h]:
+                    for i in range(nq):
+                        rows[(b * H + h) * nq + i] = select_topp(S[b, h, i], p)
+            if not members:
+                continue
+            m = len(members)
+            W = np.stack([np.asarray(S[b, h], np.float64) * qs[:, None] / (N * m)
+                          for h in members])            # [m, nq, nkv], pool index order
+            chosen = select_topp(W.reshape(-1), p)
+            k, rem = np.divmod(chosen, nq * nkv)
+            I, J = np.divmod(rem, nkv)
+            for kk, h in enumerate(members):
+                for i in range(nq):
+                    rows[(b * H + h) * nq + i] = np.sort(J[(k == kk) & (I == i)])
+    return [rows[r] for r in range(B * H * nq)]
+
+
+def select_eg(S: np.ndarray, p: float, qsizes, theta: float,
+              group_size: int) -> Tuple[List[np.ndarray], np.ndarray, np.ndarray]:
+    """[EG] entropy-routed selection: (rows, entropy [B, H], pooled [B, H]) with
+    pooled = entropy < theta."""
+    ent = head_entropy(S, qsizes)
+    pooled = ent < theta
+    return select_group(S, p, qsizes, pooled, group_size), ent, pooled
 
 
 def to_csr(rows: Sequence[np.ndarray]) -> Tuple[np.ndarray, np.ndarray]:
