@@ -69,6 +69,42 @@ def read_traffic(kernel_src, workload):
         return None
 
 
+def entropy_routed(w, L, q, k, v, out, tm, group_size=4, calls=5):
+    """The same layer with EG-Sparse's entropy-routed selection (bsa_select_eg) in place of the
+    per-row one, timed outside the step: pooled heads, the selection's time, the density and
+    the output-only attention time on its block sets. theta is the median of the heads'
+    entropies, so about half of the heads compete in a pool of group_size heads."""
+    import numpy as np
+    import torch
+    L.pool(q, k)
+    L.score(0)
+    L.select_eg(w.p, float("-inf"), group_size)          # entropies only
+    torch.cuda.synchronize()
+    ent = L.head_entropy.cpu().numpy().astype(np.float64)
+    theta = float(np.median(ent))
+    for _ in range(calls):
+        with tm("select_eg"):
+            L.select_eg(w.p, theta, group_size)
+        with tm("attn_eg"):
+            L.attention(q, k, v, out=out, with_lse=False)
+    torch.cuda.synchronize()
+    rp, ci = L.csr_host()
+    qs, ks = np.diff(L.plan.blocks(0)[1]), np.diff(L.plan.blocks(1)[1])
+    f = attention_flops(csr_rows(rp, ci), qs, ks, w.d)
+    attn_ms = tm.mean_ms("attn_eg")
+    return {"group_size": group_size, "theta": theta,
+            "pooled_heads": int(L.head_pooled.sum().item()), "heads": int(ent.size),
+            "select_ms": round(tm.mean_ms("select_eg"), 4),
+            "density": round(f / (4.0 * w.B * w.H * w.N * w.N * w.d), 4),
+            "empty_row_fraction": round(float(np.mean(np.diff(rp) == 0)), 4),
+            "attn_ms": round(attn_ms, 4), "attn_tflops": f / (attn_ms * 1e-3) / 1e12}
+
+
+def csr_rows(row_ptr, col_idx):
+    """The CSR's rows as a list of index arrays (for the FLOP count of the selected blocks)."""
+    return [col_idx[row_ptr[r]:row_ptr[r + 1]] for r in range(len(row_ptr) - 1)]
+
+
 def attention_flops(rows, qsizes, kvsizes, d, per_pair=4):
     nq = len(qsizes)
     tot = 0
@@ -225,7 +261,6 @@ def main():
     import numpy as np
     import torch
 
-    import oracle
     from gen import CONFIGS, drift_step, kv_partition_for_layer, make_inputs
     from block_sparse_attention_bsa_amd.layer import BlockSparseAttention
 
@@ -286,7 +321,7 @@ def main():
     fwd_flops, dens, empty = [], [], []
     for L in layers:
         rp, ci = L.csr_host()
-        rows = oracle.csr_rows(rp, ci)
+        rows = csr_rows(rp, ci)
         qs, ks = np.diff(L.plan.blocks(0)[1]), np.diff(L.plan.blocks(1)[1])
         f = attention_flops(rows, qs, ks, w.d)
         fwd_flops.append(f)
@@ -365,6 +400,8 @@ def main():
         torch.cuda.synchronize()
         res["stage_ms"]["calibrate_masses_only"] = round(tm.mean_ms("calibrate_masses_only"), 4)
         res["calibrate_then_reuse"] = retained_mass(w, x, layers[0], dev)
+    if w.mode in ("row", "hybrid") and w.dtype == "bf16":
+        res["entropy_routed"] = entropy_routed(w, layers[0], q, k, v, out, tm)
     if not w.backward:
         # the same attention call with the LSE requested as well (the training kernel), untimed
         # in the step
@@ -387,10 +424,10 @@ def main():
     if not args.no_cpu_baseline and w.mode in ("row", "hybrid") and args.config in (1, 2):
         L = layers[0]
         rp, ci = L.csr_host()
-        res["cpu_baseline"] = cpu_baseline(w, x, oracle.csr_rows(rp, ci), fwd_flops[0],
+        res["cpu_baseline"] = cpu_baseline(w, x, csr_rows(rp, ci), fwd_flops[0],
                                            args.cpu_seconds)
         if args.config == 1:
-            res["cpu_baseline_1thread"] = cpu_baseline(w, x, oracle.csr_rows(rp, ci),
+            res["cpu_baseline_1thread"] = cpu_baseline(w, x, csr_rows(rp, ci),
                                                        fwd_flops[0], args.cpu_seconds, threads=1)
     print(json.dumps(res), flush=True)
 

@@ -5,7 +5,7 @@ declared in include/bsa.h, and every step of the computation runs in the library
 PyTorch is used for device memory and streams. There is no CPU fallback: if the library is missing
 or a call fails, an exception is raised.
 
-Names follow the C ABI: bsa_pool, bsa_score, bsa_calibrate_mass(_fwd), bsa_select, bsa_attn_fwd,
+Names follow the C ABI: bsa_pool, bsa_score, bsa_calibrate_mass(_fwd), bsa_select(_eg), bsa_attn_fwd,
 bsa_attn_bwd, bsa_partition_build; a Plan wraps bsa_plan_create / bsa_plan_info /
 bsa_plan_blocks / bsa_plan_destroy.
 """
@@ -30,8 +30,8 @@ BSA_MINK_NONE, BSA_MINK_FIXED, BSA_MINK_WEIGHTED_MEAN = 0, 1, 2
 
 EXPORTED = ("bsa_partition_build", "bsa_plan_create", "bsa_plan_destroy", "bsa_plan_info",
             "bsa_plan_blocks", "bsa_pool", "bsa_score", "bsa_calibrate_mass",
-            "bsa_calibrate_mass_fwd", "bsa_select", "bsa_attn_fwd", "bsa_attn_bwd",
-            "bsa_last_error")
+            "bsa_calibrate_mass_fwd", "bsa_select", "bsa_select_eg", "bsa_attn_fwd",
+            "bsa_attn_bwd", "bsa_last_error")
 
 
 class BsaError(RuntimeError):
@@ -55,6 +55,11 @@ class Problem(ctypes.Structure):
 class SelectParams(ctypes.Structure):
     _fields_ = [("p", ctypes.c_double), ("pool", ctypes.c_int32),
                 ("min_k_mode", ctypes.c_int32), ("fixed_k", ctypes.c_int32)]
+
+
+class EgParams(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_double), ("theta", ctypes.c_double),
+                ("group_size", ctypes.c_int32)]
 
 
 _lib = None
@@ -91,6 +96,7 @@ def lib():
         "bsa_calibrate_mass": [P, P, P, P, P, SZ, P],
         "bsa_calibrate_mass_fwd": [P, P, P, P, P, P, P, P, SZ, P],
         "bsa_select": [P, P, ctypes.POINTER(SelectParams), P, P, I64, P, P, P, SZ, P],
+        "bsa_select_eg": [P, P, ctypes.POINTER(EgParams), P, P, I64, P, P, P, P, SZ, P],
         "bsa_attn_fwd": [P, P, P, P, P, P, P, P, P, SZ, P],
         "bsa_attn_bwd": [P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     }
@@ -226,6 +232,15 @@ def bsa_select(plan: Plan, S, p: float, pool: int, min_k_mode: int, fixed_k: int
     _check(lib().bsa_select(plan.handle, _ptr(S), ctypes.byref(prm), _ptr(row_ptr),
                             _ptr(col_idx), int(col_cap), _ptr(counts), _ptr(head_k), _ptr(ws),
                             ws_bytes, _stream(stream)))
+
+
+def bsa_select_eg(plan: Plan, S, p: float, theta: float, group_size: int, row_ptr, col_idx,
+                  col_cap: int, counts, head_entropy, head_pooled, ws, ws_bytes: int,
+                  stream=None):
+    prm = EgParams(float(p), float(theta), int(group_size))
+    _check(lib().bsa_select_eg(plan.handle, _ptr(S), ctypes.byref(prm), _ptr(row_ptr),
+                               _ptr(col_idx), int(col_cap), _ptr(counts), _ptr(head_entropy),
+                               _ptr(head_pooled), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def bsa_attn_fwd(plan: Plan, Q, K, V, row_ptr, col_idx, O, lse, ws, ws_bytes: int, stream=None):

@@ -122,7 +122,15 @@ SelectWs select_ws_layout(const bsa_plan& p) {
   w.bitmap = 0;
   w.base_counts = align_up(rows * w.nwords * 4);
   w.head_k = w.base_counts + align_up(rows * 4);
-  w.total = w.head_k + align_up((size_t)p.prob.B * p.prob.H * 4);
+  const size_t BH = (size_t)p.prob.B * p.prob.H;
+  w.eg_nrchunk = (int)(((size_t)p.prob.H * p.nq + kEgRowChunk - 1) / kEgRowChunk);
+  w.eg_rowent = w.head_k + align_up(BH * 4);
+  w.eg_route = w.eg_rowent + align_up(rows * 8);
+  w.eg_members = w.eg_route + align_up(BH * 4);
+  w.eg_groups = w.eg_members + align_up(BH * 4);
+  w.eg_hist = w.eg_groups + align_up(BH * kEgGroupBytes);
+  w.eg_bnd = w.eg_hist + align_up(BH * kEgHistBytes);
+  w.total = w.eg_bnd + align_up(BH * (size_t)w.eg_nrchunk * 4);
   return w;
 }
 
@@ -379,6 +387,36 @@ int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* pr
   return launch_status(launch_select(*plan, S, *prm, row_ptr, col_idx, counts, head_k, ws,
                                      (hipStream_t)stream),
                        "bsa_select");
+}
+
+int bsa_select_eg(const bsa_plan* plan, const float* S, const bsa_eg_params* prm,
+                  int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
+                  float* head_entropy, int32_t* head_pooled, void* ws, size_t ws_bytes,
+                  void* stream) {
+  if (!plan || !S || !prm || !row_ptr || !col_idx)
+    return fail(BSA_EINVAL, "bsa_select_eg: NULL argument");
+  if (!(prm->p > 0.0 && prm->p <= 1.0))
+    return fail(BSA_EINVAL, "bsa_select_eg: p must lie in (0, 1]");
+  if (std::isnan(prm->theta)) return fail(BSA_EINVAL, "bsa_select_eg: theta is NaN");
+  if (prm->group_size < 1)
+    return fail(BSA_EINVAL, "bsa_select_eg: group_size must be >= 1");
+  if (plan->nkv > kMaxSelectBlocks)
+    return fail(BSA_EUNSUPPORTED, "bsa_select_eg: %d kv blocks exceed the supported %d",
+                plan->nkv, kMaxSelectBlocks);
+  if ((int64_t)plan->prob.H * plan->nq * plan->nkv > (int64_t)INT32_MAX)
+    return fail(BSA_EUNSUPPORTED, "bsa_select_eg: H * nq * nkv exceeds 2^31 - 1");
+  const int64_t need_cols = (int64_t)plan->prob.B * plan->prob.H * plan->nq * plan->nkv;
+  if (col_cap < need_cols)
+    return fail(BSA_ECAPACITY, "bsa_select_eg: col_idx capacity %lld < %lld",
+                (long long)col_cap, (long long)need_cols);
+  const size_t need = select_ws_layout(*plan).total;
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ECAPACITY, "bsa_select_eg: workspace %zu < %zu bytes", ws_bytes, need);
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_select_eg(*plan, S, *prm, row_ptr, col_idx, counts, head_entropy,
+                                        head_pooled, ws, (hipStream_t)stream),
+                       "bsa_select_eg");
 }
 
 int bsa_attn_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,

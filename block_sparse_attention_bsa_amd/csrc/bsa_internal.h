@@ -37,10 +37,22 @@ struct bsa_plan {
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
+// Entropy-routed selection (bsa_select_eg): pool rows per marking workgroup, and the device
+// sizes of a group's radix state and of its 256-bin histogram (counts and 2^-56 sums).
+constexpr int kEgRowChunk = 32;
+constexpr size_t kEgGroupBytes = 64;
+constexpr size_t kEgHistBytes = 256 * 4 + 256 * 8;
+
 // Workspace layouts (byte offsets), derived from the plan.
 struct SelectWs {
-  size_t bitmap, base_counts, head_k, total;
+  size_t bitmap, base_counts, head_k;
+  // bsa_select_eg: per row its entropy (fp64); per head the routing flag and its group's member
+  // slot; per group (at most B*H groups) the radix state, the histogram and the boundary-class
+  // count of each row chunk
+  size_t eg_rowent, eg_route, eg_members, eg_groups, eg_hist, eg_bnd;
+  size_t total;
   int nwords;
+  int eg_nrchunk;  // row chunks of the largest possible pool (all H heads of a batch)
 };
 SelectWs select_ws_layout(const bsa_plan& p);
 
@@ -78,6 +90,9 @@ hipError_t launch_score(const bsa_plan& p, const float* Qbar, const float* Kbar,
 hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_params& prm,
                          int32_t* row_ptr, int32_t* col_idx, int32_t* counts, int32_t* head_k,
                          void* ws, hipStream_t s);
+hipError_t launch_select_eg(const bsa_plan& p, const float* S, const bsa_eg_params& prm,
+                            int32_t* row_ptr, int32_t* col_idx, int32_t* counts,
+                            float* head_entropy, int32_t* head_pooled, void* ws, hipStream_t s);
 hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
                            const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse,
                            void* ws, hipStream_t s);

@@ -209,14 +209,18 @@ __device__ void mark_pool(const float* __restrict__ vals, int nrows, int nkv, in
   }
 }
 
-// ROW pool: one workgroup per row (b, h, I).
+// ROW pool: one workgroup per row (b, h, I). Rows of heads flagged in skip_head (nullable; the
+// pooled heads of bsa_select_eg, whose rows are written later) are left alone.
 __global__ __launch_bounds__(256) void mark_row_kernel(const float* __restrict__ S, int nkv,
                                                        int nwords, unsigned long long target,
                                                        bool select_all,
                                                        uint32_t* __restrict__ bitmap,
-                                                       int32_t* __restrict__ base_counts) {
+                                                       int32_t* __restrict__ base_counts,
+                                                       int nq,
+                                                       const int32_t* __restrict__ skip_head) {
   __shared__ RadixShared sh;
   const int64_t r = blockIdx.x;
+  if (skip_head && skip_head[r / nq]) return;
   const float* row = S + r * nkv;
   RadixResult res;
   if (select_all) {
@@ -511,11 +515,14 @@ __global__ __launch_bounds__(256) void mark_row_wave_kernel(const float* __restr
                                                             unsigned long long target,
                                                             bool select_all,
                                                             uint32_t* __restrict__ bitmap,
-                                                            int32_t* __restrict__ base_counts) {
+                                                            int32_t* __restrict__ base_counts,
+                                                            int nq,
+                                                            const int32_t* __restrict__ skip_head) {
   __shared__ WaveHist hist[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t r = (int64_t)blockIdx.x * 4 + wave;
   if (r >= rows) return;  // whole wavefronts
+  if (skip_head && skip_head[r / nq]) return;  // as mark_row_kernel
   const float* row = S + r * nkv;
   float v[kVpl];
 #pragma unroll
@@ -570,7 +577,412 @@ __global__ __launch_bounds__(256) void emit_wave_kernel(const uint32_t* __restri
   }
 }
 
+
+// ---------------------------------------------------- entropy-routed competition domains
+//
+// EG-Sparse abstract (readsearch page "Competition Domains Matter: Selective Head Globalization
+// for Training-Free Sparse Attention in Video Diffusion Transformers"): heads whose block scores
+// have low entropy compete in a pool shared by their group of heads, the others keep per-row
+// selection, and only the scores already computed are used. Here a head's entropy is the
+// |I|-weighted mean of its rows' Shannon entropies over ln nkv; a group is a run of group_size
+// consecutive heads; a group's pool holds every (h, I, J) of its pooled heads, weighted
+// S * |I| / (N m) so that it sums to 1, with the prefix rule, tie order and exact sums of the
+// other pools. A pool can hold millions of candidates, so its radix select is spread over many
+// workgroups: per 8-bit digit, workgroup histograms in LDS are added into one global histogram
+// per group, and one wavefront per group picks the digit bin from it.
+
+constexpr int kEgHistChunk = 4096;  // pool candidates per histogram workgroup (16 per thread)
+
+struct EgGroup {
+  uint32_t prefix, mask;
+  unsigned long long above_sum;
+  uint32_t above_cnt, eq_cnt;
+  int32_t m;       // pooled heads of the group
+  int32_t done;    // no further digit pass
+  int32_t all;     // every candidate is kept
+  uint32_t keep;   // members of the boundary class kept, lowest pool indices first
+  int32_t eq_all;  // keep == eq_cnt
+  int32_t pad[5];
+};
+struct EgHist {
+  unsigned int cnt[256];
+  unsigned long long sum[256];
+};
+static_assert(sizeof(EgGroup) == kEgGroupBytes, "group state size");
+static_assert(sizeof(EgHist) == kEgHistBytes, "group histogram size");
+
+// Pool weight of one score: S * |I| / (N m), the same float on every pass.
+__device__ __forceinline__ float eg_weight(float s, int qsize, int N, int m) {
+  return s * (float)((double)qsize / ((double)N * (double)m));
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+// Shannon entropy of every score row in fp64, one wavefront per row (a fixed butterfly sum).
+__global__ __launch_bounds__(256) void eg_row_entropy_kernel(const float* __restrict__ S,
+                                                             int64_t rows, int nkv,
+                                                             double* __restrict__ row_ent) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const float* row = S + r * nkv;
+  double h = 0.0;
+  for (int J = lane; J < nkv; J += 64) {
+    const double x = (double)row[J];
+    if (x > 0.0) h -= x * log(x);
+  }
+  h = wave_sum_f64(h);
+  if (lane == 0) row_ent[r] = h;
+}
+
+// One wavefront per head (b, h): the |I|-weighted mean of its rows' entropies over ln nkv (lane
+// l sums rows l, l + 64, ... in order, then a fixed butterfly), and the routing flag.
+__global__ __launch_bounds__(64) void eg_head_entropy_kernel(const double* __restrict__ row_ent,
+                                                             const int32_t* __restrict__ qstart,
+                                                             int nq, int nkv, int N,
+                                                             double theta,
+                                                             int32_t* __restrict__ route,
+                                                             float* __restrict__ ent_out,
+                                                             int32_t* __restrict__ pooled_out) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  double acc = 0.0;
+  for (int I = lane; I < nq; I += 64)
+    acc += (double)(qstart[I + 1] - qstart[I]) * row_ent[(int64_t)bh * nq + I];
+  acc = wave_sum_f64(acc);
+  if (lane == 0) {
+    const double e = nkv > 1 ? acc / ((double)N * log((double)nkv)) : 0.0;
+    const int pooled = e < theta ? 1 : 0;
+    route[bh] = pooled;
+    if (ent_out) ent_out[bh] = (float)e;
+    if (pooled_out) pooled_out[bh] = pooled;
+  }
+}
+
+// One wavefront per group (b, g): its pooled heads in head order, the radix state, a cleared
+// histogram.
+__global__ __launch_bounds__(64) void eg_setup_kernel(const int32_t* __restrict__ route, int H,
+                                                      int G, int ngh, int keep_all,
+                                                      int32_t* __restrict__ members,
+                                                      EgGroup* __restrict__ groups,
+                                                      EgHist* __restrict__ hist) {
+  const int gi = blockIdx.x, b = gi / ngh, g = gi % ngh, lane = threadIdx.x;
+  if (lane == 0) {
+    int m = 0;
+    const int h1 = min(H, (g + 1) * G);
+    for (int h = g * G; h < h1; ++h)
+      if (route[b * H + h]) members[b * H + g * G + m++] = h;
+    EgGroup st{};
+    st.m = m;
+    st.done = (m == 0 || keep_all) ? 1 : 0;
+    st.all = keep_all;
+    groups[gi] = st;
+  }
+  for (int i = lane; i < 256; i += 64) {
+    hist[gi].cnt[i] = 0u;
+    hist[gi].sum[i] = 0ull;
+  }
+}
+
+// Candidate j of group gi's pool: pooled head k = j / (nq nkv), then (I, J). Returns its weight
+// and its score row (b * H + h) * nq + I.
+__device__ __forceinline__ float eg_candidate(const float* __restrict__ S,
+                                              const int32_t* __restrict__ qstart,
+                                              const int32_t* __restrict__ members, int b, int g,
+                                              int H, int G, int nq, int nkv, int N, int m, int j,
+                                              int64_t& row, int& J) {
+  const int per = nq * nkv;
+  const int k = j / per, rem = j - k * per;
+  const int I = rem / nkv;
+  J = rem - I * nkv;
+  const int h = members[b * H + g * G + k];
+  row = ((int64_t)b * H + h) * nq + I;
+  return eg_weight(S[row * nkv + J], qstart[I + 1] - qstart[I], N, m);
+}
+
+// Digit pass: the candidates still matching the radix prefix add their count and 2^-56 sum to
+// their digit's bin, through an LDS histogram per workgroup.
+__global__ __launch_bounds__(256) void eg_hist_kernel(const float* __restrict__ S,
+                                                      const int32_t* __restrict__ qstart, int H,
+                                                      int G, int ngh, int nq, int nkv, int N,
+                                                      int pass,
+                                                      const int32_t* __restrict__ members,
+                                                      const EgGroup* __restrict__ groups,
+                                                      EgHist* __restrict__ hist) {
+  __shared__ unsigned int scnt[256];
+  __shared__ unsigned long long ssum[256];
+  const int gi = blockIdx.y;
+  const EgGroup st = groups[gi];
+  if (st.done) return;
+  const int pool_n = st.m * nq * nkv;
+  const int base = blockIdx.x * kEgHistChunk;
+  if (base >= pool_n) return;
+  const int t = threadIdx.x;
+  scnt[t] = 0u;
+  ssum[t] = 0ull;
+  __syncthreads();
+  const int b = gi / ngh, g = gi % ngh, shift = 24 - 8 * pass;
+  // 16 consecutive candidates per thread (mostly one score row): neighbours usually share a
+  // digit bin in the early passes, so runs of equal bins are summed in registers and added to
+  // the LDS histogram once per run
+  constexpr int kPer = kEgHistChunk / 256;
+  const int j0 = base + kPer * t;
+  uint32_t run_bin = 256u, run_cnt = 0u;
+  unsigned long long run_sum = 0ull;
+  for (int u = 0; u < kPer; ++u) {
+    const int j = j0 + u;
+    if (j >= pool_n) break;
+    int64_t row;
+    int J;
+    const float v = eg_candidate(S, qstart, members, b, g, H, G, nq, nkv, N, st.m, j, row, J);
+    const uint32_t key = sel_key(v);
+    if ((key & st.mask) == st.prefix) {
+      const uint32_t bin = (key >> shift) & 255u;
+      if (bin != run_bin) {
+        if (run_cnt) {
+          atomicAdd(&scnt[run_bin], run_cnt);
+          atomicAdd(&ssum[run_bin], run_sum);
+        }
+        run_bin = bin;
+        run_cnt = 0u;
+        run_sum = 0ull;
+      }
+      ++run_cnt;
+      run_sum += sel_fix(v);
+    }
+  }
+  if (run_cnt) {
+    atomicAdd(&scnt[run_bin], run_cnt);
+    atomicAdd(&ssum[run_bin], run_sum);
+  }
+  __syncthreads();
+  if (scnt[t]) {
+    atomicAdd(&hist[gi].cnt[t], scnt[t]);
+    atomicAdd(&hist[gi].sum[t], ssum[t]);
+  }
+}
+
+// One wavefront per group: the bin (in descending digit order) where the cumulative sum first
+// reaches the target narrows the prefix; none means the pool never reaches it (keep all). The
+// histogram is cleared for the next digit.
+__global__ __launch_bounds__(64) void eg_pick_kernel(int pass, unsigned long long target,
+                                                     EgGroup* __restrict__ groups,
+                                                     EgHist* __restrict__ hist) {
+  const int gi = blockIdx.x, lane = threadIdx.x;
+  EgGroup st = groups[gi];
+  if (st.done) return;
+  EgHist& hs = hist[gi];
+  unsigned long long bsum[4];
+  unsigned int bcnt[4];
+  unsigned long long lsum = 0;
+  unsigned int lcnt = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int bin = 255 - 4 * lane - i;
+    bsum[i] = hs.sum[bin];
+    bcnt[i] = hs.cnt[bin];
+    lsum += bsum[i];
+    lcnt += bcnt[i];
+  }
+  const unsigned long long isum = wave_incl_scan_u64(lsum);
+  const unsigned long long icnt = wave_incl_scan_u64(lcnt);
+  unsigned long long asum = st.above_sum + (isum - lsum);
+  unsigned long long acnt = st.above_cnt + (icnt - lcnt);
+  int found = -1;
+  unsigned long long fsum = 0, fcnt = 0;
+  unsigned int feq = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (found < 0 && asum < target && asum + bsum[i] >= target) {
+      found = 255 - 4 * lane - i;
+      fsum = asum;
+      fcnt = acnt;
+      feq = bcnt[i];
+    }
+    asum += bsum[i];
+    acnt += bcnt[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int bin = 255 - 4 * lane - i;
+    hs.sum[bin] = 0ull;
+    hs.cnt[bin] = 0u;
+  }
+  const bool any = __ballot(found >= 0) != 0ull;
+  if (!any) {
+    if (lane == 0) {
+      st.all = 1;
+      st.done = 1;
+      groups[gi] = st;
+    }
+    return;
+  }
+  if (found >= 0) {  // exactly one lane: the cumulative sums are monotone
+    const int shift = 24 - 8 * pass;
+    st.prefix |= (uint32_t)found << shift;
+    st.mask |= 255u << shift;
+    st.above_sum = fsum;
+    st.above_cnt = (uint32_t)fcnt;
+    st.eq_cnt = feq;
+    if (feq == 1u || pass == 3) {
+      st.done = 1;
+      uint32_t keep;
+      if (feq == 1u) {
+        keep = 1u;
+      } else {
+        const unsigned long long v = sel_fix(__uint_as_float(st.prefix));
+        keep = (uint32_t)((target - st.above_sum + v - 1) / v);
+      }
+      if (keep > feq) keep = feq;
+      st.keep = keep;
+      st.eq_all = keep == feq ? 1 : 0;
+    }
+    groups[gi] = st;
+  }
+}
+
+__device__ __forceinline__ bool eg_selected(const EgGroup& st, uint32_t key) {
+  if (st.all) return true;
+  const uint32_t k = key & st.mask;
+  return k > st.prefix || (k == st.prefix && st.eq_all);
+}
+
+// Bitmap words and counts of the pooled heads' rows (overwriting their per-row selection), and
+// the number of boundary-class candidates in each chunk of kEgRowChunk pool rows.
+__global__ __launch_bounds__(256) void eg_mark_kernel(const float* __restrict__ S,
+                                                      const int32_t* __restrict__ qstart, int H,
+                                                      int G, int ngh, int nq, int nkv, int N,
+                                                      int nwords, int nrchunk,
+                                                      const int32_t* __restrict__ members,
+                                                      const EgGroup* __restrict__ groups,
+                                                      uint32_t* __restrict__ bitmap,
+                                                      int32_t* __restrict__ base_counts,
+                                                      int32_t* __restrict__ bnd) {
+  __shared__ int rcnt[kEgRowChunk];
+  __shared__ int sbnd;
+  const int gi = blockIdx.y;
+  const EgGroup st = groups[gi];
+  if (st.m == 0) return;
+  const int prow = st.m * nq, R0 = blockIdx.x * kEgRowChunk;
+  if (R0 >= prow) return;
+  const int nr = min(kEgRowChunk, prow - R0), t = threadIdx.x;
+  if (t < kEgRowChunk) rcnt[t] = 0;
+  if (t == 0) sbnd = 0;
+  __syncthreads();
+  const int b = gi / ngh, g = gi % ngh;
+  int my_bnd = 0;
+  for (int wi = t; wi < nr * nwords; wi += 256) {
+    const int rr = wi / nwords, w = wi - rr * nwords;
+    const int R = R0 + rr, k = R / nq, I = R - k * nq;
+    const int64_t row = ((int64_t)b * H + members[b * H + g * G + k]) * nq + I;
+    const float* srow = S + row * nkv;
+    const int qsize = qstart[I + 1] - qstart[I];
+    uint32_t word = 0;
+    for (int bit = 0; bit < 32; ++bit) {
+      const int J = 32 * w + bit;
+      if (J >= nkv) break;
+      const uint32_t key = sel_key(eg_weight(srow[J], qsize, N, st.m));
+      if (eg_selected(st, key))
+        word |= 1u << bit;
+      else if (!st.all && (key & st.mask) == st.prefix)
+        ++my_bnd;
+    }
+    bitmap[row * nwords + w] = word;
+    if (word) atomicAdd(&rcnt[rr], __popc(word));
+  }
+  if (my_bnd) atomicAdd(&sbnd, my_bnd);
+  __syncthreads();
+  if (t < nr) {
+    const int R = R0 + t, k = R / nq, I = R - k * nq;
+    base_counts[((int64_t)b * H + members[b * H + g * G + k]) * nq + I] = rcnt[t];
+  }
+  if (t == 0) bnd[(int64_t)gi * nrchunk + blockIdx.x] = sbnd;
+}
+
+// When only part of the boundary class is kept: its members in pool index order, chunk by chunk
+// (the counts of the earlier chunks give each chunk's starting rank), the first `keep` of them.
+__global__ __launch_bounds__(64) void eg_boundary_kernel(const float* __restrict__ S,
+                                                         const int32_t* __restrict__ qstart,
+                                                         int H, int G, int ngh, int nq, int nkv,
+                                                         int N, int nwords, int nrchunk,
+                                                         const int32_t* __restrict__ members,
+                                                         const EgGroup* __restrict__ groups,
+                                                         const int32_t* __restrict__ bnd,
+                                                         uint32_t* __restrict__ bitmap,
+                                                         int32_t* __restrict__ base_counts) {
+  const int gi = blockIdx.y, c = blockIdx.x, lane = threadIdx.x;
+  const EgGroup st = groups[gi];
+  if (st.m == 0 || st.all || st.eq_all) return;
+  const int prow = st.m * nq, R0 = c * kEgRowChunk;
+  if (R0 >= prow) return;
+  const int32_t* gb = bnd + (int64_t)gi * nrchunk;
+  if (gb[c] == 0) return;
+  int before = 0;
+  for (int i = lane; i < c; i += 64) before += gb[i];
+  before = wave_sum_i32(before);
+  if ((uint32_t)before >= st.keep) return;
+  const int b = gi / ngh, g = gi % ngh;
+  const int j0 = R0 * nkv, n = min(kEgRowChunk, prow - R0) * nkv;
+  uint32_t taken = (uint32_t)before;
+  for (int base = 0; base < n && taken < st.keep; base += 64) {
+    const int jj = base + lane;
+    bool eq = false;
+    int64_t row = 0;
+    int J = 0;
+    if (jj < n) {
+      const float v =
+          eg_candidate(S, qstart, members, b, g, H, G, nq, nkv, N, st.m, j0 + jj, row, J);
+      eq = (sel_key(v) & st.mask) == st.prefix;
+    }
+    const unsigned long long bal = __ballot(eq);
+    const uint32_t rank = taken + __popcll(bal & ((1ull << lane) - 1ull));
+    if (eq && rank < st.keep) {
+      atomicOr(&bitmap[row * nwords + J / 32], 1u << (J % 32));
+      atomicAdd(&base_counts[row], 1);
+    }
+    taken += __popcll(bal);
+  }
+}
+
 }  // namespace
+
+// ROW-pool marks of every row (bitmap and counts), except the rows of heads flagged in
+// skip_head (nullable).
+static hipError_t mark_rows(const bsa_plan& p, const float* S, unsigned long long target,
+                            bool all, const SelectWs& L, uint32_t* bitmap, int32_t* base_counts,
+                            const int32_t* skip_head, hipStream_t s) {
+  const int64_t rows = (int64_t)p.prob.B * p.prob.H * p.nq;
+  const unsigned wgrid = (unsigned)((rows + 3) / 4);
+  if (p.nkv <= 1024)
+    mark_row_wave_kernel<16><<<wgrid, 256, 0, s>>>(S, rows, p.nkv, L.nwords, target, all, bitmap,
+                                                   base_counts, p.nq, skip_head);
+  else if (p.nkv <= kWaveRowMax)
+    mark_row_wave_kernel<32><<<wgrid, 256, 0, s>>>(S, rows, p.nkv, L.nwords, target, all, bitmap,
+                                                   base_counts, p.nq, skip_head);
+  else
+    mark_row_kernel<<<(unsigned)rows, 256, 0, s>>>(S, p.nkv, L.nwords, target, all, bitmap,
+                                                   base_counts, p.nq, skip_head);
+  return hipGetLastError();
+}
+
+// row_ptr from the final counts, then the column lists from the bitmap.
+static hipError_t scan_emit(const bsa_plan& p, const SelectWs& L, const uint32_t* bitmap,
+                            const int32_t* base_counts, const int32_t* head_k_ws, bool use_min_k,
+                            int32_t* row_ptr, int32_t* col_idx, int32_t* counts, hipStream_t s) {
+  const int64_t rows = (int64_t)p.prob.B * p.prob.H * p.nq;
+  scan_kernel<<<1, 1024, 0, s>>>(base_counts, head_k_ws, use_min_k, rows, p.nq, row_ptr, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (L.nwords <= 64)
+    emit_wave_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(bitmap, L.nwords, rows, row_ptr,
+                                                                col_idx);
+  else
+    emit_kernel<<<(unsigned)rows, 256, 0, s>>>(bitmap, L.nwords, row_ptr, col_idx);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_params& prm,
                          int32_t* row_ptr, int32_t* col_idx, int32_t* counts, int32_t* head_k,
@@ -588,19 +1000,14 @@ hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_par
 
   const bool wave_rows = p.nkv <= kWaveRowMax;
   const unsigned wgrid = (unsigned)((rows + 3) / 4);
-  if (prm.pool == BSA_POOL_ROW && p.nkv <= 1024)
-    mark_row_wave_kernel<16><<<wgrid, 256, 0, s>>>(S, rows, p.nkv, L.nwords, target, all, bitmap,
-                                                   base_counts);
-  else if (prm.pool == BSA_POOL_ROW && wave_rows)
-    mark_row_wave_kernel<32><<<wgrid, 256, 0, s>>>(S, rows, p.nkv, L.nwords, target, all, bitmap,
-                                                   base_counts);
-  else if (prm.pool == BSA_POOL_ROW)
-    mark_row_kernel<<<(unsigned)rows, 256, 0, s>>>(S, p.nkv, L.nwords, target, all, bitmap,
-                                                   base_counts);
-  else
+  hipError_t e;
+  if (prm.pool == BSA_POOL_ROW) {
+    e = mark_rows(p, S, target, all, L, bitmap, base_counts, nullptr, s);
+  } else {
     mark_head_kernel<<<BH, 1024, 0, s>>>(S, p.nq, p.nkv, L.nwords, target, all, bitmap,
                                          base_counts);
-  hipError_t e = hipGetLastError();
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   const bool use_min_k = prm.min_k_mode != BSA_MINK_NONE;
   if (use_min_k || head_k) {
@@ -621,12 +1028,54 @@ hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_par
                                                 head_k_ws, bitmap);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  scan_kernel<<<1, 1024, 0, s>>>(base_counts, head_k_ws, use_min_k, rows, p.nq, row_ptr, counts);
+  return scan_emit(p, L, bitmap, base_counts, head_k_ws, use_min_k, row_ptr, col_idx, counts, s);
+}
+
+hipError_t launch_select_eg(const bsa_plan& p, const float* S, const bsa_eg_params& prm,
+                            int32_t* row_ptr, int32_t* col_idx, int32_t* counts,
+                            float* head_entropy, int32_t* head_pooled, void* ws, hipStream_t s) {
+  const SelectWs L = select_ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.bitmap);
+  int32_t* base_counts = reinterpret_cast<int32_t*>(base + L.base_counts);
+  int32_t* route = reinterpret_cast<int32_t*>(base + L.eg_route);
+  int32_t* members = reinterpret_cast<int32_t*>(base + L.eg_members);
+  EgGroup* groups = reinterpret_cast<EgGroup*>(base + L.eg_groups);
+  EgHist* hist = reinterpret_cast<EgHist*>(base + L.eg_hist);
+  int32_t* bnd = reinterpret_cast<int32_t*>(base + L.eg_bnd);
+  const int B = p.prob.B, H = p.prob.H, N = p.prob.N, nq = p.nq, nkv = p.nkv;
+  const int G = std::min(std::max(prm.group_size, 1), H), ngh = (H + G - 1) / G;
+  const int ngroups = B * ngh;
+  const int64_t rows = (int64_t)B * H * nq;
+  if (rows == 0) return hipSuccess;
+  const bool all = prm.p >= 1.0;
+  const unsigned long long target = all ? 0ull : (unsigned long long)ceil(prm.p * kFix);
+
+  eg_row_entropy_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(
+      S, rows, nkv, reinterpret_cast<double*>(base + L.eg_rowent));
+  eg_head_entropy_kernel<<<B * H, 64, 0, s>>>(reinterpret_cast<const double*>(base + L.eg_rowent),
+                                              p.qstart, nq, nkv, N, prm.theta, route,
+                                              head_entropy, head_pooled);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = mark_rows(p, S, target, all, L, bitmap, base_counts, route, s);
+  if (e != hipSuccess) return e;
+  eg_setup_kernel<<<ngroups, 64, 0, s>>>(route, H, G, ngh, all ? 1 : 0, members, groups, hist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (L.nwords <= 64)
-    emit_wave_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(bitmap, L.nwords, rows, row_ptr,
-                                                                col_idx);
-  else
-    emit_kernel<<<(unsigned)rows, 256, 0, s>>>(bitmap, L.nwords, row_ptr, col_idx);
-  return hipGetLastError();
+  // grids sized for a pool of all G heads; workgroups past a group's pool return at once
+  const unsigned nchunk = (unsigned)(((int64_t)G * nq * nkv + kEgHistChunk - 1) / kEgHistChunk);
+  for (int pass = 0; pass < 4; ++pass) {
+    eg_hist_kernel<<<dim3(nchunk, ngroups), 256, 0, s>>>(S, p.qstart, H, G, ngh, nq, nkv, N, pass,
+                                                         members, groups, hist);
+    eg_pick_kernel<<<ngroups, 64, 0, s>>>(pass, target, groups, hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const unsigned nrc = (unsigned)(((int64_t)G * nq + kEgRowChunk - 1) / kEgRowChunk);
+  eg_mark_kernel<<<dim3(nrc, ngroups), 256, 0, s>>>(S, p.qstart, H, G, ngh, nq, nkv, N, L.nwords,
+                                                    L.eg_nrchunk, members, groups, bitmap,
+                                                    base_counts, bnd);
+  eg_boundary_kernel<<<dim3(nrc, ngroups), 64, 0, s>>>(S, p.qstart, H, G, ngh, nq, nkv, N,
+                                                       L.nwords, L.eg_nrchunk, members, groups,
+                                                       bnd, bitmap, base_counts);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return scan_emit(p, L, bitmap, base_counts, nullptr, false, row_ptr, col_idx, counts, s);
 }

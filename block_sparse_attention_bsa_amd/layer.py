@@ -1,8 +1,8 @@
 """One block-sparse attention layer call, built from the C-ABI entry points.
 
 Allocates the block-level buffers, CSR and workspaces with PyTorch on the current device and
-calls bsa_pool / bsa_score / bsa_select / bsa_attn_fwd (and bsa_calibrate_mass, bsa_attn_bwd) in
-order on one stream. No arithmetic happens here.
+calls bsa_pool / bsa_score / bsa_select (or bsa_select_eg) / bsa_attn_fwd (and bsa_calibrate_mass,
+bsa_attn_bwd) in order on one stream. No arithmetic happens here.
 """
 from __future__ import annotations
 
@@ -12,7 +12,7 @@ import torch
 
 from . import (BSA_MINK_NONE, BSA_NORM_HEAD, BSA_NORM_ROW, BSA_POOL_HEAD, BSA_POOL_ROW, Plan,
                bsa_attn_bwd, bsa_attn_fwd, bsa_calibrate_mass, bsa_calibrate_mass_fwd, bsa_pool,
-               bsa_score, bsa_select)
+               bsa_score, bsa_select, bsa_select_eg)
 
 
 class BlockSparseAttention:
@@ -32,6 +32,8 @@ class BlockSparseAttention:
         self.col_idx = torch.empty(self.col_cap, **i32)
         self.counts = torch.empty(self.rows, **i32)
         self.head_k = torch.empty(B * H, **i32)
+        self.head_entropy = torch.empty(B * H, **f32)
+        self.head_pooled = torch.empty(B * H, **i32)
         self.ws_select = torch.empty(max(p.ws_select, 1), dtype=torch.uint8, device=self.device)
         self._ws_calib = None
         self._ws_bwd = None
@@ -68,6 +70,14 @@ class BlockSparseAttention:
         bsa_select(self.plan, self.S if scores is None else scores, p, pool, min_k_mode, fixed_k,
                    self.row_ptr, self.col_idx, self.col_cap, self.counts, self.head_k,
                    self.ws_select, self.plan.ws_select, stream)
+        return self.row_ptr, self.col_idx
+
+    def select_eg(self, p, theta, group_size, stream=None, scores=None):
+        """Entropy-routed selection from the row-normalised scores (score(BSA_NORM_ROW) first);
+        fills head_entropy and head_pooled too."""
+        bsa_select_eg(self.plan, self.S if scores is None else scores, p, theta, group_size,
+                      self.row_ptr, self.col_idx, self.col_cap, self.counts, self.head_entropy,
+                      self.head_pooled, self.ws_select, self.plan.ws_select, stream)
         return self.row_ptr, self.col_idx
 
     def attention(self, q, k, v, row_ptr=None, col_idx=None, out=None, lse=None, stream=None,

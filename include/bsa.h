@@ -19,6 +19,9 @@
  *                         or ranked over a head-global pool of (q-block, kv-block) pairs (VMoBA
  *                         Eq. 3). The result is an int32 CSR list that callers may freeze and
  *                         reuse across denoising steps (LoSA abstract).
+ *      bsa_select_eg      the same rule with the competition domain chosen per head by the
+ *                         entropy of its scores: a pool shared by a group of low-entropy heads,
+ *                         per-row selection for the rest (EG-Sparse abstract).
  *   4. bsa_attn_fwd       online-softmax attention of every query over the tokens of its selected
  *                         kv blocks only (VMoBA review, Figure 2 caption), and bsa_attn_bwd, its
  *                         gradient for training through the sparse attention (VMoBA review,
@@ -106,6 +109,16 @@ typedef struct {
   int32_t fixed_k;       /* BSA_MINK_FIXED: the per-head minimum (>= 0)                         */
 } bsa_select_params;
 
+/* Entropy-routed competition domains (EG-Sparse abstract, readsearch page "Competition Domains
+ * Matter: Selective Head Globalization for Training-Free Sparse Attention in Video Diffusion
+ * Transformers"): heads whose row-normalised scores have low entropy compete in a pool shared
+ * by their group of heads; the others keep per-row selection. */
+typedef struct {
+  double p;              /* threshold in (0, 1] for the per-row selections and for every pool  */
+  double theta;          /* a head is pooled when its normalised entropy is < theta (not NaN)  */
+  int32_t group_size;    /* heads per group: runs of consecutive heads (>= 1; >= H is one group) */
+} bsa_eg_params;
+
 typedef struct bsa_plan bsa_plan;
 
 /* Host only, no device call: fill perm[N] (block-major token order: block j's tokens are
@@ -173,6 +186,22 @@ int bsa_calibrate_mass_fwd(const bsa_plan* plan, const void* Q, const void* K, c
 int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* params,
                int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
                int32_t* head_k, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 3, entropy-routed (EG-Sparse abstract). S: row-normalised scores from bsa_score
+ * (BSA_NORM_ROW). Per head, E_h = sum_I |I| H_I / (N ln nkv) with H_I = -sum_J S ln S over row
+ * (h, I) (fp64; 0 when nkv = 1); the head is pooled when E_h < theta. Heads are grouped in runs
+ * of group_size; within a group the pooled heads' (h, I, J) candidates, weighted
+ * S[h, I, J] * |I| / (N m) for m pooled heads (the pool sums to 1), are ranked by (weight desc,
+ * index asc over (pooled head in head order, I, J)) and the shortest prefix reaching p is kept,
+ * with the exact 2^-56 fixed-point sums of bsa_select; a pooled query block may keep no block.
+ * Heads not pooled select per row as bsa_select with BSA_POOL_ROW. Outputs as bsa_select, plus
+ * head_entropy (nullable, fp32 [B*H], E_h) and head_pooled (nullable, int32 [B*H], 0 or 1).
+ * ws must hold the ws_select bytes of bsa_plan_info. BSA_EUNSUPPORTED when H * nq * nkv
+ * exceeds 2^31 - 1 (the pool index is 32-bit). */
+int bsa_select_eg(const bsa_plan* plan, const float* S, const bsa_eg_params* params,
+                  int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
+                  float* head_entropy, int32_t* head_pooled, void* ws, size_t ws_bytes,
+                  void* stream);
 
 /* Step 4. For every query i of block I: O_i = sum_j softmax_j(sigma_h q_i . k_j) v_j over the
  * tokens j of the kv blocks listed in CSR row I, and lse_i = log sum_j exp(sigma_h q_i . k_j).

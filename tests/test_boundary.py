@@ -91,6 +91,9 @@ def test_null_arguments_rejected(L):
     prm = bsa.SelectParams(0.9, 0, 0, 0)
     assert L.bsa_select(P, None, ctypes.byref(prm), None, None, 0, None, None, None, 0,
                         None) == bsa.BSA_EINVAL
+    eg = bsa.EgParams(0.9, 0.5, 2)
+    assert L.bsa_select_eg(P, None, ctypes.byref(eg), None, None, 0, None, None, None, None, 0,
+                           None) == bsa.BSA_EINVAL
     assert L.bsa_attn_fwd(P, None, None, None, None, None, None, None, None, 0,
                           None) == bsa.BSA_EINVAL
     assert L.bsa_attn_bwd(P, *([None] * 12), 0, None) == bsa.BSA_EINVAL
