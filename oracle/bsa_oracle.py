@@ -42,7 +42,11 @@ reasoning in the design notes):
     heads with weight S[h, I, J] * |I| / (N * m) (m pooled heads, so the pool sums to 1) and
     keeps the shortest prefix, in (weight desc, pool index asc) order, reaching p; pool index
     runs over (pooled head in head order, I, J). High-entropy heads select per row with the
-    same p.
+    same p;
+  * [VMoBA] "Local + TopK" (the training-free selection the referee report's major comment 2
+    and the free-parameter list name, with k = 2, 6 or 18): a query block keeps its local kv
+    blocks, those holding at least one of its own tokens, plus the k highest-scoring other kv
+    blocks (score desc, index asc); fewer when fewer remain.
 """
 from __future__ import annotations
 
@@ -54,7 +58,8 @@ import numpy as np
 __all__ = [
     "partition", "block_sizes", "pool", "block_logits", "score_row", "score_head",
     "exact_mass", "exact_mass_row", "select_topp", "select_row", "head_min_k",
-    "select_hybrid", "select_head", "head_entropy", "select_group", "select_eg", "to_csr",
+    "select_hybrid", "select_head", "head_entropy", "select_group", "select_eg",
+    "local_blocks", "select_local_topk", "to_csr",
     "csr_rows", "attention_rows", "attention_fwd",
     "attention_bwd", "row_backward", "density",
 ]
@@ -304,6 +309,34 @@ def select_eg(S: np.ndarray, p: float, qsizes, theta: float,
     ent = head_entropy(S, qsizes)
     pooled = ent < theta
     return select_group(S, p, qsizes, pooled, group_size), ent, pooled
+
+
+def local_blocks(qblocks, kvblocks) -> List[np.ndarray]:
+    """[VMoBA] the local kv blocks of each query block: those sharing at least one token with
+    it, ascending."""
+    kv_sets = [set(np.asarray(b).tolist()) for b in kvblocks]
+    out = []
+    for qb in qblocks:
+        toks = set(np.asarray(qb).tolist())
+        out.append(np.asarray([j for j, ks in enumerate(kv_sets) if toks & ks], np.int64))
+    return out
+
+
+def select_local_topk(S: np.ndarray, k: int, local: Sequence[np.ndarray]) -> List[np.ndarray]:
+    """[VMoBA] Local + TopK per (b, h, I) row of S [B, H, nq, nkv]: the local blocks of I plus
+    the k highest-scoring others in (score desc, index asc) order; rows in (b*H + h)*nq + I
+    order, ascending."""
+    B, H, nq, nkv = S.shape
+    rows = []
+    for b in range(B):
+        for h in range(H):
+            for i in range(nq):
+                loc = np.asarray(local[i], np.int64)
+                others = np.setdiff1d(np.arange(nkv), loc)
+                s = np.asarray(S[b, h, i], np.float64)[others]
+                order = np.lexsort((others, -s))
+                rows.append(np.sort(np.concatenate([loc, others[order[:k]]])))
+    return rows
 
 
 def to_csr(rows: Sequence[np.ndarray]) -> Tuple[np.ndarray, np.ndarray]:
