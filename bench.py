@@ -100,6 +100,34 @@ def entropy_routed(w, L, q, k, v, out, tm, group_size=4, calls=5):
             "attn_ms": round(attn_ms, 4), "attn_tflops": f / (attn_ms * 1e-3) / 1e12}
 
 
+def local_topk(w, L, q, k, v, out, tm, ks=(2, 6, 18), calls=5):
+    """VMoBA's training-free Local + TopK selection (BSA_POOL_LOCAL_TOPK) for k = 2, 6, 18,
+    timed outside the step: the selection's time, the density and the output-only attention
+    time on its block sets."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_bsa_amd import BSA_POOL_LOCAL_TOPK
+    L.pool(q, k)
+    L.score(0)
+    qs, ksz = np.diff(L.plan.blocks(0)[1]), np.diff(L.plan.blocks(1)[1])
+    res = {}
+    for kk in ks:
+        for _ in range(calls):
+            with tm(f"select_lt{kk}"):
+                L.select(w.p, pool=BSA_POOL_LOCAL_TOPK, fixed_k=kk)
+            with tm(f"attn_lt{kk}"):
+                L.attention(q, k, v, out=out, with_lse=False)
+        torch.cuda.synchronize()
+        rp, ci = L.csr_host()
+        f = attention_flops(csr_rows(rp, ci), qs, ksz, w.d)
+        attn_ms = tm.mean_ms(f"attn_lt{kk}")
+        res[str(kk)] = {"select_ms": round(tm.mean_ms(f"select_lt{kk}"), 4),
+                        "density": round(f / (4.0 * w.B * w.H * w.N * w.N * w.d), 4),
+                        "attn_ms": round(attn_ms, 4),
+                        "attn_tflops": f / (attn_ms * 1e-3) / 1e12}
+    return res
+
+
 def csr_rows(row_ptr, col_idx):
     """The CSR's rows as a list of index arrays (for the FLOP count of the selected blocks)."""
     return [col_idx[row_ptr[r]:row_ptr[r + 1]] for r in range(len(row_ptr) - 1)]
@@ -402,6 +430,7 @@ def main():
         res["calibrate_then_reuse"] = retained_mass(w, x, layers[0], dev)
     if w.mode in ("row", "hybrid") and w.dtype == "bf16":
         res["entropy_routed"] = entropy_routed(w, layers[0], q, k, v, out, tm)
+        res["local_topk"] = local_topk(w, layers[0], q, k, v, out, tm)
     if not w.backward:
         # the same attention call with the LSE requested as well (the training kernel), untimed
         # in the step

@@ -25,7 +25,7 @@ BSA_OK, BSA_EINVAL, BSA_EUNSUPPORTED, BSA_ECAPACITY, BSA_EHIP = 0, -1, -2, -3, -
 BSA_PART_FLAT, BSA_PART_TILE = 0, 1
 BSA_BF16, BSA_FP32 = 0, 1
 BSA_NORM_ROW, BSA_NORM_HEAD = 0, 1
-BSA_POOL_ROW, BSA_POOL_HEAD = 0, 1
+BSA_POOL_ROW, BSA_POOL_HEAD, BSA_POOL_LOCAL_TOPK = 0, 1, 2
 BSA_MINK_NONE, BSA_MINK_FIXED, BSA_MINK_WEIGHTED_MEAN = 0, 1, 2
 
 EXPORTED = ("bsa_partition_build", "bsa_plan_create", "bsa_plan_destroy", "bsa_plan_info",

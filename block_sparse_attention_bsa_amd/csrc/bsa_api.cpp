@@ -108,7 +108,8 @@ int upload(const std::vector<T>& h, T** d) {
 void free_plan(bsa_plan* p) {
   if (!p) return;
   for (void* ptr : {(void*)p->qperm, (void*)p->qstart, (void*)p->kvperm, (void*)p->kvstart,
-                    (void*)p->items, (void*)p->qitem0, (void*)p->kvitems, (void*)p->scale})
+                    (void*)p->items, (void*)p->qitem0, (void*)p->kvitems, (void*)p->scale,
+                    (void*)p->local_ptr, (void*)p->local_idx})
     if (ptr) (void)hipFree(ptr);
   delete p;
 }
@@ -253,6 +254,25 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
   }
   p->n_kvitems = (int)(p->h_kvitems.size() / 2);
   p->n_items = (int)(p->h_items.size() / 2);
+  {  // local kv blocks of every query block, from each token's kv block
+    std::vector<int32_t> kv_of(pr.N);
+    for (int j = 0; j < p->nkv; ++j)
+      for (int t = p->h_kvstart[j]; t < p->h_kvstart[j + 1]; ++t) kv_of[p->h_kvperm[t]] = j;
+    p->h_local_ptr.assign(1, 0);
+    std::vector<int32_t> seen(p->nkv, -1);
+    for (int i = 0; i < p->nq; ++i) {
+      const size_t first = p->h_local_idx.size();
+      for (int t = p->h_qstart[i]; t < p->h_qstart[i + 1]; ++t) {
+        const int j = kv_of[p->h_qperm[t]];
+        if (seen[j] != i) {
+          seen[j] = i;
+          p->h_local_idx.push_back(j);
+        }
+      }
+      std::sort(p->h_local_idx.begin() + first, p->h_local_idx.end());
+      p->h_local_ptr.push_back((int32_t)p->h_local_idx.size());
+    }
+  }
   p->h_scale.resize(pr.H);
   for (int h = 0; h < pr.H; ++h)
     p->h_scale[h] = head_scale ? head_scale[h] : (float)(1.0 / std::sqrt((double)pr.d));
@@ -269,8 +289,8 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
   if (upload(qperm_pad, &p->qperm) || upload(p->h_qstart, &p->qstart) ||
       upload(kvperm_pad, &p->kvperm) || upload(p->h_kvstart, &p->kvstart) ||
       upload(p->h_items, &p->items) || upload(p->h_qitem0, &p->qitem0) ||
-      upload(p->h_kvitems, &p->kvitems) ||
-      upload(p->h_scale, &p->scale)) {
+      upload(p->h_kvitems, &p->kvitems) || upload(p->h_scale, &p->scale) ||
+      upload(p->h_local_ptr, &p->local_ptr) || upload(p->h_local_idx, &p->local_idx)) {
     free_plan(p);
     return fail(BSA_EHIP, "bsa_plan_create: device allocation or upload failed");
   }
@@ -362,14 +382,19 @@ int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* pr
                int32_t* head_k, void* ws, size_t ws_bytes, void* stream) {
   if (!plan || !S || !prm || !row_ptr || !col_idx)
     return fail(BSA_EINVAL, "bsa_select: NULL argument");
-  if (!(prm->p > 0.0 && prm->p <= 1.0))
-    return fail(BSA_EINVAL, "bsa_select: p must lie in (0, 1]");
-  if (prm->pool != BSA_POOL_ROW && prm->pool != BSA_POOL_HEAD)
+  if (prm->pool != BSA_POOL_ROW && prm->pool != BSA_POOL_HEAD &&
+      prm->pool != BSA_POOL_LOCAL_TOPK)
     return fail(BSA_EINVAL, "bsa_select: unknown pool %d", prm->pool);
+  if (prm->pool != BSA_POOL_LOCAL_TOPK && !(prm->p > 0.0 && prm->p <= 1.0))
+    return fail(BSA_EINVAL, "bsa_select: p must lie in (0, 1]");
+  if (prm->pool == BSA_POOL_LOCAL_TOPK && (prm->fixed_k < 0 || prm->min_k_mode != BSA_MINK_NONE))
+    return fail(BSA_EINVAL, "bsa_select: LOCAL_TOPK takes fixed_k >= 0 and no minimum count");
   if (prm->min_k_mode < BSA_MINK_NONE || prm->min_k_mode > BSA_MINK_WEIGHTED_MEAN)
     return fail(BSA_EINVAL, "bsa_select: unknown min_k_mode %d", prm->min_k_mode);
   if (prm->min_k_mode == BSA_MINK_FIXED && prm->fixed_k < 0)
     return fail(BSA_EINVAL, "bsa_select: fixed_k must be >= 0");
+  if (prm->pool == BSA_POOL_LOCAL_TOPK && plan->nkv > 2048)
+    return fail(BSA_EUNSUPPORTED, "bsa_select: LOCAL_TOPK supports up to 2048 kv blocks");
   if (prm->pool == BSA_POOL_HEAD && prm->min_k_mode != BSA_MINK_NONE)
     return fail(BSA_EUNSUPPORTED, "bsa_select: a minimum count applies to the ROW pool only");
   if (plan->nkv > kMaxSelectBlocks)

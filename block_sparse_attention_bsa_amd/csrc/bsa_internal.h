@@ -33,6 +33,11 @@ struct bsa_plan {
   int n_kvitems = 0;
   float* scale = nullptr;     // sigma_h, [H]
   std::vector<float> h_scale;
+  // local kv blocks of each query block (those holding one of its tokens), ascending:
+  // local_idx[local_ptr[I] .. local_ptr[I + 1])
+  std::vector<int32_t> h_local_ptr, h_local_idx;
+  int32_t* local_ptr = nullptr;
+  int32_t* local_idx = nullptr;
 };
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }

@@ -40,6 +40,12 @@ __device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, 
   return ((unsigned long long)hi << 32) | lo;
 }
 
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
+  uint32_t lo = __shfl_xor((uint32_t)v, mask, 64);
+  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), mask, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v) {
   const int lane = threadIdx.x & 63;

@@ -554,6 +554,59 @@ __global__ __launch_bounds__(256) void topup_wave_kernel(const float* __restrict
   write_row_bits(sel, nwords, bitmap + r * nwords);
 }
 
+// Local + TopK (VMoBA review: the training-free selection, referee report major comment 2): row
+// (b, h, I) keeps the local kv blocks of I (those holding one of its tokens, from the plan) and
+// then, k times, the best remaining block by (score desc, index asc): one wavefront per row, a
+// 64-bit wavefront max of (score bits, ~index) per round. Rows of at most 64 * kVpl blocks.
+template <int kVpl>
+__global__ __launch_bounds__(256) void mark_local_topk_kernel(
+    const float* __restrict__ S, int64_t rows, int nq, int nkv, int nwords, int k,
+    const int32_t* __restrict__ local_ptr, const int32_t* __restrict__ local_idx,
+    uint32_t* __restrict__ bitmap, int32_t* __restrict__ base_counts) {
+  static_assert(kVpl <= 32, "one mask bit per value");
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int I = (int)(r % nq);
+  const float* row = S + r * nkv;
+  uint32_t key[kVpl];
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) key[i] = lane + 64 * i < nkv ? sel_key(row[lane + 64 * i]) : 0u;
+  uint32_t lmask = 0u, pmask = 0u;  // bit i: value i of this lane is local / picked
+  for (int e = local_ptr[I]; e < local_ptr[I + 1]; ++e) {
+    const int J = local_idx[e];
+    if ((J & 63) == lane) lmask |= 1u << (J >> 6);
+  }
+  for (int round = 0; round < k; ++round) {
+    unsigned long long best = 0ull;  // (key << 32) | ~J; 0 = nothing left in this lane
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i) {
+      const int J = lane + 64 * i;
+      if (J < nkv && !(((lmask | pmask) >> i) & 1u)) {
+        const unsigned long long c = ((unsigned long long)key[i] << 32) | (uint32_t)~J;
+        best = c > best ? c : best;
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const unsigned long long o = shfl_xor_u64(best, d);
+      best = o > best ? o : best;
+    }
+    if (best == 0ull) break;  // every block is taken
+    const int J = (int)~(uint32_t)best;
+    if ((J & 63) == lane) pmask |= 1u << (J >> 6);
+  }
+  bool sel[kVpl];
+  int count = 0;
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) {
+    sel[i] = lane + 64 * i < nkv && (((lmask | pmask) >> i) & 1u);
+    count += __popcll(__ballot(sel[i]));
+  }
+  write_row_bits(sel, nwords, bitmap + r * nwords);
+  if (lane == 0) base_counts[r] = count;
+}
+
 // CSR columns of one row from its bitmap (at most 64 words), one wavefront per row: each 64-bit
 // word pair is a mask over 64 consecutive candidates; every set lane writes its column at the
 // running position plus its rank, so the stores of a wavefront are consecutive.
@@ -1003,6 +1056,16 @@ hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_par
   hipError_t e;
   if (prm.pool == BSA_POOL_ROW) {
     e = mark_rows(p, S, target, all, L, bitmap, base_counts, nullptr, s);
+  } else if (prm.pool == BSA_POOL_LOCAL_TOPK) {
+    if (p.nkv <= 1024)
+      mark_local_topk_kernel<16><<<wgrid, 256, 0, s>>>(S, rows, p.nq, p.nkv, L.nwords,
+                                                       prm.fixed_k, p.local_ptr, p.local_idx,
+                                                       bitmap, base_counts);
+    else
+      mark_local_topk_kernel<32><<<wgrid, 256, 0, s>>>(S, rows, p.nq, p.nkv, L.nwords,
+                                                       prm.fixed_k, p.local_ptr, p.local_idx,
+                                                       bitmap, base_counts);
+    e = hipGetLastError();
   } else {
     mark_head_kernel<<<BH, 1024, 0, s>>>(S, p.nq, p.nkv, L.nwords, target, all, bitmap,
                                          base_counts);

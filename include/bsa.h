@@ -73,6 +73,7 @@ extern "C" {
 #define BSA_NORM_HEAD 1        /* |I|-weighted softmax over all (I, J) pairs of a head            */
 #define BSA_POOL_ROW 0         /* select per (head, query block)                                  */
 #define BSA_POOL_HEAD 1        /* select over all (I, J) pairs of a head                          */
+#define BSA_POOL_LOCAL_TOPK 2  /* local blocks of I plus the fixed_k best others (VMoBA review)   */
 
 /* per-head minimum count after top-p (bsa_select) */
 #define BSA_MINK_NONE 0
@@ -104,9 +105,9 @@ typedef struct {
                             Selection keeps the shortest prefix of the (score descending, index
                             ascending) order whose cumulative sum is >= p; p >= 1, or a sum
                             that never reaches p, keeps every block (pair).                     */
-  int32_t pool;          /* BSA_POOL_ROW or BSA_POOL_HEAD                                       */
+  int32_t pool;          /* BSA_POOL_ROW, BSA_POOL_HEAD or BSA_POOL_LOCAL_TOPK (p unused)       */
   int32_t min_k_mode;    /* BSA_MINK_*; ROW pool only                                           */
-  int32_t fixed_k;       /* BSA_MINK_FIXED: the per-head minimum (>= 0)                         */
+  int32_t fixed_k;       /* BSA_MINK_FIXED: the per-head minimum (>= 0); LOCAL_TOPK: k (>= 0)  */
 } bsa_select_params;
 
 /* Entropy-routed competition domains (EG-Sparse abstract, readsearch page "Competition Domains
@@ -182,7 +183,11 @@ int bsa_calibrate_mass_fwd(const bsa_plan* plan, const void* Q, const void* K, c
  * [B*H*nq]) receives each row's final count; head_k (nullable, [B*H]) receives the per-head
  * minimum used (0 when min_k_mode is NONE). ws must hold the ws_select bytes of bsa_plan_info.
  * With BSA_POOL_HEAD a query block may receive no block at all (an empty row, as the VMoBA
- * referee report points out); attention then returns O = 0 and LSE = -inf for its queries. */
+ * referee report points out); attention then returns O = 0 and LSE = -inf for its queries.
+ * BSA_POOL_LOCAL_TOPK is VMoBA's training-free "Local + TopK" (VMoBA review, referee report
+ * major comment 2; free parameters k = 2, 6, 18): query block I keeps its local kv blocks (those
+ * holding at least one of its tokens) plus the fixed_k highest-scoring other blocks (score desc,
+ * index asc), fewer when fewer remain; p is not used and min_k_mode must be NONE. */
 int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* params,
                int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
                int32_t* head_k, void* ws, size_t ws_bytes, void* stream);
