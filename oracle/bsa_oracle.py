@@ -46,7 +46,10 @@ reasoning in the design notes):
   * [VMoBA] "Local + TopK" (the training-free selection the referee report's major comment 2
     and the free-parameter list name, with k = 2, 6 or 18): a query block keeps its local kv
     blocks, those holding at least one of its own tokens, plus the k highest-scoring other kv
-    blocks (score desc, index asc); fewer when fewer remain.
+    blocks (score desc, index asc); fewer when fewer remain;
+  * [VMoBA] per-token Local + TopK (queries score the block means token by token, "What carries
+    the argument"): query token i keeps the kv block holding i plus the k others with the highest
+    gate sigma_h q_i . kbar_J (gate desc, index asc), and attends over those blocks' tokens.
 """
 from __future__ import annotations
 
@@ -59,7 +62,8 @@ __all__ = [
     "partition", "block_sizes", "pool", "block_logits", "score_row", "score_head",
     "exact_mass", "exact_mass_row", "select_topp", "select_row", "head_min_k",
     "select_hybrid", "select_head", "head_entropy", "select_group", "select_eg",
-    "local_blocks", "select_local_topk", "to_csr",
+    "local_blocks", "select_local_topk", "token_gates", "select_tokens", "attention_tokens",
+    "to_csr",
     "csr_rows", "attention_rows", "attention_fwd",
     "attention_bwd", "row_backward", "density",
 ]
@@ -337,6 +341,54 @@ def select_local_topk(S: np.ndarray, k: int, local: Sequence[np.ndarray]) -> Lis
                 order = np.lexsort((others, -s))
                 rows.append(np.sort(np.concatenate([loc, others[order[:k]]])))
     return rows
+
+
+def token_gates(Q: np.ndarray, Kbar: np.ndarray, head_scale: np.ndarray) -> np.ndarray:
+    """[VMoBA] per-token gates G[b, h, i, J] = sigma_h * <q_i, kbar_J> (each query token scores
+    every block mean)."""
+    Q = np.asarray(Q, np.float64)
+    Kbar = np.asarray(Kbar, np.float64)
+    sig = np.asarray(head_scale, np.float64)[None, :, None, None]
+    return sig * np.einsum("bhnd,bhjd->bhnj", Q, Kbar)
+
+
+def select_tokens(G: np.ndarray, k: int, kvblocks) -> np.ndarray:
+    """[VMoBA] per-token Local + TopK: sel[b, h, i] = the kv block holding token i plus the k
+    highest-gate others (gate desc, index asc), ascending, as an int array [B, H, N, 1 + k'],
+    k' = min(k, nkv - 1)."""
+    B, H, N, nkv = G.shape
+    own = np.empty(N, np.int64)
+    for j, blk in enumerate(kvblocks):
+        own[np.asarray(blk)] = j
+    kk = min(int(k), nkv - 1)
+    out = np.empty((B, H, N, 1 + kk), np.int64)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                others = np.delete(np.arange(nkv), own[i])
+                order = np.lexsort((others, -np.asarray(G[b, h, i], np.float64)[others]))
+                out[b, h, i] = np.sort(np.concatenate([[own[i]], others[order[:kk]]]))
+    return out
+
+
+def attention_tokens(Q, K, V, head_scale, sel: np.ndarray, kvblocks,
+                     tokens: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """O[b, h, i] and LSE[b, h, i] of each query token over the tokens of its own selected blocks
+    sel[b, h, i] (or only the listed (b, h, i); other entries stay NaN)."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    B, H, N, _ = Q.shape
+    O = np.full((B, H, N, V.shape[3]), np.nan)
+    LSE = np.full((B, H, N), np.nan)
+    if tokens is None:
+        tokens = [(b, h, i) for b in range(B) for h in range(H) for i in range(N)]
+    for b, h, i in tokens:
+        keys = _selected_keys(np.asarray(sel[b, h, i]), kvblocks)
+        o, lse = attention_rows(Q[b, h, i:i + 1], K[b, h], V[b, h], float(head_scale[h]), keys)
+        O[b, h, i] = o[0]
+        LSE[b, h, i] = lse[0]
+    return O, LSE
 
 
 def to_csr(rows: Sequence[np.ndarray]) -> Tuple[np.ndarray, np.ndarray]:
