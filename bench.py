@@ -128,6 +128,37 @@ def local_topk(w, L, q, k, v, out, tm, ks=(2, 6, 18), calls=5):
     return res
 
 
+def token_topk(w, L, q, k, v, out, tm, ks=(2, 6, 18), calls=3):
+    """Per-token Local + TopK (bsa_select_tokens + bsa_attn_fwd_tokens) for k = 2, 6, 18, timed
+    outside the step. FLOPs: `token` counts each token's own selected keys (4 d per query-key
+    pair), `executed` the union blocks its query block streams."""
+    import numpy as np
+    import torch
+    L.pool(q, k)
+    qs, ksz = np.diff(L.plan.blocks(0)[1]), np.diff(L.plan.blocks(1)[1])
+    res = {}
+    for kk in ks:
+        for _ in range(calls):
+            with tm(f"select_tok{kk}"):
+                sel = L.select_tokens(q, kk)
+            with tm(f"attn_tok{kk}"):
+                L.attention_tokens(q, k, v, sel, kk, out=out, with_lse=False)
+        torch.cuda.synchronize()
+        keys_per_token = ksz[sel.cpu().numpy()].sum(-1)          # [B, H, N]
+        f_tok = 4.0 * w.d * float(keys_per_token.sum())
+        rp, ci = L.csr_host()
+        f_exec = attention_flops(csr_rows(rp, ci), qs, ksz, w.d)
+        attn_ms = tm.mean_ms(f"attn_tok{kk}")
+        dense = 4.0 * w.B * w.H * w.N * w.N * w.d
+        res[str(kk)] = {"select_ms": round(tm.mean_ms(f"select_tok{kk}"), 4),
+                        "density_token": round(f_tok / dense, 4),
+                        "density_executed": round(f_exec / dense, 4),
+                        "attn_ms": round(attn_ms, 4),
+                        "attn_tflops_token": f_tok / (attn_ms * 1e-3) / 1e12,
+                        "attn_tflops_executed": f_exec / (attn_ms * 1e-3) / 1e12}
+    return res
+
+
 def csr_rows(row_ptr, col_idx):
     """The CSR's rows as a list of index arrays (for the FLOP count of the selected blocks)."""
     return [col_idx[row_ptr[r]:row_ptr[r + 1]] for r in range(len(row_ptr) - 1)]
@@ -431,6 +462,7 @@ def main():
     if w.mode in ("row", "hybrid") and w.dtype == "bf16":
         res["entropy_routed"] = entropy_routed(w, layers[0], q, k, v, out, tm)
         res["local_topk"] = local_topk(w, layers[0], q, k, v, out, tm)
+        res["token_topk"] = token_topk(w, layers[0], q, k, v, out, tm)
     if not w.backward:
         # the same attention call with the LSE requested as well (the training kernel), untimed
         # in the step

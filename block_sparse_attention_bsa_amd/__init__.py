@@ -30,8 +30,9 @@ BSA_MINK_NONE, BSA_MINK_FIXED, BSA_MINK_WEIGHTED_MEAN = 0, 1, 2
 
 EXPORTED = ("bsa_partition_build", "bsa_plan_create", "bsa_plan_destroy", "bsa_plan_info",
             "bsa_plan_blocks", "bsa_pool", "bsa_score", "bsa_calibrate_mass",
-            "bsa_calibrate_mass_fwd", "bsa_select", "bsa_select_eg", "bsa_attn_fwd",
-            "bsa_attn_bwd", "bsa_last_error")
+            "bsa_calibrate_mass_fwd", "bsa_select", "bsa_select_eg", "bsa_tokens_ws",
+            "bsa_select_tokens", "bsa_attn_fwd", "bsa_attn_fwd_tokens", "bsa_attn_bwd",
+            "bsa_last_error")
 
 
 class BsaError(RuntimeError):
@@ -97,6 +98,9 @@ def lib():
         "bsa_calibrate_mass_fwd": [P, P, P, P, P, P, P, P, SZ, P],
         "bsa_select": [P, P, ctypes.POINTER(SelectParams), P, P, I64, P, P, P, SZ, P],
         "bsa_select_eg": [P, P, ctypes.POINTER(EgParams), P, P, I64, P, P, P, P, SZ, P],
+        "bsa_tokens_ws": [P, ctypes.POINTER(SZ)],
+        "bsa_select_tokens": [P, P, P, I32, P, P, P, I64, P, SZ, P],
+        "bsa_attn_fwd_tokens": [P, P, P, P, P, P, P, I32, P, P, P, SZ, P],
         "bsa_attn_fwd": [P, P, P, P, P, P, P, P, P, SZ, P],
         "bsa_attn_bwd": [P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     }
@@ -241,6 +245,26 @@ def bsa_select_eg(plan: Plan, S, p: float, theta: float, group_size: int, row_pt
     _check(lib().bsa_select_eg(plan.handle, _ptr(S), ctypes.byref(prm), _ptr(row_ptr),
                                _ptr(col_idx), int(col_cap), _ptr(counts), _ptr(head_entropy),
                                _ptr(head_pooled), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def bsa_tokens_ws(plan: Plan) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().bsa_tokens_ws(plan.handle, ctypes.byref(n)))
+    return int(n.value)
+
+
+def bsa_select_tokens(plan: Plan, Q, Kbar, k: int, sel, row_ptr, col_idx, col_cap: int, ws,
+                      ws_bytes: int, stream=None):
+    _check(lib().bsa_select_tokens(plan.handle, _ptr(Q), _ptr(Kbar), int(k), _ptr(sel),
+                                   _ptr(row_ptr), _ptr(col_idx), int(col_cap), _ptr(ws), ws_bytes,
+                                   _stream(stream)))
+
+
+def bsa_attn_fwd_tokens(plan: Plan, Q, K, V, row_ptr, col_idx, sel, k: int, O, lse, ws,
+                        ws_bytes: int, stream=None):
+    _check(lib().bsa_attn_fwd_tokens(plan.handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(row_ptr),
+                                     _ptr(col_idx), _ptr(sel), int(k), _ptr(O), _ptr(lse),
+                                     _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def bsa_attn_fwd(plan: Plan, Q, K, V, row_ptr, col_idx, O, lse, ws, ws_bytes: int, stream=None):

@@ -29,6 +29,8 @@
 // 2^32, which is detected from the row sum the softmax needs anyway, so no per-tile max is formed
 // and the O rescale is rare. When no LSE is requested (an inference call) the fp32 row sum is not
 // formed: the sum of the bf16-rounded weights, which O is normalised by, serves as the bound.
+#include <climits>
+
 #include "bsa_internal.h"
 #include "device_common.h"
 #include "kv_cursor.h"
@@ -75,10 +77,19 @@ struct MfmaArgs {
   float* part;          // kMass: [bh][item][wave][nkv] per-wave block sums
   int n_items, H, N, nq, nkv;
   int Npad;  // K and V are permuted into block order: [B*H][Npad][d], Npad = N + kPermPad
+  // per-token block lists (the TOK variant): [B*H][N][tslots], ascending
+  const int32_t* tsel;
+  int tslots;
 };
 
+// LDS row stride of the per-token lists in the TOK variant (at most 1 + kMaxTokenK blocks).
+constexpr int kTokSlots = kMaxTokenK + 1;
+
 // Two LDS stages: tile t is computed while tile t+1 streams in.
-template <int MODE>
+// TOK: each query token attends only to the blocks of its own list (VMoBA review: each query
+// token scores the block means and keeps its best blocks); the workgroup walks the union of its
+// tokens' lists (the CSR row) and masks, per lane, the chunks of blocks its token did not pick.
+template <int MODE, bool TOK = false>
 __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   constexpr int D = 128;
   constexpr bool kDense = MODE == kLse || MODE == kMass || MODE == kMassO;  // all kv blocks
@@ -86,6 +97,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   constexpr bool kNeedV = kPV;
   constexpr int kStage = kNeedV ? 2 * kTileBytes : kTileBytes;
   __shared__ __attribute__((aligned(1024))) char lds[2 * kStage];
+  __shared__ int32_t tlist[TOK ? kAttnRows * kTokSlots : 1];
   char* const lds_a = lds;
   char* const lds_b = lds + kStage;
 
@@ -129,7 +141,9 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   }
   // l_run: fp32 sum of the weights (for the LSE); lb_run: sum of the same weights rounded to bf16
   // as the PV product uses them (O is normalised by it, an exactly normalised combination)
-  float m_run = -INFINITY, l_run = 0.f, lb_run = 0.f;
+  // TOK: a finite floor instead of -inf, so that a tile whose chunks this lane's token did not
+  // pick (all scores -inf) gives weights 0, not exp2(-inf + inf)
+  float m_run = TOK ? -1e30f : -INFINITY, l_run = 0.f, lb_run = 0.f;
   // kMass: log2-domain lse of this lane's query (+inf for padding rows, so they add nothing)
   float nlse2 = 0.f, blk_acc = 0.f;
   if constexpr (MODE == kMass || MODE == kMassO)
@@ -179,8 +193,20 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   if (a0.nv > 0) tile_issue(a0, b0, m0_a);
   Chunk a1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
   Chunk b1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+  if constexpr (TOK) {  // the block lists of this item's query rows (INT_MAX past the rows)
+    for (int idx = t; idx < kAttnRows * a.tslots; idx += 256) {
+      const int row = idx / a.tslots, slot = idx - row * a.tslots;
+      int v = INT_MAX;
+      if (row < nrows)
+        v = a.tsel[((size_t)bh * a.N + a.qperm[q0 + row]) * a.tslots + slot];
+      tlist[row * kTokSlots + slot] = v;
+    }
+  }
   vmem_wait_all();
   __syncthreads();
+  // TOK: position in this lane's list and the block there (lists and the CSR row ascend)
+  int tptr = 0;
+  int tcur = TOK && qvalid ? tlist[qrow * kTokSlots] : INT_MAX;
 
   // V transposed reads: row 16*kc + 8*sh + 4*hl + (lane%16)/4, column 32*dm + 16*((lane/16)&1)
   // + 4*(lane&3): 16-byte unit 4*dm + 2*((lane/16)&1) + ((lane&3)>>1), 8-byte half (lane&1).
@@ -245,6 +271,22 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
 #pragma unroll
           for (int e = 0; e < 16; ++e)
             if (8 * (e >> 2) + 4 * hl + (e & 3) >= nv) sacc[mb][e] = -INFINITY;
+        }
+      }
+      if constexpr (TOK) {  // chunks of blocks this lane's token did not pick
+        auto picked = [&](int J) {
+          while (tcur < J) {
+            ++tptr;
+            tcur = tptr < a.tslots ? tlist[qrow * kTokSlots + tptr] : INT_MAX;
+          }
+          return tcur == J;
+        };
+        const bool pa = picked(a0.J);
+        const bool pb = b0.nv > 0 && picked(b0.J);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (!pa) sacc[0][e] = -INFINITY;
+          if (!pb) sacc[1][e] = -INFINITY;
         }
       }
 
@@ -475,6 +517,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_d128(const MfmaArgs a) {
   attn_mfma_body<MODE>(a);
 }
 
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void attn_mfma_d128_tok(const MfmaArgs a) {
+  attn_mfma_body<MODE, true>(a);
+}
+
 // M[bh, I, J] = (sum over I's work items and their active waves of the block sums) / |I|, in fp64
 // and in a fixed order. Wave w of an item is active iff it holds a valid query row (32 w < rows).
 __global__ __launch_bounds__(256) void mass_combine_kernel(const float* __restrict__ part,
@@ -686,6 +733,33 @@ hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, cons
     return launch_valu<uint16_t, 64>(p, Q, K, V, row_ptr, col_idx, O, lse, s);
   if (p.prob.d == 128) return launch_valu<float, 128>(p, Q, K, V, row_ptr, col_idx, O, lse, s);
   return launch_valu<float, 64>(p, Q, K, V, row_ptr, col_idx, O, lse, s);
+}
+
+hipError_t launch_attn_fwd_tokens(const bsa_plan& p, const void* Q, const void* K, const void* V,
+                                  const int32_t* row_ptr, const int32_t* col_idx,
+                                  const int32_t* sel, int nslots, void* O, float* lse, void* ws,
+                                  hipStream_t s) {
+  const FwdWs L = fwd_ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  hipError_t e = launch_permute_rows(p, K, base + L.kp, s);
+  if (e == hipSuccess) e = launch_permute_rows(p, V, base + L.vp, s);
+  if (e != hipSuccess) return e;
+  MfmaArgs a = mfma_args(p);
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = reinterpret_cast<const uint16_t*>(base + L.kp);
+  a.V = reinterpret_cast<const uint16_t*>(base + L.vp);
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.O = static_cast<uint16_t*>(O);
+  a.lse = lse;
+  a.tsel = sel;
+  a.tslots = nslots;
+  const dim3 grid(p.n_items, p.prob.B * p.prob.H);
+  if (lse)
+    attn_mfma_d128_tok<kFwd><<<grid, 256, 0, s>>>(a);
+  else
+    attn_mfma_d128_tok<kFwdO><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, const void* V,

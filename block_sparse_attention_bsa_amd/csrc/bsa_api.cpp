@@ -109,7 +109,7 @@ void free_plan(bsa_plan* p) {
   if (!p) return;
   for (void* ptr : {(void*)p->qperm, (void*)p->qstart, (void*)p->kvperm, (void*)p->kvstart,
                     (void*)p->items, (void*)p->qitem0, (void*)p->kvitems, (void*)p->scale,
-                    (void*)p->local_ptr, (void*)p->local_idx})
+                    (void*)p->local_ptr, (void*)p->local_idx, (void*)p->kv_of})
     if (ptr) (void)hipFree(ptr);
   delete p;
 }
@@ -132,6 +132,17 @@ SelectWs select_ws_layout(const bsa_plan& p) {
   w.eg_hist = w.eg_groups + align_up(BH * kEgGroupBytes);
   w.eg_bnd = w.eg_hist + align_up(BH * kEgHistBytes);
   w.total = w.eg_bnd + align_up(BH * (size_t)w.eg_nrchunk * 4);
+  return w;
+}
+
+TokWs tok_ws_layout(const bsa_plan& p) {
+  TokWs w;
+  const size_t rows = (size_t)p.prob.B * p.prob.H * p.nq;
+  w.nwords = (p.nkv + 31) / 32;
+  w.gates = 0;
+  w.bitmap = align_up((size_t)p.prob.N * p.nkv * 4);
+  w.counts = w.bitmap + align_up(rows * w.nwords * 4);
+  w.total = w.counts + align_up(rows * 4);
   return w;
 }
 
@@ -255,7 +266,8 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
   p->n_kvitems = (int)(p->h_kvitems.size() / 2);
   p->n_items = (int)(p->h_items.size() / 2);
   {  // local kv blocks of every query block, from each token's kv block
-    std::vector<int32_t> kv_of(pr.N);
+    std::vector<int32_t>& kv_of = p->h_kv_of;
+    kv_of.assign(pr.N, 0);
     for (int j = 0; j < p->nkv; ++j)
       for (int t = p->h_kvstart[j]; t < p->h_kvstart[j + 1]; ++t) kv_of[p->h_kvperm[t]] = j;
     p->h_local_ptr.assign(1, 0);
@@ -290,7 +302,8 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
       upload(kvperm_pad, &p->kvperm) || upload(p->h_kvstart, &p->kvstart) ||
       upload(p->h_items, &p->items) || upload(p->h_qitem0, &p->qitem0) ||
       upload(p->h_kvitems, &p->kvitems) || upload(p->h_scale, &p->scale) ||
-      upload(p->h_local_ptr, &p->local_ptr) || upload(p->h_local_idx, &p->local_idx)) {
+      upload(p->h_local_ptr, &p->local_ptr) || upload(p->h_local_idx, &p->local_idx) ||
+      upload(p->h_kv_of, &p->kv_of)) {
     free_plan(p);
     return fail(BSA_EHIP, "bsa_plan_create: device allocation or upload failed");
   }
@@ -442,6 +455,62 @@ int bsa_select_eg(const bsa_plan* plan, const float* S, const bsa_eg_params* prm
   return launch_status(launch_select_eg(*plan, S, *prm, row_ptr, col_idx, counts, head_entropy,
                                         head_pooled, ws, (hipStream_t)stream),
                        "bsa_select_eg");
+}
+
+int bsa_tokens_ws(const bsa_plan* plan, size_t* ws_bytes) {
+  if (!plan || !ws_bytes) return fail(BSA_EINVAL, "bsa_tokens_ws: NULL argument");
+  *ws_bytes = tok_ws_layout(*plan).total;
+  return BSA_OK;
+}
+
+static int check_tokens(const bsa_plan* plan, int32_t k, const char* who) {
+  if (plan->prob.dtype != BSA_BF16 || plan->prob.d != 128)
+    return fail(BSA_EUNSUPPORTED, "%s: bf16 and d = 128 only", who);
+  if (k < 0) return fail(BSA_EINVAL, "%s: k must be >= 0", who);
+  if (k > kMaxTokenK) return fail(BSA_EUNSUPPORTED, "%s: k above %d", who, kMaxTokenK);
+  if (plan->nkv > 2048)
+    return fail(BSA_EUNSUPPORTED, "%s: more than 2048 kv blocks", who);
+  return BSA_OK;
+}
+
+int bsa_select_tokens(const bsa_plan* plan, const void* Q, const float* Kbar, int32_t k,
+                      int32_t* sel, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || !Q || !Kbar || !sel || !row_ptr || !col_idx)
+    return fail(BSA_EINVAL, "bsa_select_tokens: NULL argument");
+  int rc = check_tokens(plan, k, "bsa_select_tokens");
+  if (rc) return rc;
+  const int64_t need_cols = (int64_t)plan->prob.B * plan->prob.H * plan->nq * plan->nkv;
+  if (col_cap < need_cols)
+    return fail(BSA_ECAPACITY, "bsa_select_tokens: col_idx capacity %lld < %lld",
+                (long long)col_cap, (long long)need_cols);
+  const size_t need = tok_ws_layout(*plan).total;
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ECAPACITY, "bsa_select_tokens: workspace %zu < %zu bytes", ws_bytes, need);
+  rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_select_tokens(*plan, Q, Kbar, k, sel, row_ptr, col_idx, ws,
+                                            (hipStream_t)stream),
+                       "bsa_select_tokens");
+}
+
+int bsa_attn_fwd_tokens(const bsa_plan* plan, const void* Q, const void* K, const void* V,
+                        const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sel,
+                        int32_t k, void* O, float* lse, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (!plan || !Q || !K || !V || !row_ptr || !col_idx || !sel || !O)
+    return fail(BSA_EINVAL, "bsa_attn_fwd_tokens: NULL argument");
+  int rc = check_tokens(plan, k, "bsa_attn_fwd_tokens");
+  if (rc) return rc;
+  const size_t need = fwd_ws_layout(*plan).total;
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ECAPACITY, "bsa_attn_fwd_tokens: workspace %zu < %zu bytes", ws_bytes, need);
+  rc = check_device(plan);
+  if (rc) return rc;
+  const int nslots = 1 + std::min<int>(k, plan->nkv - 1);
+  return launch_status(launch_attn_fwd_tokens(*plan, Q, K, V, row_ptr, col_idx, sel, nslots, O,
+                                              lse, ws, (hipStream_t)stream),
+                       "bsa_attn_fwd_tokens");
 }
 
 int bsa_attn_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,

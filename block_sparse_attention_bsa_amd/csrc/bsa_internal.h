@@ -38,6 +38,9 @@ struct bsa_plan {
   std::vector<int32_t> h_local_ptr, h_local_idx;
   int32_t* local_ptr = nullptr;
   int32_t* local_idx = nullptr;
+  // kv block of every token (frame-major), for per-token selection
+  std::vector<int32_t> h_kv_of;
+  int32_t* kv_of = nullptr;
 };
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
@@ -83,6 +86,15 @@ CalibWs calib_ws_layout(const bsa_plan& p);
 // query chunk, 128 for the K/V rows of a backward kv item.
 constexpr int kPermPad = 128;
 
+// Per-token Local + TopK (bsa_select_tokens): the gates of one head [N][nkv] (fp32), and the
+// bitmap and counts of the per-query-block unions. At most kMaxTokenK others per token.
+constexpr int kMaxTokenK = 24;
+struct TokWs {
+  size_t gates, bitmap, counts, total;
+  int nwords;
+};
+TokWs tok_ws_layout(const bsa_plan& p);
+
 struct FwdWs {
   size_t kp, vp, total;  // K and V in block order, [B*H][N + kPermPad][d] (bf16, d = 128 path)
 };
@@ -101,6 +113,17 @@ hipError_t launch_select_eg(const bsa_plan& p, const float* S, const bsa_eg_para
 hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, const void* V,
                            const int32_t* row_ptr, const int32_t* col_idx, void* O, float* lse,
                            void* ws, hipStream_t s);
+// sel: per-token block lists [B*H][N][nslots] (ascending), walked alongside the union CSR.
+hipError_t launch_attn_fwd_tokens(const bsa_plan& p, const void* Q, const void* K, const void* V,
+                                  const int32_t* row_ptr, const int32_t* col_idx,
+                                  const int32_t* sel, int nslots, void* O, float* lse, void* ws,
+                                  hipStream_t s);
+// Gates of head bh: G[n][J] = sigma_h q_n . Kbar_J for all N tokens (bf16 Q, d = 128).
+hipError_t launch_token_gates(const bsa_plan& p, const void* Q, const float* Kbar, int bh,
+                              float* G, hipStream_t s);
+hipError_t launch_select_tokens(const bsa_plan& p, const void* Q, const float* Kbar, int k,
+                                int32_t* sel, int32_t* row_ptr, int32_t* col_idx, void* ws,
+                                hipStream_t s);
 // dst = src ([B, H, N, 128] bf16) with rows in block order (plan kvperm) and kPermPad zero rows
 // per head.
 hipError_t launch_permute_rows(const bsa_plan& p, const void* src, void* dst, hipStream_t s);

@@ -607,6 +607,95 @@ __global__ __launch_bounds__(256) void mark_local_topk_kernel(
   if (lane == 0) base_counts[r] = count;
 }
 
+// Per-token Local + TopK of one head (VMoBA review: each query token scores the block means):
+// token n keeps its own kv block and the k best others of its gate row G[n, :] by (gate desc,
+// index asc; the gate's fp32 bits, made monotone for negative values, then ~index), one
+// wavefront per token, k rounds of a 64-bit wavefront max. Writes the nslots = 1 + min(k,
+// nkv - 1) chosen blocks ascending at sel[n * nslots].
+__device__ __forceinline__ uint32_t gate_key(float g) {
+  const uint32_t b = __float_as_uint(g);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // order-preserving for every float
+}
+
+template <int kVpl>
+__global__ __launch_bounds__(256) void tok_topk_kernel(const float* __restrict__ G, int N,
+                                                       int nkv, int k, int nslots,
+                                                       const int32_t* __restrict__ kv_of,
+                                                       int32_t* __restrict__ sel) {
+  static_assert(kVpl <= 32, "one mask bit per value");
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const float* row = G + (size_t)n * nkv;
+  uint32_t key[kVpl];
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) key[i] = lane + 64 * i < nkv ? gate_key(row[lane + 64 * i]) : 0u;
+  const int own = kv_of[n];
+  uint32_t mask = (own & 63) == lane ? 1u << (own >> 6) : 0u;  // bit i: value i is chosen
+  for (int round = 0; round < k; ++round) {
+    unsigned long long best = 0ull;  // (key << 32) | ~J; 0 = nothing left in this lane
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i) {
+      const int J = lane + 64 * i;
+      if (J < nkv && !((mask >> i) & 1u)) {
+        const unsigned long long c = ((unsigned long long)key[i] << 32) | (uint32_t)~J;
+        best = c > best ? c : best;
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const unsigned long long o = shfl_xor_u64(best, d);
+      best = o > best ? o : best;
+    }
+    if (best == 0ull) break;
+    const int J = (int)~(uint32_t)best;
+    if ((J & 63) == lane) mask |= 1u << (J >> 6);
+  }
+  // ascending: value i of lane l is block 64 i + l, so ranks follow (i, lane)
+  int before = 0;
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) {
+    const bool on = (mask >> i) & 1u;
+    const unsigned long long bal = __ballot(on);
+    const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
+    if (on && pos < nslots) sel[(size_t)n * nslots + pos] = lane + 64 * i;
+    before += __popcll(bal);
+  }
+}
+
+// Union of the token lists of each query block (b, h, I), one wavefront per row: an LDS bitmap
+// of nkv bits per wavefront (at most 2048 blocks), then the row's bitmap words and count.
+__global__ __launch_bounds__(256) void tok_union_kernel(const int32_t* __restrict__ sel,
+                                                        int nslots, int H, int N, int nq,
+                                                        int nwords,
+                                                        const int32_t* __restrict__ qstart,
+                                                        const int32_t* __restrict__ qperm,
+                                                        int64_t rows,
+                                                        uint32_t* __restrict__ bitmap,
+                                                        int32_t* __restrict__ counts) {
+  __shared__ uint32_t words[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+  if (r >= rows) return;
+  const int I = (int)(r % nq);
+  const int64_t bh = r / nq;
+  words[wave][lane] = 0u;
+  __builtin_amdgcn_wave_barrier();
+  const int t0 = qstart[I], n_entries = (qstart[I + 1] - t0) * nslots;
+  for (int e = lane; e < n_entries; e += 64) {
+    const int tok = qperm[t0 + e / nslots];
+    const int J = sel[((size_t)bh * N + tok) * nslots + e % nslots];
+    atomicOr(&words[wave][J >> 5], 1u << (J & 31));
+  }
+  __builtin_amdgcn_wave_barrier();
+  const uint32_t w = lane < nwords ? words[wave][lane] : 0u;
+  if (lane < nwords) bitmap[r * nwords + lane] = w;
+  int c = __popc(w);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+  if (lane == 0) counts[r] = c;
+}
+
 // CSR columns of one row from its bitmap (at most 64 words), one wavefront per row: each 64-bit
 // word pair is a mask over 64 consecutive candidates; every set lane writes its column at the
 // running position plus its rank, so the stores of a wavefront are consecutive.
@@ -1141,4 +1230,37 @@ hipError_t launch_select_eg(const bsa_plan& p, const float* S, const bsa_eg_para
                                                        bnd, bitmap, base_counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return scan_emit(p, L, bitmap, base_counts, nullptr, false, row_ptr, col_idx, counts, s);
+}
+
+hipError_t launch_select_tokens(const bsa_plan& p, const void* Q, const float* Kbar, int k,
+                                int32_t* sel, int32_t* row_ptr, int32_t* col_idx, void* ws,
+                                hipStream_t s) {
+  const TokWs L = tok_ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  float* G = reinterpret_cast<float*>(base + L.gates);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.bitmap);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  const int BH = p.prob.B * p.prob.H, N = p.prob.N, nkv = p.nkv;
+  const int kk = std::min(k, nkv - 1), nslots = 1 + kk;
+  const int64_t rows = (int64_t)BH * p.nq;
+  hipError_t e = hipSuccess;
+  for (int bh = 0; bh < BH && e == hipSuccess; ++bh) {  // one head's gates at a time
+    e = launch_token_gates(p, Q, Kbar, bh, G, s);
+    if (e != hipSuccess) break;
+    int32_t* hsel = sel + (size_t)bh * N * nslots;
+    if (nkv <= 1024)
+      tok_topk_kernel<16><<<(N + 3) / 4, 256, 0, s>>>(G, N, nkv, kk, nslots, p.kv_of, hsel);
+    else
+      tok_topk_kernel<32><<<(N + 3) / 4, 256, 0, s>>>(G, N, nkv, kk, nslots, p.kv_of, hsel);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  tok_union_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(
+      sel, nslots, p.prob.H, N, p.nq, L.nwords, p.qstart, p.qperm, rows, bitmap, counts);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  scan_kernel<<<1, 1024, 0, s>>>(counts, nullptr, false, rows, p.nq, row_ptr, nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  emit_wave_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(bitmap, L.nwords, rows, row_ptr,
+                                                              col_idx);
+  return hipGetLastError();
 }

@@ -12,7 +12,8 @@ import torch
 
 from . import (BSA_MINK_NONE, BSA_NORM_HEAD, BSA_NORM_ROW, BSA_POOL_HEAD, BSA_POOL_ROW, Plan,
                bsa_attn_bwd, bsa_attn_fwd, bsa_calibrate_mass, bsa_calibrate_mass_fwd, bsa_pool,
-               bsa_score, bsa_select, bsa_select_eg)
+               bsa_attn_fwd_tokens, bsa_score, bsa_select, bsa_select_eg, bsa_select_tokens,
+               bsa_tokens_ws)
 
 
 class BlockSparseAttention:
@@ -38,6 +39,7 @@ class BlockSparseAttention:
         self._ws_calib = None
         self._ws_bwd = None
         self._ws_fwd = None
+        self._ws_tok = None
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
 
     # -- stages -----------------------------------------------------------------------------
@@ -79,6 +81,33 @@ class BlockSparseAttention:
                       self.row_ptr, self.col_idx, self.col_cap, self.counts, self.head_entropy,
                       self.head_pooled, self.ws_select, self.plan.ws_select, stream)
         return self.row_ptr, self.col_idx
+
+    def select_tokens(self, q, k_best, stream=None):
+        """Per-token Local + TopK from Q and the pooled K (pool() first): returns sel
+        [B, H, N, 1 + min(k, nkv - 1)] and fills row_ptr / col_idx with each query block's
+        union."""
+        B, H, N = q.shape[:3]
+        ns = 1 + min(int(k_best), self.plan.nkv - 1)
+        sel = torch.empty((B, H, N, ns), dtype=torch.int32, device=self.device)
+        n = bsa_tokens_ws(self.plan)
+        if self._ws_tok is None or self._ws_tok.numel() < n:
+            self._ws_tok = torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
+        bsa_select_tokens(self.plan, q, self.kbar, k_best, sel, self.row_ptr, self.col_idx,
+                          self.col_cap, self._ws_tok, self._ws_tok.numel(), stream)
+        return sel
+
+    def attention_tokens(self, q, k, v, sel, k_best, out=None, lse=None, with_lse=True,
+                         stream=None):
+        """Attention of every token over its own blocks (sel from select_tokens)."""
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and with_lse:
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=self.device)
+        if self._ws_fwd is None and self.plan.ws_fwd > 0:
+            self._ws_fwd = torch.empty(self.plan.ws_fwd, dtype=torch.uint8, device=self.device)
+        bsa_attn_fwd_tokens(self.plan, q, k, v, self.row_ptr, self.col_idx, sel, k_best, out,
+                            lse, self._ws_fwd, self.plan.ws_fwd, stream)
+        return out, lse
 
     def attention(self, q, k, v, row_ptr=None, col_idx=None, out=None, lse=None, stream=None,
                   with_lse=True):

@@ -19,6 +19,8 @@
  *                         or ranked over a head-global pool of (q-block, kv-block) pairs (VMoBA
  *                         Eq. 3). The result is an int32 CSR list that callers may freeze and
  *                         reuse across denoising steps (LoSA abstract).
+ *      bsa_select_tokens  per query token, its own block plus the k blocks of highest gate (VMoBA
+ *                         review), with bsa_attn_fwd_tokens to attend over them.
  *      bsa_select_eg      the same rule with the competition domain chosen per head by the
  *                         entropy of its scores: a pool shared by a group of low-entropy heads,
  *                         per-row selection for the rest (EG-Sparse abstract).
@@ -207,6 +209,30 @@ int bsa_select_eg(const bsa_plan* plan, const float* S, const bsa_eg_params* par
                   int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
                   float* head_entropy, int32_t* head_pooled, void* ws, size_t ws_bytes,
                   void* stream);
+
+/* Step 3, per token (VMoBA review, "What carries the argument": each query token scores the
+ * block means; the training-free experiments keep "Local + TopK" blocks, k = 2, 6 or 18). Q
+ * [B, H, N, 128] bf16; Kbar fp32 [B, H, nkv, 128] from bsa_pool(which = 1). For every token i:
+ * sel[b, h, i, 0 .. ns) with ns = 1 + min(k, nkv - 1) holds, ascending, the kv block holding i
+ * and the min(k, nkv - 1) others with the highest gate sigma_h q_i . kbar_J (fp32 on the matrix
+ * cores; gate desc, index asc). row_ptr / col_idx (as bsa_select) receive, per query block, the
+ * union of its tokens' lists, which bsa_attn_fwd_tokens walks. ws >= the bytes bsa_tokens_ws
+ * reports (one head's gates, N * nkv * 4, plus the union's bitmap). k in [0, 24]; bf16, d = 128
+ * and nkv <= 2048 only (BSA_EUNSUPPORTED otherwise). */
+int bsa_tokens_ws(const bsa_plan* plan, size_t* ws_bytes);
+int bsa_select_tokens(const bsa_plan* plan, const void* Q, const float* Kbar, int32_t k,
+                      int32_t* sel, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Step 4 over per-token block sets: O_i = sum_j softmax_j(sigma_h q_i . k_j) v_j over the tokens
+ * j of the blocks in sel[b, h, i] (and lse_i, nullable), with sel, row_ptr and col_idx from
+ * bsa_select_tokens with the same k. Each query block's workgroup streams the union of its
+ * tokens' blocks and masks, per token, the blocks that token did not pick. Numerics as
+ * bsa_attn_fwd; ws as bsa_attn_fwd (ws_fwd bytes). */
+int bsa_attn_fwd_tokens(const bsa_plan* plan, const void* Q, const void* K, const void* V,
+                        const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sel,
+                        int32_t k, void* O, float* lse, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Step 4. For every query i of block I: O_i = sum_j softmax_j(sigma_h q_i . k_j) v_j over the
  * tokens j of the kv blocks listed in CSR row I, and lse_i = log sum_j exp(sigma_h q_i . k_j).

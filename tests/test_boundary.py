@@ -94,6 +94,11 @@ def test_null_arguments_rejected(L):
     eg = bsa.EgParams(0.9, 0.5, 2)
     assert L.bsa_select_eg(P, None, ctypes.byref(eg), None, None, 0, None, None, None, None, 0,
                            None) == bsa.BSA_EINVAL
+    assert L.bsa_select_tokens(P, None, None, 2, None, None, None, 0, None, 0,
+                               None) == bsa.BSA_EINVAL
+    assert L.bsa_attn_fwd_tokens(P, *([None] * 6), 2, None, None, None, 0,
+                                 None) == bsa.BSA_EINVAL
+    assert L.bsa_tokens_ws(P, None) == bsa.BSA_EINVAL
     assert L.bsa_attn_fwd(P, None, None, None, None, None, None, None, None, 0,
                           None) == bsa.BSA_EINVAL
     assert L.bsa_attn_bwd(P, *([None] * 12), 0, None) == bsa.BSA_EINVAL
