@@ -139,8 +139,10 @@ TokWs tok_ws_layout(const bsa_plan& p) {
   TokWs w;
   const size_t rows = (size_t)p.prob.B * p.prob.H * p.nq;
   w.nwords = (p.nkv + 31) / 32;
-  w.gates = 0;
-  w.bitmap = align_up((size_t)p.prob.N * p.nkv * 4);
+  const size_t kb = (size_t)p.prob.B * p.prob.H * p.nkv * 128 * 2;
+  w.khi = 0;
+  w.klo = align_up(kb);
+  w.bitmap = w.klo + align_up(kb);
   w.counts = w.bitmap + align_up(rows * w.nwords * 4);
   w.total = w.counts + align_up(rows * 4);
   return w;

@@ -86,11 +86,12 @@ CalibWs calib_ws_layout(const bsa_plan& p);
 // query chunk, 128 for the K/V rows of a backward kv item.
 constexpr int kPermPad = 128;
 
-// Per-token Local + TopK (bsa_select_tokens): the gates of one head [N][nkv] (fp32), and the
-// bitmap and counts of the per-query-block unions. At most kMaxTokenK others per token.
+// Per-token Local + TopK (bsa_select_tokens): Kbar as two bf16 terms (hi, lo; [B*H][nkv][128]
+// each), and the bitmap and counts of the per-query-block unions. At most kMaxTokenK others per
+// token.
 constexpr int kMaxTokenK = 24;
 struct TokWs {
-  size_t gates, bitmap, counts, total;
+  size_t khi, klo, bitmap, counts, total;
   int nwords;
 };
 TokWs tok_ws_layout(const bsa_plan& p);
@@ -118,9 +119,6 @@ hipError_t launch_attn_fwd_tokens(const bsa_plan& p, const void* Q, const void* 
                                   const int32_t* row_ptr, const int32_t* col_idx,
                                   const int32_t* sel, int nslots, void* O, float* lse, void* ws,
                                   hipStream_t s);
-// Gates of head bh: G[n][J] = sigma_h q_n . Kbar_J for all N tokens (bf16 Q, d = 128).
-hipError_t launch_token_gates(const bsa_plan& p, const void* Q, const float* Kbar, int bh,
-                              float* G, hipStream_t s);
 hipError_t launch_select_tokens(const bsa_plan& p, const void* Q, const float* Kbar, int k,
                                 int32_t* sel, int32_t* row_ptr, int32_t* col_idx, void* ws,
                                 hipStream_t s);

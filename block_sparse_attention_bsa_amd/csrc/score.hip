@@ -60,45 +60,6 @@ __global__ __launch_bounds__(64) void logits_kernel(const float* __restrict__ Qb
   }
 }
 
-// Per-token gates of one head (VMoBA review, "What carries the argument": each query token
-// scores the block means): G[n, J] = sigma_h * <q_n, Kbar_J> for every token n (frame-major)
-// and kv block J, the logits kernel's tiling with bf16 query rows widened to fp32 on load.
-__global__ __launch_bounds__(64) void token_gate_kernel(const uint16_t* __restrict__ Q,
-                                                        const float* __restrict__ Kbar,
-                                                        float sig, int N, int nkv,
-                                                        float* __restrict__ G) {
-  constexpr int D = 128, kHalf = D / 2;
-  const int I0 = blockIdx.y * kTI, J0 = blockIdx.x * kTJ;
-  const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
-  // rows and columns past the edge read the last row (in bounds); they are not stored
-  const uint4* qp = reinterpret_cast<const uint4*>(Q + (size_t)min(I0 + l32, N - 1) * D + kHalf * h);
-  const float4* kp =
-      reinterpret_cast<const float4*>(Kbar + (size_t)min(J0 + l32, nkv - 1) * D + kHalf * h);
-  f32x16_t acc;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int i = 0; i < kHalf / 8; ++i) {
-    const uint4 qw = qp[i];
-    const float4 k0 = kp[2 * i], k1 = kp[2 * i + 1];
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_lo(qw.x), k0.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_hi(qw.x), k0.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_lo(qw.y), k0.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_hi(qw.y), k0.w, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_lo(qw.z), k1.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_hi(qw.z), k1.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_lo(qw.w), k1.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_hi(qw.w), k1.w, acc, 0, 0, 0);
-  }
-  const int J = J0 + l32;
-  if (J >= nkv) return;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int I = I0 + 8 * (e >> 2) + 4 * h + (e & 3);
-    if (I < N) G[(size_t)I * nkv + J] = sig * acc[e];
-  }
-}
-
 // 4 rows per 256-thread workgroup, one wavefront each.
 __global__ __launch_bounds__(256) void row_softmax_kernel(float* __restrict__ S, int64_t rows,
                                                           int nkv) {
@@ -152,16 +113,6 @@ __global__ __launch_bounds__(1024) void head_softmax_kernel(float* __restrict__ 
 }
 
 }  // namespace
-
-hipError_t launch_token_gates(const bsa_plan& p, const void* Q, const float* Kbar, int bh,
-                              float* G, hipStream_t s) {
-  const int N = p.prob.N, nkv = p.nkv;
-  const dim3 grid((nkv + kTJ - 1) / kTJ, (N + kTI - 1) / kTI);
-  token_gate_kernel<<<grid, 64, 0, s>>>(static_cast<const uint16_t*>(Q) + (size_t)bh * N * 128,
-                                        Kbar + (size_t)bh * nkv * 128, p.h_scale[bh % p.prob.H],
-                                        N, nkv, G);
-  return hipGetLastError();
-}
 
 hipError_t launch_score(const bsa_plan& p, const float* Qbar, const float* Kbar, int norm,
                         float* S, hipStream_t s) {

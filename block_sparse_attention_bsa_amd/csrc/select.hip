@@ -18,6 +18,8 @@
 //
 // The chosen set is written as a bitmap (one bit per (row, kv block)); a scan over the final row
 // counts gives row_ptr, and a per-row pass expands the bitmap into ascending column indices.
+#include <climits>
+
 #include "bsa_internal.h"
 #include "device_common.h"
 
@@ -607,59 +609,150 @@ __global__ __launch_bounds__(256) void mark_local_topk_kernel(
   if (lane == 0) base_counts[r] = count;
 }
 
-// Per-token Local + TopK of one head (VMoBA review: each query token scores the block means):
-// token n keeps its own kv block and the k best others of its gate row G[n, :] by (gate desc,
-// index asc; the gate's fp32 bits, made monotone for negative values, then ~index), one
-// wavefront per token, k rounds of a 64-bit wavefront max. Writes the nslots = 1 + min(k,
-// nkv - 1) chosen blocks ascending at sel[n * nslots].
+// Order-preserving key of a float (for every sign): larger gates give larger keys.
 __device__ __forceinline__ uint32_t gate_key(float g) {
   const uint32_t b = __float_as_uint(g);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // order-preserving for every float
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-template <int kVpl>
-__global__ __launch_bounds__(256) void tok_topk_kernel(const float* __restrict__ G, int N,
-                                                       int nkv, int k, int nslots,
-                                                       const int32_t* __restrict__ kv_of,
-                                                       int32_t* __restrict__ sel) {
-  static_assert(kVpl <= 32, "one mask bit per value");
-  const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
-  const float* row = G + (size_t)n * nkv;
-  uint32_t key[kVpl];
+// Kbar split into two bf16 terms, hi = bf16(Kbar) and lo = bf16(Kbar - hi), so that the gates
+// can run on the bf16 matrix cores: hi + lo carries Kbar to 2^-17 relative (Q is bf16 already).
+__global__ __launch_bounds__(256) void kbar_split_kernel(const float* __restrict__ Kbar,
+                                                         int64_t n, uint16_t* __restrict__ hi,
+                                                         uint16_t* __restrict__ lo) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float x = Kbar[i];
+  const uint32_t h2 = pack_bf16x2(x, 0.f);
+  const float xh = bf16_lo(h2);
+  hi[i] = (uint16_t)(h2 & 0xffffu);
+  lo[i] = (uint16_t)(pack_bf16x2(x - xh, 0.f) & 0xffffu);
+}
+
+// Per-token gates and their top-k in one pass (no gate matrix in memory). A workgroup owns 128
+// tokens of one head (frame-major n0 .. n0 + 128), a wavefront 32 of them. Per 32-block tile the
+// workgroup stages the blocks' hi and lo rows in LDS; each wavefront forms G^T = Kbar Q^T for its
+// tokens with 16 bf16 MFMAs (Kbar's two terms as A, Q as B), so each lane holds 16 gates of one
+// token (lanes l and l + 32 different blocks of the same token) and keeps that token's best k
+// (key, ~J) pairs in registers (capacity KM), sorted: a candidate enters only above the current
+// k-th. The two halves' lists are merged at the end; the own block is never a candidate.
+constexpr int kGateTile = 32;
+template <int KM>  // list capacity: k <= KM
+__global__ __launch_bounds__(256) void tok_gate_topk_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Khi,
+    const uint16_t* __restrict__ Klo, const float* __restrict__ scale, int H, int N, int nkv,
+    int k, int nslots, const int32_t* __restrict__ kv_of, int32_t* __restrict__ sel) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][2][kGateTile * D];  // [stage][hi/lo]
+  const int bh = blockIdx.y, n0 = blockIdx.x * 128;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, hl = lane >> 5;
+  const float sig = scale[bh % H];
+  const int n = n0 + 32 * wave + l32;
+  const bool valid = n < N;
+  const int own = valid ? kv_of[n] : -1;
+  bf16x8_t qf[8];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + min(n, N - 1)) * D +
+                                                     8 * hl);
 #pragma unroll
-  for (int i = 0; i < kVpl; ++i) key[i] = lane + 64 * i < nkv ? gate_key(row[lane + 64 * i]) : 0u;
-  const int own = kv_of[n];
-  uint32_t mask = (own & 63) == lane ? 1u << (own >> 6) : 0u;  // bit i: value i is chosen
-  for (int round = 0; round < k; ++round) {
-    unsigned long long best = 0ull;  // (key << 32) | ~J; 0 = nothing left in this lane
+    for (int kc = 0; kc < 8; ++kc) qf[kc] = __builtin_bit_cast(bf16x8_t, qp[2 * kc]);
+  }
+  const uint16_t* kh = Khi + (size_t)bh * nkv * D;
+  const uint16_t* kl = Klo + (size_t)bh * nkv * D;
+  // tile `tile` (rows J0 .. J0 + 32, clamped at nkv - 1) is 2 x 8 KB: 64 B per thread, loaded
+  // into registers one tile ahead and written to LDS after the current tile's work
+  // thread t moves 16-byte units t and t + 256: rows t / 16 and t / 16 + 16, unit t % 16
+  uint4 ph0, pl0, ph1, pl1;
+  const int off0 = (t >> 4) * D + 8 * (t & 15), off1 = off0 + 16 * D;
+  auto load = [&](int tile) {
+    const int r0 = tile * kGateTile + (t >> 4);
+    const size_t s0 = (size_t)min(r0, nkv - 1) * D + 8 * (t & 15);
+    const size_t s1 = (size_t)min(r0 + 16, nkv - 1) * D + 8 * (t & 15);
+    ph0 = *reinterpret_cast<const uint4*>(kh + s0);
+    pl0 = *reinterpret_cast<const uint4*>(kl + s0);
+    ph1 = *reinterpret_cast<const uint4*>(kh + s1);
+    pl1 = *reinterpret_cast<const uint4*>(kl + s1);
+  };
+  auto store = [&](int st) {
+    *reinterpret_cast<uint4*>(&kt[st][0][off0]) = ph0;
+    *reinterpret_cast<uint4*>(&kt[st][1][off0]) = pl0;
+    *reinterpret_cast<uint4*>(&kt[st][0][off1]) = ph1;
+    *reinterpret_cast<uint4*>(&kt[st][1][off1]) = pl1;
+  };
+  unsigned long long top[KM];  // best first; 0 = empty
 #pragma unroll
-    for (int i = 0; i < kVpl; ++i) {
-      const int J = lane + 64 * i;
-      if (J < nkv && !((mask >> i) & 1u)) {
-        const unsigned long long c = ((unsigned long long)key[i] << 32) | (uint32_t)~J;
-        best = c > best ? c : best;
+  for (int s = 0; s < KM; ++s) top[s] = 0ull;
+  unsigned long long thr = 0ull;  // the k-th best so far (0 while fewer than k)
+  // sorted insertion (the last entry falls off), then the new k-th best; every index static
+  auto insert = [&](unsigned long long c) {
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {
+      const bool in = s < k && c > top[s];
+      const unsigned long long x = top[s];
+      top[s] = in ? c : x;
+      c = in ? x : c;
+    }
+#pragma unroll
+    for (int s = 0; s < KM; ++s) thr = s == k - 1 ? top[s] : thr;
+  };
+  const int ntiles = (nkv + kGateTile - 1) / kGateTile;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int st = tile & 1;
+    if (tile + 1 < ntiles) load(tile + 1);
+    f32x16_t acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    // A operand: block row l32 of the tile, d = 16 kc + 8 hl .. + 8
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8_t ah =
+          *reinterpret_cast<const bf16x8_t*>(&kt[st][0][l32 * D + 16 * kc + 8 * hl]);
+      const bf16x8_t al =
+          *reinterpret_cast<const bf16x8_t*>(&kt[st][1][l32 * D + 16 * kc + 8 * hl]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[kc], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[kc], acc, 0, 0, 0);
+    }
+    // lane holds token column l32 and block rows 8 (e / 4) + 4 hl + e % 4 of the tile
+    const int J0 = tile * kGateTile;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int J = J0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+      const unsigned long long c0 =
+          ((unsigned long long)gate_key(sig * acc[e]) << 32) | (uint32_t)~J;
+      const bool in = J < nkv && J != own && c0 > thr;
+      if (__ballot(in) != 0ull) {  // skipped by the whole wavefront when no lane inserts
+        if (in) insert(c0);
       }
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const unsigned long long o = shfl_xor_u64(best, d);
-      best = o > best ? o : best;
-    }
-    if (best == 0ull) break;
-    const int J = (int)~(uint32_t)best;
-    if ((J & 63) == lane) mask |= 1u << (J >> 6);
+    if (tile + 1 < ntiles) store(st ^ 1);  // the stage tile - 1 used, free since its barrier
+    __syncthreads();  // tile + 1 staged; every wavefront done with tile
   }
-  // ascending: value i of lane l is block 64 i + l, so ranks follow (i, lane)
-  int before = 0;
+  // merge the other half's list (lanes l and l ^ 32 hold the same token)
+  unsigned long long other[KM];
 #pragma unroll
-  for (int i = 0; i < kVpl; ++i) {
-    const bool on = (mask >> i) & 1u;
-    const unsigned long long bal = __ballot(on);
-    const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
-    if (on && pos < nslots) sel[(size_t)n * nslots + pos] = lane + 64 * i;
-    before += __popcll(bal);
+  for (int s = 0; s < KM; ++s) other[s] = shfl_xor_u64(top[s], 32);
+#pragma unroll
+  for (int s = 0; s < KM; ++s)
+    if (s < k && other[s] > thr) insert(other[s]);
+  if (!valid || hl) return;
+  // own block plus the k picks, ascending: each value's rank is the count of smaller ones
+  int32_t* out = sel + ((size_t)bh * N + n) * nslots;
+  int jv[KM];
+#pragma unroll
+  for (int s = 0; s < KM; ++s) jv[s] = s < k ? (int)~(uint32_t)top[s] : INT_MAX;
+  int r_own = 0;
+#pragma unroll
+  for (int s = 0; s < KM; ++s) r_own += jv[s] < own;
+  out[r_own] = own;
+#pragma unroll
+  for (int s = 0; s < KM; ++s) {
+    int r = jv[s] > own;
+#pragma unroll
+    for (int u = 0; u < KM; ++u) r += jv[u] < jv[s];
+    if (s < k) out[r] = jv[s];
   }
 }
 
@@ -1237,24 +1330,29 @@ hipError_t launch_select_tokens(const bsa_plan& p, const void* Q, const float* K
                                 hipStream_t s) {
   const TokWs L = tok_ws_layout(p);
   char* base = static_cast<char*>(ws);
-  float* G = reinterpret_cast<float*>(base + L.gates);
+  uint16_t* khi = reinterpret_cast<uint16_t*>(base + L.khi);
+  uint16_t* klo = reinterpret_cast<uint16_t*>(base + L.klo);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.bitmap);
   int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
   const int BH = p.prob.B * p.prob.H, N = p.prob.N, nkv = p.nkv;
   const int kk = std::min(k, nkv - 1), nslots = 1 + kk;
   const int64_t rows = (int64_t)BH * p.nq;
-  hipError_t e = hipSuccess;
-  for (int bh = 0; bh < BH && e == hipSuccess; ++bh) {  // one head's gates at a time
-    e = launch_token_gates(p, Q, Kbar, bh, G, s);
-    if (e != hipSuccess) break;
-    int32_t* hsel = sel + (size_t)bh * N * nslots;
-    if (nkv <= 1024)
-      tok_topk_kernel<16><<<(N + 3) / 4, 256, 0, s>>>(G, N, nkv, kk, nslots, p.kv_of, hsel);
-    else
-      tok_topk_kernel<32><<<(N + 3) / 4, 256, 0, s>>>(G, N, nkv, kk, nslots, p.kv_of, hsel);
-    e = hipGetLastError();
-  }
+  const int64_t nk = (int64_t)BH * nkv * 128;
+  kbar_split_kernel<<<(unsigned)((nk + 255) / 256), 256, 0, s>>>(Kbar, nk, khi, klo);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const dim3 grid((N + 127) / 128, BH);
+  const uint16_t* q16 = static_cast<const uint16_t*>(Q);
+  if (kk <= 8)
+    tok_gate_topk_kernel<8><<<grid, 256, 0, s>>>(q16, khi, klo, p.scale, p.prob.H, N, nkv, kk,
+                                                 nslots, p.kv_of, sel);
+  else if (kk <= 16)
+    tok_gate_topk_kernel<16><<<grid, 256, 0, s>>>(q16, khi, klo, p.scale, p.prob.H, N, nkv, kk,
+                                                  nslots, p.kv_of, sel);
+  else
+    tok_gate_topk_kernel<kMaxTokenK><<<grid, 256, 0, s>>>(q16, khi, klo, p.scale, p.prob.H, N,
+                                                          nkv, kk, nslots, p.kv_of, sel);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   tok_union_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(
       sel, nslots, p.prob.H, N, p.nq, L.nwords, p.qstart, p.qperm, rows, bitmap, counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
