@@ -214,11 +214,13 @@ int bsa_select_eg(const bsa_plan* plan, const float* S, const bsa_eg_params* par
  * block means; the training-free experiments keep "Local + TopK" blocks, k = 2, 6 or 18). Q
  * [B, H, N, 128] bf16; Kbar fp32 [B, H, nkv, 128] from bsa_pool(which = 1). For every token i:
  * sel[b, h, i, 0 .. ns) with ns = 1 + min(k, nkv - 1) holds, ascending, the kv block holding i
- * and the min(k, nkv - 1) others with the highest gate sigma_h q_i . kbar_J (fp32 on the matrix
- * cores; gate desc, index asc). row_ptr / col_idx (as bsa_select) receive, per query block, the
- * union of its tokens' lists, which bsa_attn_fwd_tokens walks. ws >= the bytes bsa_tokens_ws
- * reports (one head's gates, N * nkv * 4, plus the union's bitmap). k in [0, 24]; bf16, d = 128
- * and nkv <= 2048 only (BSA_EUNSUPPORTED otherwise). */
+ * and the min(k, nkv - 1) others with the highest gate sigma_h q_i . kbar_J (gate desc, index
+ * asc), the gates formed on the bf16 matrix cores with kbar split into two bf16 terms (2^-17
+ * relative) and fp32 accumulation, and never written to memory. row_ptr / col_idx (as
+ * bsa_select) receive, per query block, the union of its tokens' lists, which
+ * bsa_attn_fwd_tokens walks. ws >= the bytes bsa_tokens_ws reports (kbar's two bf16 terms plus
+ * the union's bitmap and counts). k in [0, 24]; bf16, d = 128 and nkv <= 2048 only
+ * (BSA_EUNSUPPORTED otherwise). */
 int bsa_tokens_ws(const bsa_plan* plan, size_t* ws_bytes);
 int bsa_select_tokens(const bsa_plan* plan, const void* Q, const float* Kbar, int32_t k,
                       int32_t* sel, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
