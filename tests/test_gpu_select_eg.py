@@ -3,7 +3,7 @@ the oracle's select_eg on the same seeded inputs (each side pools and scores the
 
 Bar: head entropies within 1e-5 absolute (fp32 scores on the GPU, fp64 in the oracle); the
 pooled-head flags identical (theta is placed in a gap of the oracle's entropies, at least 1e-4
-from every head); block sets bit-exact except near-ties, judged by the tie-tolerant rule of the
+from every head); block sets bit-exact except near-ties, accepted by the tie-tolerant rule of the
 other selections: per row for per-row heads, over the flattened pool weights for a group."""
 from dataclasses import replace
 
