@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle's attention sample")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the untimed extra measurements (entropy-routed, Local + TopK and "
+                         "per-token selection, attention with LSE), e.g. under a profiler")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
     return ap.parse_args()
@@ -232,7 +235,7 @@ def host_info():
     return model, blas
 
 
-def cpu_baseline(w, x, rows, total_flops, target_s, threads=None):
+def cpu_baseline(w, x, total_flops, target_s, threads=None):
     """Time the oracle: pool + score + select over the whole layer, attention over a sample of
     query blocks, extrapolated to the layer's selected FLOPs. threads=1 limits BLAS to one
     thread (otherwise it uses every core this process may run on)."""
@@ -242,7 +245,7 @@ def cpu_baseline(w, x, rows, total_flops, target_s, threads=None):
     if threads is not None:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=threads):
-            r = cpu_baseline(w, x, rows, total_flops, target_s)
+            r = cpu_baseline(w, x, total_flops, target_s)
         r["cores"] = threads
         return r
     cores = len(os.sched_getaffinity(0))
@@ -459,11 +462,7 @@ def main():
         torch.cuda.synchronize()
         res["stage_ms"]["calibrate_masses_only"] = round(tm.mean_ms("calibrate_masses_only"), 4)
         res["calibrate_then_reuse"] = retained_mass(w, x, layers[0], dev)
-    if w.mode in ("row", "hybrid") and w.dtype == "bf16":
-        res["entropy_routed"] = entropy_routed(w, layers[0], q, k, v, out, tm)
-        res["local_topk"] = local_topk(w, layers[0], q, k, v, out, tm)
-        res["token_topk"] = token_topk(w, layers[0], q, k, v, out, tm)
-    if not w.backward:
+    if not w.backward and not args.no_extras:
         # the same attention call with the LSE requested as well (the training kernel), untimed
         # in the step
         lse_x = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
@@ -475,6 +474,11 @@ def main():
         res["attn_with_lse"] = {"ms": round(tm.mean_ms("attn_with_lse"), 4),
                                 "tflops": attn_flops / (tm.mean_ms("attn_with_lse") * 1e-3)
                                 / 1e12}
+    if w.mode in ("row", "hybrid") and w.dtype == "bf16" and not args.no_extras:
+        # other selections on the same inputs (they replace the layer's CSR: keep them last)
+        res["entropy_routed"] = entropy_routed(w, layers[0], q, k, v, out, tm)
+        res["local_topk"] = local_topk(w, layers[0], q, k, v, out, tm)
+        res["token_topk"] = token_topk(w, layers[0], q, k, v, out, tm)
     if args.copy_ref_mib:
         n = args.copy_ref_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -483,13 +487,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline and w.mode in ("row", "hybrid") and args.config in (1, 2):
-        L = layers[0]
-        rp, ci = L.csr_host()
-        res["cpu_baseline"] = cpu_baseline(w, x, csr_rows(rp, ci), fwd_flops[0],
-                                           args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, x, fwd_flops[0], args.cpu_seconds)
         if args.config == 1:
-            res["cpu_baseline_1thread"] = cpu_baseline(w, x, csr_rows(rp, ci),
-                                                       fwd_flops[0], args.cpu_seconds, threads=1)
+            res["cpu_baseline_1thread"] = cpu_baseline(w, x, fwd_flops[0], args.cpu_seconds,
+                                                       threads=1)
     print(json.dumps(res), flush=True)
 
 
