@@ -86,3 +86,16 @@ def test_local_topk_full_size_480p():
 
 def test_local_topk_full_size_720p_wide_rows():
     _run(CONFIGS[4], 18)          # 1080 kv blocks: the 32-values-per-lane path
+
+
+def test_local_topk_rejects_bad_parameters():
+    import torch
+    import block_sparse_attention_bsa_amd as bsa
+    from block_sparse_attention_bsa_amd.layer import BlockSparseAttention
+    w = replace(CONFIGS[2], grid=(5, 8, 16), H=2)
+    layer = BlockSparseAttention(w.B, w.H, w.d, w.grid, w.qpart, w.kvpart)
+    for fixed_k, mink in ((-1, bsa.BSA_MINK_NONE), (2, bsa.BSA_MINK_FIXED)):
+        with pytest.raises(bsa.BsaError) as ei:
+            layer.select(0.5, pool=bsa.BSA_POOL_LOCAL_TOPK, min_k_mode=mink, fixed_k=fixed_k)
+        assert ei.value.code == bsa.BSA_EINVAL
+    torch.cuda.synchronize()

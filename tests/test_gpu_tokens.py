@@ -109,3 +109,25 @@ def test_tokens_one_token_blocks_wide_rows():
 
 def test_tokens_full_size_480p():
     _run(CONFIGS[2], 6, heads=[0, 11], o_sample=384)
+
+
+def test_tokens_reject_bad_parameters():
+    import torch
+    import block_sparse_attention_bsa_amd as bsa
+    from block_sparse_attention_bsa_amd.layer import BlockSparseAttention
+    w = replace(CONFIGS[2], grid=(5, 8, 16), H=2)
+    layer = BlockSparseAttention(w.B, w.H, w.d, w.grid, w.qpart, w.kvpart)
+    q = torch.zeros((1, 2, w.N, 128), dtype=torch.bfloat16, device="cuda")
+    for k, code in ((-1, bsa.BSA_EINVAL), (25, bsa.BSA_EUNSUPPORTED)):
+        with pytest.raises(bsa.BsaError) as ei:
+            layer.select_tokens(q, k)
+        assert ei.value.code == code
+    # fp32 plans have no per-token path
+    w32 = CONFIGS[1]
+    layer32 = BlockSparseAttention(w32.B, w32.H, w32.d, w32.grid, w32.qpart, w32.kvpart,
+                                   dtype="fp32")
+    q32 = torch.zeros((1, w32.H, w32.N, w32.d), dtype=torch.float32, device="cuda")
+    with pytest.raises(bsa.BsaError) as ei:
+        layer32.select_tokens(q32, 2)
+    assert ei.value.code == bsa.BSA_EUNSUPPORTED
+    torch.cuda.synchronize()
