@@ -29,7 +29,7 @@ BSA_POOL_ROW, BSA_POOL_HEAD, BSA_POOL_LOCAL_TOPK = 0, 1, 2
 BSA_MINK_NONE, BSA_MINK_FIXED, BSA_MINK_WEIGHTED_MEAN = 0, 1, 2
 
 EXPORTED = ("bsa_partition_build", "bsa_plan_create", "bsa_plan_destroy", "bsa_plan_info",
-            "bsa_plan_blocks", "bsa_pool", "bsa_score", "bsa_calibrate_mass",
+            "bsa_plan_blocks", "bsa_pool", "bsa_pool_qk", "bsa_score", "bsa_calibrate_mass",
             "bsa_calibrate_mass_fwd", "bsa_select", "bsa_select_eg", "bsa_tokens_ws",
             "bsa_select_tokens", "bsa_attn_fwd", "bsa_attn_fwd_tokens", "bsa_attn_bwd",
             "bsa_last_error")
@@ -93,6 +93,7 @@ def lib():
                           ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
         "bsa_plan_blocks": [P, I32, P, P],
         "bsa_pool": [P, I32, P, P, P],
+        "bsa_pool_qk": [P, P, P, P, P, P],
         "bsa_score": [P, P, P, I32, P, P],
         "bsa_calibrate_mass": [P, P, P, P, P, SZ, P],
         "bsa_calibrate_mass_fwd": [P, P, P, P, P, P, P, P, SZ, P],
@@ -214,6 +215,11 @@ class Plan:
 
 def bsa_pool(plan: Plan, which: int, X, Xbar, stream=None):
     _check(lib().bsa_pool(plan.handle, which, _ptr(X), _ptr(Xbar), _stream(stream)))
+
+
+def bsa_pool_qk(plan: Plan, Q, K, Qbar, Kbar, stream=None):
+    _check(lib().bsa_pool_qk(plan.handle, _ptr(Q), _ptr(K), _ptr(Qbar), _ptr(Kbar),
+                             _stream(stream)))
 
 
 def bsa_score(plan: Plan, Qbar, Kbar, norm: int, S, stream=None):

@@ -349,6 +349,15 @@ int bsa_pool(const bsa_plan* plan, int32_t which, const void* X, float* Xbar, vo
   return launch_status(launch_pool(*plan, which, X, Xbar, (hipStream_t)stream), "bsa_pool");
 }
 
+int bsa_pool_qk(const bsa_plan* plan, const void* Q, const void* K, float* Qbar, float* Kbar,
+                void* stream) {
+  if (!plan || !Q || !K || !Qbar || !Kbar) return fail(BSA_EINVAL, "bsa_pool_qk: NULL argument");
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_pool_qk(*plan, Q, Qbar, K, Kbar, (hipStream_t)stream),
+                       "bsa_pool_qk");
+}
+
 int bsa_score(const bsa_plan* plan, const float* Qbar, const float* Kbar, int32_t norm, float* S,
               void* stream) {
   if (!plan || !Qbar || !Kbar || !S) return fail(BSA_EINVAL, "bsa_score: NULL argument");

@@ -103,6 +103,8 @@ FwdWs fwd_ws_layout(const bsa_plan& p);
 
 // Kernel launchers (defined in the .hip files). Each returns the launch status.
 hipError_t launch_pool(const bsa_plan& p, int which, const void* X, float* Xbar, hipStream_t s);
+hipError_t launch_pool_qk(const bsa_plan& p, const void* Q, float* Qbar, const void* K,
+                          float* Kbar, hipStream_t s);
 hipError_t launch_score(const bsa_plan& p, const float* Qbar, const float* Kbar, int norm,
                         float* S, hipStream_t s);
 hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_params& prm,

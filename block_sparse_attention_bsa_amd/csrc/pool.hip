@@ -38,19 +38,35 @@ struct Seg<float> {  // fp32: 4 per 16 bytes
   }
 };
 
+// One pooling pass: X over the blocks of a partition (perm, start) into Xbar.
+template <typename T>
+struct PoolSide {
+  const T* X;
+  float* Xbar;
+  const int32_t* perm;
+  const int32_t* start;
+  int nblk;
+};
+
+// blockIdx.x < a.nblk pools side a, the rest side b (both in one launch: more workgroups in
+// flight than either alone, for the short 480p passes).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
-                                                   float* __restrict__ Xbar,
-                                                   const int32_t* __restrict__ perm,
-                                                   const int32_t* __restrict__ start, int N,
-                                                   int nblk) {
+__global__ __launch_bounds__(256) void pool_kernel(const PoolSide<T> a, const PoolSide<T> b,
+                                                   int N) {
   constexpr int VEC = Seg<T>::kVec;
   constexpr int SEGS = D / VEC;
   constexpr int GROUPS = 256 / SEGS;
   constexpr int UNROLL = 8;  // one pass covers a 128-token block: all its rows in flight
   __shared__ float red[GROUPS][D + 1];
 
-  const int J = blockIdx.x;
+  const bool first = (int)blockIdx.x < a.nblk;
+  const PoolSide<T>& sd = first ? a : b;
+  const T* __restrict__ X = sd.X;
+  float* __restrict__ Xbar = sd.Xbar;
+  const int32_t* __restrict__ perm = sd.perm;
+  const int32_t* __restrict__ start = sd.start;
+  const int nblk = sd.nblk;
+  const int J = first ? (int)blockIdx.x : (int)blockIdx.x - a.nblk;
   const int bh = blockIdx.y;
   const int seg = threadIdx.x % SEGS;
   const int grp = threadIdx.x / SEGS;
@@ -89,22 +105,44 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ X,
   }
 }
 
+template <typename T>
+PoolSide<T> side(const bsa_plan& p, int which, const void* X, float* Xbar) {
+  PoolSide<T> sd;
+  sd.X = static_cast<const T*>(X);
+  sd.Xbar = Xbar;
+  sd.perm = which == 0 ? p.qperm : p.kvperm;
+  sd.start = which == 0 ? p.qstart : p.kvstart;
+  sd.nblk = X ? (which == 0 ? p.nq : p.nkv) : 0;
+  return sd;
+}
+
+// Q (which 0) and/or K (which 1); a NULL X skips that side.
 template <typename T, int D>
-hipError_t launch(const bsa_plan& p, int which, const void* X, float* Xbar, hipStream_t s) {
-  const int nblk = which == 0 ? p.nq : p.nkv;
-  dim3 grid(nblk, p.prob.B * p.prob.H);
-  pool_kernel<T, D><<<grid, 256, 0, s>>>(static_cast<const T*>(X), Xbar,
-                                         which == 0 ? p.qperm : p.kvperm,
-                                         which == 0 ? p.qstart : p.kvstart, p.prob.N, nblk);
+hipError_t launch(const bsa_plan& p, const void* Q, float* Qbar, const void* K, float* Kbar,
+                  hipStream_t s) {
+  const PoolSide<T> a = side<T>(p, 0, Q, Qbar), b = side<T>(p, 1, K, Kbar);
+  const dim3 grid(a.nblk + b.nblk, p.prob.B * p.prob.H);
+  pool_kernel<T, D><<<grid, 256, 0, s>>>(a, b, p.prob.N);
   return hipGetLastError();
+}
+
+hipError_t launch_any(const bsa_plan& p, const void* Q, float* Qbar, const void* K, float* Kbar,
+                      hipStream_t s) {
+  if (p.prob.dtype == BSA_BF16)
+    return p.prob.d == 128 ? launch<uint16_t, 128>(p, Q, Qbar, K, Kbar, s)
+                           : launch<uint16_t, 64>(p, Q, Qbar, K, Kbar, s);
+  return p.prob.d == 128 ? launch<float, 128>(p, Q, Qbar, K, Kbar, s)
+                         : launch<float, 64>(p, Q, Qbar, K, Kbar, s);
 }
 
 }  // namespace
 
 hipError_t launch_pool(const bsa_plan& p, int which, const void* X, float* Xbar, hipStream_t s) {
-  if (p.prob.dtype == BSA_BF16)
-    return p.prob.d == 128 ? launch<uint16_t, 128>(p, which, X, Xbar, s)
-                           : launch<uint16_t, 64>(p, which, X, Xbar, s);
-  return p.prob.d == 128 ? launch<float, 128>(p, which, X, Xbar, s)
-                         : launch<float, 64>(p, which, X, Xbar, s);
+  return which == 0 ? launch_any(p, X, Xbar, nullptr, nullptr, s)
+                    : launch_any(p, nullptr, nullptr, X, Xbar, s);
+}
+
+hipError_t launch_pool_qk(const bsa_plan& p, const void* Q, float* Qbar, const void* K,
+                          float* Kbar, hipStream_t s) {
+  return launch_any(p, Q, Qbar, K, Kbar, s);
 }

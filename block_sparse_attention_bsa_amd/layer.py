@@ -11,8 +11,8 @@ from typing import Optional
 import torch
 
 from . import (BSA_MINK_NONE, BSA_NORM_HEAD, BSA_NORM_ROW, BSA_POOL_HEAD, BSA_POOL_ROW, Plan,
-               bsa_attn_bwd, bsa_attn_fwd, bsa_calibrate_mass, bsa_calibrate_mass_fwd, bsa_pool,
-               bsa_attn_fwd_tokens, bsa_score, bsa_select, bsa_select_eg, bsa_select_tokens,
+               bsa_attn_bwd, bsa_attn_fwd, bsa_calibrate_mass, bsa_calibrate_mass_fwd,
+               bsa_attn_fwd_tokens, bsa_pool_qk, bsa_score, bsa_select, bsa_select_eg, bsa_select_tokens,
                bsa_tokens_ws)
 
 
@@ -44,8 +44,7 @@ class BlockSparseAttention:
 
     # -- stages -----------------------------------------------------------------------------
     def pool(self, q, k, stream=None):
-        bsa_pool(self.plan, 0, q, self.qbar, stream)
-        bsa_pool(self.plan, 1, k, self.kbar, stream)
+        bsa_pool_qk(self.plan, q, k, self.qbar, self.kbar, stream)
 
     def score(self, norm=BSA_NORM_ROW, stream=None):
         bsa_score(self.plan, self.qbar, self.kbar, norm, self.S, stream)

@@ -154,6 +154,12 @@ int bsa_plan_blocks(const bsa_plan* plan, int32_t which, int32_t* perm, int32_t*
  * [B, H, nblk, d]. */
 int bsa_pool(const bsa_plan* plan, int32_t which, const void* X, float* Xbar, void* stream);
 
+/* Step 1 for both sides in one launch: Qbar over qpart and Kbar over kvpart, each identical to
+ * its bsa_pool call (the same kernel and summation order); more workgroups in flight than either
+ * pass alone, which matters for short passes. */
+int bsa_pool_qk(const bsa_plan* plan, const void* Q, const void* K, float* Qbar, float* Kbar,
+                void* stream);
+
 /* Step 2. L[b, h, I, J] = sigma_h <Qbar_I, Kbar_J>, then
  *   norm = BSA_NORM_ROW : S = softmax over J of each row;
  *   norm = BSA_NORM_HEAD: S[I, J] = |I| exp(L[I, J]) / sum_{I', J'} |I'| exp(L[I', J']) per head.

@@ -85,6 +85,7 @@ def test_bad_partitions_rejected(L):
 def test_null_arguments_rejected(L):
     P = None
     assert L.bsa_pool(P, 0, None, None, None) == bsa.BSA_EINVAL
+    assert L.bsa_pool_qk(P, None, None, None, None, None) == bsa.BSA_EINVAL
     assert L.bsa_score(P, None, None, 0, None, None) == bsa.BSA_EINVAL
     assert L.bsa_calibrate_mass(P, None, None, None, None, 0, None) == bsa.BSA_EINVAL
     assert L.bsa_calibrate_mass_fwd(P, *([None] * 7), 0, None) == bsa.BSA_EINVAL

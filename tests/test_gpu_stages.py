@@ -44,6 +44,12 @@ def test_pool_parity(name, w):
         err = np.abs(dev_to_f64(got) - ref).max()
         log(f"  which={which} max-abs {err:.2e}")
         assert err <= 1e-5
+        # the one-sided entry point gives the same bits as the combined launch
+        import block_sparse_attention_bsa_amd as bsa
+        single = torch.empty_like(got)
+        bsa.bsa_pool(layer.plan, which, to_dev(X), single)
+        torch.cuda.synchronize()
+        assert torch.equal(single, got)
 
 
 # ----------------------------------------------------------------------------------- scoring
