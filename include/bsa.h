@@ -58,7 +58,7 @@ extern "C" {
 /* status codes */
 #define BSA_OK 0
 #define BSA_EINVAL (-1)        /* a NULL pointer, a bad shape or parameter                       */
-#define BSA_EUNSUPPORTED (-2)  /* a valid request this build does not implement (d, dtype, size) */
+#define BSA_EUNSUPPORTED (-2)  /* a valid request the library does not implement (d, dtype, size) */
 #define BSA_ECAPACITY (-3)     /* an output or workspace buffer is smaller than required          */
 #define BSA_EHIP (-4)          /* the HIP runtime reported an error (no device, launch failure)   */
 
