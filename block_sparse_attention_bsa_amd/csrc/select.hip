@@ -695,13 +695,19 @@ __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
 #pragma unroll
     for (int s = 0; s < KM; ++s) thr = s == k - 1 ? top[s] : thr;
   };
+  // The walk over the block tiles starts at the tile holding the own block of the workgroup's
+  // middle token and wraps around: blocks near a token tend to score high, so the threshold
+  // rises early and later candidates mostly skip the insertion. The top k by key (score, then
+  // lower index) do not depend on the order the candidates arrive in.
   const int ntiles = (nkv + kGateTile - 1) / kGateTile;
-  load(0);
+  const int tile0 = kv_of[min(n0 + 64, N - 1)] / kGateTile;
+  auto tile_at = [&](int it) { return tile0 + it < ntiles ? tile0 + it : tile0 + it - ntiles; };
+  load(tile_at(0));
   store(0);
   __syncthreads();
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int st = tile & 1;
-    if (tile + 1 < ntiles) load(tile + 1);
+  for (int it = 0; it < ntiles; ++it) {
+    const int st = it & 1, tile = tile_at(it);
+    if (it + 1 < ntiles) load(tile_at(it + 1));
     f32x16_t acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
@@ -727,8 +733,8 @@ __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
         if (in) insert(c0);
       }
     }
-    if (tile + 1 < ntiles) store(st ^ 1);  // the stage tile - 1 used, free since its barrier
-    __syncthreads();  // tile + 1 staged; every wavefront done with tile
+    if (it + 1 < ntiles) store(st ^ 1);  // the stage step it - 1 used, free since its barrier
+    __syncthreads();  // the next tile staged; every wavefront done with this one
   }
   // merge the other half's list (lanes l and l ^ 32 hold the same token)
   unsigned long long other[KM];
