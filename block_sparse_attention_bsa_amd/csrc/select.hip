@@ -20,6 +20,9 @@
 // counts gives row_ptr, and a per-row pass expands the bitmap into ascending column indices.
 #include <climits>
 
+#include <array>
+#include <utility>
+
 #include "bsa_internal.h"
 #include "device_common.h"
 
@@ -634,16 +637,20 @@ __global__ __launch_bounds__(256) void kbar_split_kernel(const float* __restrict
 // workgroup stages the blocks' hi and lo rows in LDS; each wavefront forms G^T = Kbar Q^T for its
 // tokens with 16 bf16 MFMAs (Kbar's two terms as A, Q as B), so each lane holds 16 gates of one
 // token (lanes l and l + 32 different blocks of the same token) and keeps that token's best k
-// (key, ~J) pairs in registers (capacity KM), sorted: a candidate enters only above the current
-// k-th. The two halves' lists are merged at the end; the own block is never a candidate.
+// (key, ~J) pairs in registers, sorted: a candidate enters only above the current k-th. One
+// instantiation per k, so the list has exactly k slots. The two halves' lists are merged at the
+// end; the own block is never a candidate.
 constexpr int kGateTile = 32;
-template <int KM>  // list capacity: k <= KM
+template <int K>
 __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Khi,
     const uint16_t* __restrict__ Klo, const float* __restrict__ scale, int H, int N, int nkv,
-    int k, int nslots, const int32_t* __restrict__ kv_of, int32_t* __restrict__ sel) {
+    int nslots, const int32_t* __restrict__ kv_of, int32_t* __restrict__ sel) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(16))) uint16_t kt[2][2][kGateTile * D];  // [stage][hi/lo]
+  // [stage][hi/lo]; rows padded by 16 bytes so that the 32 rows an operand read touches start
+  // in different banks
+  constexpr int R = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][2][kGateTile * R];
   const int bh = blockIdx.y, n0 = blockIdx.x * 128;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, hl = lane >> 5;
   const float sig = scale[bh % H];
@@ -663,7 +670,7 @@ __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
   // into registers one tile ahead and written to LDS after the current tile's work
   // thread t moves 16-byte units t and t + 256: rows t / 16 and t / 16 + 16, unit t % 16
   uint4 ph0, pl0, ph1, pl1;
-  const int off0 = (t >> 4) * D + 8 * (t & 15), off1 = off0 + 16 * D;
+  const int off0 = (t >> 4) * R + 8 * (t & 15), off1 = off0 + 16 * R;
   auto load = [&](int tile) {
     const int r0 = tile * kGateTile + (t >> 4);
     const size_t s0 = (size_t)min(r0, nkv - 1) * D + 8 * (t & 15);
@@ -679,21 +686,18 @@ __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
     *reinterpret_cast<uint4*>(&kt[st][0][off1]) = ph1;
     *reinterpret_cast<uint4*>(&kt[st][1][off1]) = pl1;
   };
-  unsigned long long top[KM];  // best first; 0 = empty
+  unsigned long long top[K];  // best first; 0 = empty; top[K - 1] is the k-th best so far
 #pragma unroll
-  for (int s = 0; s < KM; ++s) top[s] = 0ull;
-  unsigned long long thr = 0ull;  // the k-th best so far (0 while fewer than k)
-  // sorted insertion (the last entry falls off), then the new k-th best; every index static
+  for (int s = 0; s < K; ++s) top[s] = 0ull;
+  // sorted insertion (the last entry falls off); every index static
   auto insert = [&](unsigned long long c) {
 #pragma unroll
-    for (int s = 0; s < KM; ++s) {
-      const bool in = s < k && c > top[s];
+    for (int s = 0; s < K; ++s) {
+      const bool in = c > top[s];
       const unsigned long long x = top[s];
       top[s] = in ? c : x;
       c = in ? x : c;
     }
-#pragma unroll
-    for (int s = 0; s < KM; ++s) thr = s == k - 1 ? top[s] : thr;
   };
   // The walk over the block tiles starts at the tile holding the own block of the workgroup's
   // middle token and wraps around: blocks near a token tend to score high, so the threshold
@@ -715,9 +719,9 @@ __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       const bf16x8_t ah =
-          *reinterpret_cast<const bf16x8_t*>(&kt[st][0][l32 * D + 16 * kc + 8 * hl]);
+          *reinterpret_cast<const bf16x8_t*>(&kt[st][0][l32 * R + 16 * kc + 8 * hl]);
       const bf16x8_t al =
-          *reinterpret_cast<const bf16x8_t*>(&kt[st][1][l32 * D + 16 * kc + 8 * hl]);
+          *reinterpret_cast<const bf16x8_t*>(&kt[st][1][l32 * R + 16 * kc + 8 * hl]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[kc], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[kc], acc, 0, 0, 0);
     }
@@ -728,7 +732,7 @@ __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
       const int J = J0 + 8 * (e >> 2) + 4 * hl + (e & 3);
       const unsigned long long c0 =
           ((unsigned long long)gate_key(sig * acc[e]) << 32) | (uint32_t)~J;
-      const bool in = J < nkv && J != own && c0 > thr;
+      const bool in = J < nkv && J != own && c0 > top[K - 1];
       if (__ballot(in) != 0ull) {  // skipped by the whole wavefront when no lane inserts
         if (in) insert(c0);
       }
@@ -737,29 +741,51 @@ __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
     __syncthreads();  // the next tile staged; every wavefront done with this one
   }
   // merge the other half's list (lanes l and l ^ 32 hold the same token)
-  unsigned long long other[KM];
+  unsigned long long other[K];
 #pragma unroll
-  for (int s = 0; s < KM; ++s) other[s] = shfl_xor_u64(top[s], 32);
+  for (int s = 0; s < K; ++s) other[s] = shfl_xor_u64(top[s], 32);
 #pragma unroll
-  for (int s = 0; s < KM; ++s)
-    if (s < k && other[s] > thr) insert(other[s]);
+  for (int s = 0; s < K; ++s)
+    if (other[s] > top[K - 1]) insert(other[s]);
   if (!valid || hl) return;
   // own block plus the k picks, ascending: each value's rank is the count of smaller ones
   int32_t* out = sel + ((size_t)bh * N + n) * nslots;
-  int jv[KM];
+  int jv[K];
 #pragma unroll
-  for (int s = 0; s < KM; ++s) jv[s] = s < k ? (int)~(uint32_t)top[s] : INT_MAX;
+  for (int s = 0; s < K; ++s) jv[s] = (int)~(uint32_t)top[s];
   int r_own = 0;
 #pragma unroll
-  for (int s = 0; s < KM; ++s) r_own += jv[s] < own;
+  for (int s = 0; s < K; ++s) r_own += jv[s] < own;
   out[r_own] = own;
 #pragma unroll
-  for (int s = 0; s < KM; ++s) {
+  for (int s = 0; s < K; ++s) {
     int r = jv[s] > own;
 #pragma unroll
-    for (int u = 0; u < KM; ++u) r += jv[u] < jv[s];
-    if (s < k) out[r] = jv[s];
+    for (int u = 0; u < K; ++u) r += jv[u] < jv[s];
+    out[r] = jv[s];
   }
+}
+
+// k = 0: each token's list is its own block alone.
+__global__ __launch_bounds__(256) void tok_own_kernel(const int32_t* __restrict__ kv_of, int N,
+                                                      int64_t n_tokens,
+                                                      int32_t* __restrict__ sel) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n_tokens) sel[i] = kv_of[i % N];
+}
+
+using GateLaunch = void (*)(dim3, hipStream_t, const uint16_t*, const uint16_t*, const uint16_t*,
+                            const float*, int, int, int, int, const int32_t*, int32_t*);
+template <int K>
+void gate_launch(dim3 grid, hipStream_t s, const uint16_t* Q, const uint16_t* khi,
+                 const uint16_t* klo, const float* scale, int H, int N, int nkv, int nslots,
+                 const int32_t* kv_of, int32_t* sel) {
+  tok_gate_topk_kernel<K><<<grid, 256, 0, s>>>(Q, khi, klo, scale, H, N, nkv, nslots, kv_of, sel);
+}
+// entry k - 1 launches the instantiation for k
+template <int... Ks>
+constexpr std::array<GateLaunch, sizeof...(Ks)> gate_table(std::integer_sequence<int, Ks...>) {
+  return {{&gate_launch<Ks + 1>...}};
 }
 
 // Union of the token lists of each query block (b, h, I), one wavefront per row: an LDS bitmap
@@ -1349,15 +1375,13 @@ hipError_t launch_select_tokens(const bsa_plan& p, const void* Q, const float* K
   if (e != hipSuccess) return e;
   const dim3 grid((N + 127) / 128, BH);
   const uint16_t* q16 = static_cast<const uint16_t*>(Q);
-  if (kk <= 8)
-    tok_gate_topk_kernel<8><<<grid, 256, 0, s>>>(q16, khi, klo, p.scale, p.prob.H, N, nkv, kk,
-                                                 nslots, p.kv_of, sel);
-  else if (kk <= 16)
-    tok_gate_topk_kernel<16><<<grid, 256, 0, s>>>(q16, khi, klo, p.scale, p.prob.H, N, nkv, kk,
-                                                  nslots, p.kv_of, sel);
-  else
-    tok_gate_topk_kernel<kMaxTokenK><<<grid, 256, 0, s>>>(q16, khi, klo, p.scale, p.prob.H, N,
-                                                          nkv, kk, nslots, p.kv_of, sel);
+  if (kk == 0) {
+    const int64_t nt = (int64_t)BH * N;
+    tok_own_kernel<<<(unsigned)((nt + 255) / 256), 256, 0, s>>>(p.kv_of, N, nt, sel);
+  } else {
+    static constexpr auto table = gate_table(std::make_integer_sequence<int, kMaxTokenK>());
+    table[kk - 1](grid, s, q16, khi, klo, p.scale, p.prob.H, N, nkv, nslots, p.kv_of, sel);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   tok_union_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(
       sel, nslots, p.prob.H, N, p.nq, L.nwords, p.qstart, p.qperm, rows, bitmap, counts);

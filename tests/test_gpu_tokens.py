@@ -92,9 +92,15 @@ def _run(w, k, heads=None, o_sample=None, seed=0):
 SMALL = replace(CONFIGS[2], grid=(5, 12, 16), H=3)
 
 
-@pytest.mark.parametrize("k", [0, 2, 6, 18])
+@pytest.mark.parametrize("k", [0, 1, 2, 6, 9, 18, 24])
 def test_tokens_reduced(k):
     _run(SMALL, k)
+
+
+@pytest.mark.parametrize("k", [17, 24])
+def test_tokens_large_k(k):
+    # 32 kv blocks, so the largest lists are not clamped
+    _run(replace(CONFIGS[2], grid=(8, 16, 32), H=2), k, o_sample=256)
 
 
 def test_tokens_temporal_blocks_and_batch2():
