@@ -641,6 +641,7 @@ __global__ __launch_bounds__(256) void kbar_split_kernel(const float* __restrict
 // instantiation per k, so the list has exactly k slots. The two halves' lists are merged at the
 // end; the own block is never a candidate.
 constexpr int kGateTile = 32;
+constexpr int kGateQueueK = 4;  // from this k on, candidates go through a per-lane queue
 template <int K>
 __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Khi,
@@ -651,6 +652,8 @@ __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
   // in different banks
   constexpr int R = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][2][kGateTile * R];
+  // per-lane candidate queue of the current tile: [wave][tile position][lane]
+  __shared__ uint32_t gq[K >= kGateQueueK ? 4 * 16 * 64 : 1];
   const int bh = blockIdx.y, n0 = blockIdx.x * 128;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, hl = lane >> 5;
   const float sig = scale[bh % H];
@@ -727,14 +730,41 @@ __global__ __launch_bounds__(256) void tok_gate_topk_kernel(
     }
     // lane holds token column l32 and block rows 8 (e / 4) + 4 hl + e % 4 of the tile
     const int J0 = tile * kGateTile;
+    if constexpr (K < kGateQueueK) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int J = J0 + 8 * (e >> 2) + 4 * hl + (e & 3);
-      const unsigned long long c0 =
-          ((unsigned long long)gate_key(sig * acc[e]) << 32) | (uint32_t)~J;
-      const bool in = J < nkv && J != own && c0 > top[K - 1];
-      if (__ballot(in) != 0ull) {  // skipped by the whole wavefront when no lane inserts
-        if (in) insert(c0);
+      for (int e = 0; e < 16; ++e) {
+        const int J = J0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+        const unsigned long long c0 =
+            ((unsigned long long)gate_key(sig * acc[e]) << 32) | (uint32_t)~J;
+        const bool in = J < nkv && J != own && c0 > top[K - 1];
+        if (__ballot(in) != 0ull) {  // skipped by the whole wavefront when no lane inserts
+          if (in) insert(c0);
+        }
+      }
+    } else {
+      // Candidates above the k-th best as the tile starts are queued (their gate bits, in
+      // LDS) and inserted one per lane per round: the wavefront runs as many insertion rounds
+      // as its longest queue, not one per tile position some lane inserts at.
+      uint32_t pend = 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int J = J0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+        const uint32_t g = gate_key(sig * acc[e]);
+        const unsigned long long c0 = ((unsigned long long)g << 32) | (uint32_t)~J;
+        if (J < nkv && J != own && c0 > top[K - 1]) {
+          gq[(wave * 16 + e) * 64 + lane] = g;
+          pend |= 1u << e;
+        }
+      }
+      while (__ballot(pend != 0u) != 0ull) {
+        if (pend != 0u) {
+          const int e = __builtin_ctz(pend);
+          pend &= pend - 1u;
+          const int J = J0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+          const unsigned long long c =
+              ((unsigned long long)gq[(wave * 16 + e) * 64 + lane] << 32) | (uint32_t)~J;
+          if (c > top[K - 1]) insert(c);  // the k-th best may have risen since it was queued
+        }
       }
     }
     if (it + 1 < ntiles) store(st ^ 1);  // the stage step it - 1 used, free since its barrier
