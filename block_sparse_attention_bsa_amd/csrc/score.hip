@@ -3,7 +3,8 @@
 // Eq. 3 ranks entries of the whole query-by-block matrix of a head).
 //
 //   logits_kernel   L[bh, I, J] = sigma_h * <Qbar_I, Kbar_J> in fp32 on the matrix cores
-//                   (v_mfma_f32_32x32x2_f32), one wavefront per 32 x 32 tile.
+//                   (v_mfma_f32_32x32x2_f32), one wavefront per 32 x 32 tile, four per
+//                   workgroup sharing their operand rows through LDS.
 //   row_softmax     one wavefront per row: S = exp(L - max) / sum, fp32, fixed reduction order.
 //   head_softmax    one 1024-thread workgroup per head: W = |I| exp(L - M) / Z with the head max
 //                   M and Z = sum |I| exp(L - M) accumulated in fp64 (fixed order).
@@ -12,46 +13,56 @@
 
 namespace {
 
-constexpr int kTI = 32, kTJ = 32;
+constexpr int kWI = 64, kWJ = 64;  // one workgroup: a 64 x 64 region of L, four 32 x 32 tiles
 
-// One wavefront per 32 x 32 tile of L. In each k-step of the MFMA the two 32-lane halves supply
-// the two k-indices; half h takes d = (D/2) h + s at step s, so that every lane streams one
+// A workgroup stages the region's 64 rows of Qbar and of Kbar in LDS with coalesced 16-byte
+// loads (rows padded by 16 bytes, so that the 16 lanes of a read start in different banks), and
+// wavefront w forms tile (w / 2, w % 2) of the region. In each k-step of the MFMA the two 32-lane
+// halves supply the two k-indices; half h takes d = (D/2) h + s at step s, reading one
 // contiguous half row of Qbar (A operand, row I0 + lane % 32) and of Kbar (B operand, column
-// J0 + lane % 32) with 16-byte loads. The products and sums are fp32; the summation order over d
-// is the matrix core's.
+// J0 + lane % 32). The products and sums are fp32; the summation order over d is the matrix
+// core's.
 template <int D>
-__global__ __launch_bounds__(64) void logits_kernel(const float* __restrict__ Qbar,
-                                                    const float* __restrict__ Kbar,
-                                                    const float* __restrict__ scale, int H,
-                                                    int nq, int nkv, float* __restrict__ S) {
-  constexpr int kHalf = D / 2, kVec = kHalf / 4;
+__global__ __launch_bounds__(256) void logits_kernel(const float* __restrict__ Qbar,
+                                                     const float* __restrict__ Kbar,
+                                                     const float* __restrict__ scale, int H,
+                                                     int nq, int nkv, float* __restrict__ S) {
+  constexpr int kHalf = D / 2, kVec = kHalf / 4, R = D + 4;
+  __shared__ __attribute__((aligned(16))) float qs[kWI * R];
+  __shared__ __attribute__((aligned(16))) float ks[kWJ * R];
   const int bh = blockIdx.z;
-  const int I0 = blockIdx.y * kTI, J0 = blockIdx.x * kTJ;
-  const int lane = threadIdx.x, l32 = lane & 31, h = lane >> 5;
-  // rows and columns past the matrix edge read the last row (in bounds); they are not stored
-  const float4* qp = reinterpret_cast<const float4*>(
-      Qbar + ((size_t)bh * nq + min(I0 + l32, nq - 1)) * D + kHalf * h);
-  const float4* kp = reinterpret_cast<const float4*>(
-      Kbar + ((size_t)bh * nkv + min(J0 + l32, nkv - 1)) * D + kHalf * h);
-  float4 qa[kVec], kb[kVec];
-#pragma unroll
-  for (int i = 0; i < kVec; ++i) {
-    qa[i] = qp[i];
-    kb[i] = kp[i];
+  const int IW = blockIdx.y * kWI, JW = blockIdx.x * kWJ;
+  const int t = threadIdx.x;
+  // rows past the matrix edge load the last row (in bounds); their results are not stored
+  constexpr int kUnits = D / 4;  // 16-byte units per row
+  for (int u = t; u < kWI * kUnits; u += 256) {
+    const int row = u / kUnits, c = u % kUnits;
+    const float4 qv = reinterpret_cast<const float4*>(
+        Qbar + ((size_t)bh * nq + min(IW + row, nq - 1)) * D)[c];
+    const float4 kv = reinterpret_cast<const float4*>(
+        Kbar + ((size_t)bh * nkv + min(JW + row, nkv - 1)) * D)[c];
+    *reinterpret_cast<float4*>(&qs[row * R + 4 * c]) = qv;
+    *reinterpret_cast<float4*>(&ks[row * R + 4 * c]) = kv;
   }
+  __syncthreads();
+  const int lane = t & 63, wave = t >> 6, l32 = lane & 31, h = lane >> 5;
+  const int ti = 32 * (wave >> 1), tj = 32 * (wave & 1);
+  const float4* qp = reinterpret_cast<const float4*>(&qs[(ti + l32) * R + kHalf * h]);
+  const float4* kp = reinterpret_cast<const float4*>(&ks[(tj + l32) * R + kHalf * h]);
   f32x16_t acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int i = 0; i < kVec; ++i) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i].x, kb[i].x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i].y, kb[i].y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i].z, kb[i].z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[i].w, kb[i].w, acc, 0, 0, 0);
+    const float4 qa = qp[i], kb = kp[i];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.x, kb.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.y, kb.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.z, kb.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa.w, kb.w, acc, 0, 0, 0);
   }
   // lane holds column J0 + lane % 32 and rows I0 + 8 (e / 4) + 4 h + e % 4
   const float sig = scale[bh % H];
-  const int J = J0 + l32;
+  const int I0 = IW + ti, J = JW + tj + l32;
   if (J >= nkv) return;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -117,11 +128,11 @@ __global__ __launch_bounds__(1024) void head_softmax_kernel(float* __restrict__ 
 hipError_t launch_score(const bsa_plan& p, const float* Qbar, const float* Kbar, int norm,
                         float* S, hipStream_t s) {
   const int BH = p.prob.B * p.prob.H;
-  dim3 grid((p.nkv + kTJ - 1) / kTJ, (p.nq + kTI - 1) / kTI, BH);
+  dim3 grid((p.nkv + kWJ - 1) / kWJ, (p.nq + kWI - 1) / kWI, BH);
   if (p.prob.d == 128)
-    logits_kernel<128><<<grid, 64, 0, s>>>(Qbar, Kbar, p.scale, p.prob.H, p.nq, p.nkv, S);
+    logits_kernel<128><<<grid, 256, 0, s>>>(Qbar, Kbar, p.scale, p.prob.H, p.nq, p.nkv, S);
   else
-    logits_kernel<64><<<grid, 64, 0, s>>>(Qbar, Kbar, p.scale, p.prob.H, p.nq, p.nkv, S);
+    logits_kernel<64><<<grid, 256, 0, s>>>(Qbar, Kbar, p.scale, p.prob.H, p.nq, p.nkv, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (norm == BSA_NORM_ROW) {
