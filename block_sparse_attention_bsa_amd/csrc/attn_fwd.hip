@@ -222,7 +222,25 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     // resident workgroup.
     // S^T for this wave's 32 queries: two 32-kv M blocks (raw, unscaled scores).
     f32x16_t sacc[2];
-    if (active) {
+    // TOK: whether this lane's token picked each chunk's block. A wavefront none of whose tokens
+    // picked either skips the tile's matrix and vector work: all its weights would be exactly 0,
+    // adding nothing to O or the sums.
+    bool pa = true, pb = true, act = active;
+    if constexpr (TOK) {
+      if (active) {
+        auto picked = [&](int J) {
+          while (tcur < J) {
+            ++tptr;
+            tcur = tptr < a.tslots ? tlist[qrow * kTokSlots + tptr] : INT_MAX;
+          }
+          return tcur == J;
+        };
+        pa = picked(a0.J);
+        pb = b0.nv > 0 && picked(b0.J);
+        act = __ballot(pa || pb) != 0ull;
+      }
+    }
+    if (act) {
       // Raised wave priority while the matrix phases issue: the co-resident wavefront (the other
       // workgroup) then fills the gaps with its VALU work instead of competing for issue.
       __builtin_amdgcn_s_setprio(2);
@@ -263,7 +281,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     const Chunk bn = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
     if (a1.nv > 0) tile_issue(a1, b1, nx_m0);
 
-    if (active) {
+    if (act) {
       if (a0.nv < 32 || b0.nv < 32) {  // partial chunk(s): mask padded kv rows
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -274,15 +292,6 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         }
       }
       if constexpr (TOK) {  // chunks of blocks this lane's token did not pick
-        auto picked = [&](int J) {
-          while (tcur < J) {
-            ++tptr;
-            tcur = tptr < a.tslots ? tlist[qrow * kTokSlots + tptr] : INT_MAX;
-          }
-          return tcur == J;
-        };
-        const bool pa = picked(a0.J);
-        const bool pb = b0.nv > 0 && picked(b0.J);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           if (!pa) sacc[0][e] = -INFINITY;
