@@ -181,6 +181,8 @@ class Plan:
         hs = None
         if head_scale is not None:
             hs = np.ascontiguousarray(np.asarray(head_scale, np.float32).reshape(-1))
+            if hs.size != self.H:  # the C ABI reads exactly H host floats
+                raise ValueError(f"head_scale has {hs.size} entries, expected H = {self.H}")
         self._hs = hs
         handle = ctypes.c_void_p(None)
         _check(lib().bsa_plan_create(ctypes.byref(prob), None if hs is None else hs.ctypes.data,

@@ -74,17 +74,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   }
 }
 
-// Selection bitmap of one CSR row (one workgroup per row, nwords <= 256).
+// Selection bitmap of one CSR row (one workgroup per row, nwords <= 256); entries outside
+// [0, nkv) are skipped, as the forward's cursor skips them.
 __global__ __launch_bounds__(256) void csr_bitmap_kernel(const int32_t* __restrict__ row_ptr,
                                                          const int32_t* __restrict__ col_idx,
-                                                         int nwords, uint32_t* __restrict__ bm) {
+                                                         int nkv, int nwords,
+                                                         uint32_t* __restrict__ bm) {
   __shared__ uint32_t w[256];
   const int64_t r = blockIdx.x;
   for (int i = threadIdx.x; i < nwords; i += 256) w[i] = 0u;
   __syncthreads();
   for (int s = row_ptr[r] + threadIdx.x; s < row_ptr[r + 1]; s += 256) {
     const int J = col_idx[s];
-    atomicOr(&w[J >> 5], 1u << (J & 31));
+    if ((uint32_t)J < (uint32_t)nkv) atomicOr(&w[J >> 5], 1u << (J & 31));
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nwords; i += 256) bm[r * nwords + i] = w[i];
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const DqArgs a) {
   cur.slot = ld_ro(a.row_ptr + r);
   cur.end = ld_ro(a.row_ptr + r + 1);
   cur.sub = 0;
-  cursor_load<false>(cur, a.col_idx, a.kvstart);
+  cursor_load<false>(cur, a.col_idx, a.kvstart, a.nkv);
 
   // Loader: wave w copies rows 16 w + 4 i + lane / 16 (i = 0..3) of the 64-row K and V tiles
   // (chunk w / 2, rows 16 (w % 2) + 4 i + lane / 16 of it), from the block-ordered copies.
@@ -561,11 +563,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const DqArgs a) {
   const int vhalf_l = 8 * (lane & 1);
 
   const uint32_t m0_a = lds_addr(lds_a), m0_b = lds_addr(lds_b);
-  Chunk a0 = take_chunk<false>(cur, a.col_idx, a.kvstart);
-  Chunk b0 = take_chunk<false>(cur, a.col_idx, a.kvstart);
+  Chunk a0 = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
+  Chunk b0 = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
   if (a0.nv > 0) tile_issue(a0, b0, m0_a);
-  Chunk a1 = take_chunk<false>(cur, a.col_idx, a.kvstart);
-  Chunk b1 = take_chunk<false>(cur, a.col_idx, a.kvstart);
+  Chunk a1 = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
+  Chunk b1 = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
   vmem_wait_all();
   __syncthreads();
 
@@ -628,8 +630,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const DqArgs a) {
       if (b0.nv > 0) chunk(st, 1, b0.nv);
     }
     // The next tile's copies (issued after this tile's matrix work has been issued).
-    const Chunk an = take_chunk<false>(cur, a.col_idx, a.kvstart);
-    const Chunk bn = take_chunk<false>(cur, a.col_idx, a.kvstart);
+    const Chunk an = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
+    const Chunk bn = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
     if (a1.nv > 0) tile_issue(a1, b1, nx_m0);
     vmem_wait_all();
     __syncthreads();
@@ -687,7 +689,7 @@ hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, cons
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_permute_rows(p, K, base + L.kp, s)) != hipSuccess) return e;
   if ((e = launch_permute_rows(p, V, base + L.vp, s)) != hipSuccess) return e;
-  csr_bitmap_kernel<<<(unsigned)rows, 256, 0, s>>>(row_ptr, col_idx, L.nwords, bm);
+  csr_bitmap_kernel<<<(unsigned)rows, 256, 0, s>>>(row_ptr, col_idx, p.nkv, L.nwords, bm);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned cblocks = (unsigned)((cols + 255) / 256);
   csc_kernel<<<cblocks, 256, 0, s>>>(bm, p.nq, p.nkv, L.nwords, cols, false, col_cnt, nullptr,

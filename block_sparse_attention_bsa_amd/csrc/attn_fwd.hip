@@ -162,7 +162,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   cur.slot = kDense ? 0 : ld_ro(a.row_ptr + r);
   cur.end = kDense ? a.nkv : ld_ro(a.row_ptr + r + 1);
   cur.sub = 0;
-  cursor_load<kDense>(cur, a.col_idx, a.kvstart);
+  cursor_load<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
 
   const size_t kv_off = (size_t)bh * a.Npad * D;
   const uint16_t* const kbase = a.K + kv_off;
@@ -188,11 +188,11 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   // Pipeline: tile t (chunks a0, b0) is in LDS and tile t+1 (a1, b1) is copied into the other
   // stage while tile t is computed.
   const uint32_t m0_a = lds_addr(lds_a), m0_b = lds_addr(lds_b);
-  Chunk a0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-  Chunk b0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+  Chunk a0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
+  Chunk b0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
   if (a0.nv > 0) tile_issue(a0, b0, m0_a);
-  Chunk a1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-  Chunk b1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+  Chunk a1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
+  Chunk b1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
   if constexpr (TOK) {  // the block lists of this item's query rows (INT_MAX past the rows)
     for (int idx = t; idx < kAttnRows * a.tslots; idx += 256) {
       const int row = idx / a.tslots, slot = idx - row * a.tslots;
@@ -277,8 +277,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
       __builtin_amdgcn_s_setprio(0);
     }
     // The next tile's copies are issued while the score MFMAs execute.
-    const Chunk an = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
-    const Chunk bn = take_chunk<kDense>(cur, a.col_idx, a.kvstart);
+    const Chunk an = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
+    const Chunk bn = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
     if (a1.nv > 0) tile_issue(a1, b1, nx_m0);
 
     if (act) {
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(128) void attn_fwd_valu(
     const int32_t* __restrict__ qperm, const int32_t* __restrict__ qstart,
     const int32_t* __restrict__ kvperm, const int32_t* __restrict__ kvstart,
     const int32_t* __restrict__ items, int n_items, const float* __restrict__ scale, int H,
-    int N, int nq, T* __restrict__ O, float* __restrict__ lse) {
+    int N, int nq, int nkv, T* __restrict__ O, float* __restrict__ lse) {
   __shared__ float ks[32][D + 1];
   __shared__ float vs[32][D + 1];
   const int bh = blockIdx.y, item = blockIdx.x;
@@ -643,9 +643,9 @@ __global__ __launch_bounds__(128) void attn_fwd_valu(
   cur.slot = row_ptr[r];
   cur.end = row_ptr[r + 1];
   cur.sub = 0;
-  cursor_load<false>(cur, col_idx, kvstart);
+  cursor_load<false>(cur, col_idx, kvstart, nkv);
   while (true) {
-    const Chunk c = take_chunk<false>(cur, col_idx, kvstart);
+    const Chunk c = take_chunk<false>(cur, col_idx, kvstart, nkv);
     if (c.nv == 0) break;
     __syncthreads();
     for (int e = t; e < 32 * D; e += 128) {
@@ -700,7 +700,7 @@ hipError_t launch_valu(const bsa_plan& p, const void* Q, const void* K, const vo
   attn_fwd_valu<T, D><<<grid, 128, 0, s>>>(
       static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V), row_ptr,
       col_idx, p.qperm, p.qstart, p.kvperm, p.kvstart, p.items, p.n_items, p.scale, p.prob.H,
-      p.prob.N, p.nq, static_cast<T*>(O), lse);
+      p.prob.N, p.nq, p.nkv, static_cast<T*>(O), lse);
   return hipGetLastError();
 }
 

@@ -425,6 +425,8 @@ int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* pr
     return fail(BSA_EUNSUPPORTED, "bsa_select: %d kv blocks exceed the supported %d", plan->nkv,
                 kMaxSelectBlocks);
   const int64_t need_cols = (int64_t)plan->prob.B * plan->prob.H * plan->nq * plan->nkv;
+  if (need_cols > (int64_t)INT32_MAX)  // row_ptr and the scan carries are 32-bit
+    return fail(BSA_EUNSUPPORTED, "bsa_select: B * H * nq * nkv exceeds 2^31 - 1");
   if (col_cap < need_cols)
     return fail(BSA_ECAPACITY, "bsa_select: col_idx capacity %lld < %lld", (long long)col_cap,
                 (long long)need_cols);
@@ -492,6 +494,8 @@ int bsa_select_tokens(const bsa_plan* plan, const void* Q, const float* Kbar, in
   int rc = check_tokens(plan, k, "bsa_select_tokens");
   if (rc) return rc;
   const int64_t need_cols = (int64_t)plan->prob.B * plan->prob.H * plan->nq * plan->nkv;
+  if (need_cols > (int64_t)INT32_MAX)  // row_ptr and the scan carries are 32-bit
+    return fail(BSA_EUNSUPPORTED, "bsa_select_tokens: B * H * nq * nkv exceeds 2^31 - 1");
   if (col_cap < need_cols)
     return fail(BSA_ECAPACITY, "bsa_select_tokens: col_idx capacity %lld < %lld",
                 (long long)col_cap, (long long)need_cols);
@@ -549,6 +553,11 @@ int bsa_attn_bwd(const bsa_plan* plan, const void* Q, const void* K, const void*
     return fail(BSA_EINVAL, "bsa_attn_bwd: NULL argument");
   if (plan->prob.dtype != BSA_BF16 || plan->prob.d != 128)
     return fail(BSA_EUNSUPPORTED, "bsa_attn_bwd: bf16 with d = 128 only");
+  if ((int64_t)plan->prob.B * plan->prob.H * plan->nq * plan->nkv > (int64_t)INT32_MAX)
+    return fail(BSA_EUNSUPPORTED, "bsa_attn_bwd: B * H * nq * nkv exceeds 2^31 - 1 (32-bit CSC)");
+  if (plan->nkv > kMaxSelectBlocks)
+    return fail(BSA_EUNSUPPORTED, "bsa_attn_bwd: %d kv blocks exceed the supported %d",
+                plan->nkv, kMaxSelectBlocks);
   const size_t need = bwd_ws_layout(*plan).total;
   if (!ws || ws_bytes < need)
     return fail(BSA_ECAPACITY, "bsa_attn_bwd: workspace %zu < %zu bytes", ws_bytes, need);

@@ -9,9 +9,14 @@ struct Cursor {
   int slot, end, sub, base, size, J;  // position in the block list, current block and its tokens
 };
 
+// A CSR entry outside [0, nkv) is skipped, so that a bad caller-provided index never addresses
+// the plan's block table out of bounds.
 template <bool kDense>
 __device__ __forceinline__ void cursor_load(Cursor& c, const int32_t* __restrict__ col_idx,
-                                            const int32_t* __restrict__ kvstart) {
+                                            const int32_t* __restrict__ kvstart, int nkv) {
+  if constexpr (!kDense) {
+    while (c.slot < c.end && (uint32_t)ld_ro(col_idx + c.slot) >= (uint32_t)nkv) ++c.slot;
+  }
   if (c.slot < c.end) {
     c.J = kDense ? c.slot : ld_ro(col_idx + c.slot);
     c.base = ld_ro(kvstart + c.J);
@@ -31,7 +36,7 @@ struct Chunk {
 
 template <bool kDense>
 __device__ __forceinline__ Chunk take_chunk(Cursor& c, const int32_t* __restrict__ col_idx,
-                                            const int32_t* __restrict__ kvstart) {
+                                            const int32_t* __restrict__ kvstart, int nkv) {
   Chunk k;
   if (c.slot < c.end) {
     k.pos = c.base + 32 * c.sub;
@@ -42,7 +47,7 @@ __device__ __forceinline__ Chunk take_chunk(Cursor& c, const int32_t* __restrict
     if (k.last) {
       ++c.slot;
       c.sub = 0;
-      cursor_load<kDense>(c, col_idx, kvstart);
+      cursor_load<kDense>(c, col_idx, kvstart, nkv);
     }
   } else {
     k.pos = 0;

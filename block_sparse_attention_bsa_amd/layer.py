@@ -41,9 +41,47 @@ class BlockSparseAttention:
         self._ws_fwd = None
         self._ws_tok = None
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.shape = (B, H, p.N, d)
+
+    # -- argument checks (the C ABI sees only pointers) -----------------------------------------
+    def _act(self, name, t):
+        """A [B, H, N, d] activation of the plan's dtype, contiguous, on the layer's device."""
+        if t is None:
+            return t
+        if tuple(t.shape) != self.shape:
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {self.shape}")
+        if t.dtype != self.tdtype:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {self.tdtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous ([B, H, N, d], d fastest)")
+        if t.device != self._dev():
+            raise ValueError(f"{name}: on {t.device}, the layer is on {self._dev()}")
+        return t
+
+    def _i32(self, name, t, n=None):
+        if t is None:
+            return t
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != self._dev():
+            raise TypeError(f"{name}: must be a contiguous int32 tensor on {self._dev()}")
+        if n is not None and t.numel() < n:
+            raise ValueError(f"{name}: {t.numel()} entries, at least {n} needed")
+        return t
+
+    def _f32(self, name, t, shape):
+        if t is None:
+            return t
+        if (tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous()
+                or t.device != self._dev()):
+            raise TypeError(f"{name}: must be a contiguous float32 tensor of shape {tuple(shape)} "
+                            f"on {self._dev()}")
+        return t
+
+    def _dev(self):
+        return self.qbar.device
 
     # -- stages -----------------------------------------------------------------------------
     def pool(self, q, k, stream=None):
+        self._act("q", q), self._act("k", k)
         bsa_pool_qk(self.plan, q, k, self.qbar, self.kbar, stream)
 
     def score(self, norm=BSA_NORM_ROW, stream=None):
@@ -51,6 +89,7 @@ class BlockSparseAttention:
         return self.S
 
     def calibrate(self, q, k, stream=None):
+        self._act("q", q), self._act("k", k)
         if self._ws_calib is None:
             self._ws_calib = torch.empty(self.plan.ws_calib, dtype=torch.uint8, device=self.device)
         bsa_calibrate_mass(self.plan, q, k, self.S, self._ws_calib, self.plan.ws_calib, stream)
@@ -60,8 +99,10 @@ class BlockSparseAttention:
         """The dense step: exact block masses into self.S and the dense attention output."""
         if self._ws_calib is None:
             self._ws_calib = torch.empty(self.plan.ws_calib, dtype=torch.uint8, device=self.device)
+        self._act("q", q), self._act("k", k), self._act("v", v)
         if out is None:
             out = torch.empty_like(q)
+        self._act("out", out), self._f32("lse", lse, self.shape[:3])
         bsa_calibrate_mass_fwd(self.plan, q, k, v, self.S, out, lse, self._ws_calib,
                                self.plan.ws_calib, stream)
         return self.S, out
@@ -85,6 +126,7 @@ class BlockSparseAttention:
         """Per-token Local + TopK from Q and the pooled K (pool() first): returns sel
         [B, H, N, 1 + min(k, nkv - 1)] and fills row_ptr / col_idx with each query block's
         union."""
+        self._act("q", q)
         B, H, N = q.shape[:3]
         ns = 1 + min(int(k_best), self.plan.nkv - 1)
         sel = torch.empty((B, H, N, ns), dtype=torch.int32, device=self.device)
@@ -98,10 +140,14 @@ class BlockSparseAttention:
     def attention_tokens(self, q, k, v, sel, k_best, out=None, lse=None, with_lse=True,
                          stream=None):
         """Attention of every token over its own blocks (sel from select_tokens)."""
+        self._act("q", q), self._act("k", k), self._act("v", v)
+        ns = 1 + min(int(k_best), self.plan.nkv - 1)
+        self._i32("sel", sel, q.shape[0] * q.shape[1] * q.shape[2] * ns)
         if out is None:
             out = torch.empty_like(q)
         if lse is None and with_lse:
             lse = torch.empty(q.shape[:3], dtype=torch.float32, device=self.device)
+        self._act("out", out), self._f32("lse", lse, self.shape[:3])
         if self._ws_fwd is None and self.plan.ws_fwd > 0:
             self._ws_fwd = torch.empty(self.plan.ws_fwd, dtype=torch.uint8, device=self.device)
         bsa_attn_fwd_tokens(self.plan, q, k, v, self.row_ptr, self.col_idx, sel, k_best, out,
@@ -112,10 +158,13 @@ class BlockSparseAttention:
                   with_lse=True):
         """O (and the LSE, unless with_lse is False: then the output-only kernel runs and the
         returned lse is None)."""
+        self._act("q", q), self._act("k", k), self._act("v", v)
+        self._i32("row_ptr", row_ptr, self.rows + 1), self._i32("col_idx", col_idx)
         if out is None:
             out = torch.empty_like(q)
         if lse is None and with_lse:
             lse = torch.empty(q.shape[:3], dtype=torch.float32, device=self.device)
+        self._act("out", out), self._f32("lse", lse, self.shape[:3])
         if self._ws_fwd is None and self.plan.ws_fwd > 0:
             self._ws_fwd = torch.empty(self.plan.ws_fwd, dtype=torch.uint8, device=self.device)
         bsa_attn_fwd(self.plan, q, k, v, self.row_ptr if row_ptr is None else row_ptr,
@@ -124,6 +173,10 @@ class BlockSparseAttention:
         return out, lse
 
     def backward(self, q, k, v, o, do, lse, row_ptr=None, col_idx=None, stream=None):
+        for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+            self._act(name, t)
+        self._f32("lse", lse, self.shape[:3])
+        self._i32("row_ptr", row_ptr, self.rows + 1), self._i32("col_idx", col_idx)
         if self._ws_bwd is None:
             self._ws_bwd = torch.empty(self.plan.ws_bwd, dtype=torch.uint8, device=self.device)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)

@@ -190,6 +190,7 @@ int bsa_calibrate_mass_fwd(const bsa_plan* plan, const void* Q, const void* K, c
  * used is row_ptr[B*H*nq], left on the device; nothing is synchronised). counts (nullable,
  * [B*H*nq]) receives each row's final count; head_k (nullable, [B*H]) receives the per-head
  * minimum used (0 when min_k_mode is NONE). ws must hold the ws_select bytes of bsa_plan_info.
+ * BSA_EUNSUPPORTED when nkv > 8192 or B*H*nq*nkv exceeds 2^31 - 1 (row_ptr is 32-bit).
  * With BSA_POOL_HEAD a query block may receive no block at all (an empty row, as the VMoBA
  * referee report points out); attention then returns O = 0 and LSE = -inf for its queries.
  * BSA_POOL_LOCAL_TOPK is VMoBA's training-free "Local + TopK" (VMoBA review, referee report
@@ -225,8 +226,8 @@ int bsa_select_eg(const bsa_plan* plan, const float* S, const bsa_eg_params* par
  * relative) and fp32 accumulation, and never written to memory. row_ptr / col_idx (as
  * bsa_select) receive, per query block, the union of its tokens' lists, which
  * bsa_attn_fwd_tokens walks. ws >= the bytes bsa_tokens_ws reports (kbar's two bf16 terms plus
- * the union's bitmap and counts). k in [0, 24]; bf16, d = 128 and nkv <= 2048 only
- * (BSA_EUNSUPPORTED otherwise). */
+ * the union's bitmap and counts). k in [0, 24]; bf16, d = 128, nkv <= 2048 and
+ * B*H*nq*nkv <= 2^31 - 1 only (BSA_EUNSUPPORTED otherwise). */
 int bsa_tokens_ws(const bsa_plan* plan, size_t* ws_bytes);
 int bsa_select_tokens(const bsa_plan* plan, const void* Q, const float* Kbar, int32_t k,
                       int32_t* sel, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
@@ -249,8 +250,10 @@ int bsa_attn_fwd_tokens(const bsa_plan* plan, const void* Q, const void* K, cons
  * the PV product, and O is normalised by the sum of those rounded weights. With lse NULL the
  * fp32 row sums that only the LSE needs are not formed (the same O; a faster kernel for bf16,
  * d = 128).
- * The CSR must come from bsa_select for this plan (or be equivalent: indices
- * in [0, nkv), no duplicates within a row). ws (device, ws_bytes >= ws_fwd of bsa_plan_info;
+ * The CSR should come from bsa_select for this plan (or be equivalent: indices in [0, nkv),
+ * ascending or not, no duplicates within a row). The device cannot report an error, so an entry
+ * outside [0, nkv) is skipped (as if absent) rather than read; a duplicate counts its block's
+ * tokens twice. ws (device, ws_bytes >= ws_fwd of bsa_plan_info;
  * may be NULL when ws_fwd is 0) receives K and V copied into block order; BSA_ECAPACITY if it
  * is too small. */
 int bsa_attn_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
@@ -261,8 +264,10 @@ int bsa_attn_fwd(const bsa_plan* plan, const void* Q, const void* K, const void*
  * bsa_attn_fwd and the upstream gradient dO, writes dQ, dK, dV ([B, H, N, d], plan dtype):
  *   D_i = dO_i . O_i; P_ij = exp(sigma_h q_i . k_j - lse_i) on selected pairs;
  *   dV = P^T dO; dS = P * (dO V^T - D); dQ = sigma_h dS K; dK = sigma_h dS^T Q.
- * Tokens no selected pair touches get zero gradient. bf16, d = 128 only. ws must hold the
- * ws_bwd bytes of bsa_plan_info. No atomics: results are deterministic. */
+ * Tokens no selected pair touches get zero gradient. bf16, d = 128 only; BSA_EUNSUPPORTED when
+ * nkv > 8192 or B*H*nq*nkv exceeds 2^31 - 1 (32-bit column lists). The CSR as for bsa_attn_fwd
+ * (entries outside [0, nkv) are skipped). ws must hold the ws_bwd bytes of bsa_plan_info. No
+ * atomics: results are deterministic. */
 int bsa_attn_bwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
                  const void* O, const void* dO, const float* lse, const int32_t* row_ptr,
                  const int32_t* col_idx, void* dQ, void* dK, void* dV, void* ws,

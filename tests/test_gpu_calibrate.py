@@ -170,3 +170,58 @@ def test_calibrate_dense_output_full_size_sampled():
     log(f"dense step full size: O max-abs {err_o:.2e}, LSE max-abs {err_l:.2e} over "
         f"{len(rows)} sampled query blocks")
     assert err_o <= 1e-2 and err_l <= 1e-3
+
+
+def test_calibrate_full_shape_two_heads_and_ten_frozen_steps():
+    # The calibrate-then-reuse workload at its own 21 x 30 x 52 x 12 shape. The GPU computes the
+    # masses and the selection for every head; the oracle computes two whole heads (672 rows of
+    # exact masses over all 32 760 keys) and selects from its own masses. Then the GPU's CSR is
+    # frozen (LoSA abstract: the indices are reused for the remaining steps) and all ten drifted
+    # steps run on it, with O sampled per step on rows whose selection equals the oracle's.
+    import torch
+    w = CONFIGS[3]
+    x = make_inputs(w)
+    rng = np.random.default_rng(33)
+    heads = sorted(rng.choice(w.H, size=2, replace=False).tolist())
+    qb, kb = oracle.partition(w.grid, w.qpart), oracle.partition(w.grid, w.kvpart)
+    nq = len(qb)
+    rows = [(0, h, i) for h in heads for i in range(nq)]
+    layer, M, M_ref, _, _ = _calibrate(w, x, rows=rows)
+    err = max(float(np.abs(M[0, h] - M_ref[0, h]).max()) for h in heads)
+    log(f"full shape heads {heads}: masses max-abs {err:.2e} over {len(rows)} rows")
+    assert err <= 1e-5
+    layer.select(w.p)
+    torch.cuda.synchronize()
+    rp, ci = layer.csr_host()
+    rows_gpu = oracle.csr_rows(rp, ci)
+    ref_rows = {h: oracle.select_row(M_ref[:, h:h + 1], w.p) for h in heads}
+    same = []
+    for h in heads:
+        g = rows_gpu[h * nq:(h + 1) * nq]
+        exact, tol, bad = check_csr_rows(g, ref_rows[h], M_ref[0, h], w.p)
+        log(f"  head {h}: rows exact {exact} tolerated {tol} bad {len(bad)}")
+        assert not bad
+        same += [(h, i) for i in range(nq) if np.array_equal(g[i], ref_rows[h][i])]
+    # the oracle's own CSR for the checked heads (other heads' rows empty; they are not sampled)
+    all_ref = [np.zeros(0, np.int64)] * (w.H * nq)
+    for h in heads:
+        all_ref[h * nq:(h + 1) * nq] = ref_rows[h]
+    rp_ref, ci_ref = oracle.to_csr(all_ref)
+    frozen_rp, frozen_ci = layer.row_ptr.clone(), layer.col_idx.clone()
+    masters = {k: x[k + "32"].copy() for k in ("q", "k", "v")}
+    hs = x["head_scale"].astype(np.float64)
+    for step in range(1, w.drift_steps + 1):
+        xs = drift_step(w, masters, step)
+        q, k, v = (to_dev(xs[n]) for n in ("q", "k", "v"))
+        O, _ = layer.attention(q, k, v, row_ptr=frozen_rp, col_idx=frozen_ci)
+        torch.cuda.synchronize()
+        assert torch.equal(frozen_rp, layer.row_ptr) and torch.equal(frozen_ci, layer.col_idx)
+        pick = [same[j] for j in rng.choice(len(same), size=4, replace=False)]
+        sample = [(0, h, i) for h, i in pick]
+        O_ref, _ = oracle.attention_fwd(*(to_f64(xs[n]) for n in ("q", "k", "v")), hs, qb, kb,
+                                        rp_ref, ci_ref, rows=sample)
+        Og = dev_to_f64(O)
+        worst = max(float(np.abs(Og[0, h, qb[i]] - O_ref[0, h, qb[i]]).max())
+                    for _, h, i in sample)
+        log(f"  step {step}: O max-abs {worst:.2e} over {len(sample)} q-blocks")
+        assert worst <= 1e-2
