@@ -49,7 +49,11 @@ reasoning in the design notes):
     blocks (score desc, index asc); fewer when fewer remain;
   * [VMoBA] per-token Local + TopK (queries score the block means token by token, "What carries
     the argument"): query token i keeps the kv block holding i plus the k others with the highest
-    gate sigma_h q_i . kbar_J (gate desc, index asc), and attends over those blocks' tokens.
+    gate sigma_h q_i . kbar_J (gate desc, index asc), and attends over those blocks' tokens;
+  * [VMoBA] per-token global threshold selection: the token gates of a head are normalised by one
+    softmax over the head's whole N x nkv matrix (each token counts once, the token-level form
+    of the |I|-weighted block pool) and the head keeps the shortest prefix, in (weight desc,
+    pair index asc) order, reaching tau; no block is forced per token, so a token can keep none.
 """
 from __future__ import annotations
 
@@ -63,6 +67,7 @@ __all__ = [
     "exact_mass", "exact_mass_row", "select_topp", "select_row", "head_min_k",
     "select_hybrid", "select_head", "head_entropy", "select_group", "select_eg",
     "local_blocks", "select_local_topk", "token_gates", "select_tokens", "attention_tokens",
+    "select_tokens_global", "attention_token_sets",
     "to_csr",
     "csr_rows", "attention_rows", "attention_fwd",
     "attention_bwd", "row_backward", "density",
@@ -369,6 +374,51 @@ def select_tokens(G: np.ndarray, k: int, kvblocks) -> np.ndarray:
                 order = np.lexsort((others, -np.asarray(G[b, h, i], np.float64)[others]))
                 out[b, h, i] = np.sort(np.concatenate([[own[i]], others[order[:kk]]]))
     return out
+
+
+def select_tokens_global(G: np.ndarray, tau: float) -> List[np.ndarray]:
+    """[VMoBA] global selection at token granularity ("What carries the argument": global
+    selection pools scores across all queries in a head; referee report major comment 1: Eq. 3
+    takes the top entries of the whole query-by-block matrix and Eq. 4 the smallest count k'
+    whose cumulative normalised similarity reaches tau; a query may keep no block at all).
+    Per head, every (query token i, kv block J) gate G[b, h, i, J] is normalised by one softmax
+    over the head's whole N x nkv gate matrix, the pairs are ranked by (weight desc, pair index
+    i * nkv + J asc), and the shortest prefix whose cumulative weight reaches tau is kept (the
+    prefix rule of select_topp). Returns, in (b, h, i) order, each token's kept blocks ascending
+    (an empty array for a token that keeps none)."""
+    B, H, N, nkv = G.shape
+    out: List[np.ndarray] = []
+    for b in range(B):
+        for h in range(H):
+            g = np.asarray(G[b, h], np.float64).reshape(-1)
+            w = np.exp(g - g.max())
+            w /= w.sum()
+            pairs = select_topp(w, tau)            # ascending pair indices
+            tok, J = np.divmod(pairs, nkv)
+            bounds = np.searchsorted(tok, np.arange(N + 1))
+            out.extend(J[bounds[i]:bounds[i + 1]] for i in range(N))
+    return out
+
+
+def attention_token_sets(Q, K, V, head_scale, sets: Sequence[np.ndarray], kvblocks,
+                         tokens: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """O[b, h, i] and LSE[b, h, i] of each query token over the tokens of its own block set
+    sets[(b * H + h) * N + i] (any length, possibly empty: then O = 0, LSE = -inf), for every
+    token or only the listed (b, h, i); other entries stay NaN."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    B, H, N, _ = Q.shape
+    O = np.full((B, H, N, V.shape[3]), np.nan)
+    LSE = np.full((B, H, N), np.nan)
+    if tokens is None:
+        tokens = [(b, h, i) for b in range(B) for h in range(H) for i in range(N)]
+    for b, h, i in tokens:
+        keys = _selected_keys(np.asarray(sets[(b * H + h) * N + i], np.int64), kvblocks)
+        o, lse = attention_rows(Q[b, h, i:i + 1], K[b, h], V[b, h], float(head_scale[h]), keys)
+        O[b, h, i] = o[0]
+        LSE[b, h, i] = lse[0]
+    return O, LSE
 
 
 def attention_tokens(Q, K, V, head_scale, sel: np.ndarray, kvblocks,
