@@ -47,6 +47,9 @@ def parse():
                          "per-token selection, attention with LSE), e.g. under a profiler")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
+    ap.add_argument("--score-path", choices=("fused", "unfused"), default="unfused",
+                    help="ROW-pool workloads: scores and selection in one kernel "
+                         "(bsa_score_select) or bsa_score then bsa_select")
     return ap.parse_args()
 
 
@@ -160,6 +163,29 @@ def token_topk(w, L, q, k, v, out, tm, ks=(2, 6, 18), calls=3):
                         "attn_tflops_token": f_tok / (attn_ms * 1e-3) / 1e12,
                         "attn_tflops_executed": f_exec / (attn_ms * 1e-3) / 1e12}
     return res
+
+
+def score_paths(w, L, q, k, mink, tm, calls=10):
+    """Scores and selection as one kernel (bsa_score_select: S never goes through memory, except
+    for the per-head minimum's top-up) against bsa_score followed by bsa_select, on the same
+    pooled inputs; both give the same CSR."""
+    import torch
+    L.pool(q, k)
+    for _ in range(2):
+        L.score_select(w.p, min_k_mode=mink)
+        L.score(0)
+        L.select(w.p, 0, mink)
+    for _ in range(calls):
+        with tm("sp_fused"):
+            L.score_select(w.p, min_k_mode=mink)
+        with tm("sp_score"):
+            L.score(0)
+        with tm("sp_select"):
+            L.select(w.p, 0, mink)
+    torch.cuda.synchronize()
+    f, a, b = tm.mean_ms("sp_fused"), tm.mean_ms("sp_score"), tm.mean_ms("sp_select")
+    return {"fused_ms": round(f, 4), "score_ms": round(a, 4), "select_ms": round(b, 4),
+            "unfused_ms": round(a + b, 4), "speedup": round((a + b) / f, 2)}
 
 
 def csr_rows(row_ptr, col_idx):
@@ -367,10 +393,14 @@ def main():
         for L, tag in zip(layers, tags):
             with tm("pool"):
                 L.pool(q, k)
-            with tm("score"):
-                L.score(1 if head else 0)
-            with tm("select"):
-                L.select(w.p, 1 if head else 0, mink)
+            if head or args.score_path == "unfused":
+                with tm("score"):
+                    L.score(1 if head else 0)
+                with tm("select"):
+                    L.select(w.p, 1 if head else 0, mink)
+            else:
+                with tm("score_select"):
+                    L.score_select(w.p, min_k_mode=mink)
             with tm("attn"), (tm("attn" + tag) if tag else nullcontext()):
                 L.attention(q, k, v, out=out, lse=lse, with_lse=w.backward)
             if w.backward:
@@ -474,6 +504,8 @@ def main():
         res["attn_with_lse"] = {"ms": round(tm.mean_ms("attn_with_lse"), 4),
                                 "tflops": attn_flops / (tm.mean_ms("attn_with_lse") * 1e-3)
                                 / 1e12}
+    if w.mode in ("row", "hybrid") and not args.no_extras:
+        res["score_paths"] = score_paths(w, layers[0], q, k, mink, tm)
     if w.mode in ("row", "hybrid") and w.dtype == "bf16" and not args.no_extras:
         # other selections on the same inputs (they replace the layer's CSR: keep them last)
         res["entropy_routed"] = entropy_routed(w, layers[0], q, k, v, out, tm)

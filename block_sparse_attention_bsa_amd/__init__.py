@@ -30,7 +30,9 @@ BSA_MINK_NONE, BSA_MINK_FIXED, BSA_MINK_WEIGHTED_MEAN = 0, 1, 2
 
 EXPORTED = ("bsa_partition_build", "bsa_plan_create", "bsa_plan_destroy", "bsa_plan_info",
             "bsa_plan_blocks", "bsa_pool", "bsa_pool_qk", "bsa_score", "bsa_calibrate_mass",
-            "bsa_calibrate_mass_fwd", "bsa_select", "bsa_select_eg", "bsa_tokens_ws",
+            "bsa_calibrate_mass_fwd", "bsa_select", "bsa_score_select",
+            "bsa_select_eg",
+            "bsa_tokens_ws",
             "bsa_select_tokens", "bsa_attn_fwd", "bsa_attn_fwd_tokens", "bsa_attn_bwd",
             "bsa_last_error")
 
@@ -98,6 +100,8 @@ def lib():
         "bsa_calibrate_mass": [P, P, P, P, P, SZ, P],
         "bsa_calibrate_mass_fwd": [P, P, P, P, P, P, P, P, SZ, P],
         "bsa_select": [P, P, ctypes.POINTER(SelectParams), P, P, I64, P, P, P, SZ, P],
+        "bsa_score_select": [P, P, P, ctypes.POINTER(SelectParams), P, P, P, I64, P, P, P, SZ,
+                             P],
         "bsa_select_eg": [P, P, ctypes.POINTER(EgParams), P, P, I64, P, P, P, P, SZ, P],
         "bsa_tokens_ws": [P, ctypes.POINTER(SZ)],
         "bsa_select_tokens": [P, P, P, I32, P, P, P, I64, P, SZ, P],
@@ -244,6 +248,16 @@ def bsa_select(plan: Plan, S, p: float, pool: int, min_k_mode: int, fixed_k: int
     _check(lib().bsa_select(plan.handle, _ptr(S), ctypes.byref(prm), _ptr(row_ptr),
                             _ptr(col_idx), int(col_cap), _ptr(counts), _ptr(head_k), _ptr(ws),
                             ws_bytes, _stream(stream)))
+
+
+def bsa_score_select(plan: Plan, Qbar, Kbar, p: float, min_k_mode: int, fixed_k: int, S,
+                     row_ptr, col_idx, col_cap: int, counts, head_k, ws, ws_bytes: int,
+                     stream=None):
+    prm = SelectParams(float(p), BSA_POOL_ROW, int(min_k_mode), int(fixed_k))
+    _check(lib().bsa_score_select(plan.handle, _ptr(Qbar), _ptr(Kbar), ctypes.byref(prm),
+                                  _ptr(S), _ptr(row_ptr), _ptr(col_idx), int(col_cap),
+                                  _ptr(counts), _ptr(head_k), _ptr(ws), ws_bytes,
+                                  _stream(stream)))
 
 
 def bsa_select_eg(plan: Plan, S, p: float, theta: float, group_size: int, row_ptr, col_idx,

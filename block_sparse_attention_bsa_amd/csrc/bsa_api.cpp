@@ -124,8 +124,10 @@ SelectWs select_ws_layout(const bsa_plan& p) {
   w.base_counts = align_up(rows * w.nwords * 4);
   w.head_k = w.base_counts + align_up(rows * 4);
   const size_t BH = (size_t)p.prob.B * p.prob.H;
+  w.partial = w.head_k + align_up(BH * 4);
+  w.core = w.partial + align_up((rows + 1023) / 1024 * 4);
   w.eg_nrchunk = (int)(((size_t)p.prob.H * p.nq + kEgRowChunk - 1) / kEgRowChunk);
-  w.eg_rowent = w.head_k + align_up(BH * 4);
+  w.eg_rowent = w.core;
   w.eg_route = w.eg_rowent + align_up(rows * 8);
   w.eg_members = w.eg_route + align_up(BH * 4);
   w.eg_groups = w.eg_members + align_up(BH * 4);
@@ -144,7 +146,8 @@ TokWs tok_ws_layout(const bsa_plan& p) {
   w.klo = align_up(kb);
   w.bitmap = w.klo + align_up(kb);
   w.counts = w.bitmap + align_up(rows * w.nwords * 4);
-  w.total = w.counts + align_up(rows * 4);
+  w.partial = w.counts + align_up(rows * 4);
+  w.total = w.partial + align_up((rows + 1023) / 1024 * 4);
   return w;
 }
 
@@ -401,43 +404,80 @@ int bsa_calibrate_mass_fwd(const bsa_plan* plan, const void* Q, const void* K, c
                        "bsa_calibrate_mass_fwd");
 }
 
-int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* prm,
-               int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
-               int32_t* head_k, void* ws, size_t ws_bytes, void* stream) {
-  if (!plan || !S || !prm || !row_ptr || !col_idx)
-    return fail(BSA_EINVAL, "bsa_select: NULL argument");
+}  // extern "C"
+
+// Argument checks shared by the selection entry points (`who` names the caller).
+static int check_select(const bsa_plan* plan, const float* S, const bsa_select_params* prm,
+                        const int32_t* row_ptr, const int32_t* col_idx, int64_t col_cap,
+                        const char* who, bool need_S = true) {
+  if (!plan || (need_S && !S) || !prm || !row_ptr || !col_idx)
+    return fail(BSA_EINVAL, "%s: NULL argument", who);
   if (prm->pool != BSA_POOL_ROW && prm->pool != BSA_POOL_HEAD &&
       prm->pool != BSA_POOL_LOCAL_TOPK)
-    return fail(BSA_EINVAL, "bsa_select: unknown pool %d", prm->pool);
+    return fail(BSA_EINVAL, "%s: unknown pool %d", who, prm->pool);
   if (prm->pool != BSA_POOL_LOCAL_TOPK && !(prm->p > 0.0 && prm->p <= 1.0))
-    return fail(BSA_EINVAL, "bsa_select: p must lie in (0, 1]");
+    return fail(BSA_EINVAL, "%s: p must lie in (0, 1]", who);
   if (prm->pool == BSA_POOL_LOCAL_TOPK && (prm->fixed_k < 0 || prm->min_k_mode != BSA_MINK_NONE))
-    return fail(BSA_EINVAL, "bsa_select: LOCAL_TOPK takes fixed_k >= 0 and no minimum count");
+    return fail(BSA_EINVAL, "%s: LOCAL_TOPK takes fixed_k >= 0 and no minimum count", who);
   if (prm->min_k_mode < BSA_MINK_NONE || prm->min_k_mode > BSA_MINK_WEIGHTED_MEAN)
-    return fail(BSA_EINVAL, "bsa_select: unknown min_k_mode %d", prm->min_k_mode);
+    return fail(BSA_EINVAL, "%s: unknown min_k_mode %d", who, prm->min_k_mode);
   if (prm->min_k_mode == BSA_MINK_FIXED && prm->fixed_k < 0)
-    return fail(BSA_EINVAL, "bsa_select: fixed_k must be >= 0");
+    return fail(BSA_EINVAL, "%s: fixed_k must be >= 0", who);
   if (prm->pool == BSA_POOL_LOCAL_TOPK && plan->nkv > 2048)
-    return fail(BSA_EUNSUPPORTED, "bsa_select: LOCAL_TOPK supports up to 2048 kv blocks");
+    return fail(BSA_EUNSUPPORTED, "%s: LOCAL_TOPK supports up to 2048 kv blocks", who);
   if (prm->pool == BSA_POOL_HEAD && prm->min_k_mode != BSA_MINK_NONE)
-    return fail(BSA_EUNSUPPORTED, "bsa_select: a minimum count applies to the ROW pool only");
+    return fail(BSA_EUNSUPPORTED, "%s: a minimum count applies to the ROW pool only", who);
   if (plan->nkv > kMaxSelectBlocks)
-    return fail(BSA_EUNSUPPORTED, "bsa_select: %d kv blocks exceed the supported %d", plan->nkv,
+    return fail(BSA_EUNSUPPORTED, "%s: %d kv blocks exceed the supported %d", who, plan->nkv,
                 kMaxSelectBlocks);
   const int64_t need_cols = (int64_t)plan->prob.B * plan->prob.H * plan->nq * plan->nkv;
   if (need_cols > (int64_t)INT32_MAX)  // row_ptr and the scan carries are 32-bit
-    return fail(BSA_EUNSUPPORTED, "bsa_select: B * H * nq * nkv exceeds 2^31 - 1");
+    return fail(BSA_EUNSUPPORTED, "%s: B * H * nq * nkv exceeds 2^31 - 1", who);
   if (col_cap < need_cols)
-    return fail(BSA_ECAPACITY, "bsa_select: col_idx capacity %lld < %lld", (long long)col_cap,
+    return fail(BSA_ECAPACITY, "%s: col_idx capacity %lld < %lld", who, (long long)col_cap,
                 (long long)need_cols);
+  return BSA_OK;
+}
+
+extern "C" {
+
+int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* prm,
+               int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
+               int32_t* head_k, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_select(plan, S, prm, row_ptr, col_idx, col_cap, "bsa_select");
+  if (rc) return rc;
   const size_t need = select_ws_layout(*plan).total;
   if (!ws || ws_bytes < need)
     return fail(BSA_ECAPACITY, "bsa_select: workspace %zu < %zu bytes", ws_bytes, need);
-  int rc = check_device(plan);
+  rc = check_device(plan);
   if (rc) return rc;
   return launch_status(launch_select(*plan, S, *prm, row_ptr, col_idx, counts, head_k, ws,
                                      (hipStream_t)stream),
                        "bsa_select");
+}
+
+int bsa_score_select(const bsa_plan* plan, const float* Qbar, const float* Kbar,
+                     const bsa_select_params* prm, float* S, int32_t* row_ptr, int32_t* col_idx,
+                     int64_t col_cap, int32_t* counts, int32_t* head_k, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!Qbar || !Kbar) return fail(BSA_EINVAL, "bsa_score_select: NULL argument");
+  int rc = check_select(plan, S, prm, row_ptr, col_idx, col_cap, "bsa_score_select", false);
+  if (rc) return rc;
+  if (prm->pool != BSA_POOL_ROW)
+    return fail(BSA_EUNSUPPORTED, "bsa_score_select: the ROW pool only (bsa_score then "
+                "bsa_select for the others)");
+  if (plan->nkv > kWaveRowMaxBlocks)
+    return fail(BSA_EUNSUPPORTED, "bsa_score_select: more than %d kv blocks", kWaveRowMaxBlocks);
+  if (prm->min_k_mode != BSA_MINK_NONE && !S)
+    return fail(BSA_EINVAL, "bsa_score_select: a minimum count needs S (its top-up reads it)");
+  const size_t need = select_ws_layout(*plan).total;
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ECAPACITY, "bsa_score_select: workspace %zu < %zu bytes", ws_bytes, need);
+  rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_score_select_csr(*plan, Qbar, Kbar, *prm, S, row_ptr, col_idx,
+                                               counts, head_k, ws, (hipStream_t)stream),
+                       "bsa_score_select");
 }
 
 int bsa_select_eg(const bsa_plan* plan, const float* S, const bsa_eg_params* prm,

@@ -12,6 +12,9 @@
 // Largest kv-block count a row selection supports: one bitmap word per thread of a 256-thread
 // workgroup in the CSR emit pass.
 constexpr int kMaxSelectBlocks = 8192;
+// Largest kv-block count of the one-wavefront-per-row kernels (the row held in registers) and of
+// the fused score-and-select kernel.
+constexpr int kWaveRowMaxBlocks = 2048;
 // Query rows one attention workgroup owns (4 wavefronts x 32 rows).
 constexpr int kAttnRows = 128;
 
@@ -53,7 +56,8 @@ constexpr size_t kEgHistBytes = 256 * 4 + 256 * 8;
 
 // Workspace layouts (byte offsets), derived from the plan.
 struct SelectWs {
-  size_t bitmap, base_counts, head_k;
+  size_t bitmap, base_counts, head_k, partial;  // partial: 1024-row chunk totals of the scan
+  size_t core;  // bytes bsa_select itself uses (bitmap, counts, per-head minimum, scan totals)
   // bsa_select_eg: per row its entropy (fp64); per head the routing flag and its group's member
   // slot; per group (at most B*H groups) the radix state, the histogram and the boundary-class
   // count of each row chunk
@@ -91,7 +95,7 @@ constexpr int kPermPad = 128;
 // token.
 constexpr int kMaxTokenK = 24;
 struct TokWs {
-  size_t khi, klo, bitmap, counts, total;
+  size_t khi, klo, bitmap, counts, partial, total;
   int nwords;
 };
 TokWs tok_ws_layout(const bsa_plan& p);
@@ -107,6 +111,15 @@ hipError_t launch_pool_qk(const bsa_plan& p, const void* Q, float* Qbar, const v
                           float* Kbar, hipStream_t s);
 hipError_t launch_score(const bsa_plan& p, const float* Qbar, const float* Kbar, int norm,
                         float* S, hipStream_t s);
+// Fused score and ROW-pool selection (nkv <= 2048): the marking pass of bsa_select computed in
+// the scoring kernel (S written only when not NULL), then the rest of bsa_select.
+hipError_t launch_score_select(const bsa_plan& p, const float* Qbar, const float* Kbar, float* S,
+                               unsigned long long target, bool all, int nwords,
+                               uint32_t* bitmap, int32_t* base_counts, hipStream_t s);
+hipError_t launch_score_select_csr(const bsa_plan& p, const float* Qbar, const float* Kbar,
+                                   const bsa_select_params& prm, float* S, int32_t* row_ptr,
+                                   int32_t* col_idx, int32_t* counts, int32_t* head_k, void* ws,
+                                   hipStream_t s);
 hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_params& prm,
                          int32_t* row_ptr, int32_t* col_idx, int32_t* counts, int32_t* head_k,
                          void* ws, hipStream_t s);

@@ -21,26 +21,14 @@
 #include <climits>
 
 #include <array>
+#include <type_traits>
 #include <utility>
 
 #include "bsa_internal.h"
 #include "device_common.h"
+#include "row_select.h"
 
 namespace {
-
-constexpr double kFix = 72057594037927936.0;  // 2^56
-
-__device__ __forceinline__ uint32_t sel_key(float s) {
-  const uint32_t k = __float_as_uint(s);
-  return (k & 0x80000000u) ? 0u : k;  // negative values rank below every non-negative one
-}
-
-__device__ __forceinline__ unsigned long long sel_fix(float s) {
-  double x = (double)s * kFix;
-  if (!(x > 0.0)) return 0ull;  // also NaN
-  if (x > kFix) x = kFix;
-  return (unsigned long long)rint(x);
-}
 
 struct RadixShared {
   unsigned int cnt[256];
@@ -316,42 +304,64 @@ __global__ __launch_bounds__(256) void topup_kernel(const float* __restrict__ S,
   mark_pool<256>(row, 1, nkv, nwords, bitmap + r * nwords, res, nullptr);
 }
 
-// row_ptr = exclusive scan of the final counts (one workgroup, any number of rows).
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ base_counts,
-                                                    const int32_t* __restrict__ head_k,
-                                                    bool use_min_k, int64_t rows, int nq,
-                                                    int32_t* __restrict__ row_ptr,
-                                                    int32_t* __restrict__ counts_out) {
+// row_ptr = exclusive scan of the final counts, in two passes over 1024-row chunks: the first
+// scans each chunk locally and records its total, the second adds the totals of the chunks
+// before it (summed by each workgroup from the totals array).
+__device__ __forceinline__ int final_count(const int32_t* __restrict__ base_counts,
+                                           const int32_t* __restrict__ head_k, bool use_min_k,
+                                           int64_t r, int nq) {
+  const int f = base_counts[r];
+  return use_min_k ? max(f, head_k[r / nq]) : f;
+}
+
+__global__ __launch_bounds__(1024) void scan_local_kernel(const int32_t* __restrict__ base_counts,
+                                                          const int32_t* __restrict__ head_k,
+                                                          bool use_min_k, int64_t rows, int nq,
+                                                          int32_t* __restrict__ row_ptr,
+                                                          int32_t* __restrict__ counts_out,
+                                                          int32_t* __restrict__ partial) {
   __shared__ int wtot[16];
-  __shared__ int carry_s;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  if (t == 0) {
-    carry_s = 0;
-    row_ptr[0] = 0;
-  }
+  const int64_t r = (int64_t)blockIdx.x * 1024 + t;
+  const int f = r < rows ? final_count(base_counts, head_k, use_min_k, r, nq) : 0;
+  const int incl = wave_incl_scan_i32(f);
+  if (lane == 63) wtot[wave] = incl;
   __syncthreads();
-  for (int64_t base = 0; base < rows; base += 1024) {
-    const int64_t r = base + t;
-    int f = 0;
-    if (r < rows) {
-      f = base_counts[r];
-      if (use_min_k) f = max(f, head_k[r / nq]);
-      if (counts_out) counts_out[r] = f;
-    }
-    const int incl = wave_incl_scan_i32(f);
-    if (lane == 63) wtot[wave] = incl;
-    __syncthreads();
-    int before = carry_s;
-    for (int w = 0; w < wave; ++w) before += wtot[w];
-    if (r < rows) row_ptr[r + 1] = before + incl;
-    __syncthreads();
-    if (t == 0) {
-      int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += wtot[w];
-      carry_s += tot;
-    }
-    __syncthreads();
+  int pos = incl;
+  for (int w = 0; w < wave; ++w) pos += wtot[w];
+  if (r < rows) {
+    row_ptr[r + 1] = pos;
+    if (counts_out) counts_out[r] = f;
   }
+  if (t == 1023) partial[blockIdx.x] = pos;
+}
+
+__global__ __launch_bounds__(1024) void scan_add_kernel(int64_t rows,
+                                                        const int32_t* __restrict__ partial,
+                                                        int32_t* __restrict__ row_ptr) {
+  __shared__ int wtot[16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int off = 0;
+  for (int b = t; b < (int)blockIdx.x; b += 1024) off += partial[b];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) off += __shfl_xor(off, d, 64);
+  if (lane == 0) wtot[wave] = off;
+  __syncthreads();
+  off = 0;
+  for (int w = 0; w < 16; ++w) off += wtot[w];
+  const int64_t r = (int64_t)blockIdx.x * 1024 + t;
+  if (r < rows) row_ptr[r + 1] += off;
+  if (blockIdx.x == 0 && t == 0) row_ptr[0] = 0;
+}
+
+hipError_t launch_scan(const int32_t* base_counts, const int32_t* head_k, bool use_min_k,
+                       int64_t rows, int nq, int32_t* row_ptr, int32_t* counts_out,
+                       int32_t* partial, hipStream_t s) {
+  const unsigned nb = (unsigned)((rows + 1023) / 1024);
+  scan_local_kernel<<<nb, 1024, 0, s>>>(base_counts, head_k, use_min_k, rows, nq, row_ptr,
+                                        counts_out, partial);
+  scan_add_kernel<<<nb, 1024, 0, s>>>(rows, partial, row_ptr);
+  return hipGetLastError();
 }
 
 // Expand each row's bitmap into ascending kv-block indices at row_ptr[r].
@@ -380,139 +390,6 @@ __global__ __launch_bounds__(256) void emit_kernel(const uint32_t* __restrict__ 
 
 
 // ------------------------------------------------------------------ one wavefront per row
-
-// ROW-pool selection for rows of at most 64 * VPL candidates (VPL = 16 or 32): one wavefront per
-// row (four rows per workgroup), the row held in registers (value j = lane + 64 i), a wave-private
-// LDS histogram per radix pass, and no workgroup barrier at all. Same rule, same exact 2^-56 sums
-// and the same tie order as radix_select: results are identical.
-constexpr int kWaveRowMax = 2048;
-
-struct WaveHist {
-  unsigned int cnt[256];
-  unsigned long long sum[256];
-};
-
-// by_count: target is a count (top-k); else a 2^-56 fixed-point sum. Returns the chosen flags in
-// `sel` (value i of this lane) and the selected count.
-template <int kVpl>
-__device__ uint32_t wave_select(const float (&v)[kVpl], int n, unsigned long long target,
-                                bool by_count, bool all, WaveHist& h, bool (&sel)[kVpl]) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[kVpl];
-#pragma unroll
-  for (int i = 0; i < kVpl; ++i) key[i] = (lane + 64 * i < n) ? sel_key(v[i]) : 0u;
-  if (all) {
-#pragma unroll
-    for (int i = 0; i < kVpl; ++i) sel[i] = lane + 64 * i < n;
-    return (uint32_t)n;
-  }
-  uint32_t prefix = 0, mask = 0, eq_cnt = 0;
-  unsigned long long above_sum = 0;
-  uint32_t above_cnt = 0;
-  bool every = false;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      h.cnt[4 * lane + k] = 0u;
-      h.sum[4 * lane + k] = 0ull;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int i = 0; i < kVpl; ++i) {
-      if (lane + 64 * i < n && (key[i] & mask) == prefix) {
-        const uint32_t b = (key[i] >> shift) & 255u;
-        atomicAdd(&h.cnt[b], 1u);
-        if (!by_count) atomicAdd(&h.sum[b], sel_fix(v[i]));
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // Bins in descending order: lane l holds bins 255 - 4l - k (k = 0..3).
-    unsigned long long lsum = 0, lcnt = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      lsum += h.sum[255 - 4 * lane - k];
-      lcnt += h.cnt[255 - 4 * lane - k];
-    }
-    const unsigned long long isum = wave_incl_scan_u64(lsum);
-    const unsigned long long icnt = wave_incl_scan_u64(lcnt);
-    unsigned long long asum = above_sum + (isum - lsum);
-    unsigned long long acnt = above_cnt + (icnt - lcnt);
-    int my_bin = -1;
-    unsigned long long my_asum = 0, my_acnt = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int b = 255 - 4 * lane - k;
-      const unsigned long long cur = by_count ? acnt : asum;
-      const unsigned long long mb = by_count ? (unsigned long long)h.cnt[b] : h.sum[b];
-      if (my_bin < 0 && cur < target && cur + mb >= target) {
-        my_bin = b;
-        my_asum = asum;
-        my_acnt = acnt;
-      }
-      asum += h.sum[b];
-      acnt += h.cnt[b];
-    }
-    const unsigned long long found = __ballot(my_bin >= 0);
-    if (found == 0) {  // the target is never reached: keep every candidate
-      every = true;
-      break;
-    }
-    const int src = __ffsll((long long)found) - 1;
-    const int b = __shfl(my_bin, src, 64);
-    above_sum = ((unsigned long long)(uint32_t)__shfl((int)(my_asum >> 32), src, 64) << 32) |
-                (uint32_t)__shfl((int)(uint32_t)my_asum, src, 64);
-    above_cnt = (uint32_t)__shfl((int)my_acnt, src, 64);
-    prefix |= (uint32_t)b << shift;
-    mask |= 255u << shift;
-    eq_cnt = h.cnt[b];
-    __builtin_amdgcn_wave_barrier();
-    if (eq_cnt == 1) break;
-  }
-  if (every) {
-#pragma unroll
-    for (int i = 0; i < kVpl; ++i) sel[i] = lane + 64 * i < n;
-    return (uint32_t)n;
-  }
-  uint32_t m;
-  if (by_count) {
-    m = (uint32_t)(target - above_cnt);
-  } else if (eq_cnt == 1) {
-    m = 1;
-  } else {
-    const unsigned long long vfix = sel_fix(__uint_as_float(prefix));
-    m = (uint32_t)((target - above_sum + vfix - 1) / vfix);
-  }
-  if (m > eq_cnt) m = eq_cnt;
-  // Everything strictly above the boundary class, plus its m lowest-index members.
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < kVpl; ++i) {
-    const bool valid = lane + 64 * i < n;
-    const uint32_t k = key[i] & mask;
-    const bool eq = valid && k == prefix;
-    const unsigned long long bal = __ballot(eq);
-    const uint32_t rank = taken + __popcll(bal & ((1ull << lane) - 1ull));
-    sel[i] = valid && (k > prefix || (eq && rank < m));
-    taken += __popcll(bal);
-  }
-  return above_cnt + m;
-}
-
-// Bitmap words of one row from per-value flags (value j = lane + 64 i): words 2i and 2i + 1.
-template <int kVpl>
-__device__ __forceinline__ void write_row_bits(const bool (&sel)[kVpl], int nwords,
-                                               uint32_t* __restrict__ words) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < kVpl; ++i) {
-    const unsigned long long bal = __ballot(sel[i]);
-    const int w = 2 * i + lane;
-    if (lane < 2 && w < nwords) words[w] = (uint32_t)(bal >> (32 * lane));
-  }
-}
 
 template <int kVpl>
 __global__ __launch_bounds__(256) void mark_row_wave_kernel(const float* __restrict__ S,
@@ -1253,12 +1130,11 @@ static hipError_t mark_rows(const bsa_plan& p, const float* S, unsigned long lon
                             const int32_t* skip_head, hipStream_t s) {
   const int64_t rows = (int64_t)p.prob.B * p.prob.H * p.nq;
   const unsigned wgrid = (unsigned)((rows + 3) / 4);
-  if (p.nkv <= 1024)
-    mark_row_wave_kernel<16><<<wgrid, 256, 0, s>>>(S, rows, p.nkv, L.nwords, target, all, bitmap,
-                                                   base_counts, p.nq, skip_head);
-  else if (p.nkv <= kWaveRowMax)
-    mark_row_wave_kernel<32><<<wgrid, 256, 0, s>>>(S, rows, p.nkv, L.nwords, target, all, bitmap,
-                                                   base_counts, p.nq, skip_head);
+  if (p.nkv <= kWaveRowMax)
+    with_vpl(p.nkv, [&](auto vpl) {
+      mark_row_wave_kernel<decltype(vpl)::value><<<wgrid, 256, 0, s>>>(
+          S, rows, p.nkv, L.nwords, target, all, bitmap, base_counts, p.nq, skip_head);
+    });
   else
     mark_row_kernel<<<(unsigned)rows, 256, 0, s>>>(S, p.nkv, L.nwords, target, all, bitmap,
                                                    base_counts, p.nq, skip_head);
@@ -1268,10 +1144,11 @@ static hipError_t mark_rows(const bsa_plan& p, const float* S, unsigned long lon
 // row_ptr from the final counts, then the column lists from the bitmap.
 static hipError_t scan_emit(const bsa_plan& p, const SelectWs& L, const uint32_t* bitmap,
                             const int32_t* base_counts, const int32_t* head_k_ws, bool use_min_k,
-                            int32_t* row_ptr, int32_t* col_idx, int32_t* counts, hipStream_t s) {
+                            int32_t* row_ptr, int32_t* col_idx, int32_t* counts,
+                            int32_t* partial, hipStream_t s) {
   const int64_t rows = (int64_t)p.prob.B * p.prob.H * p.nq;
-  scan_kernel<<<1, 1024, 0, s>>>(base_counts, head_k_ws, use_min_k, rows, p.nq, row_ptr, counts);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_scan(base_counts, head_k_ws, use_min_k, rows, p.nq, row_ptr, counts,
+                             partial, s);
   if (e != hipSuccess) return e;
   if (L.nwords <= 64)
     emit_wave_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(bitmap, L.nwords, rows, row_ptr,
@@ -1280,6 +1157,10 @@ static hipError_t scan_emit(const bsa_plan& p, const SelectWs& L, const uint32_t
     emit_kernel<<<(unsigned)rows, 256, 0, s>>>(bitmap, L.nwords, row_ptr, col_idx);
   return hipGetLastError();
 }
+
+static hipError_t select_finish(const bsa_plan& p, const float* S, const bsa_select_params& prm,
+                                void* ws, int32_t* row_ptr, int32_t* col_idx, int32_t* counts,
+                                int32_t* head_k, hipStream_t s);
 
 hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_params& prm,
                          int32_t* row_ptr, int32_t* col_idx, int32_t* counts, int32_t* head_k,
@@ -1316,6 +1197,24 @@ hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_par
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
+  return select_finish(p, S, prm, ws, row_ptr, col_idx, counts, head_k, s);
+}
+
+// After the marking pass: the per-head minimum and the top-up of the rows below it (ROW pool),
+// then row_ptr and the column lists.
+static hipError_t select_finish(const bsa_plan& p, const float* S, const bsa_select_params& prm,
+                                void* ws, int32_t* row_ptr, int32_t* col_idx, int32_t* counts,
+                                int32_t* head_k, hipStream_t s) {
+  const SelectWs L = select_ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + L.bitmap);
+  int32_t* base_counts = reinterpret_cast<int32_t*>(base + L.base_counts);
+  int32_t* head_k_ws = reinterpret_cast<int32_t*>(base + L.head_k);
+  const int BH = p.prob.B * p.prob.H;
+  const int64_t rows = (int64_t)BH * p.nq;
+  const bool wave_rows = p.nkv <= kWaveRowMax;
+  const unsigned wgrid = (unsigned)((rows + 3) / 4);
+  hipError_t e;
   const bool use_min_k = prm.min_k_mode != BSA_MINK_NONE;
   if (use_min_k || head_k) {
     head_k_kernel<<<BH, 256, 0, s>>>(base_counts, p.qstart, p.nq, p.nkv, prm.min_k_mode,
@@ -1323,19 +1222,35 @@ hipError_t launch_select(const bsa_plan& p, const float* S, const bsa_select_par
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (use_min_k && wave_rows) {
-    if (p.nkv <= 1024)
-      topup_wave_kernel<16><<<wgrid, 256, 0, s>>>(S, rows, p.nq, p.nkv, L.nwords, base_counts,
-                                                  head_k_ws, bitmap);
-    else
-      topup_wave_kernel<32><<<wgrid, 256, 0, s>>>(S, rows, p.nq, p.nkv, L.nwords, base_counts,
-                                                  head_k_ws, bitmap);
+    with_vpl(p.nkv, [&](auto vpl) {
+      topup_wave_kernel<decltype(vpl)::value><<<wgrid, 256, 0, s>>>(
+          S, rows, p.nq, p.nkv, L.nwords, base_counts, head_k_ws, bitmap);
+    });
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else if (use_min_k) {
     topup_kernel<<<(unsigned)rows, 256, 0, s>>>(S, p.nq, p.nkv, L.nwords, base_counts,
                                                 head_k_ws, bitmap);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return scan_emit(p, L, bitmap, base_counts, head_k_ws, use_min_k, row_ptr, col_idx, counts, s);
+  return scan_emit(p, L, bitmap, base_counts, head_k_ws, use_min_k, row_ptr, col_idx, counts,
+                   reinterpret_cast<int32_t*>(base + L.partial), s);
+}
+
+hipError_t launch_score_select_csr(const bsa_plan& p, const float* Qbar, const float* Kbar,
+                                   const bsa_select_params& prm, float* S, int32_t* row_ptr,
+                                   int32_t* col_idx, int32_t* counts, int32_t* head_k, void* ws,
+                                   hipStream_t s) {
+  const SelectWs L = select_ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  const int64_t rows = (int64_t)p.prob.B * p.prob.H * p.nq;
+  if (rows == 0) return hipSuccess;
+  const bool all = prm.p >= 1.0;
+  const unsigned long long target = all ? 0ull : (unsigned long long)ceil(prm.p * kFix);
+  hipError_t e = launch_score_select(p, Qbar, Kbar, S, target, all, L.nwords,
+                                     reinterpret_cast<uint32_t*>(base + L.bitmap),
+                                     reinterpret_cast<int32_t*>(base + L.base_counts), s);
+  if (e != hipSuccess) return e;
+  return select_finish(p, S, prm, ws, row_ptr, col_idx, counts, head_k, s);
 }
 
 hipError_t launch_select_eg(const bsa_plan& p, const float* S, const bsa_eg_params& prm,
@@ -1384,7 +1299,8 @@ hipError_t launch_select_eg(const bsa_plan& p, const float* S, const bsa_eg_para
                                                        L.nwords, L.eg_nrchunk, members, groups,
                                                        bnd, bitmap, base_counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return scan_emit(p, L, bitmap, base_counts, nullptr, false, row_ptr, col_idx, counts, s);
+  return scan_emit(p, L, bitmap, base_counts, nullptr, false, row_ptr, col_idx, counts,
+                   reinterpret_cast<int32_t*>(base + L.partial), s);
 }
 
 hipError_t launch_select_tokens(const bsa_plan& p, const void* Q, const float* Kbar, int k,
@@ -1416,8 +1332,9 @@ hipError_t launch_select_tokens(const bsa_plan& p, const void* Q, const float* K
   tok_union_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(
       sel, nslots, p.prob.H, N, p.nq, L.nwords, p.qstart, p.qperm, rows, bitmap, counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  scan_kernel<<<1, 1024, 0, s>>>(counts, nullptr, false, rows, p.nq, row_ptr, nullptr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = launch_scan(counts, nullptr, false, rows, p.nq, row_ptr, nullptr,
+                  reinterpret_cast<int32_t*>(base + L.partial), s);
+  if (e != hipSuccess) return e;
   emit_wave_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(bitmap, L.nwords, rows, row_ptr,
                                                               col_idx);
   return hipGetLastError();

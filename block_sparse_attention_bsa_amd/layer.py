@@ -12,8 +12,8 @@ import torch
 
 from . import (BSA_MINK_NONE, BSA_NORM_HEAD, BSA_NORM_ROW, BSA_POOL_HEAD, BSA_POOL_ROW, Plan,
                bsa_attn_bwd, bsa_attn_fwd, bsa_calibrate_mass, bsa_calibrate_mass_fwd,
-               bsa_attn_fwd_tokens, bsa_pool_qk, bsa_score, bsa_select, bsa_select_eg, bsa_select_tokens,
-               bsa_tokens_ws)
+               bsa_attn_fwd_tokens, bsa_pool_qk, bsa_score, bsa_score_select, bsa_select,
+               bsa_select_eg, bsa_select_tokens, bsa_tokens_ws)
 
 
 class BlockSparseAttention:
@@ -112,6 +112,17 @@ class BlockSparseAttention:
         bsa_select(self.plan, self.S if scores is None else scores, p, pool, min_k_mode, fixed_k,
                    self.row_ptr, self.col_idx, self.col_cap, self.counts, self.head_k,
                    self.ws_select, self.plan.ws_select, stream)
+        return self.row_ptr, self.col_idx
+
+    def score_select(self, p, min_k_mode=BSA_MINK_NONE, fixed_k=0, stream=None, write_scores=None):
+        """Scores and ROW-pool selection in one pass from the pooled Q and K (pool() first). The
+        scores go to self.S only when asked (write_scores) or when a minimum count needs them."""
+        if write_scores is None:
+            write_scores = min_k_mode != BSA_MINK_NONE
+        bsa_score_select(self.plan, self.qbar, self.kbar, p, min_k_mode, fixed_k,
+                         self.S if write_scores else None, self.row_ptr, self.col_idx,
+                         self.col_cap, self.counts, self.head_k, self.ws_select,
+                         self.plan.ws_select, stream)
         return self.row_ptr, self.col_idx
 
     def select_eg(self, p, theta, group_size, stream=None, scores=None):

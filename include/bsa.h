@@ -201,6 +201,21 @@ int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* pa
                int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
                int32_t* head_k, void* ws, size_t ws_bytes, void* stream);
 
+/* Steps 2 and 3 in one pass for the ROW pool (ROW normalisation, then top-p with an optional
+ * per-head minimum count): the same CSR, counts and head_k as bsa_score(BSA_NORM_ROW) followed
+ * by bsa_select, bit for bit, without the scores going through memory: each workgroup forms the
+ * block-mean logits of 16 query blocks against every kv block, applies the row softmax and
+ * selects every row in registers. The selection overhead of dynamic sparse attention is what
+ * the pages flag (mlsift listing: the HyperVAttention abstract's clustering overhead and the
+ * ScalingAttention abstract's runtime overhead of dynamic pruning). S [B, H, nq, nkv] (nullable)
+ * receives the scores when given; it is required with a minimum count, whose top-up reads it.
+ * Qbar, Kbar as bsa_score; the rest as bsa_select (ws: its ws_select bytes). BSA_EUNSUPPORTED
+ * for another pool or nkv > 2048. */
+int bsa_score_select(const bsa_plan* plan, const float* Qbar, const float* Kbar,
+                     const bsa_select_params* params, float* S, int32_t* row_ptr,
+                     int32_t* col_idx, int64_t col_cap, int32_t* counts, int32_t* head_k,
+                     void* ws, size_t ws_bytes, void* stream);
+
 /* Step 3, entropy-routed (EG-Sparse abstract). S: row-normalised scores from bsa_score
  * (BSA_NORM_ROW). Per head, E_h = sum_I |I| H_I / (N ln nkv) with H_I = -sum_J S ln S over row
  * (h, I) (fp64; 0 when nkv = 1); the head is pooled when E_h < theta. Heads are grouped in runs

@@ -112,6 +112,25 @@ static void exercise(int B, int H, int d, int dtype, int T, int Hg, int Wg, bsa_
   const bsa_select_params head_mink{0.9, BSA_POOL_HEAD, BSA_MINK_WEIGHTED_MEAN, 0};
   CHECK(bsa_select(plan, (float*)S.p(), &head_mink, (int32_t*)rp.p(), (int32_t*)ci.p(), cap,
                    nullptr, nullptr, ws_s.p(), wss, nullptr) == BSA_EUNSUPPORTED);
+  for (const auto& pm : prm) {  // the fused score-and-select: ROW pool only
+    const int rc = bsa_score_select(plan, qbar.f(), kbar.f(), &pm, S.f(), rp.i(), ci.i(), cap,
+                                    cnt.i(), hk.i(), ws_s.p(), wss, nullptr);
+    if (pm.pool != BSA_POOL_ROW || nkv > 2048)
+      CHECK(rc == BSA_EUNSUPPORTED);
+    else
+      CHECK(rc == BSA_OK);
+  }
+  {
+    const bsa_select_params mk{0.9, BSA_POOL_ROW, BSA_MINK_WEIGHTED_MEAN, 0};
+    CHECK(bsa_score_select(plan, qbar.f(), kbar.f(), &mk, nullptr, rp.i(), ci.i(), cap, nullptr,
+                           nullptr, ws_s.p(), wss, nullptr) ==
+          (nkv > 2048 ? BSA_EUNSUPPORTED : BSA_EINVAL));
+    const bsa_select_params p0{0.9, BSA_POOL_ROW, BSA_MINK_NONE, 0};
+    CHECK(bsa_score_select(plan, qbar.f(), kbar.f(), &p0, nullptr, rp.i(), ci.i(), cap, nullptr,
+                           nullptr, ws_s.p(), wss - 1, nullptr) != BSA_OK);
+    CHECK(bsa_score_select(plan, nullptr, kbar.f(), &p0, nullptr, rp.i(), ci.i(), cap, nullptr,
+                           nullptr, ws_s.p(), wss, nullptr) == BSA_EINVAL);
+  }
   const bsa_eg_params eg{0.9, 0.5, 4};
   CHECK(bsa_select_eg(plan, (float*)S.p(), &eg, (int32_t*)rp.p(), (int32_t*)ci.p(), cap,
                       (int32_t*)cnt.p(), nullptr, nullptr, ws_s.p(), wss, nullptr) == BSA_OK);
