@@ -30,7 +30,7 @@ BSA_MINK_NONE, BSA_MINK_FIXED, BSA_MINK_WEIGHTED_MEAN = 0, 1, 2
 
 EXPORTED = ("bsa_partition_build", "bsa_plan_create", "bsa_plan_destroy", "bsa_plan_info",
             "bsa_plan_blocks", "bsa_pool", "bsa_pool_qk", "bsa_score", "bsa_calibrate_mass",
-            "bsa_calibrate_mass_fwd", "bsa_select", "bsa_score_select",
+            "bsa_calibrate_mass_fwd", "bsa_select", "bsa_select_noalloc", "bsa_score_select",
             "bsa_select_eg",
             "bsa_tokens_ws",
             "bsa_select_tokens", "bsa_attn_fwd", "bsa_attn_fwd_tokens", "bsa_attn_bwd",
@@ -100,6 +100,7 @@ def lib():
         "bsa_calibrate_mass": [P, P, P, P, P, SZ, P],
         "bsa_calibrate_mass_fwd": [P, P, P, P, P, P, P, P, SZ, P],
         "bsa_select": [P, P, ctypes.POINTER(SelectParams), P, P, I64, P, P, P, SZ, P],
+        "bsa_select_noalloc": [P, P, ctypes.POINTER(SelectParams), P, P, I64, P, P, P],
         "bsa_score_select": [P, P, P, ctypes.POINTER(SelectParams), P, P, P, I64, P, P, P, SZ,
                              P],
         "bsa_select_eg": [P, P, ctypes.POINTER(EgParams), P, P, I64, P, P, P, P, SZ, P],
@@ -258,6 +259,14 @@ def bsa_score_select(plan: Plan, Qbar, Kbar, p: float, min_k_mode: int, fixed_k:
                                   _ptr(S), _ptr(row_ptr), _ptr(col_idx), int(col_cap),
                                   _ptr(counts), _ptr(head_k), _ptr(ws), ws_bytes,
                                   _stream(stream)))
+
+
+def bsa_select_noalloc(plan: Plan, S, p: float, pool: int, min_k_mode: int, fixed_k: int,
+                       row_ptr, col_idx, col_cap: int, counts, head_k, stream=None):
+    prm = SelectParams(float(p), int(pool), int(min_k_mode), int(fixed_k))
+    _check(lib().bsa_select_noalloc(plan.handle, _ptr(S), ctypes.byref(prm), _ptr(row_ptr),
+                                    _ptr(col_idx), int(col_cap), _ptr(counts), _ptr(head_k),
+                                    _stream(stream)))
 
 
 def bsa_select_eg(plan: Plan, S, p: float, theta: float, group_size: int, row_ptr, col_idx,

@@ -456,6 +456,28 @@ int bsa_select(const bsa_plan* plan, const float* S, const bsa_select_params* pr
                        "bsa_select");
 }
 
+int bsa_select_noalloc(const bsa_plan* plan, const float* S, const bsa_select_params* prm,
+                       int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
+                       int32_t* head_k, void* stream) {
+  int rc = check_select(plan, S, prm, row_ptr, col_idx, col_cap, "bsa_select_noalloc");
+  if (rc) return rc;
+  const size_t need = select_ws_layout(*plan).core;
+  if (need > kSelectScratchBytes)
+    return fail(BSA_ECAPACITY,
+                "bsa_select_noalloc: this plan needs %zu bytes of scratch, above the library's "
+                "fixed %zu (B * H * nq * ceil(nkv / 32) words); use bsa_select with a workspace",
+                need, kSelectScratchBytes);
+  rc = check_device(plan);
+  if (rc) return rc;
+  void* scratch_ptr = nullptr;
+  const hipError_t e = select_scratch(&scratch_ptr);
+  if (e != hipSuccess)
+    return fail(BSA_EHIP, "bsa_select_noalloc: scratch address: %s", hipGetErrorString(e));
+  return launch_status(launch_select(*plan, S, *prm, row_ptr, col_idx, counts, head_k,
+                                     scratch_ptr, (hipStream_t)stream),
+                       "bsa_select_noalloc");
+}
+
 int bsa_score_select(const bsa_plan* plan, const float* Qbar, const float* Kbar,
                      const bsa_select_params* prm, float* S, int32_t* row_ptr, int32_t* col_idx,
                      int64_t col_cap, int32_t* counts, int32_t* head_k, void* ws,

@@ -105,6 +105,12 @@ struct FwdWs {
 };
 FwdWs fwd_ws_layout(const bsa_plan& p);
 
+// The allocation-free selection (bsa_select_noalloc) keeps its workspace in a static device
+// array of this many bytes, one per GPU; select_scratch returns its address on the current
+// device (looked up once per device).
+constexpr size_t kSelectScratchBytes = size_t(8) << 20;
+hipError_t select_scratch(void** ptr);
+
 // Kernel launchers (defined in the .hip files). Each returns the launch status.
 hipError_t launch_pool(const bsa_plan& p, int which, const void* X, float* Xbar, hipStream_t s);
 hipError_t launch_pool_qk(const bsa_plan& p, const void* Q, float* Qbar, const void* K,

@@ -19,6 +19,8 @@
 // The chosen set is written as a bitmap (one bit per (row, kv block)); a scan over the final row
 // counts gives row_ptr, and a per-row pass expands the bitmap into ascending column indices.
 #include <climits>
+#include <mutex>
+#include <unordered_map>
 
 #include <array>
 #include <type_traits>
@@ -1338,4 +1340,27 @@ hipError_t launch_select_tokens(const bsa_plan& p, const void* Q, const float* K
   emit_wave_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(bitmap, L.nwords, rows, row_ptr,
                                                               col_idx);
   return hipGetLastError();
+}
+
+// Workspace of the allocation-free selection entry point: a file-scope device array (each GPU
+// holds its own copy for the life of the process). Host code never uses the array's name as an
+// address; it asks the runtime for the device address once per device and keeps it.
+static __device__ __align__(256) unsigned char scratch[kSelectScratchBytes];
+
+hipError_t select_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::unordered_map<int, void*> addr;  // device -> address of its copy of `scratch`
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
 }

@@ -216,6 +216,20 @@ int bsa_score_select(const bsa_plan* plan, const float* Qbar, const float* Kbar,
                      int32_t* col_idx, int64_t col_cap, int32_t* counts, int32_t* head_k,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* Step 3 without a workspace argument, for callers that cannot allocate device memory (code
+ * under stream capture into a graph, tight serving loops, harnesses that forbid allocation):
+ * the same selection, bit for bit, as bsa_select with the same arguments, and the same checks
+ * and errors. The workspace is a static device array inside the library, 8 MiB on each GPU,
+ * held until the process ends; the call allocates and frees nothing. A plan whose selection
+ * needs more (bitmap of B*H*nq*ceil(nkv/32) words, plus B*H*nq + B*H counts) returns
+ * BSA_ECAPACITY; use bsa_select with a workspace then. Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (different streams, or several threads)
+ * race and must be serialised by the caller; calls on one stream are ordered. Nothing in the
+ * array needs to start at zero: every word a call reads was written earlier by that call. */
+int bsa_select_noalloc(const bsa_plan* plan, const float* S, const bsa_select_params* params,
+                       int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, int32_t* counts,
+                       int32_t* head_k, void* stream);
+
 /* Step 3, entropy-routed (EG-Sparse abstract). S: row-normalised scores from bsa_score
  * (BSA_NORM_ROW). Per head, E_h = sum_I |I| H_I / (N ln nkv) with H_I = -sum_J S ln S over row
  * (h, I) (fp64; 0 when nkv = 1); the head is pooled when E_h < theta. Heads are grouped in runs

@@ -112,6 +112,18 @@ static void exercise(int B, int H, int d, int dtype, int T, int Hg, int Wg, bsa_
   const bsa_select_params head_mink{0.9, BSA_POOL_HEAD, BSA_MINK_WEIGHTED_MEAN, 0};
   CHECK(bsa_select(plan, (float*)S.p(), &head_mink, (int32_t*)rp.p(), (int32_t*)ci.p(), cap,
                    nullptr, nullptr, ws_s.p(), wss, nullptr) == BSA_EUNSUPPORTED);
+  for (const auto& pm : prm) {  // the allocation-free variant: same checks, no workspace
+    const int rc = bsa_select_noalloc(plan, (float*)S.p(), &pm, (int32_t*)rp.p(),
+                                      (int32_t*)ci.p(), cap, nullptr, nullptr, nullptr);
+    const bool fits = (size_t)rows * ((nkv + 31) / 32) * 4 + rows * 4 + B * H * 4 + 1024 <=
+                      (size_t(8) << 20);
+    if (pm.pool == BSA_POOL_LOCAL_TOPK && nkv > 2048)
+      CHECK(rc == BSA_EUNSUPPORTED);
+    else if (fits)
+      CHECK(rc == BSA_OK);
+    CHECK(bsa_select_noalloc(plan, (float*)S.p(), &pm, (int32_t*)rp.p(), (int32_t*)ci.p(),
+                             cap - 1, nullptr, nullptr, nullptr) != BSA_OK);
+  }
   for (const auto& pm : prm) {  // the fused score-and-select: ROW pool only
     const int rc = bsa_score_select(plan, qbar.f(), kbar.f(), &pm, S.f(), rp.i(), ci.i(), cap,
                                     cnt.i(), hk.i(), ws_s.p(), wss, nullptr);
@@ -218,9 +230,21 @@ int main() {
     const bsa_select_params pm{0.9, BSA_POOL_ROW, BSA_MINK_NONE, 0};
     CHECK(bsa_select(plan, (float*)fake, &pm, (int32_t*)fake, (int32_t*)fake, INT64_MAX, nullptr,
                      nullptr, fake, SIZE_MAX, nullptr) == BSA_EUNSUPPORTED);
+    CHECK(bsa_select_noalloc(plan, (float*)fake, &pm, (int32_t*)fake, (int32_t*)fake,
+                             INT64_MAX, nullptr, nullptr, nullptr) == BSA_EUNSUPPORTED);
     CHECK(bsa_attn_bwd(plan, fake, fake, fake, fake, fake, (float*)fake, (int32_t*)fake,
                        (int32_t*)fake, fake, fake, fake, fake, SIZE_MAX,
                        nullptr) == BSA_EUNSUPPORTED);
+    CHECK(bsa_plan_destroy(plan) == BSA_OK);
+  }
+  // a selection whose workspace exceeds the fixed scratch: 64 heads of the 720p shape
+  bsa_problem wide{1, 64, 33 * 45 * 80, 128, BSA_BF16, 33, 45, 80, tile(4, 4, 8), tile(4, 4, 8)};
+  CHECK(bsa_plan_create(&wide, nullptr, &plan) == BSA_OK);
+  if (plan) {
+    char fake[16];
+    const bsa_select_params pm{0.9, BSA_POOL_ROW, BSA_MINK_NONE, 0};
+    CHECK(bsa_select_noalloc(plan, (float*)fake, &pm, (int32_t*)fake, (int32_t*)fake, INT64_MAX,
+                             nullptr, nullptr, nullptr) == BSA_ECAPACITY);
     CHECK(bsa_plan_destroy(plan) == BSA_OK);
   }
   if (g_fail) {

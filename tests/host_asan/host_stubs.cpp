@@ -58,6 +58,13 @@ hipError_t launch_calibrate(const bsa_plan&, const void*, const void*, const voi
 hipError_t launch_attn_bwd(const bsa_plan&, const void*, const void*, const void*, const void*,
                            const void*, const float*, const int32_t*, const int32_t*, void*,
                            void*, void*, void*, hipStream_t) COUNT;
+
+// The allocation-free selection's device scratch: a host buffer of the same size here.
+static unsigned char g_scratch[kSelectScratchBytes];
+hipError_t select_scratch(void** ptr) {
+  *ptr = g_scratch;
+  return hipSuccess;
+}
 hipError_t launch_score_select_csr(const bsa_plan&, const float*, const float*,
                                    const bsa_select_params&, float*, int32_t*, int32_t*, int32_t*,
                                    int32_t*, void*, hipStream_t) COUNT;
