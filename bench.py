@@ -165,6 +165,39 @@ def token_topk(w, L, q, k, v, out, tm, ks=(2, 6, 18), calls=3):
     return res
 
 
+def token_global(w, L, q, k, v, out, tm, tau=0.25, calls=5):
+    """VMoBA's per-token global threshold selection (bsa_select_tokens_global, tau = 0.25 of the
+    review's free parameters) on the same inputs, timed outside the step: the selection's time,
+    the token-level density (pairs each token attends / N^2), the density the union walk
+    executes, the share of tokens that keep no block, and the output-only attention time over
+    the per-token bitmaps."""
+    import numpy as np
+    import torch
+    L.pool(q, k)
+    for _ in range(calls):
+        with tm("select_tg"):
+            bits = L.select_tokens_global(q, tau)
+        with tm("attn_tg"):
+            L.attention_token_bits(q, k, v, bits, out=out, with_lse=False)
+    torch.cuda.synchronize()
+    qs, ksz = np.diff(L.plan.blocks(0)[1]), np.diff(L.plan.blocks(1)[1])
+    nkv = len(ksz)
+    b = np.ascontiguousarray(bits.cpu().numpy().reshape(-1, bits.shape[-1])).view(np.uint32)
+    flags = np.unpackbits(b.view(np.uint8), axis=1, bitorder="little")[:, :nkv]
+    keys_per_token = flags.astype(np.int64) @ ksz.astype(np.int64)
+    f_tok = 4.0 * w.d * float(keys_per_token.sum())
+    rp, ci = L.csr_host()
+    f_exec = attention_flops(csr_rows(rp, ci), qs, ksz, w.d)
+    attn_ms = tm.mean_ms("attn_tg")
+    dense = 4.0 * w.B * w.H * w.N * w.N * w.d
+    return {"tau": tau, "select_ms": round(tm.mean_ms("select_tg"), 4),
+            "density_token": round(f_tok / dense, 4), "density_executed": round(f_exec / dense, 4),
+            "empty_token_fraction": round(float(np.mean(flags.sum(axis=1) == 0)), 4),
+            "attn_ms": round(attn_ms, 4),
+            "attn_tflops_token": f_tok / (attn_ms * 1e-3) / 1e12,
+            "attn_tflops_executed": f_exec / (attn_ms * 1e-3) / 1e12}
+
+
 def score_paths(w, L, q, k, mink, tm, calls=10):
     """Scores and selection as one kernel (bsa_score_select: S never goes through memory, except
     for the per-head minimum's top-up) against bsa_score followed by bsa_select, on the same
@@ -511,6 +544,8 @@ def main():
         res["entropy_routed"] = entropy_routed(w, layers[0], q, k, v, out, tm)
         res["local_topk"] = local_topk(w, layers[0], q, k, v, out, tm)
         res["token_topk"] = token_topk(w, layers[0], q, k, v, out, tm)
+        if layers[0].plan.nkv <= 768:  # the per-token bitmap attention's limit
+            res["token_global"] = token_global(w, layers[0], q, k, v, out, tm)
     if args.copy_ref_mib:
         n = args.copy_ref_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")

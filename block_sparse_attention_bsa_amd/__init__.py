@@ -34,6 +34,7 @@ EXPORTED = ("bsa_partition_build", "bsa_plan_create", "bsa_plan_destroy", "bsa_p
             "bsa_select_eg",
             "bsa_tokens_ws",
             "bsa_select_tokens", "bsa_attn_fwd", "bsa_attn_fwd_tokens", "bsa_attn_bwd",
+            "bsa_tokens_global_ws", "bsa_select_tokens_global", "bsa_attn_fwd_token_bits",
             "bsa_last_error")
 
 
@@ -108,6 +109,9 @@ def lib():
         "bsa_select_tokens": [P, P, P, I32, P, P, P, I64, P, SZ, P],
         "bsa_attn_fwd_tokens": [P, P, P, P, P, P, P, I32, P, P, P, SZ, P],
         "bsa_attn_fwd": [P, P, P, P, P, P, P, P, P, SZ, P],
+        "bsa_tokens_global_ws": [P, ctypes.POINTER(SZ)],
+        "bsa_select_tokens_global": [P, P, P, D, P, P, P, I64, P, SZ, P],
+        "bsa_attn_fwd_token_bits": [P, P, P, P, P, P, P, P, P, P, SZ, P],
         "bsa_attn_bwd": [P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
@@ -296,6 +300,26 @@ def bsa_attn_fwd_tokens(plan: Plan, Q, K, V, row_ptr, col_idx, sel, k: int, O, l
     _check(lib().bsa_attn_fwd_tokens(plan.handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(row_ptr),
                                      _ptr(col_idx), _ptr(sel), int(k), _ptr(O), _ptr(lse),
                                      _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def bsa_tokens_global_ws(plan: Plan) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().bsa_tokens_global_ws(plan.handle, ctypes.byref(n)))
+    return int(n.value)
+
+
+def bsa_select_tokens_global(plan: Plan, Q, Kbar, tau: float, tbits, row_ptr, col_idx,
+                             col_cap: int, ws, ws_bytes: int, stream=None):
+    _check(lib().bsa_select_tokens_global(plan.handle, _ptr(Q), _ptr(Kbar), float(tau),
+                                          _ptr(tbits), _ptr(row_ptr), _ptr(col_idx),
+                                          int(col_cap), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def bsa_attn_fwd_token_bits(plan: Plan, Q, K, V, row_ptr, col_idx, tbits, O, lse, ws,
+                            ws_bytes: int, stream=None):
+    _check(lib().bsa_attn_fwd_token_bits(plan.handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(row_ptr),
+                                         _ptr(col_idx), _ptr(tbits), _ptr(O), _ptr(lse),
+                                         _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def bsa_attn_fwd(plan: Plan, Q, K, V, row_ptr, col_idx, O, lse, ws, ws_bytes: int, stream=None):

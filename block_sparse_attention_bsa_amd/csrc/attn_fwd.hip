@@ -77,19 +77,27 @@ struct MfmaArgs {
   float* part;          // kMass: [bh][item][wave][nkv] per-wave block sums
   int n_items, H, N, nq, nkv;
   int Npad;  // K and V are permuted into block order: [B*H][Npad][d], Npad = N + kPermPad
-  // per-token block lists (the TOK variant): [B*H][N][tslots], ascending
+  // per-token block lists (the list variant): [B*H][N][tslots], ascending
   const int32_t* tsel;
   int tslots;
+  // per-token block bitmaps (the bitmap variant): [B*H][N][twords]
+  const uint32_t* tbits;
+  int twords;
 };
+
+// Per-token block sets: none (every query of a block attends to the block's CSR row), sorted
+// lists of a fixed length, or bitmaps of any number of blocks.
+enum TokSets { kTokNone = 0, kTokList = 1, kTokBits = 2 };
 
 // LDS row stride of the per-token lists in the TOK variant (at most 1 + kMaxTokenK blocks).
 constexpr int kTokSlots = kMaxTokenK + 1;
 
 // Two LDS stages: tile t is computed while tile t+1 streams in.
-// TOK: each query token attends only to the blocks of its own list (VMoBA review: each query
-// token scores the block means and keeps its best blocks); the workgroup walks the union of its
-// tokens' lists (the CSR row) and masks, per lane, the chunks of blocks its token did not pick.
-template <int MODE, bool TOK = false>
+// TOK (kTokList, kTokBits): each query token attends only to the blocks of its own set (VMoBA
+// review: each query token scores the block means and keeps its best blocks, or the head's
+// global threshold keeps its pairs); the workgroup walks the union of its tokens' sets (the CSR
+// row) and masks, per lane, the chunks of blocks its token did not pick.
+template <int MODE, int TOK = kTokNone>
 __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   constexpr int D = 128;
   constexpr bool kDense = MODE == kLse || MODE == kMass || MODE == kMassO;  // all kv blocks
@@ -97,7 +105,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   constexpr bool kNeedV = kPV;
   constexpr int kStage = kNeedV ? 2 * kTileBytes : kTileBytes;
   __shared__ __attribute__((aligned(1024))) char lds[2 * kStage];
-  __shared__ int32_t tlist[TOK ? kAttnRows * kTokSlots : 1];
+  constexpr int kTokRow = TOK == kTokBits ? kTokBitsWords : kTokSlots;
+  __shared__ int32_t tlist[TOK ? kAttnRows * kTokRow : 1];
   char* const lds_a = lds;
   char* const lds_b = lds + kStage;
 
@@ -193,7 +202,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   if (a0.nv > 0) tile_issue(a0, b0, m0_a);
   Chunk a1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
   Chunk b1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
-  if constexpr (TOK) {  // the block lists of this item's query rows (INT_MAX past the rows)
+  if constexpr (TOK == kTokList) {  // the block lists of this item's rows (INT_MAX past them)
     for (int idx = t; idx < kAttnRows * a.tslots; idx += 256) {
       const int row = idx / a.tslots, slot = idx - row * a.tslots;
       int v = INT_MAX;
@@ -201,12 +210,19 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
         v = a.tsel[((size_t)bh * a.N + a.qperm[q0 + row]) * a.tslots + slot];
       tlist[row * kTokSlots + slot] = v;
     }
+  } else if constexpr (TOK == kTokBits) {  // the block bitmaps of this item's rows (0 past them)
+    for (int idx = t; idx < kAttnRows * a.twords; idx += 256) {
+      const int row = idx / a.twords, wd = idx - row * a.twords;
+      uint32_t v = 0u;
+      if (row < nrows) v = a.tbits[((size_t)bh * a.N + a.qperm[q0 + row]) * a.twords + wd];
+      tlist[row * kTokBitsWords + wd] = (int32_t)v;
+    }
   }
   vmem_wait_all();
   __syncthreads();
   // TOK: position in this lane's list and the block there (lists and the CSR row ascend)
   int tptr = 0;
-  int tcur = TOK && qvalid ? tlist[qrow * kTokSlots] : INT_MAX;
+  int tcur = TOK == kTokList && qvalid ? tlist[qrow * kTokSlots] : INT_MAX;
 
   // V transposed reads: row 16*kc + 8*sh + 4*hl + (lane%16)/4, column 32*dm + 16*((lane/16)&1)
   // + 4*(lane&3): 16-byte unit 4*dm + 2*((lane/16)&1) + ((lane&3)>>1), 8-byte half (lane&1).
@@ -229,11 +245,15 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     if constexpr (TOK) {
       if (active) {
         auto picked = [&](int J) {
-          while (tcur < J) {
-            ++tptr;
-            tcur = tptr < a.tslots ? tlist[qrow * kTokSlots + tptr] : INT_MAX;
+          if constexpr (TOK == kTokBits) {
+            return ((uint32_t)tlist[qrow * kTokBitsWords + (J >> 5)] >> (J & 31)) & 1u;
+          } else {
+            while (tcur < J) {
+              ++tptr;
+              tcur = tptr < a.tslots ? tlist[qrow * kTokSlots + tptr] : INT_MAX;
+            }
+            return (uint32_t)(tcur == J);
           }
-          return tcur == J;
         };
         pa = picked(a0.J);
         pb = b0.nv > 0 && picked(b0.J);
@@ -528,7 +548,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_d128(const MfmaArgs a) {
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void attn_mfma_d128_tok(const MfmaArgs a) {
-  attn_mfma_body<MODE, true>(a);
+  attn_mfma_body<MODE, kTokList>(a);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void attn_mfma_d128_tokbits(const MfmaArgs a) {
+  attn_mfma_body<MODE, kTokBits>(a);
 }
 
 // M[bh, I, J] = (sum over I's work items and their active waves of the block sums) / |I|, in fp64
@@ -768,6 +793,33 @@ hipError_t launch_attn_fwd_tokens(const bsa_plan& p, const void* Q, const void* 
     attn_mfma_d128_tok<kFwd><<<grid, 256, 0, s>>>(a);
   else
     attn_mfma_d128_tok<kFwdO><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_token_bits(const bsa_plan& p, const void* Q, const void* K,
+                                      const void* V, const int32_t* row_ptr,
+                                      const int32_t* col_idx, const uint32_t* tbits, void* O,
+                                      float* lse, void* ws, hipStream_t s) {
+  const FwdWs L = fwd_ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  hipError_t e = launch_permute_rows(p, K, base + L.kp, s);
+  if (e == hipSuccess) e = launch_permute_rows(p, V, base + L.vp, s);
+  if (e != hipSuccess) return e;
+  MfmaArgs a = mfma_args(p);
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = reinterpret_cast<const uint16_t*>(base + L.kp);
+  a.V = reinterpret_cast<const uint16_t*>(base + L.vp);
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.O = static_cast<uint16_t*>(O);
+  a.lse = lse;
+  a.tbits = tbits;
+  a.twords = (p.nkv + 31) / 32;
+  const dim3 grid(p.n_items, p.prob.B * p.prob.H);
+  if (lse)
+    attn_mfma_d128_tokbits<kFwd><<<grid, 256, 0, s>>>(a);
+  else
+    attn_mfma_d128_tokbits<kFwdO><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

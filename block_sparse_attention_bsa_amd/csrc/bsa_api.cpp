@@ -172,6 +172,26 @@ BwdWs bwd_ws_layout(const bsa_plan& p) {
   return w;
 }
 
+TgWs tg_ws_layout(const bsa_plan& p) {
+  TgWs w;
+  const size_t BH = (size_t)p.prob.B * p.prob.H, N = (size_t)p.prob.N;
+  const size_t rows = BH * p.nq;
+  w.nwords = (p.nkv + 31) / 32;
+  w.nchunk = (int)((N + 31) / 32);
+  const size_t kb = BH * p.nkv * 128 * 2;
+  w.khi = 0;
+  w.klo = align_up(kb);
+  w.e = w.klo + align_up(kb);
+  w.heads = w.e + align_up(BH * N * p.nkv * 4);
+  w.hist = w.heads + align_up(BH * kTgHeadBytes);
+  w.bnd = w.hist + align_up(BH * (256 * 4 + 256 * 8));
+  w.bitmap = w.bnd + align_up(BH * w.nchunk * 4);
+  w.counts = w.bitmap + align_up(rows * w.nwords * 4);
+  w.partial = w.counts + align_up(rows * 4);
+  w.total = w.partial + align_up((rows + 1023) / 1024 * 4);
+  return w;
+}
+
 FwdWs fwd_ws_layout(const bsa_plan& p) {
   FwdWs w{0, 0, 0};
   if (p.prob.dtype != BSA_BF16 || p.prob.d != 128) return w;  // the VALU paths need none
@@ -588,6 +608,63 @@ int bsa_attn_fwd_tokens(const bsa_plan* plan, const void* Q, const void* K, cons
   return launch_status(launch_attn_fwd_tokens(*plan, Q, K, V, row_ptr, col_idx, sel, nslots, O,
                                               lse, ws, (hipStream_t)stream),
                        "bsa_attn_fwd_tokens");
+}
+
+int bsa_tokens_global_ws(const bsa_plan* plan, size_t* ws_bytes) {
+  if (!plan || !ws_bytes) return fail(BSA_EINVAL, "bsa_tokens_global_ws: NULL argument");
+  *ws_bytes = tg_ws_layout(*plan).total;
+  return BSA_OK;
+}
+
+int bsa_select_tokens_global(const bsa_plan* plan, const void* Q, const float* Kbar, double tau,
+                             uint32_t* tbits, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_cap, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || !Q || !Kbar || !tbits || !row_ptr || !col_idx)
+    return fail(BSA_EINVAL, "bsa_select_tokens_global: NULL argument");
+  if (plan->prob.dtype != BSA_BF16 || plan->prob.d != 128)
+    return fail(BSA_EUNSUPPORTED, "bsa_select_tokens_global: bf16 and d = 128 only");
+  if (!(tau > 0.0 && tau <= 1.0))
+    return fail(BSA_EINVAL, "bsa_select_tokens_global: tau must lie in (0, 1]");
+  if (plan->nkv > kWaveRowMaxBlocks)
+    return fail(BSA_EUNSUPPORTED, "bsa_select_tokens_global: more than %d kv blocks",
+                kWaveRowMaxBlocks);
+  const int64_t need_cols = (int64_t)plan->prob.B * plan->prob.H * plan->nq * plan->nkv;
+  if (need_cols > (int64_t)INT32_MAX)
+    return fail(BSA_EUNSUPPORTED, "bsa_select_tokens_global: B * H * nq * nkv exceeds 2^31 - 1");
+  if (col_cap < need_cols)
+    return fail(BSA_ECAPACITY, "bsa_select_tokens_global: col_idx capacity %lld < %lld",
+                (long long)col_cap, (long long)need_cols);
+  const size_t need = tg_ws_layout(*plan).total;
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ECAPACITY, "bsa_select_tokens_global: workspace %zu < %zu bytes", ws_bytes,
+                need);
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_select_tokens_global(*plan, Q, Kbar, tau, tbits, row_ptr, col_idx,
+                                                   ws, (hipStream_t)stream),
+                       "bsa_select_tokens_global");
+}
+
+int bsa_attn_fwd_token_bits(const bsa_plan* plan, const void* Q, const void* K, const void* V,
+                            const int32_t* row_ptr, const int32_t* col_idx,
+                            const uint32_t* tbits, void* O, float* lse, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!plan || !Q || !K || !V || !row_ptr || !col_idx || !tbits || !O)
+    return fail(BSA_EINVAL, "bsa_attn_fwd_token_bits: NULL argument");
+  if (plan->prob.dtype != BSA_BF16 || plan->prob.d != 128)
+    return fail(BSA_EUNSUPPORTED, "bsa_attn_fwd_token_bits: bf16 and d = 128 only");
+  if (plan->nkv > 32 * kTokBitsWords)
+    return fail(BSA_EUNSUPPORTED, "bsa_attn_fwd_token_bits: more than %d kv blocks",
+                32 * kTokBitsWords);
+  const size_t need = fwd_ws_layout(*plan).total;
+  if (!ws || ws_bytes < need)
+    return fail(BSA_ECAPACITY, "bsa_attn_fwd_token_bits: workspace %zu < %zu bytes", ws_bytes,
+                need);
+  int rc = check_device(plan);
+  if (rc) return rc;
+  return launch_status(launch_attn_fwd_token_bits(*plan, Q, K, V, row_ptr, col_idx, tbits, O,
+                                                  lse, ws, (hipStream_t)stream),
+                       "bsa_attn_fwd_token_bits");
 }
 
 int bsa_attn_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,

@@ -100,6 +100,27 @@ struct TokWs {
 };
 TokWs tok_ws_layout(const bsa_plan& p);
 
+// Per-token global threshold selection (bsa_select_tokens_global): Kbar's two bf16 terms, the
+// head pools' gates (then their exp) [B*H][N][nkv] fp32, per-head radix state and histogram,
+// boundary counts per 32-token chunk, and the per-query-block union (bitmap, counts, scan).
+constexpr size_t kTgHeadBytes = 80;
+struct TgWs {
+  size_t khi, klo, e, heads, hist, bnd, bitmap, counts, partial, total;
+  int nwords, nchunk;
+};
+TgWs tg_ws_layout(const bsa_plan& p);
+hipError_t launch_select_tokens_global(const bsa_plan& p, const void* Q, const float* Kbar,
+                                       double tau, uint32_t* tbits, int32_t* row_ptr,
+                                       int32_t* col_idx, void* ws, hipStream_t s);
+// Attention of each token over the blocks set in its bitmap tbits[B*H][N][nwords] (the union
+// CSR walked per query block).
+hipError_t launch_attn_fwd_token_bits(const bsa_plan& p, const void* Q, const void* K,
+                                      const void* V, const int32_t* row_ptr,
+                                      const int32_t* col_idx, const uint32_t* tbits, void* O,
+                                      float* lse, void* ws, hipStream_t s);
+// Largest kv-block count of the per-token bitmap attention (one LDS row of words per token).
+constexpr int kTokBitsWords = 24;
+
 struct FwdWs {
   size_t kp, vp, total;  // K and V in block order, [B*H][N + kPermPad][d] (bf16, d = 128 path)
 };
@@ -112,6 +133,15 @@ constexpr size_t kSelectScratchBytes = size_t(8) << 20;
 hipError_t select_scratch(void** ptr);
 
 // Kernel launchers (defined in the .hip files). Each returns the launch status.
+// Shared pieces of the selections: row_ptr from per-row counts (exclusive scan in 1024-row
+// chunks, partial: one int per chunk); Kbar split into two bf16 terms; CSR columns from bitmaps.
+hipError_t launch_scan(const int32_t* base_counts, const int32_t* head_k, bool use_min_k,
+                       int64_t rows, int nq, int32_t* row_ptr, int32_t* counts_out,
+                       int32_t* partial, hipStream_t s);
+hipError_t launch_kbar_split(const float* Kbar, int64_t n, uint16_t* hi, uint16_t* lo,
+                             hipStream_t s);
+hipError_t launch_emit(const uint32_t* bitmap, int nwords, int64_t rows, const int32_t* row_ptr,
+                       int32_t* col_idx, hipStream_t s);
 hipError_t launch_pool(const bsa_plan& p, int which, const void* X, float* Xbar, hipStream_t s);
 hipError_t launch_pool_qk(const bsa_plan& p, const void* Q, float* Qbar, const void* K,
                           float* Kbar, hipStream_t s);

@@ -356,15 +356,6 @@ __global__ __launch_bounds__(1024) void scan_add_kernel(int64_t rows,
   if (blockIdx.x == 0 && t == 0) row_ptr[0] = 0;
 }
 
-hipError_t launch_scan(const int32_t* base_counts, const int32_t* head_k, bool use_min_k,
-                       int64_t rows, int nq, int32_t* row_ptr, int32_t* counts_out,
-                       int32_t* partial, hipStream_t s) {
-  const unsigned nb = (unsigned)((rows + 1023) / 1024);
-  scan_local_kernel<<<nb, 1024, 0, s>>>(base_counts, head_k, use_min_k, rows, nq, row_ptr,
-                                        counts_out, partial);
-  scan_add_kernel<<<nb, 1024, 0, s>>>(rows, partial, row_ptr);
-  return hipGetLastError();
-}
 
 // Expand each row's bitmap into ascending kv-block indices at row_ptr[r].
 __global__ __launch_bounds__(256) void emit_kernel(const uint32_t* __restrict__ bitmap,
@@ -1124,6 +1115,32 @@ __global__ __launch_bounds__(64) void eg_boundary_kernel(const float* __restrict
 }
 
 }  // namespace
+
+hipError_t launch_scan(const int32_t* base_counts, const int32_t* head_k, bool use_min_k,
+                       int64_t rows, int nq, int32_t* row_ptr, int32_t* counts_out,
+                       int32_t* partial, hipStream_t s) {
+  const unsigned nb = (unsigned)((rows + 1023) / 1024);
+  scan_local_kernel<<<nb, 1024, 0, s>>>(base_counts, head_k, use_min_k, rows, nq, row_ptr,
+                                        counts_out, partial);
+  scan_add_kernel<<<nb, 1024, 0, s>>>(rows, partial, row_ptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_kbar_split(const float* Kbar, int64_t n, uint16_t* hi, uint16_t* lo,
+                             hipStream_t s) {
+  kbar_split_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(Kbar, n, hi, lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_emit(const uint32_t* bitmap, int nwords, int64_t rows, const int32_t* row_ptr,
+                       int32_t* col_idx, hipStream_t s) {
+  if (nwords <= 64)
+    emit_wave_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(bitmap, nwords, rows, row_ptr,
+                                                                col_idx);
+  else
+    emit_kernel<<<(unsigned)rows, 256, 0, s>>>(bitmap, nwords, row_ptr, col_idx);
+  return hipGetLastError();
+}
 
 // ROW-pool marks of every row (bitmap and counts), except the rows of heads flagged in
 // skip_head (nullable).

@@ -13,7 +13,8 @@ import torch
 from . import (BSA_MINK_NONE, BSA_NORM_HEAD, BSA_NORM_ROW, BSA_POOL_HEAD, BSA_POOL_ROW, Plan,
                bsa_attn_bwd, bsa_attn_fwd, bsa_calibrate_mass, bsa_calibrate_mass_fwd,
                bsa_attn_fwd_tokens, bsa_pool_qk, bsa_score, bsa_score_select, bsa_select,
-               bsa_select_eg, bsa_select_tokens, bsa_tokens_ws)
+               bsa_select_eg, bsa_select_tokens, bsa_tokens_ws, bsa_tokens_global_ws,
+               bsa_select_tokens_global, bsa_attn_fwd_token_bits)
 
 
 class BlockSparseAttention:
@@ -163,6 +164,38 @@ class BlockSparseAttention:
             self._ws_fwd = torch.empty(self.plan.ws_fwd, dtype=torch.uint8, device=self.device)
         bsa_attn_fwd_tokens(self.plan, q, k, v, self.row_ptr, self.col_idx, sel, k_best, out,
                             lse, self._ws_fwd, self.plan.ws_fwd, stream)
+        return out, lse
+
+    def select_tokens_global(self, q, tau, stream=None):
+        """Per-token head-global selection from Q and the pooled K (pool() first): returns the
+        per-token block bitmaps [B, H, N, ceil(nkv / 32)] (int32 words) and fills row_ptr /
+        col_idx with each query block's union."""
+        self._act("q", q)
+        B, H, N = q.shape[:3]
+        nw = (self.plan.nkv + 31) // 32
+        bits = torch.empty((B, H, N, nw), dtype=torch.int32, device=self.device)
+        n = bsa_tokens_global_ws(self.plan)
+        if getattr(self, "_ws_tg", None) is None or self._ws_tg.numel() < n:
+            self._ws_tg = torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
+        bsa_select_tokens_global(self.plan, q, self.kbar, tau, bits, self.row_ptr, self.col_idx,
+                                 self.col_cap, self._ws_tg, self._ws_tg.numel(), stream)
+        return bits
+
+    def attention_token_bits(self, q, k, v, bits, out=None, lse=None, with_lse=True,
+                             stream=None):
+        """Attention of every token over the blocks of its bitmap (from select_tokens_global)."""
+        self._act("q", q), self._act("k", k), self._act("v", v)
+        nw = (self.plan.nkv + 31) // 32
+        self._i32("bits", bits, q.shape[0] * q.shape[1] * q.shape[2] * nw)
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and with_lse:
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=self.device)
+        self._act("out", out), self._f32("lse", lse, self.shape[:3])
+        if self._ws_fwd is None and self.plan.ws_fwd > 0:
+            self._ws_fwd = torch.empty(self.plan.ws_fwd, dtype=torch.uint8, device=self.device)
+        bsa_attn_fwd_token_bits(self.plan, q, k, v, self.row_ptr, self.col_idx, bits, out, lse,
+                                self._ws_fwd, self.plan.ws_fwd, stream)
         return out, lse
 
     def attention(self, q, k, v, row_ptr=None, col_idx=None, out=None, lse=None, stream=None,

@@ -21,6 +21,8 @@
  *                         reuse across denoising steps (LoSA abstract).
  *      bsa_select_tokens  per query token, its own block plus the k blocks of highest gate (VMoBA
  *                         review), with bsa_attn_fwd_tokens to attend over them.
+ *      bsa_select_tokens_global  per head, the (token, block) gates ranked as one pool with the
+ *                         threshold tau (VMoBA Eq. 3-4), with bsa_attn_fwd_token_bits.
  *      bsa_select_eg      the same rule with the competition domain chosen per head by the
  *                         entropy of its scores: a pool shared by a group of low-entropy heads,
  *                         per-row selection for the rest (EG-Sparse abstract).
@@ -271,6 +273,36 @@ int bsa_attn_fwd_tokens(const bsa_plan* plan, const void* Q, const void* K, cons
                         const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sel,
                         int32_t k, void* O, float* lse, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* Step 3, per token and head-global (VMoBA review: "What carries the argument" -- global
+ * selection pools the scores of all queries of a head; referee report major comment 1 -- Eq. 3
+ * keeps the top entries of the whole query-by-block matrix and Eq. 4 the smallest count k'
+ * whose cumulative normalised similarity reaches tau, so a query may keep no block; tau = 0.25
+ * under "Assumptions & free parameters"). Per head, the gates g[i, J] = sigma_h q_i . kbar_J of
+ * every query token i and kv block J (bf16 matrix cores, kbar split into two bf16 terms, fp32
+ * sums) are normalised by one softmax over the head's whole N x nkv matrix; the pairs are ranked
+ * by (weight desc, pair index i * nkv + J asc) and the shortest prefix reaching tau is kept, with
+ * exact fixed-point sums of exp(g - max g) (the prefix of e reaching tau * sum e). tbits
+ * [B, H, N, ceil(nkv / 32)] (uint32 words, bit J % 32 of word J / 32) receives each token's kept
+ * blocks; a token may keep none (an empty row: its attention gives O = 0, LSE = -inf).
+ * row_ptr / col_idx (as bsa_select) receive each query block's union of its tokens' blocks, which
+ * bsa_attn_fwd_token_bits walks. Q [B, H, N, 128] bf16; Kbar fp32 [B, H, nkv, 128] from
+ * bsa_pool(which = 1). ws >= the bytes bsa_tokens_global_ws reports (it holds the B*H*N*nkv fp32
+ * gates). BSA_EUNSUPPORTED unless bf16, d = 128, nkv <= 2048 and B*H*nq*nkv <= 2^31 - 1. */
+int bsa_tokens_global_ws(const bsa_plan* plan, size_t* ws_bytes);
+int bsa_select_tokens_global(const bsa_plan* plan, const void* Q, const float* Kbar, double tau,
+                             uint32_t* tbits, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_cap, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 4 over per-token block bitmaps (from bsa_select_tokens_global): O_i and lse_i (nullable)
+ * over the tokens of the blocks set in tbits[b, h, i]; a token with no block gets O = 0 and
+ * lse = -inf. Each query block's workgroup walks its union CSR row and masks, per token, the
+ * blocks that token did not keep. Numerics and ws as bsa_attn_fwd (ws_fwd bytes). bf16,
+ * d = 128 and nkv <= 768 only (BSA_EUNSUPPORTED otherwise). */
+int bsa_attn_fwd_token_bits(const bsa_plan* plan, const void* Q, const void* K, const void* V,
+                            const int32_t* row_ptr, const int32_t* col_idx,
+                            const uint32_t* tbits, void* O, float* lse, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* Step 4. For every query i of block I: O_i = sum_j softmax_j(sigma_h q_i . k_j) v_j over the
  * tokens j of the kv blocks listed in CSR row I, and lse_i = log sum_j exp(sigma_h q_i . k_j).

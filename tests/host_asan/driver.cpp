@@ -177,6 +177,19 @@ static void exercise(int B, int H, int d, int dtype, int T, int Hg, int Wg, bsa_
     CHECK(bsa_select_tokens(plan, q.p(), (float*)kbar.p(), 25, (int32_t*)sel.p(),
                             (int32_t*)rp.p(), (int32_t*)ci.p(), cap, ws_t.p(), wst,
                             nullptr) == BSA_EUNSUPPORTED);
+    size_t wsg = 0;
+    CHECK(bsa_tokens_global_ws(plan, &wsg) == BSA_OK);
+    Buf ws_g(wsg);
+    CHECK(bsa_select_tokens_global(plan, q.p(), kbar.f(), 0.25, (uint32_t*)sel.p(), rp.i(),
+                                   ci.i(), cap, ws_g.p(), wsg, nullptr) ==
+          (nkv > 2048 ? BSA_EUNSUPPORTED : BSA_OK));
+    CHECK(bsa_select_tokens_global(plan, q.p(), kbar.f(), 0.0, (uint32_t*)sel.p(), rp.i(),
+                                   ci.i(), cap, ws_g.p(), wsg, nullptr) == BSA_EINVAL);
+    CHECK(bsa_select_tokens_global(plan, q.p(), kbar.f(), 0.25, (uint32_t*)sel.p(), rp.i(),
+                                   ci.i(), cap, ws_g.p(), wsg - 1, nullptr) != BSA_OK);
+    CHECK(bsa_attn_fwd_token_bits(plan, q.p(), k.p(), v.p(), rp.i(), ci.i(), (uint32_t*)sel.p(),
+                                  o.p(), nullptr, ws_f.p(), wsf, nullptr) ==
+          (nkv > 768 ? BSA_EUNSUPPORTED : BSA_OK));
     if (nkv <= 2048)
       CHECK(bsa_attn_fwd_tokens(plan, q.p(), k.p(), v.p(), (int32_t*)rp.p(), (int32_t*)ci.p(),
                                 (int32_t*)sel.p(), 6, o.p(), nullptr, ws_f.p(), wsf,

@@ -68,3 +68,8 @@ hipError_t select_scratch(void** ptr) {
 hipError_t launch_score_select_csr(const bsa_plan&, const float*, const float*,
                                    const bsa_select_params&, float*, int32_t*, int32_t*, int32_t*,
                                    int32_t*, void*, hipStream_t) COUNT;
+hipError_t launch_select_tokens_global(const bsa_plan&, const void*, const float*, double,
+                                       uint32_t*, int32_t*, int32_t*, void*, hipStream_t) COUNT;
+hipError_t launch_attn_fwd_token_bits(const bsa_plan&, const void*, const void*, const void*,
+                                      const int32_t*, const int32_t*, const uint32_t*, void*,
+                                      float*, void*, hipStream_t) COUNT;
