@@ -29,6 +29,7 @@
 // 2^32, which is detected from the row sum the softmax needs anyway, so no per-tile max is formed
 // and the O rescale is rare. When no LSE is requested (an inference call) the fp32 row sum is not
 // formed: the sum of the bf16-rounded weights, which O is normalised by, serves as the bound.
+#include <algorithm>
 #include <climits>
 
 #include "bsa_internal.h"
@@ -83,6 +84,10 @@ struct MfmaArgs {
   // per-token block bitmaps (the bitmap variant): [B*H][N][twords]
   const uint32_t* tbits;
   int twords;
+  // forward work items (kFItemInts ints each, see bsa_internal.h): a query block's 128-row
+  // chunk, or the 32-row slots of up to four query blocks packed into one workgroup
+  const int32_t* fitems;
+  int n_fitems;
 };
 
 // Per-token block sets: none (every query of a block attends to the block's CSR row), sorted
@@ -97,24 +102,31 @@ constexpr int kTokSlots = kMaxTokenK + 1;
 // review: each query token scores the block means and keeps its best blocks, or the head's
 // global threshold keeps its pairs); the workgroup walks the union of its tokens' sets (the CSR
 // row) and masks, per lane, the chunks of blocks its token did not pick.
-template <int MODE, int TOK = kTokNone>
-__device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
+//
+// PACK (sparse forward only): the workgroup's four wavefronts hold the 32-row slots of up to four
+// query blocks (the rows of blocks smaller than 128 tokens, at the grid's edges, packed so that
+// no wavefront idles); the tile stream is the merged walk of their CSR rows, and a wavefront
+// computes only the tiles whose blocks its own query block selected (the chunks of the others
+// masked like padding rows, a tile of none skipped).
+template <int MODE, int TOK = kTokNone, bool PACK = false>
+__device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int32_t* tlist) {
   constexpr int D = 128;
   constexpr bool kDense = MODE == kLse || MODE == kMass || MODE == kMassO;  // all kv blocks
   constexpr bool kPV = MODE == kFwd || MODE == kFwdO || MODE == kMassO;  // O = P V is formed
   constexpr bool kNeedV = kPV;
   constexpr int kStage = kNeedV ? 2 * kTileBytes : kTileBytes;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kStage];
-  constexpr int kTokRow = TOK == kTokBits ? kTokBitsWords : kTokSlots;
-  __shared__ int32_t tlist[TOK ? kAttnRows * kTokRow : 1];
+  // the sparse forward reads the forward work items, the other passes one block per item
+  constexpr bool kFItems = (MODE == kFwd || MODE == kFwdO) && TOK == kTokNone;
   char* const lds_a = lds;
   char* const lds_b = lds + kStage;
 
-  const int n_items = a.n_items;
+  const int n_items = kFItems ? a.n_fitems : a.n_items;
   const int total = n_items * (int)gridDim.y;
   const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
   const int bh = lin / n_items, item = lin % n_items;
-  const int I = ld_ro(a.items + 2 * item), off = ld_ro(a.items + 2 * item + 1);
+  const int32_t* const desc = kFItems ? a.fitems + kFItemInts * item : a.items;
+  const int I = kFItems ? ld_ro(desc + 1) : ld_ro(a.items + 2 * item);
+  const int off = kFItems ? ld_ro(desc + 6) : ld_ro(a.items + 2 * item + 1);
   const int q0 = ld_ro(a.qstart + I) + off;
   const int nrows = min(128, ld_ro(a.qstart + I + 1) - q0);
   const int64_t r = (int64_t)bh * a.nq + I;
@@ -123,13 +135,22 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const bool active = 32 * wave < nrows;  // wave-uniform
   const int l32 = lane & 31, hl = lane >> 5;
+  // This wavefront's 32 query rows: rows q0w .. q0w + nroww of the block order (nroww <= 0: none),
+  // and (PACK) which of the merged CSR rows is its block's.
+  int q0w = q0 + 32 * wave, nroww = nrows - 32 * wave, lw = 0;
+  if constexpr (PACK) {
+    lw = ld_ro(desc + 5 + 2 * wave);
+    const int Iw = ld_ro(desc + 1 + (lw < 0 ? 0 : lw));
+    q0w = ld_ro(a.qstart + Iw) + ld_ro(desc + 6 + 2 * wave);
+    nroww = lw < 0 ? 0 : min(32, ld_ro(a.qstart + Iw + 1) - q0w);
+  }
+  const bool active = nroww > 0;  // wave-uniform
 
   // Q fragments (B operand of S^T = K Q^T): query row 32*wave + l32, d = 16*kc + 8*hl .. +8.
   const int qrow = 32 * wave + l32;
-  const bool qvalid = qrow < nrows;
-  const int qtok = qvalid ? a.qperm[q0 + qrow] : 0;
+  const bool qvalid = l32 < nroww;
+  const int qtok = qvalid ? a.qperm[q0w + l32] : 0;
   bf16x8_t qf[8];
   {
     const uint4* qp =
@@ -168,10 +189,28 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   const int lchunk = wave >> 1, loff = 16 * (wave & 1), lgrp = lane >> 4;
 
   Cursor cur;
-  cur.slot = kDense ? 0 : ld_ro(a.row_ptr + r);
-  cur.end = kDense ? a.nkv : ld_ro(a.row_ptr + r + 1);
-  cur.sub = 0;
-  cursor_load<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
+  MultiCursor mc;
+  if constexpr (PACK) {
+    mc.nl = ld_ro(desc);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const int64_t rl = (int64_t)bh * a.nq + ld_ro(desc + 1 + l);
+      mc.slot[l] = l < mc.nl ? ld_ro(a.row_ptr + rl) : 0;
+      mc.end[l] = l < mc.nl ? ld_ro(a.row_ptr + rl + 1) : 0;
+    }
+    mcursor_load(mc, a.col_idx, a.kvstart, a.nkv);
+  } else {
+    cur.slot = kDense ? 0 : ld_ro(a.row_ptr + r);
+    cur.end = kDense ? a.nkv : ld_ro(a.row_ptr + r + 1);
+    cur.sub = 0;
+    cursor_load<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
+  }
+  auto take = [&]() {
+    if constexpr (PACK)
+      return mtake_chunk(mc, a.col_idx, a.kvstart, a.nkv);
+    else
+      return take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
+  };
 
   const size_t kv_off = (size_t)bh * a.Npad * D;
   const uint16_t* const kbase = a.K + kv_off;
@@ -197,11 +236,11 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
   // Pipeline: tile t (chunks a0, b0) is in LDS and tile t+1 (a1, b1) is copied into the other
   // stage while tile t is computed.
   const uint32_t m0_a = lds_addr(lds_a), m0_b = lds_addr(lds_b);
-  Chunk a0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
-  Chunk b0 = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
+  Chunk a0 = take();
+  Chunk b0 = take();
   if (a0.nv > 0) tile_issue(a0, b0, m0_a);
-  Chunk a1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
-  Chunk b1 = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
+  Chunk a1 = take();
+  Chunk b1 = take();
   if constexpr (TOK == kTokList) {  // the block lists of this item's rows (INT_MAX past them)
     for (int idx = t; idx < kAttnRows * a.tslots; idx += 256) {
       const int row = idx / a.tslots, slot = idx - row * a.tslots;
@@ -242,6 +281,11 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     // picked either skips the tile's matrix and vector work: all its weights would be exactly 0,
     // adding nothing to O or the sums.
     bool pa = true, pb = true, act = active;
+    if constexpr (PACK) {  // chunks of blocks this wavefront's query block selected
+      pa = (a0.lmask >> lw) & 1;
+      pb = b0.nv > 0 && ((b0.lmask >> lw) & 1);
+      act = active && (pa || pb);
+    }
     if constexpr (TOK) {
       if (active) {
         auto picked = [&](int J) {
@@ -297,8 +341,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
       __builtin_amdgcn_s_setprio(0);
     }
     // The next tile's copies are issued while the score MFMAs execute.
-    const Chunk an = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
-    const Chunk bn = take_chunk<kDense>(cur, a.col_idx, a.kvstart, a.nkv);
+    const Chunk an = take();
+    const Chunk bn = take();
     if (a1.nv > 0) tile_issue(a1, b1, nx_m0);
 
     if (act) {
@@ -311,7 +355,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
             if (8 * (e >> 2) + 4 * hl + (e & 3) >= nv) sacc[mb][e] = -INFINITY;
         }
       }
-      if constexpr (TOK) {  // chunks of blocks this lane's token did not pick
+      if constexpr (TOK || PACK) {  // chunks of blocks this lane's row did not select
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           if (!pa) sacc[0][e] = -INFINITY;
@@ -540,20 +584,42 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a) {
     a.lse[(size_t)bh * a.N + qtok] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-// Two waves per SIMD: two workgroups share a CU.
+// LDS of the two K (and V) stages.
+template <int MODE>
+constexpr int stage_bytes() {
+  return 2 * ((MODE == kFwd || MODE == kFwdO || MODE == kMassO) ? 2 * kTileBytes : kTileBytes);
+}
+
+// Two waves per SIMD: two workgroups share a CU. The sparse forward's items are either one
+// query block's rows or several blocks' packed slots; both bodies share the kernel's LDS.
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void attn_mfma_d128(const MfmaArgs a) {
-  attn_mfma_body<MODE>(a);
+  __shared__ __attribute__((aligned(1024))) char lds[stage_bytes<MODE>()];
+  __shared__ int32_t none[1];
+  if constexpr (MODE == kFwd || MODE == kFwdO) {
+    const int total = a.n_fitems * (int)gridDim.y;
+    const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
+    if (ld_ro(a.fitems + kFItemInts * (lin % a.n_fitems)) > 1)
+      attn_mfma_body<MODE, kTokNone, true>(a, lds, none);
+    else
+      attn_mfma_body<MODE, kTokNone, false>(a, lds, none);
+  } else {
+    attn_mfma_body<MODE>(a, lds, none);
+  }
 }
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void attn_mfma_d128_tok(const MfmaArgs a) {
-  attn_mfma_body<MODE, kTokList>(a);
+  __shared__ __attribute__((aligned(1024))) char lds[stage_bytes<MODE>()];
+  __shared__ int32_t tlist[kAttnRows * kTokSlots];
+  attn_mfma_body<MODE, kTokList>(a, lds, tlist);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void attn_mfma_d128_tokbits(const MfmaArgs a) {
-  attn_mfma_body<MODE, kTokBits>(a);
+  __shared__ __attribute__((aligned(1024))) char lds[stage_bytes<MODE>()];
+  __shared__ int32_t tlist[kAttnRows * kTokBitsWords];
+  attn_mfma_body<MODE, kTokBits>(a, lds, tlist);
 }
 
 // M[bh, I, J] = (sum over I's work items and their active waves of the block sums) / |I|, in fp64
@@ -604,6 +670,8 @@ MfmaArgs mfma_args(const bsa_plan& p) {
   a.items = p.items;
   a.scale = p.scale;
   a.n_items = p.n_items;
+  a.fitems = p.fitems;
+  a.n_fitems = p.n_fitems;
   a.H = p.prob.H;
   a.N = p.prob.N;
   a.nq = p.nq;
@@ -755,8 +823,8 @@ hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, cons
     a.col_idx = col_idx;
     a.O = static_cast<uint16_t*>(O);
     a.lse = lse;
-    // gridDim.x * gridDim.y is exactly n_items * B * H (the XCD remap is a bijection on it).
-    const dim3 grid(p.n_items, p.prob.B * p.prob.H);
+    // gridDim.x * gridDim.y is exactly n_fitems * B * H (the XCD remap is a bijection on it).
+    const dim3 grid(p.n_fitems, p.prob.B * p.prob.H);
     if (lse)
       attn_mfma_d128<kFwd><<<grid, 256, 0, s>>>(a);
     else

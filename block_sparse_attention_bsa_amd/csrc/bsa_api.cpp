@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <utility>
 
 #include "bsa_internal.h"
 
@@ -108,7 +109,8 @@ int upload(const std::vector<T>& h, T** d) {
 void free_plan(bsa_plan* p) {
   if (!p) return;
   for (void* ptr : {(void*)p->qperm, (void*)p->qstart, (void*)p->kvperm, (void*)p->kvstart,
-                    (void*)p->items, (void*)p->qitem0, (void*)p->kvitems, (void*)p->scale,
+                    (void*)p->items, (void*)p->fitems, (void*)p->qitem0, (void*)p->kvitems,
+                    (void*)p->scale,
                     (void*)p->local_ptr, (void*)p->local_idx, (void*)p->kv_of})
     if (ptr) (void)hipFree(ptr);
   delete p;
@@ -290,6 +292,47 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
   }
   p->n_kvitems = (int)(p->h_kvitems.size() / 2);
   p->n_items = (int)(p->h_items.size() / 2);
+  {  // forward work items: the 32-row slots left after 128-row chunks, packed by four, then
+     // the 128-row chunks
+    std::vector<std::pair<int, int>> slots;
+    auto push = [&](const int32_t (&d)[kFItemInts]) {
+      p->h_fitems.insert(p->h_fitems.end(), d, d + kFItemInts);
+    };
+    std::vector<int32_t> full;  // the 128-row chunks' items, placed after the packed ones
+    for (int i = 0; i < p->nq; ++i) {
+      const int sz = p->h_qstart[i + 1] - p->h_qstart[i];
+      int off = 0;
+      for (; off + kAttnRows <= sz; off += kAttnRows) {
+        int32_t d[kFItemInts] = {1, i, i, i, i};
+        for (int w = 0; w < 4; ++w) {
+          d[5 + 2 * w] = 0;
+          d[6 + 2 * w] = off + 32 * w;
+        }
+        full.insert(full.end(), d, d + kFItemInts);
+      }
+      for (; off < sz; off += 32) slots.emplace_back(i, off);
+    }
+    for (size_t s0 = 0; s0 < slots.size(); s0 += 4) {
+      int32_t d[kFItemInts] = {0};
+      int nl = 0;
+      for (int w = 0; w < 4; ++w) {
+        d[5 + 2 * w] = -1;
+        d[6 + 2 * w] = 0;
+        if (s0 + w >= slots.size()) continue;
+        const int i = slots[s0 + w].first;
+        int l = 0;
+        while (l < nl && d[1 + l] != i) ++l;
+        if (l == nl) d[1 + nl++] = i;
+        d[5 + 2 * w] = l;
+        d[6 + 2 * w] = slots[s0 + w].second;
+      }
+      d[0] = nl;
+      for (int l = nl; l < 4; ++l) d[1 + l] = d[1];
+      push(d);
+    }
+    p->h_fitems.insert(p->h_fitems.end(), full.begin(), full.end());
+    p->n_fitems = (int)(p->h_fitems.size() / kFItemInts);
+  }
   {  // local kv blocks of every query block, from each token's kv block
     std::vector<int32_t>& kv_of = p->h_kv_of;
     kv_of.assign(pr.N, 0);
@@ -326,6 +369,7 @@ int bsa_plan_create(const bsa_problem* prob, const float* head_scale, bsa_plan**
   if (upload(qperm_pad, &p->qperm) || upload(p->h_qstart, &p->qstart) ||
       upload(kvperm_pad, &p->kvperm) || upload(p->h_kvstart, &p->kvstart) ||
       upload(p->h_items, &p->items) || upload(p->h_qitem0, &p->qitem0) ||
+      upload(p->h_fitems, &p->fitems) ||
       upload(p->h_kvitems, &p->kvitems) || upload(p->h_scale, &p->scale) ||
       upload(p->h_local_ptr, &p->local_ptr) || upload(p->h_local_idx, &p->local_idx) ||
       upload(p->h_kv_of, &p->kv_of)) {

@@ -17,6 +17,14 @@ constexpr int kMaxSelectBlocks = 8192;
 constexpr int kWaveRowMaxBlocks = 2048;
 // Query rows one attention workgroup owns (4 wavefronts x 32 rows).
 constexpr int kAttnRows = 128;
+// Forward work item: [nl, I_0, I_1, I_2, I_3, (l_w, off_w) for w = 0..3, pad]: wavefront w
+// takes rows off_w .. off_w + 32 of query block I_{l_w} (l_w = -1: no rows), and the workgroup
+// walks the merged CSR rows of I_0 .. I_{nl-1}. A query block's 128-row chunks are items of
+// their own (nl = 1, offsets off + 32 w); the rest of every block is cut into 32-row slots,
+// packed four to an item in block order, and these packed items come first (they stream the
+// union of their blocks' rows, so they are the longest items; starting them first shortened the
+// 480p call by 4 % against placing them last).
+constexpr int kFItemInts = 16;
 
 struct bsa_plan {
   bsa_problem prob;
@@ -30,6 +38,9 @@ struct bsa_plan {
   int32_t* kvperm = nullptr;
   int32_t* kvstart = nullptr;
   int32_t* items = nullptr;   // attention work items: pairs (I, first row within block I)
+  std::vector<int32_t> h_fitems;
+  int32_t* fitems = nullptr;  // sparse forward work items (kFItemInts ints each)
+  int n_fitems = 0;
   int32_t* qitem0 = nullptr;  // [nq + 1]: first work item of each query block
   int n_items = 0;
   int32_t* kvitems = nullptr;  // backward work items: pairs (J, first token within block J)
