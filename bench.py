@@ -47,10 +47,33 @@ def parse():
                          "per-token selection, attention with LSE), e.g. under a profiler")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="only measure the MFMA and copy ceilings (bsa_probe_mfma, "
+                         "bsa_probe_copy) and print them")
     ap.add_argument("--score-path", choices=("fused", "unfused"), default="unfused",
                     help="ROW-pool workloads: scores and selection in one kernel "
                          "(bsa_score_select) or bsa_score then bsa_select")
     return ap.parse_args()
+
+
+def source_sha16(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def sources_sha16():
+    """{attn_fwd.hip: hash, csrc: one hash over every source and header of the library in name
+    order}, recorded with each line so that a profile can name the sources it was taken on."""
+    import glob
+    csrc = os.path.join(ROOT, "block_sparse_attention_bsa_amd", "csrc")
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(csrc, "*"))):
+        if p.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(p).encode())
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return {"attn_fwd.hip": source_sha16(os.path.join(csrc, "attn_fwd.hip")),
+            "csrc": h.hexdigest()[:16]}
 
 
 def read_traffic(kernel_src, workload):
@@ -59,14 +82,13 @@ def read_traffic(kernel_src, workload):
     path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_counters.md")
     if not os.path.exists(path):
         return None
-    with open(kernel_src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    sha = source_sha16(kernel_src)
     vals = {}
     with open(path) as f:
         for line in f:
             if line.startswith("- ") and ":" in line:
                 k, v = line[2:].split(":", 1)
-                vals[k.strip()] = v.strip().strip("`")
+                vals[k.strip()] = (v.split() or [""])[0].strip("`")
     if vals.get("kernel_source_sha256_16") != sha:
         return None
     try:
@@ -196,6 +218,65 @@ def token_global(w, L, q, k, v, out, tm, tau=0.25, calls=5):
             "attn_ms": round(attn_ms, 4),
             "attn_tflops_token": f_tok / (attn_ms * 1e-3) / 1e12,
             "attn_tflops_executed": f_exec / (attn_ms * 1e-3) / 1e12}
+
+
+def dense_reference(w, L, q, k, v, out, tm, calls=3):
+    """The same attention kernel with every block selected (a per-head minimum of nkv blocks
+    keeps every block of every row), timed outside the step: the cost of the sparse walk without
+    sparsity, to compare the step's selected-block rate with."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_bsa_amd import BSA_MINK_FIXED
+    L.pool(q, k)
+    L.score()
+    L.select(1.0, min_k_mode=BSA_MINK_FIXED, fixed_k=L.plan.nkv)
+    for _ in range(calls):
+        with tm("attn_dense"):
+            L.attention(q, k, v, out=out, with_lse=False)
+    torch.cuda.synchronize()
+    rp, ci = L.csr_host()
+    qs, ksz = np.diff(L.plan.blocks(0)[1]), np.diff(L.plan.blocks(1)[1])
+    f = attention_flops(csr_rows(rp, ci), qs, ksz, w.d)
+    attn_ms = tm.mean_ms("attn_dense")
+    tfl = f / (attn_ms * 1e-3) / 1e12
+    return {"density": round(f / (4.0 * w.B * w.H * w.N * w.N * w.d), 4),
+            "attn_ms": round(attn_ms, 4), "attn_tflops": tfl,
+            "frac": tfl / PEAK_BF16_TFLOPS}
+
+
+def measured_peaks(tm, copy_mib=1024, reps=3):
+    """The ceilings on this GPU: the bf16 MFMA rate of back-to-back v_mfma_f32_32x32x16_bf16 and
+    v_mfma_f32_16x16x32_bf16 loops (bsa_probe_mfma), and the read + write rate of a 16-byte grid-stride copy of copy_mib
+    MiB (bsa_probe_copy) and of torch's device copy of the same tensors. Best of reps calls."""
+    import torch
+    from block_sparse_attention_bsa_amd import bsa_probe_copy, bsa_probe_mfma
+    wgs = 2048
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    n = copy_mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    flops = 0.0
+    for _ in range(reps + 1):
+        with tm("probe_mfma"):
+            flops = bsa_probe_mfma(0, wgs, 256, sink)
+        with tm("probe_mfma16"):
+            bsa_probe_mfma(1, wgs, 256, sink)
+        with tm("probe_copy"):
+            bsa_probe_copy(src, dst, n)
+        with tm("probe_torch_copy"):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    best = lambda k: min(a.elapsed_time(b) for a, b in tm.marks[k][1:])  # skip the first call
+    r32 = flops / (best("probe_mfma") * 1e-3) / 1e12
+    r16 = flops / (best("probe_mfma16") * 1e-3) / 1e12
+    return {"mfma_bf16_tflops": round(max(r32, r16), 1),
+            "mfma_32x32x16_tflops": round(r32, 1), "mfma_16x16x32_tflops": round(r16, 1),
+            "copy_kernel_gbs": round(2 * n / (best("probe_copy") * 1e-3) / 1e9, 1),
+            "copy_torch_gbs": round(2 * n / (best("probe_torch_copy") * 1e-3) / 1e9, 1),
+            "copy_bytes_moved": 2 * n,
+            "method": "bsa_probe_mfma (v_mfma_f32_32x32x16_bf16 and 16x16x32 loops, 2048 x 256 "
+                      "threads; the faster counts) and bsa_probe_copy / torch copy_ of 1 GiB, "
+                      "best of 3 calls after one warm-up"}
 
 
 def score_paths(w, L, q, k, mink, tm, calls=10):
@@ -382,6 +463,11 @@ def main():
     import numpy as np
     import torch
 
+    if args.peaks_only:
+        print(json.dumps({"measured_peaks": measured_peaks(Timer(torch.cuda.current_stream())),
+                          "sources_sha256_16": sources_sha16()}), flush=True)
+        return
+
     from gen import CONFIGS, drift_step, kv_partition_for_layer, make_inputs
     from block_sparse_attention_bsa_amd.layer import BlockSparseAttention
 
@@ -493,10 +579,12 @@ def main():
         "call_stats_ms": stage_stats,
         "empty_row_fraction": [round(e, 4) for e in empty],
         "attn_tflops": achieved,
+        "sources_sha256_16": sources_sha16(),
         "pct_bf16_peak_step": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": read_traffic(kernel_src, w.name)},
+                     "traffic": read_traffic(kernel_src, w.name),
+                     "kernel_source_sha256_16": source_sha16(kernel_src)},
     }
     if w.backward:
         res["bwd_tflops"] = 2 * attn_flops / (stages["bwd"] * 1e-3) / 1e12
@@ -546,6 +634,14 @@ def main():
         res["token_topk"] = token_topk(w, layers[0], q, k, v, out, tm)
         if layers[0].plan.nkv <= 768:  # the per-token bitmap attention's limit
             res["token_global"] = token_global(w, layers[0], q, k, v, out, tm)
+        res["dense_reference"] = dense_reference(w, layers[0], q, k, v, out, tm)
+    if not args.no_extras:
+        res["measured_peaks"] = mp = measured_peaks(tm)
+        res["roofline"]["frac_of_measured"] = achieved / mp["mfma_bf16_tflops"]
+        res["roofline"]["measured_peak"] = mp["mfma_bf16_tflops"]
+        if "pool" in res:
+            res["pool"]["pct_of_measured_copy"] = round(
+                100 * res["pool"]["GB/s"] / max(mp["copy_kernel_gbs"], mp["copy_torch_gbs"]), 1)
     if args.copy_ref_mib:
         n = args.copy_ref_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")

@@ -35,6 +35,7 @@ EXPORTED = ("bsa_partition_build", "bsa_plan_create", "bsa_plan_destroy", "bsa_p
             "bsa_tokens_ws",
             "bsa_select_tokens", "bsa_attn_fwd", "bsa_attn_fwd_tokens", "bsa_attn_bwd",
             "bsa_tokens_global_ws", "bsa_select_tokens_global", "bsa_attn_fwd_token_bits",
+            "bsa_probe_mfma", "bsa_probe_copy",
             "bsa_last_error")
 
 
@@ -110,6 +111,8 @@ def lib():
         "bsa_attn_fwd_tokens": [P, P, P, P, P, P, P, I32, P, P, P, SZ, P],
         "bsa_attn_fwd": [P, P, P, P, P, P, P, P, P, SZ, P],
         "bsa_tokens_global_ws": [P, ctypes.POINTER(SZ)],
+        "bsa_probe_mfma": [I32, I32, I32, P, ctypes.POINTER(D), P],
+        "bsa_probe_copy": [P, P, SZ, P],
         "bsa_select_tokens_global": [P, P, P, D, P, P, P, I64, P, SZ, P],
         "bsa_attn_fwd_token_bits": [P, P, P, P, P, P, P, P, P, P, SZ, P],
         "bsa_attn_bwd": [P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
@@ -320,6 +323,19 @@ def bsa_attn_fwd_token_bits(plan: Plan, Q, K, V, row_ptr, col_idx, tbits, O, lse
     _check(lib().bsa_attn_fwd_token_bits(plan.handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(row_ptr),
                                          _ptr(col_idx), _ptr(tbits), _ptr(O), _ptr(lse),
                                          _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def bsa_probe_mfma(shape: int, workgroups: int, iters: int, sink, stream=None) -> float:
+    """Enqueue the bf16 MFMA peak loop (shape 0: 32x32x16, 1: 16x16x32); returns the FLOPs it
+    issues."""
+    f = ctypes.c_double(0.0)
+    _check(lib().bsa_probe_mfma(int(shape), int(workgroups), int(iters), _ptr(sink),
+                                ctypes.byref(f), _stream(stream)))
+    return f.value
+
+
+def bsa_probe_copy(src, dst, nbytes: int, stream=None):
+    _check(lib().bsa_probe_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)))
 
 
 def bsa_attn_fwd(plan: Plan, Q, K, V, row_ptr, col_idx, O, lse, ws, ws_bytes: int, stream=None):

@@ -334,6 +334,17 @@ int bsa_attn_bwd(const bsa_plan* plan, const void* Q, const void* K, const void*
                  const int32_t* col_idx, void* dQ, void* dK, void* dV, void* ws,
                  size_t ws_bytes, void* stream);
 
+/* Measurement helpers, outside the attention path: the ceilings that benches compare the
+ * kernels with, measured on the current GPU. bsa_probe_mfma runs `workgroups` x 256 threads of
+ * back-to-back bf16 MFMAs on register operands -- shape 0: v_mfma_f32_32x32x16_bf16 (iters x 8
+ * per wavefront), shape 1: v_mfma_f32_16x16x32_bf16 (iters x 16) -- and stores the FLOPs it
+ * issues in *flops (host, nullable); sink is device memory of workgroups x 256 floats (not
+ * written in practice). bsa_probe_copy copies `bytes` (a multiple of 16) from src to dst with a
+ * grid-stride 16-byte kernel. Both enqueue on `stream` and return BSA_EINVAL on bad arguments. */
+int bsa_probe_mfma(int32_t shape, int32_t workgroups, int32_t iters, float* sink, double* flops,
+                   void* stream);
+int bsa_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 /* Thread-local description of the last error on this thread ("" if none). */
 const char* bsa_last_error(void);
 

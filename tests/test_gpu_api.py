@@ -160,3 +160,23 @@ def test_backward_is_deterministic():
         for name, a, b in zip(("dQ", "dK", "dV"), first, again):
             assert torch.equal(a, b), f"{name} differs between two identical backward calls"
     log("backward: three calls bit-identical")
+
+
+def test_measurement_probes():
+    """The copy probe copies exactly; the MFMA probe reports the FLOPs it issues and rejects
+    bad arguments (the bench's measured ceilings come from these two)."""
+    import torch
+    import block_sparse_attention_bsa_amd as bsa
+    src = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    bsa.bsa_probe_copy(src, dst, src.numel() * 4)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    sink = torch.zeros(4 * 256, dtype=torch.float32, device="cuda")
+    for shape in (0, 1):
+        f = bsa.bsa_probe_mfma(shape, 4, 3, sink)
+        torch.cuda.synchronize()
+        assert f == 4 * 4 * 3 * 8 * 2 * 32 * 32 * 16
+    assert bsa.lib().bsa_probe_mfma(0, 0, 3, sink.data_ptr(), None, None) == bsa.BSA_EINVAL
+    assert bsa.lib().bsa_probe_mfma(2, 4, 3, sink.data_ptr(), None, None) == bsa.BSA_EINVAL
+    assert bsa.lib().bsa_probe_copy(src.data_ptr(), dst.data_ptr(), 10, None) == bsa.BSA_EINVAL
