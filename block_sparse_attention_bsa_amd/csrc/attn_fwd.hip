@@ -584,6 +584,400 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
     a.lse[(size_t)bh * a.N + qtok] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
+// ------------------------------------------------------- sparse forward on 16x16x32 MFMAs
+
+// The sparse forward (kFwd, kFwdO) on v_mfma_f32_16x16x32_bf16. The work per tile is the body
+// above's, cut into 16 x 16 output tiles: the same FLOPs at the same matrix-pipe rate, but each
+// instruction moves a quarter of the accumulator registers of a 32 x 32 x 16 one, and under the
+// chip's power cap that buys clock (a back-to-back loop of each sustains 2.09 vs 1.93 GHz).
+//
+// Layouts (lane = 16 g + t, g = lane / 16, t = lane % 16; wavefront w owns query rows
+// 32 w .. +32 of the item, in two 16-row tiles qt):
+//   S^T tile (kv rows 16 mt .. +16 of the 64-token step, queries 16 qt .. +16), K = d in 32s:
+//     A = K rows: lane reads row 16 mt + t, d 32 kc + 8 g .. +8 (one 16-byte LDS read);
+//     B = Q^T from registers: query 16 qt + t, d 32 kc + 8 g .. +8;
+//     lane holds S^T[16 mt + 4 g + e][16 qt + t], e = 0..3.
+//   O^T tile (d rows 16 dt .. +16, queries 16 qt .. +16), K = 32 kv rows of half s of the step,
+//   taken in the order the score tiles left them in the lanes: k = 8 g + i is kv row
+//   32 s + 4 g + i (i < 4) or 32 s + 16 + 4 g + i - 4, so
+//     B = P^T is the lane's own weights of score tiles 2 s and 2 s + 1 (no lane exchange);
+//     A = V^T: two transposing 8-byte LDS reads (ds_read_b64_tr_b16) of rows 32 s + 4 g .. +4
+//     and 32 s + 16 + 4 g .. +4, columns 16 dt .. +16 (lane t gets column 16 dt + t);
+//     lane holds O^T[16 dt + 4 g + e][16 qt + t].
+// A query's 64 scores of a step sit in the four lanes t, t + 16, t + 32, t + 48: its running
+// max is kept equal in the four (the exact max of the rare rescale is reduced over them) and its
+// sums are per-lane partials, added over the four at the end.
+//
+// LDS: logical unit u of row r at u ^ lds_key16(r), lds_key16(r) = 2 (r mod 8) + bit 3 of r.
+// The K reads (16 lanes: 16 consecutive rows, one unit) need the key distinct over 16 aligned
+// rows; the V reads (32 lanes: 8 consecutive aligned rows, units {2 dt, 2 dt + 1}, both 8-byte
+// halves) need bits 1-3 of the key distinct over 8 aligned rows. Both hold, so both read
+// patterns are free of bank conflicts.
+__device__ __forceinline__ int lds_key16(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int lds_swz16(int row, int unit) {
+  return (unit ^ lds_key16(row)) << 4;
+}
+
+template <int MODE, bool PACK>
+__device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
+  static_assert(MODE == kFwd || MODE == kFwdO, "the sparse forward only");
+  constexpr int D = 128;
+  constexpr int kStage = 2 * kTileBytes;  // K and V of one 64-token tile
+  char* const lds_a = lds;
+  char* const lds_b = lds + kStage;
+
+  const int n_items = a.n_fitems;
+  const int total = n_items * (int)gridDim.y;
+  const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
+  const int bh = lin / n_items, item = lin % n_items;
+  const int32_t* const desc = a.fitems + kFItemInts * item;
+  const int I = ld_ro(desc + 1);
+  const int q0 = ld_ro(a.qstart + I) + ld_ro(desc + 6);
+  const int nrows = min(128, ld_ro(a.qstart + I + 1) - q0);
+  const int64_t r = (int64_t)bh * a.nq + I;
+  const size_t head_off = (size_t)bh * a.N * D;
+  const float c2 = ld_ro(a.scale + bh % a.H) * kLog2e;  // sigma_h > 0 (checked at plan creation)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = lane & 15, g = lane >> 4;
+  int q0w = q0 + 32 * wave, nroww = nrows - 32 * wave, lw = 0;
+  if constexpr (PACK) {
+    lw = ld_ro(desc + 5 + 2 * wave);
+    const int Iw = ld_ro(desc + 1 + (lw < 0 ? 0 : lw));
+    q0w = ld_ro(a.qstart + Iw) + ld_ro(desc + 6 + 2 * wave);
+    nroww = lw < 0 ? 0 : min(32, ld_ro(a.qstart + Iw + 1) - q0w);
+  }
+  const bool active = nroww > 0;  // wave-uniform
+
+  // Q fragments: query 16 qt + t of the wavefront's rows, d 32 kc + 8 g .. +8.
+  bool qvalid[2];
+  int qtok[2];
+  bf16x8_t qf[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    qvalid[qt] = 16 * qt + t < nroww;
+    qtok[qt] = qvalid[qt] ? a.qperm[q0w + 16 * qt + t] : 0;
+    const uint4* qp = reinterpret_cast<const uint4*>(a.Q + head_off + (size_t)qtok[qt] * D);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const uint4 v = qvalid[qt] ? qp[4 * kc + g] : make_uint4(0, 0, 0, 0);
+      qf[qt][kc] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x4_t oacc[2][8];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oacc[qt][dt][e] = 0.f;
+  // per query: running max (log2 domain), fp32 sum of the weights (kFwd, for the LSE), sum of
+  // the bf16-rounded weights (O is normalised by it); lane partials of the sums
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f}, lb_run[2] = {0.f, 0.f};
+
+  // Loader role as in the body above (wave w fills tile rows 16 w + 4 i + lane / 16), with this
+  // kernel's LDS key.
+  const int lchunk = wave >> 1, loff = 16 * (wave & 1), lgrp = lane >> 4;
+  Cursor cur;
+  MultiCursor mc;
+  if constexpr (PACK) {
+    mc.nl = ld_ro(desc);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const int64_t rl = (int64_t)bh * a.nq + ld_ro(desc + 1 + l);
+      mc.slot[l] = l < mc.nl ? ld_ro(a.row_ptr + rl) : 0;
+      mc.end[l] = l < mc.nl ? ld_ro(a.row_ptr + rl + 1) : 0;
+    }
+    mcursor_load(mc, a.col_idx, a.kvstart, a.nkv);
+  } else {
+    cur.slot = ld_ro(a.row_ptr + r);
+    cur.end = ld_ro(a.row_ptr + r + 1);
+    cur.sub = 0;
+    cursor_load<false>(cur, a.col_idx, a.kvstart, a.nkv);
+  }
+  auto take = [&]() {
+    if constexpr (PACK)
+      return mtake_chunk(mc, a.col_idx, a.kvstart, a.nkv);
+    else
+      return take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
+  };
+  const size_t kv_off = (size_t)bh * a.Npad * D;
+  const uint16_t* const kbase = a.K + kv_off;
+  const uint16_t* const vbase = a.V + kv_off;
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    voff[i] = (uint32_t)((loff + 4 * i + lgrp) * kRowBytes) +
+              16u * (uint32_t)((lane & 15) ^ lds_key16(16 * wave + 4 * i + lgrp));
+  auto tile_issue = [&](Chunk ca, Chunk cb, uint32_t st_m0) {
+    const int pos = (lchunk && cb.nv > 0) ? cb.pos : ca.pos;
+    const uint16_t* kb = kbase + (size_t)pos * D;
+    const uint16_t* vb = vbase + (size_t)pos * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m0v = st_m0 + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
+      lds_dma16_so(kb, voff[i], m0v);
+      lds_dma16_so(vb, voff[i], m0v + kTileBytes);
+    }
+  };
+
+  // Byte offsets within a stage: K fragment (mt, kc) at kofs[kc] + 4096 mt (row 16 mt + t keeps
+  // the key of row t); V fragment (dt, s) at vofs[dt] + 8192 s, its second read 4096 further
+  // (rows 32 s + 4 g + t / 4 and 16 rows on keep the key of row 4 g + t / 4).
+  int kofs[4], vofs[8];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) kofs[kc] = t * kRowBytes + lds_swz16(t, 4 * kc + g);
+  {
+    const int vrow = 4 * g + (t >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      vofs[dt] = kTileBytes + vrow * kRowBytes + lds_swz16(vrow, 2 * dt + ((t & 3) >> 1)) +
+                 8 * (t & 1);
+  }
+
+  const uint32_t m0_a = lds_addr(lds_a), m0_b = lds_addr(lds_b);
+  Chunk a0 = take();
+  Chunk b0 = take();
+  if (a0.nv > 0) tile_issue(a0, b0, m0_a);
+  Chunk a1 = take();
+  Chunk b1 = take();
+  vmem_wait_all();
+  __syncthreads();
+
+  auto step = [&](const char* st, uint32_t nx_m0) {
+    f32x4_t sacc[2][4];  // [qt][mt]
+    bool pa = true, pb = true, act = active;
+    if constexpr (PACK) {  // chunks of blocks this wavefront's query block selected
+      pa = (a0.lmask >> lw) & 1;
+      pb = b0.nv > 0 && ((b0.lmask >> lw) & 1);
+      act = active && (pa || pb);
+    }
+    if (act) {
+      __builtin_amdgcn_s_setprio(2);
+      bf16x8_t kf[4][4];  // [kc][mt]
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          kf[kc][mt] = *reinterpret_cast<const bf16x8_t*>(st + kofs[kc] + 4096 * mt);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[qt][mt][e] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+            sacc[qt][mt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc][mt], qf[qt][kc], sacc[qt][mt], 0, 0, 0);
+      // eight K reads ahead of the MFMAs, then one read per two MFMAs, then the rest
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    const Chunk an = take();
+    const Chunk bn = take();
+    if (a1.nv > 0) tile_issue(a1, b1, nx_m0);
+
+    if (act) {
+      if (a0.nv < 32 || b0.nv < 32) {  // partial chunk(s): mask padded kv rows
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int nv = mt < 2 ? a0.nv : b0.nv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (16 * (mt & 1) + 4 * g + e >= nv) {
+              sacc[0][mt][e] = -INFINITY;
+              sacc[1][mt][e] = -INFINITY;
+            }
+        }
+      }
+      if constexpr (PACK) {  // chunks of blocks this wavefront's query block did not select
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          if (!(mt < 2 ? pa : pb))
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sacc[0][mt][e] = -INFINITY;
+              sacc[1][mt][e] = -INFINITY;
+            }
+      }
+
+      const char* vt = st;
+      auto vfrag = [&](int dt, int s) {
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((lds_char_t*)vt + vofs[dt] + 8192 * s));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)((lds_char_t*)vt + vofs[dt] + 8192 * s + 4096));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+      };
+      bf16x8_t vf0[2];
+      vf0[0] = vfrag(0, 0);
+      vf0[1] = vfrag(0, 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the VALU work below
+
+      // Weights against the running max as it stands, their bf16 packing (the B operands) and
+      // the lane partial sums: fp32 (kFwd, for the LSE) and of the rounded weights.
+      bf16x8_t pbw[2][2];  // [qt][s]
+      float ls[2], lbs[2];
+      auto weights = [&]() {
+        const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          float pv[4][4];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              pv[mt][e] = __builtin_amdgcn_exp2f(fmaf(sacc[qt][mt][e], c2, -m_run[qt]));
+          uint32_t w[8];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            w[2 * mt] = pack_bf16x2(pv[mt][0], pv[mt][1]);
+            w[2 * mt + 1] = pack_bf16x2(pv[mt][2], pv[mt][3]);
+          }
+          float lb0 = 0.f, lb1 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            lb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), one2, lb0,
+                                                  false);
+            lb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i + 1]), one2,
+                                                  lb1, false);
+          }
+          lbs[qt] = lb0 + lb1;
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            pbw[qt][s] = __builtin_bit_cast(
+                bf16x8_t, make_uint4(w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]));
+          if constexpr (MODE == kFwd) {
+            float f0 = pv[0][0], f1 = pv[0][1], f2 = pv[0][2], f3 = pv[0][3];
+#pragma unroll
+            for (int mt = 1; mt < 4; ++mt) {
+              f0 += pv[mt][0];
+              f1 += pv[mt][1];
+              f2 += pv[mt][2];
+              f3 += pv[mt][3];
+            }
+            ls[qt] = (f0 + f1) + (f2 + f3);
+          }
+        }
+      };
+      weights();
+      // The bound: every weight stays <= 2^32 while its lane's partial sum does (kFwdO: the
+      // rounded weights' sum, which bounds them as well). Otherwise (the first tile, where the
+      // max is -inf and the weights +inf, or a tile far above the running max) the running max
+      // of each query is raised to the exact max of c2 * s so far and the weights formed again.
+      const float b0s = MODE == kFwd ? ls[0] : lbs[0], b1s = MODE == kFwd ? ls[1] : lbs[1];
+      if (__ballot(!(b0s <= kSumMax) || !(b1s <= kSumMax)) != 0) {
+        asm volatile("");  // keep this a branch
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          float sm = sacc[qt][0][0];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm = fmaxf(sm, sacc[qt][mt][e]);
+          sm = fmaxf(sm, __shfl_xor(sm, 16, 64));
+          sm = fmaxf(sm, __shfl_xor(sm, 32, 64));
+          const float m_new = fmaxf(m_run[qt], sm * c2);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);  // 0 on the first tile
+          l_run[qt] *= alpha;
+          lb_run[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[qt][dt][e] *= alpha;
+          m_run[qt] = m_new;
+        }
+        weights();
+      }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        lb_run[qt] += lbs[qt];
+        if constexpr (MODE == kFwd) l_run[qt] += ls[qt];
+      }
+
+      // O^T += V^T P^T
+      __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        bf16x8_t vf[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) vf[s] = dt == 0 ? vf0[s] : vfrag(dt, s);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+            oacc[qt][dt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[s], pbw[qt][s], oacc[qt][dt], 0, 0, 0);
+      }
+      // weights first, then the MFMAs with the remaining V reads interleaved, two per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 200, 0);
+#pragma unroll
+      for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 18, 0);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    vmem_wait_all();
+    __syncthreads();
+    a0 = a1;
+    b0 = b1;
+    a1 = an;
+    b1 = bn;
+  };
+  while (true) {
+    if (a0.nv <= 0) break;
+    step(lds_a, m0_b);
+    if (a0.nv <= 0) break;
+    step(lds_b, m0_a);
+  }
+
+  // Sums over the four lanes of each query; O normalised by the rounded weights' sum.
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float lb = lb_run[qt];
+    lb += __shfl_xor(lb, 16, 64);
+    lb += __shfl_xor(lb, 32, 64);
+    float l = 0.f;
+    if constexpr (MODE == kFwd) {
+      l = l_run[qt];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+    }
+    if (qvalid[qt]) {
+      const float inv = lb > 0.f ? 1.f / lb : 0.f;
+      uint16_t* op = a.O + head_off + (size_t)qtok[qt] * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        uint2 pk;
+        pk.x = pack_bf16x2(oacc[qt][dt][0] * inv, oacc[qt][dt][1] * inv);
+        pk.y = pack_bf16x2(oacc[qt][dt][2] * inv, oacc[qt][dt][3] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * dt) = pk;
+      }
+      if constexpr (MODE == kFwd) {
+        if (g == 0)
+          a.lse[(size_t)bh * a.N + qtok[qt]] =
+              l > 0.f ? (m_run[qt] + log2f(l)) * kLn2 : -INFINITY;
+      }
+    }
+  }
+}
+
 // LDS of the two K (and V) stages.
 template <int MODE>
 constexpr int stage_bytes() {
@@ -600,9 +994,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_d128(const MfmaArgs a) {
     const int total = a.n_fitems * (int)gridDim.y;
     const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
     if (ld_ro(a.fitems + kFItemInts * (lin % a.n_fitems)) > 1)
-      attn_mfma_body<MODE, kTokNone, true>(a, lds, none);
+      attn16_body<MODE, true>(a, lds);
     else
-      attn_mfma_body<MODE, kTokNone, false>(a, lds, none);
+      attn16_body<MODE, false>(a, lds);
   } else {
     attn_mfma_body<MODE>(a, lds, none);
   }
