@@ -15,9 +15,10 @@
 //                      lse, D; double-buffered direct copies of consecutive block-order rows). Per chunk and wave: S = Q K^T and
 //                      dP = dO V^T (lane = kv token), P and dS in registers, then
 //                      dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T from transposing reads.
-//   4. dq_kernel       query-stationary over the CSR (one workgroup of four wavefronts per 128
-//                      queries, two workgroups per CU), K and V tiles from block-ordered copies,
-//                      S and dP recomputed per tile.
+//   4. dq16_kernel     query-stationary over the CSR, on the forward's work items (one
+//                      workgroup of four wavefronts per 128 queries, or the packed slots of up to
+//                      four small query blocks; two workgroups per CU), K and V tiles from
+//                      block-ordered copies, S and dP recomputed per tile, 16x16x32 MFMAs.
 #include "bsa_internal.h"
 #include "device_common.h"
 #include "kv_cursor.h"
@@ -469,82 +470,121 @@ struct DqArgs {
   const float* scale;
   uint16_t* dQ;
   int n_items, H, N, nq, nkv, Npad;
+  // the forward's work items (kFItemInts ints each): a query block's 128-row chunk, or the
+  // 32-row slots of up to four small query blocks packed into one workgroup
+  const int32_t* fitems;
+  int n_fitems;
 };
 
 // dQ_i = sigma sum_j dS_ij k_j over the CSR row of i's query block, dS = P (dP - D) with
-// P = exp(sigma q.k - lse) and dP = dO.v recomputed per tile. Query-stationary: a workgroup owns
-// 128 queries of one query block and streams the selected K/V as 64-token tiles (two 32-token
-// chunks) through two LDS stages, as the forward pass does. Eight wavefronts, two per SIMD:
-// wave w owns queries 32 (w % 4) .. +32 and chunk w / 4 of every tile; the two chunks' partial
-// dQ are summed through LDS at the end in a fixed order.
-// dQ with four wavefronts per workgroup (two workgroups per CU): wave w owns queries 32w .. +32
-// of the item and computes both 32-row chunks of every 64-token tile itself, so no partial sums
-// are combined at the end, and the two co-resident workgroups run out of phase with each other
-// (as in the forward kernel) instead of two wavefronts of one workgroup sharing a SIMD in lock
-// step. Per chunk: S^T = K Q^T and dP^T = V dO^T (8 + 8 MFMAs), dS^T = P^T (dP^T - D) in bf16,
-// dQ^T += K^T dS^T (8 MFMAs); chunk 1's matrix work is independent of chunk 0's vector work.
-__global__ __launch_bounds__(256, 2) void dq_kernel(const DqArgs a) {
+// P = exp(sigma q.k - lse) and dP = dO.v recomputed per tile. Query-stationary, as the forward
+// pass: a workgroup of four wavefronts (two workgroups per CU) streams the selected K/V as
+// 64-token tiles (two 32-token chunks) through two LDS stages; each wavefront owns 32 queries.
+//
+// dQ on v_mfma_f32_16x16x32_bf16, over the forward's work items (small query blocks packed four
+// 32-row slots to a workgroup, the tile stream the merged walk of their CSR rows, a wavefront
+// computing only the chunks its own block selected). The lane layouts are the sparse forward's
+// (lane = 16 g + t; wavefront w owns 32 query rows in two 16-row tiles qt):
+//   S^T and dP^T per 16 kv rows (mt) x 16 queries: A = K (or V) rows from LDS, row 16 mt + t,
+//     d 32 kc + 8 g .. +8; B = Q^T (dO^T) from registers; lane holds [16 mt + 4 g + e][16 qt + t];
+//   dQ^T per 16 d (dt) x 16 queries, K = the chunk's 32 kv rows in the order the score tiles
+//     left them (k = 8 g + i: row 4 g + i, or 16 + 4 g + i - 4): A = K^T from two transposing
+//     reads, B = the lane's own dS^T values; lane holds dQ^T[16 dt + 4 g + e][16 qt + t].
+// Per 32-row chunk: 16 + 16 MFMAs for S^T and dP^T, dS^T = P^T (dP^T - D) in bf16, 16 MFMAs for
+// dQ^T. No running max: P = exp(sigma s - lse) with the forward's LSE.
+template <bool PACK>
+__device__ __forceinline__ void dq16_body(const DqArgs& a, char* lds) {
   constexpr int D = 128;
   constexpr int kTile = 64 * kRowBytes;  // one of K / V
   constexpr int kDqStage = 2 * kTile;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kDqStage];
   char* const lds_a = lds;
   char* const lds_b = lds + kDqStage;
 
-  const int n_items = a.n_items;
+  const int n_items = a.n_fitems;
   const int total = n_items * (int)gridDim.y;
   const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
   const int bh = lin / n_items, item = lin % n_items;
-  const int I = ld_ro(a.items + 2 * item), off = ld_ro(a.items + 2 * item + 1);
-  const int q0 = ld_ro(a.qstart + I) + off;
+  const int32_t* const desc = a.fitems + kFItemInts * item;
+  const int I = ld_ro(desc + 1);
+  const int q0 = ld_ro(a.qstart + I) + ld_ro(desc + 6);
   const int nrows = min(128, ld_ro(a.qstart + I + 1) - q0);
   const int64_t r = (int64_t)bh * a.nq + I;
   const size_t head_off = (size_t)bh * a.N * D;
   const float c2 = ld_ro(a.scale + bh % a.H) * kLog2e;
 
-  const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int l32 = lane & 31, hl = lane >> 5;
-  const bool active = 32 * wave < nrows;  // wave-uniform
-
-  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T): query 32 wave + l32.
-  const int qrow = 32 * wave + l32;
-  const bool qvalid = qrow < nrows;
-  const int qtok = qvalid ? a.qperm[q0 + qrow] : 0;
-  bf16x8_t qf[8], dof[8];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.Q + head_off + (size_t)qtok * D + 8 * hl);
-    const uint4* gp = reinterpret_cast<const uint4*>(a.dO + head_off + (size_t)qtok * D + 8 * hl);
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      qf[kc] = __builtin_bit_cast(bf16x8_t, qvalid ? qp[2 * kc] : make_uint4(0, 0, 0, 0));
-      dof[kc] = __builtin_bit_cast(bf16x8_t, qvalid ? gp[2 * kc] : make_uint4(0, 0, 0, 0));
-    }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = lane & 15, g = lane >> 4;
+  int q0w = q0 + 32 * wave, nroww = nrows - 32 * wave, lw = 0;
+  if constexpr (PACK) {
+    lw = ld_ro(desc + 5 + 2 * wave);
+    const int Iw = ld_ro(desc + 1 + (lw < 0 ? 0 : lw));
+    q0w = ld_ro(a.qstart + Iw) + ld_ro(desc + 6 + 2 * wave);
+    nroww = lw < 0 ? 0 : min(32, ld_ro(a.qstart + Iw + 1) - q0w);
   }
-  // log2-domain -lse (-inf for padding queries, so their P is 0) and D of this lane's query.
-  const float nlse2 = qvalid ? -a.lse[(size_t)bh * a.N + qtok] * kLog2e : -INFINITY;
-  const float dq_d = qvalid ? a.delta[(size_t)bh * a.N + qtok] : 0.f;
-  f32x16_t acc[4];  // dQ^T: lane = query, registers = d
+  const bool active = nroww > 0;  // wave-uniform
+
+  // Q and dO fragments, -lse (log2 domain; -inf for padding queries, so their P is 0) and D of
+  // queries 16 qt + t of the wavefront's rows.
+  bool qvalid[2];
+  int qtok[2];
+  float nlse2[2], dq_d[2];
+  bf16x8_t qf[2][4], dof[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int qt = 0; qt < 2; ++qt) {
+    qvalid[qt] = 16 * qt + t < nroww;
+    qtok[qt] = qvalid[qt] ? a.qperm[q0w + 16 * qt + t] : 0;
+    const uint4* qp = reinterpret_cast<const uint4*>(a.Q + head_off + (size_t)qtok[qt] * D);
+    const uint4* gp = reinterpret_cast<const uint4*>(a.dO + head_off + (size_t)qtok[qt] * D);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    for (int kc = 0; kc < 4; ++kc) {
+      qf[qt][kc] = __builtin_bit_cast(bf16x8_t, qvalid[qt] ? qp[4 * kc + g] : make_uint4(0, 0, 0, 0));
+      dof[qt][kc] =
+          __builtin_bit_cast(bf16x8_t, qvalid[qt] ? gp[4 * kc + g] : make_uint4(0, 0, 0, 0));
+    }
+    nlse2[qt] = qvalid[qt] ? -a.lse[(size_t)bh * a.N + qtok[qt]] * kLog2e : -INFINITY;
+    dq_d[qt] = qvalid[qt] ? a.delta[(size_t)bh * a.N + qtok[qt]] : 0.f;
+  }
+  f32x4_t acc[2][8];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[qt][dt][e] = 0.f;
 
   Cursor cur;
-  cur.slot = ld_ro(a.row_ptr + r);
-  cur.end = ld_ro(a.row_ptr + r + 1);
-  cur.sub = 0;
-  cursor_load<false>(cur, a.col_idx, a.kvstart, a.nkv);
+  MultiCursor mc;
+  if constexpr (PACK) {
+    mc.nl = ld_ro(desc);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const int64_t rl = (int64_t)bh * a.nq + ld_ro(desc + 1 + l);
+      mc.slot[l] = l < mc.nl ? ld_ro(a.row_ptr + rl) : 0;
+      mc.end[l] = l < mc.nl ? ld_ro(a.row_ptr + rl + 1) : 0;
+    }
+    mcursor_load(mc, a.col_idx, a.kvstart, a.nkv);
+  } else {
+    cur.slot = ld_ro(a.row_ptr + r);
+    cur.end = ld_ro(a.row_ptr + r + 1);
+    cur.sub = 0;
+    cursor_load<false>(cur, a.col_idx, a.kvstart, a.nkv);
+  }
+  auto take = [&]() {
+    if constexpr (PACK)
+      return mtake_chunk(mc, a.col_idx, a.kvstart, a.nkv);
+    else
+      return take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
+  };
 
-  // Loader: wave w copies rows 16 w + 4 i + lane / 16 (i = 0..3) of the 64-row K and V tiles
-  // (chunk w / 2, rows 16 (w % 2) + 4 i + lane / 16 of it), from the block-ordered copies.
+  // Loader: wave w copies rows 16 w + 4 i + lane / 16 of the 64-row K and V tiles.
   const int lchunk = wave >> 1, loff = 16 * (wave & 1), lgrp = lane >> 4;
   const size_t kv_off = (size_t)bh * a.Npad * D;
   uint32_t voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     voff[i] = (uint32_t)((loff + 4 * i + lgrp) * kRowBytes) +
-              16u * (uint32_t)((lane & 15) ^ lds_key(16 * wave + 4 * i + lgrp));
+              16u * (uint32_t)((lane & 15) ^ lds_key16(16 * wave + 4 * i + lgrp));
   auto tile_issue = [&](Chunk ca, Chunk cb, uint32_t st_m0) {
     const int pos = (lchunk && cb.nv > 0) ? cb.pos : ca.pos;
     const uint16_t* kb = a.Kp + kv_off + (size_t)pos * D;
@@ -556,82 +596,137 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const DqArgs a) {
       lds_dma16_so(vb, voff[i], m0v + kTile);
     }
   };
-
-  // Transposing-read offsets for K^T (as for V^T in the forward kernel).
-  const int vrow_l = 4 * hl + ((lane & 15) >> 2);
-  const int vunit_l = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int vhalf_l = 8 * (lane & 1);
+  // Byte offsets within a stage: K (V) fragment (mt, kc) of chunk s at kofs[kc] + 4096 (2 s + mt)
+  // (+ kTile for V); K^T fragment dt of chunk s at tofs[dt] + 8192 s, its second read 4096 on.
+  int kofs[4], tofs[8];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) kofs[kc] = t * kRowBytes + lds_swz16(t, 4 * kc + g);
+  {
+    const int trow = 4 * g + (t >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      tofs[dt] = trow * kRowBytes + lds_swz16(trow, 2 * dt + ((t & 3) >> 1)) + 8 * (t & 1);
+  }
 
   const uint32_t m0_a = lds_addr(lds_a), m0_b = lds_addr(lds_b);
-  Chunk a0 = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
-  Chunk b0 = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
+  Chunk a0 = take();
+  Chunk b0 = take();
   if (a0.nv > 0) tile_issue(a0, b0, m0_a);
-  Chunk a1 = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
-  Chunk b1 = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
+  Chunk a1 = take();
+  Chunk b1 = take();
   vmem_wait_all();
   __syncthreads();
 
-  // One chunk (kv rows 32 ch .. +32 of the tile at st).
-  auto chunk = [&](const char* st, int ch, int nv) {
-    const int row = 32 * ch + l32;
-    const char* kp = st + row * kRowBytes;
-    const char* vp = st + kTile + row * kRowBytes;
-    f32x16_t sacc, dpacc;
+  // One 32-row chunk s of the tile at st.
+  auto chunk = [&](const char* st, int s, int nv) {
+    f32x4_t sacc[2][2], dpacc[2][2];  // [qt][mt]
+    __builtin_amdgcn_s_setprio(2);
+    {
+      bf16x8_t kf[4][2], vf[4][2];  // [kc][mt]
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sacc[e] = 0.f;
-      dpacc[e] = 0.f;
-    }
+      for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kp + lds_swz(row, 2 * kc + hl));
-      const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vp + lds_swz(row, 2 * kc + hl));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], sacc, 0, 0, 0);
-      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[kc], dpacc, 0, 0, 0);
+        for (int mt = 0; mt < 2; ++mt) {
+          kf[kc][mt] = *reinterpret_cast<const bf16x8_t*>(st + kofs[kc] + 4096 * (2 * s + mt));
+          vf[kc][mt] =
+              *reinterpret_cast<const bf16x8_t*>(st + kTile + kofs[kc] + 4096 * (2 * s + mt));
+        }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sacc[qt][mt][e] = 0.f;
+            dpacc[qt][mt][e] = 0.f;
+          }
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            sacc[qt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc][mt], qf[qt][kc],
+                                                                    sacc[qt][mt], 0, 0, 0);
+            dpacc[qt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kc][mt], dof[qt][kc],
+                                                                     dpacc[qt][mt], 0, 0, 0);
+          }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (nv < 32) {  // partial chunk: padded kv rows get P = 0
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (8 * (e >> 2) + 4 * hl + (e & 3) >= nv) sacc[e] = -INFINITY;
-    }
-    // dS^T = P^T * (dP^T - D), rounded to bf16 (the B operand of dQ^T += K^T dS^T).
-    uint32_t dw[8];
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e], c2, nlse2));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[e + 1], c2, nlse2));
-      dw[e >> 1] = pack_bf16x2(p0 * (dpacc[e] - dq_d), p1 * (dpacc[e + 1] - dq_d));
+        for (int e = 0; e < 4; ++e)
+          if (16 * mt + 4 * g + e >= nv) {
+            sacc[0][mt][e] = -INFINITY;
+            sacc[1][mt][e] = -INFINITY;
+          }
     }
-    // dQ^T += K^T dS^T over the chunk's 32 kv rows (two 16-row k-steps); each K^T fragment is
-    // two transposing 8-byte reads of the K tile.
+    // K^T fragments of the chunk, read ahead of the vector work.
+    auto tfrag = [&](int dt) {
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)((lds_char_t*)st + tofs[dt] + 8192 * s));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)((lds_char_t*)st + tofs[dt] + 8192 * s + 4096));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+    };
+    const bf16x8_t kt0 = tfrag(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // dS^T = P^T (dP^T - D), rounded to bf16: the B operand of dQ^T += K^T dS^T.
+    bf16x8_t dsb[2];
 #pragma unroll
-    for (int dm = 0; dm < 4; ++dm) {
+    for (int qt = 0; qt < 2; ++qt) {
+      uint32_t w[4];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int row_lo = 32 * ch + 16 * kk + vrow_l, row_hi = row_lo + 8;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)((lds_char_t*)st + row_lo * kRowBytes +
-                           lds_swz(row_lo, 4 * dm + vunit_l) + vhalf_l));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_t*)((lds_char_t*)st + row_hi * kRowBytes +
-                           lds_swz(row_hi, 4 * dm + vunit_l) + vhalf_l));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        const bf16x8_t kt = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
-        const bf16x8_t dsb = __builtin_bit_cast(
-            bf16x8_t, make_uint4(dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]));
-        acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb, acc[dm], 0, 0, 0);
-      }
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qt][mt][e], c2, nlse2[qt]));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qt][mt][e + 1], c2, nlse2[qt]));
+          w[2 * mt + (e >> 1)] = pack_bf16x2(p0 * (dpacc[qt][mt][e] - dq_d[qt]),
+                                             p1 * (dpacc[qt][mt][e + 1] - dq_d[qt]));
+        }
+      dsb[qt] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
     }
+    __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const bf16x8_t kt = dt == 0 ? kt0 : tfrag(dt);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, dsb[qt], acc[qt][dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 100, 0);
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   auto step = [&](const char* st, uint32_t nx_m0) {
-    if (active) {
-      chunk(st, 0, a0.nv);
-      if (b0.nv > 0) chunk(st, 1, b0.nv);
+    bool pa = true, pb = b0.nv > 0;
+    if constexpr (PACK) {  // chunks of blocks this wavefront's query block selected
+      pa = (a0.lmask >> lw) & 1;
+      pb = pb && ((b0.lmask >> lw) & 1);
     }
-    // The next tile's copies (issued after this tile's matrix work has been issued).
-    const Chunk an = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
-    const Chunk bn = take_chunk<false>(cur, a.col_idx, a.kvstart, a.nkv);
+    if (active) {
+      if (pa) chunk(st, 0, a0.nv);
+      if (pb) chunk(st, 1, b0.nv);
+    }
+    const Chunk an = take();
+    const Chunk bn = take();
     if (a1.nv > 0) tile_issue(a1, b1, nx_m0);
     vmem_wait_all();
     __syncthreads();
@@ -647,20 +742,30 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(const DqArgs a) {
     step(lds_b, m0_a);
   }
 
-  if (!qvalid) return;
   const float sig = a.scale[bh % a.H];  // dQ = sigma_h dS K
-  uint16_t* op = a.dQ + head_off + (size_t)qtok * D;
 #pragma unroll
-  for (int dm = 0; dm < 4; ++dm)
+  for (int qt = 0; qt < 2; ++qt) {
+    if (!qvalid[qt]) continue;
+    uint16_t* op = a.dQ + head_off + (size_t)qtok[qt] * D + 4 * g;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int dt = 0; dt < 8; ++dt) {
       uint2 pk;
-      pk.x = pack_bf16x2(acc[dm][4 * g] * sig, acc[dm][4 * g + 1] * sig);
-      pk.y = pack_bf16x2(acc[dm][4 * g + 2] * sig, acc[dm][4 * g + 3] * sig);
-      *reinterpret_cast<uint2*>(op + 32 * dm + 8 * g + 4 * hl) = pk;
+      pk.x = pack_bf16x2(acc[qt][dt][0] * sig, acc[qt][dt][1] * sig);
+      pk.y = pack_bf16x2(acc[qt][dt][2] * sig, acc[qt][dt][3] * sig);
+      *reinterpret_cast<uint2*>(op + 16 * dt) = pk;
     }
+  }
 }
 
+__global__ __launch_bounds__(256, 2) void dq16_kernel(const DqArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[4 * 64 * kRowBytes];
+  const int total = a.n_fitems * (int)gridDim.y;
+  const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
+  if (ld_ro(a.fitems + kFItemInts * (lin % a.n_fitems)) > 1)
+    dq16_body<true>(a, lds);
+  else
+    dq16_body<false>(a, lds);
+}
 
 }  // namespace
 
@@ -744,6 +849,8 @@ hipError_t launch_attn_bwd(const bsa_plan& p, const void* Q, const void* K, cons
   q.nq = p.nq;
   q.nkv = p.nkv;
   q.Npad = Npad;
-  dq_kernel<<<dim3(p.n_items, BH), 256, 0, s>>>(q);
+  q.fitems = p.fitems;
+  q.n_fitems = p.n_fitems;
+  dq16_kernel<<<dim3(p.n_fitems, BH), 256, 0, s>>>(q);
   return hipGetLastError();
 }

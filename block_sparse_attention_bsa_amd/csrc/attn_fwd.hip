@@ -608,15 +608,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
 // max is kept equal in the four (the exact max of the rare rescale is reduced over them) and its
 // sums are per-lane partials, added over the four at the end.
 //
-// LDS: logical unit u of row r at u ^ lds_key16(r), lds_key16(r) = 2 (r mod 8) + bit 3 of r.
-// The K reads (16 lanes: 16 consecutive rows, one unit) need the key distinct over 16 aligned
-// rows; the V reads (32 lanes: 8 consecutive aligned rows, units {2 dt, 2 dt + 1}, both 8-byte
-// halves) need bits 1-3 of the key distinct over 8 aligned rows. Both hold, so both read
-// patterns are free of bank conflicts.
-__device__ __forceinline__ int lds_key16(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
-__device__ __forceinline__ int lds_swz16(int row, int unit) {
-  return (unit ^ lds_key16(row)) << 4;
-}
+// LDS: the tiles use lds_key16 (device_common.h), under which both read patterns are free of
+// bank conflicts.
 
 template <int MODE, bool PACK>
 __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {

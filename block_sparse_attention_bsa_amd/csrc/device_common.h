@@ -114,6 +114,16 @@ __device__ __forceinline__ int lds_key(int row) {
 }
 __device__ __forceinline__ int lds_swz(int row, int unit) { return (unit ^ lds_key(row)) << 4; }
 
+// The key of the kernels on 16x16x32 MFMAs: lds_key16(r) = 2 (r mod 8) + bit 3 of r. Their
+// 16-byte operand reads take one unit from 16 consecutive aligned rows (16 lanes per LDS cycle:
+// the key must be distinct over 16 aligned rows) and their transposing 8-byte reads take units
+// {2 m, 2 m + 1}, both halves, from 8 consecutive aligned rows (32 lanes per cycle: bits 1-3 of
+// the key must be distinct over 8 aligned rows). Both hold, so both patterns are conflict free.
+__device__ __forceinline__ int lds_key16(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int lds_swz16(int row, int unit) {
+  return (unit ^ lds_key16(row)) << 4;
+}
+
 // Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane i of the
 // wavefront writes LDS bytes [lds_base + 16 i, +16). lds_base must be wave-uniform. Issued from
 // inline assembly so that the compiler does not order later LDS reads of *other* buffers behind
