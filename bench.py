@@ -244,6 +244,29 @@ def dense_reference(w, L, q, k, v, out, tm, calls=3):
             "frac": tfl / PEAK_BF16_TFLOPS}
 
 
+def p_sweep(w, L, q, k, v, out, tm, ps=(0.3, 0.6), calls=3):
+    """The same layer at lower thresholds p (sparser block sets than the workload's p), timed
+    outside the step: the attention kernel's selected-block rate across densities."""
+    import numpy as np
+    import torch
+    L.pool(q, k)
+    L.score()
+    qs, ksz = np.diff(L.plan.blocks(0)[1]), np.diff(L.plan.blocks(1)[1])
+    res = {}
+    for p in ps:
+        L.select(p)
+        for _ in range(calls):
+            with tm(f"attn_p{p}"):
+                L.attention(q, k, v, out=out, with_lse=False)
+        torch.cuda.synchronize()
+        rp, ci = L.csr_host()
+        f = attention_flops(csr_rows(rp, ci), qs, ksz, w.d)
+        ms = tm.mean_ms(f"attn_p{p}")
+        res[str(p)] = {"density": round(f / (4.0 * w.B * w.H * w.N * w.N * w.d), 4),
+                       "attn_ms": round(ms, 4), "attn_tflops": f / (ms * 1e-3) / 1e12}
+    return res
+
+
 def measured_peaks(tm, copy_mib=1024, reps=3):
     """The ceilings on this GPU: the bf16 MFMA rate of back-to-back v_mfma_f32_32x32x16_bf16 and
     v_mfma_f32_16x16x32_bf16 loops (bsa_probe_mfma), and the read + write rate of a 16-byte grid-stride copy of copy_mib
@@ -634,6 +657,7 @@ def main():
         res["token_topk"] = token_topk(w, layers[0], q, k, v, out, tm)
         if layers[0].plan.nkv <= 768:  # the per-token bitmap attention's limit
             res["token_global"] = token_global(w, layers[0], q, k, v, out, tm)
+        res["p_sweep"] = p_sweep(w, layers[0], q, k, v, out, tm)
         res["dense_reference"] = dense_reference(w, layers[0], q, k, v, out, tm)
     if not args.no_extras:
         res["measured_peaks"] = mp = measured_peaks(tm)

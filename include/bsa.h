@@ -45,7 +45,10 @@
  *     it. Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the null stream).
  *     Results are deterministic: the same inputs give the same bits.
  *   - NaN inputs propagate into scores and outputs; the selection made from NaN scores is
- *     unspecified but always a valid CSR.
+ *     unspecified but always a valid CSR. A non-finite value in V can also reach queries whose
+ *     selection does not include its token: the bf16 attention streams 32-token chunks padded
+ *     past a block's end with the next tokens' rows, whose weights are exactly 0, and 0 times a
+ *     non-finite value is NaN. Non-finite K values in padded rows are masked and do not leak.
  */
 #ifndef BSA_H
 #define BSA_H
