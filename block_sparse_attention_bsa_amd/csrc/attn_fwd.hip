@@ -594,7 +594,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
 // Layouts (lane = 16 g + t, g = lane / 16, t = lane % 16; wavefront w owns query rows
 // 32 w .. +32 of the item, in two 16-row tiles qt):
 //   S^T tile (kv rows 16 mt .. +16 of the 64-token step, queries 16 qt .. +16), K = d in 32s:
-//     A = K rows: lane reads row 16 mt + t, d 32 kc + 8 g .. +8 (one 16-byte LDS read);
+//     A = K rows: lane reads row 16 mt + t, d 32 kc + 8 g .. +8 (one 16-byte LDS read; K is
+//     stored in 1 KB fragment tiles so that these reads are contiguous);
 //     B = Q^T from registers: query 16 qt + t, d 32 kc + 8 g .. +8;
 //     lane holds S^T[16 mt + 4 g + e][16 qt + t], e = 0..3.
 //   O^T tile (d rows 16 dt .. +16, queries 16 qt .. +16), K = 32 kv rows of half s of the step,
@@ -608,8 +609,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
 // max is kept equal in the four (the exact max of the rare rescale is reduced over them) and its
 // sums are per-lane partials, added over the four at the end.
 //
-// LDS: the tiles use lds_key16 (device_common.h), under which both read patterns are free of
-// bank conflicts.
+// LDS: K in fragment tiles, V row-major under lds_key16 (device_common.h); both read patterns
+// are free of bank conflicts (measured: SQ_LDS_BANK_CONFLICT).
 
 template <int MODE, bool PACK>
 __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
@@ -699,11 +700,18 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
   const size_t kv_off = (size_t)bh * a.Npad * D;
   const uint16_t* const kbase = a.K + kv_off;
   const uint16_t* const vbase = a.V + kv_off;
-  uint32_t voff[4];
+  // K is stored tiled: the 16 rows x 4 units (d 32 kc .. +32) of fragment (mt, kc) form one
+  // 1 KB block (block 4 mt + kc), unit-major, so that a wavefront's 16-byte operand reads of a
+  // fragment are 1 KB of consecutive LDS (row-major rows read that way, 16 rows x 4 units,
+  // cost 4 bank-conflict cycles per read under any XOR key). V stays row-major under
+  // lds_key16 for its transposing reads. Copy i of wave w fills block 4 w + i of either tile.
+  uint32_t koff[4], voff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = (uint32_t)((loff + (lane & 15)) * kRowBytes) + 16u * (uint32_t)(4 * i + (lane >> 4));
     voff[i] = (uint32_t)((loff + 4 * i + lgrp) * kRowBytes) +
               16u * (uint32_t)((lane & 15) ^ lds_key16(16 * wave + 4 * i + lgrp));
+  }
   auto tile_issue = [&](Chunk ca, Chunk cb, uint32_t st_m0) {
     const int pos = (lchunk && cb.nv > 0) ? cb.pos : ca.pos;
     const uint16_t* kb = kbase + (size_t)pos * D;
@@ -711,17 +719,15 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t m0v = st_m0 + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
-      lds_dma16_so(kb, voff[i], m0v);
+      lds_dma16_so(kb, koff[i], m0v);
       lds_dma16_so(vb, voff[i], m0v + kTileBytes);
     }
   };
 
-  // Byte offsets within a stage: K fragment (mt, kc) at kofs[kc] + 4096 mt (row 16 mt + t keeps
-  // the key of row t); V fragment (dt, s) at vofs[dt] + 8192 s, its second read 4096 further
-  // (rows 32 s + 4 g + t / 4 and 16 rows on keep the key of row 4 g + t / 4).
-  int kofs[4], vofs[8];
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) kofs[kc] = t * kRowBytes + lds_swz16(t, 4 * kc + g);
+  // Byte offsets within a stage: K fragment (mt, kc) at 4096 mt + 1024 kc + 16 lane; V fragment
+  // (dt, s) at vofs[dt] + 8192 s, its second read 4096 further (rows 32 s + 4 g + t / 4 and 16
+  // rows on keep the key of row 4 g + t / 4).
+  int vofs[8];
   {
     const int vrow = 4 * g + (t >> 2);
 #pragma unroll
@@ -754,7 +760,7 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
       for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          kf[kc][mt] = *reinterpret_cast<const bf16x8_t*>(st + kofs[kc] + 4096 * mt);
+          kf[kc][mt] = *reinterpret_cast<const bf16x8_t*>(st + 4096 * mt + 1024 * kc + 16 * lane);
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
