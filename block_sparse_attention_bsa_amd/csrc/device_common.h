@@ -115,10 +115,11 @@ __device__ __forceinline__ int lds_key(int row) {
 __device__ __forceinline__ int lds_swz(int row, int unit) { return (unit ^ lds_key(row)) << 4; }
 
 // The key of the kernels on 16x16x32 MFMAs: lds_key16(r) = 2 (r mod 8) + bit 3 of r. Their
-// 16-byte operand reads take one unit from 16 consecutive aligned rows (16 lanes per LDS cycle:
-// the key must be distinct over 16 aligned rows) and their transposing 8-byte reads take units
-// {2 m, 2 m + 1}, both halves, from 8 consecutive aligned rows (32 lanes per cycle: bits 1-3 of
-// the key must be distinct over 8 aligned rows). Both hold, so both patterns are conflict free.
+// transposing 8-byte reads (a 16-lane group: 4 rows x units {2 m, 2 m + 1}; the wavefront: 16
+// consecutive rows) need bits 1-3 of the key distinct over 8 aligned rows, which holds: no bank
+// conflicts (SQ_LDS_BANK_CONFLICT = 0 in a probe). Their 16-byte row reads (lane 16 g + t: row
+// t, unit 4 c + g) conflict under this key and under the 32x32 kernels' (4 cycles per read):
+// the forward stores K in fragment tiles instead, where those reads are contiguous.
 __device__ __forceinline__ int lds_key16(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 __device__ __forceinline__ int lds_swz16(int row, int unit) {
   return (unit ^ lds_key16(row)) << 4;
