@@ -134,46 +134,78 @@ __global__ __launch_bounds__(256) void tg_gates_kernel(
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[kc], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[kc], acc, 0, 0, 0);
     }
-    // lane holds token column l32 and block rows 8 (e / 4) + 4 hl + e % 4 of the tile
+    // lane holds token column l32 and block rows 8 (e / 4) + 4 hl + e % 4 of the tile: four
+    // runs of four consecutive blocks, stored 16 bytes at a time when rows are 16-byte aligned
     const int J0 = it * kTgTile;
     if (valid) {
+      if ((nkv & 3) == 0) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int J = J0 + 8 * (e >> 2) + 4 * hl + (e & 3);
-        if (J < nkv) {
-          const float v = sig * acc[e];
-          grow[J] = v;
-          gmax = fmaxf(gmax, v);
+        for (int q = 0; q < 4; ++q) {
+          const int J = J0 + 8 * q + 4 * hl;
+          if (J < nkv) {
+            const float4 v = make_float4(sig * acc[4 * q], sig * acc[4 * q + 1],
+                                         sig * acc[4 * q + 2], sig * acc[4 * q + 3]);
+            *reinterpret_cast<float4*>(grow + J) = v;
+            gmax = fmaxf(gmax, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int J = J0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+          if (J < nkv) {
+            const float v = sig * acc[e];
+            grow[J] = v;
+            gmax = fmaxf(gmax, v);
+          }
         }
       }
     }
     if (it + 1 < ntiles) store(st ^ 1);
     __syncthreads();
   }
+  // one integer atomic per workgroup on the head's order-preserving max key
+  __shared__ float wmax[4];
   gmax = wave_max_f32(gmax);
-  if (lane == 0 && gmax > -INFINITY) atomicMax(&heads[bh].gmax, tg_gate_key(gmax));
+  if (lane == 0) wmax[wave] = gmax;
+  __syncthreads();
+  if (t == 0) {
+    const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (m > -INFINITY) atomicMax(&heads[bh].gmax, tg_gate_key(m));
+  }
 }
 
-// e = exp(g - max g) in place, and the range of e's keys per head (integer atomics).
+// e = exp(g - max g) in place (as exp2 of the log2 e-scaled difference, v_exp_f32), and the range
+// of e's keys per head (integer atomics, one pair per workgroup).
 __global__ __launch_bounds__(256) void tg_exp_kernel(float* __restrict__ g, int64_t per_head,
                                                      TgHead* __restrict__ heads) {
   const int bh = blockIdx.y;
   const float m = tg_gate_from_key(heads[bh].gmax);
   float* p = g + (size_t)bh * per_head;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
+  const float ml = m * kLog2e;
   for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < per_head;
        j += (int64_t)gridDim.x * 256) {
-    const float e = expf(p[j] - m);
+    // at most 1 (the max gate's rounding could give exp2 of a tiny positive number)
+    const float e = fminf(__builtin_amdgcn_exp2f(fmaf(p[j], kLog2e, -ml)), 1.f);
     p[j] = e;
     const uint32_t k = sel_key(e);
     kmin = min(kmin, k);
     kmax = max(kmax, k);
   }
+  // one atomic pair per workgroup (the range is an integer min / max: order-free)
+  __shared__ uint32_t wk[2][4];
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
+  const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    atomicMin(&heads[bh].kmin, kmin);
-    atomicMax(&heads[bh].kmax, kmax);
+    wk[0][w] = kmin;
+    wk[1][w] = kmax;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicMin(&heads[bh].kmin, min(min(wk[0][0], wk[0][1]), min(wk[0][2], wk[0][3])));
+    atomicMax(&heads[bh].kmax, max(max(wk[1][0], wk[1][1]), max(wk[1][2], wk[1][3])));
   }
 }
 
@@ -217,13 +249,9 @@ __global__ __launch_bounds__(256) void tg_hist_kernel(const float* __restrict__ 
   tg_digit(h, db, sh, dmask);
   const float* p = e + (size_t)bh * per_head;
   constexpr int kPer = kTgChunk / 256;
-  const int64_t j0 = base + kPer * t;
   uint32_t run_bin = 256u, run_cnt = 0u;
   unsigned long long run_sum = 0ull;
-  for (int u = 0; u < kPer; ++u) {
-    const int64_t j = j0 + u;
-    if (j >= per_head) break;
-    const float v = p[j];
+  auto add = [&](float v) {
     const uint32_t uk = sel_key(v) - h.kmin;
     if ((uk >> h.rem) == h.hi) {
       const uint32_t bin = (uk >> sh) & dmask;
@@ -238,6 +266,26 @@ __global__ __launch_bounds__(256) void tg_hist_kernel(const float* __restrict__ 
       }
       ++run_cnt;
       run_sum += tg_fix(v, h.shift);
+    }
+  };
+  // kPer / 4 rounds of 16-byte loads, each round 4 KB of consecutive pool entries (the pool of
+  // a head starts 16-byte aligned when nkv * N is a multiple of 4; else one value at a time)
+  if ((per_head & 3) == 0) {
+#pragma unroll
+    for (int q = 0; q < kPer / 4; ++q) {
+      const int64_t j = base + 4 * (t + 256 * q);
+      if (j < per_head) {
+        const float4 v = *reinterpret_cast<const float4*>(p + j);
+        add(v.x);
+        add(v.y);
+        add(v.z);
+        add(v.w);
+      }
+    }
+  } else {
+    for (int q = 0; q < kPer; ++q) {
+      const int64_t j = base + t + 256 * q;
+      if (j < per_head) add(p[j]);
     }
   }
   if (run_cnt) {
@@ -363,29 +411,29 @@ __global__ __launch_bounds__(256) void tg_mark_kernel(const float* __restrict__ 
                                                       const TgHead* __restrict__ heads,
                                                       uint32_t* __restrict__ tbits,
                                                       int32_t* __restrict__ bnd, int nchunk) {
-  __shared__ int sbnd;
-  const int bh = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
+  __shared__ int sbnd[4];
+  const int bh = blockIdx.y, c = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const TgHead h = heads[bh];
   const int r0 = c * kTgRows, nr = min(kTgRows, N - r0);
-  if (t == 0) sbnd = 0;
-  __syncthreads();
+  // wavefront w takes rows w, w + 4, ...: lane l tests blocks 64 i + l (coalesced reads), a
+  // ballot gives two bitmap words per 64 blocks
   int my = 0;
-  for (int wi = t; wi < nr * nwords; wi += 256) {
-    const int rr = wi / nwords, w = wi - rr * nwords;
+  for (int rr = wave; rr < nr; rr += 4) {
     const float* row = e + ((size_t)bh * N + r0 + rr) * nkv;
-    uint32_t word = 0u;
-    for (int b = 0; b < 32; ++b) {
-      const int J = 32 * w + b;
-      if (J >= nkv) break;
-      bool bd;
-      if (tg_selected(h, row[J], bd)) word |= 1u << b;
-      my += bd;
+    uint32_t* out = tbits + ((size_t)bh * N + r0 + rr) * nwords;
+    for (int J0 = 0; J0 < nkv; J0 += 64) {
+      const int J = J0 + lane;
+      bool sel = false, bd = false;
+      if (J < nkv) sel = tg_selected(h, row[J], bd);
+      const unsigned long long bal = __ballot(sel);
+      my += __popcll(__ballot(bd));
+      const int w = (J0 >> 5) + lane;
+      if (lane < 2 && w < nwords) out[w] = (uint32_t)(bal >> (32 * lane));
     }
-    tbits[((size_t)bh * N + r0 + rr) * nwords + w] = word;
   }
-  if (my) atomicAdd(&sbnd, my);
+  if (lane == 0) sbnd[wave] = my;
   __syncthreads();
-  if (t == 0) bnd[(size_t)bh * nchunk + c] = sbnd;
+  if (t == 0) bnd[(size_t)bh * nchunk + c] = (sbnd[0] + sbnd[1]) + (sbnd[2] + sbnd[3]);
 }
 
 // When only part of the boundary class is kept: its members in pool index order (token, then
@@ -480,7 +528,7 @@ hipError_t launch_select_tokens_global(const bsa_plan& p, const void* Q, const f
   tg_init_kernel<<<BH, 256, 0, s>>>(heads, hist, shift);
   tg_gates_kernel<<<dim3((N + 127) / 128, BH), 256, 0, s>>>(
       static_cast<const uint16_t*>(Q), khi, klo, p.scale, p.prob.H, N, nkv, e, heads);
-  const unsigned egrid = (unsigned)std::min<int64_t>((per_head + 255) / 256, 1024);
+  const unsigned egrid = (unsigned)std::min<int64_t>((per_head + 255) / 256, 256);
   tg_exp_kernel<<<dim3(egrid, BH), 256, 0, s>>>(e, per_head, heads);
   tg_setup_kernel<<<BH, 64, 0, s>>>(heads);
   if ((err = hipGetLastError()) != hipSuccess) return err;
