@@ -892,19 +892,32 @@ __global__ __launch_bounds__(256) void eg_hist_kernel(const float* __restrict__ 
   ssum[t] = 0ull;
   __syncthreads();
   const int b = gi / ngh, g = gi % ngh, shift = 24 - 8 * pass;
-  // 16 consecutive candidates per thread (mostly one score row): neighbours usually share a
-  // digit bin in the early passes, so runs of equal bins are summed in registers and added to
-  // the LDS histogram once per run
+  // Candidate j = base + t + 256 u (neighbouring lanes read neighbouring scores: coalesced),
+  // its (pooled head k, query block I, kv block J) advanced from one u to the next without a
+  // division per candidate. The early passes put most candidates into one or two bins, so runs
+  // of equal bins are summed in registers and added to the LDS histogram once per run.
   constexpr int kPer = kEgHistChunk / 256;
-  const int j0 = base + kPer * t;
+  const int per = nq * nkv, dq = 256 / nkv, dJ = 256 - dq * nkv;
+  int j = base + t;
+  int k = j / per, I = (j - k * per) / nkv, J = j - k * per - I * nkv;
   uint32_t run_bin = 256u, run_cnt = 0u;
   unsigned long long run_sum = 0ull;
-  for (int u = 0; u < kPer; ++u) {
-    const int j = j0 + u;
+  for (int u = 0; u < kPer; ++u, j += 256) {
     if (j >= pool_n) break;
-    int64_t row;
-    int J;
-    const float v = eg_candidate(S, qstart, members, b, g, H, G, nq, nkv, N, st.m, j, row, J);
+    if (u) {
+      J += dJ;
+      I += dq;
+      if (J >= nkv) {
+        J -= nkv;
+        ++I;
+      }
+      if (I >= nq) {
+        k += I / nq;
+        I %= nq;
+      }
+    }
+    const int64_t row = ((int64_t)b * H + members[b * H + g * G + k]) * nq + I;
+    const float v = eg_weight(S[row * nkv + J], qstart[I + 1] - qstart[I], N, st.m);
     const uint32_t key = sel_key(v);
     if ((key & st.mask) == st.prefix) {
       const uint32_t bin = (key >> shift) & 255u;
@@ -1028,45 +1041,42 @@ __global__ __launch_bounds__(256) void eg_mark_kernel(const float* __restrict__ 
                                                       uint32_t* __restrict__ bitmap,
                                                       int32_t* __restrict__ base_counts,
                                                       int32_t* __restrict__ bnd) {
-  __shared__ int rcnt[kEgRowChunk];
-  __shared__ int sbnd;
+  __shared__ int sbnd[4];
   const int gi = blockIdx.y;
   const EgGroup st = groups[gi];
   if (st.m == 0) return;
   const int prow = st.m * nq, R0 = blockIdx.x * kEgRowChunk;
   if (R0 >= prow) return;
-  const int nr = min(kEgRowChunk, prow - R0), t = threadIdx.x;
-  if (t < kEgRowChunk) rcnt[t] = 0;
-  if (t == 0) sbnd = 0;
-  __syncthreads();
+  const int nr = min(kEgRowChunk, prow - R0), t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int b = gi / ngh, g = gi % ngh;
+  // wavefront w takes pool rows w, w + 4, ...: lane l tests blocks 64 i + l (coalesced), a
+  // ballot gives two bitmap words per 64 blocks and the row's count
   int my_bnd = 0;
-  for (int wi = t; wi < nr * nwords; wi += 256) {
-    const int rr = wi / nwords, w = wi - rr * nwords;
+  for (int rr = wave; rr < nr; rr += 4) {
     const int R = R0 + rr, k = R / nq, I = R - k * nq;
     const int64_t row = ((int64_t)b * H + members[b * H + g * G + k]) * nq + I;
     const float* srow = S + row * nkv;
     const int qsize = qstart[I + 1] - qstart[I];
-    uint32_t word = 0;
-    for (int bit = 0; bit < 32; ++bit) {
-      const int J = 32 * w + bit;
-      if (J >= nkv) break;
-      const uint32_t key = sel_key(eg_weight(srow[J], qsize, N, st.m));
-      if (eg_selected(st, key))
-        word |= 1u << bit;
-      else if (!st.all && (key & st.mask) == st.prefix)
-        ++my_bnd;
+    int cnt = 0;
+    for (int J0 = 0; J0 < nkv; J0 += 64) {
+      const int J = J0 + lane;
+      bool sel = false, bd = false;
+      if (J < nkv) {
+        const uint32_t key = sel_key(eg_weight(srow[J], qsize, N, st.m));
+        sel = eg_selected(st, key);
+        bd = !sel && !st.all && (key & st.mask) == st.prefix;
+      }
+      const unsigned long long bal = __ballot(sel);
+      cnt += __popcll(bal);
+      my_bnd += __popcll(__ballot(bd));
+      const int w = (J0 >> 5) + lane;
+      if (lane < 2 && w < nwords) bitmap[row * nwords + w] = (uint32_t)(bal >> (32 * lane));
     }
-    bitmap[row * nwords + w] = word;
-    if (word) atomicAdd(&rcnt[rr], __popc(word));
+    if (lane == 0) base_counts[row] = cnt;
   }
-  if (my_bnd) atomicAdd(&sbnd, my_bnd);
+  if (lane == 0) sbnd[wave] = my_bnd;
   __syncthreads();
-  if (t < nr) {
-    const int R = R0 + t, k = R / nq, I = R - k * nq;
-    base_counts[((int64_t)b * H + members[b * H + g * G + k]) * nq + I] = rcnt[t];
-  }
-  if (t == 0) bnd[(int64_t)gi * nrchunk + blockIdx.x] = sbnd;
+  if (t == 0) bnd[(int64_t)gi * nrchunk + blockIdx.x] = (sbnd[0] + sbnd[1]) + (sbnd[2] + sbnd[3]);
 }
 
 // When only part of the boundary class is kept: its members in pool index order, chunk by chunk
