@@ -22,7 +22,9 @@
 
 namespace {
 
-constexpr int kTgChunk = 4096;   // pool candidates per histogram workgroup (16 per thread)
+// pool candidates per histogram workgroup (256 per thread): large enough that the workgroups'
+// additions into a head's global histogram stay few
+constexpr int kTgChunk = 65536;
 constexpr int kTgRows = 32;      // token rows per marking workgroup
 constexpr int kTgTile = 32;      // kv blocks per gate tile
 
@@ -184,14 +186,30 @@ __global__ __launch_bounds__(256) void tg_exp_kernel(float* __restrict__ g, int6
   float* p = g + (size_t)bh * per_head;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
   const float ml = m * kLog2e;
-  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < per_head;
-       j += (int64_t)gridDim.x * 256) {
-    // at most 1 (the max gate's rounding could give exp2 of a tiny positive number)
-    const float e = fminf(__builtin_amdgcn_exp2f(fmaf(p[j], kLog2e, -ml)), 1.f);
-    p[j] = e;
+  // at most 1 (the max gate's rounding could give exp2 of a tiny positive number)
+  auto ex = [&](float g) {
+    const float e = fminf(__builtin_amdgcn_exp2f(fmaf(g, kLog2e, -ml)), 1.f);
     const uint32_t k = sel_key(e);
     kmin = min(kmin, k);
     kmax = max(kmax, k);
+    return e;
+  };
+  if ((per_head & 3) == 0) {  // 16 bytes per lane (rows of the pool start 16-byte aligned)
+    float4* p4 = reinterpret_cast<float4*>(p);
+    const int64_t n4 = per_head / 4;
+    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n4;
+         j += (int64_t)gridDim.x * 256) {
+      float4 v = p4[j];
+      v.x = ex(v.x);
+      v.y = ex(v.y);
+      v.z = ex(v.z);
+      v.w = ex(v.w);
+      p4[j] = v;
+    }
+  } else {
+    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < per_head;
+         j += (int64_t)gridDim.x * 256)
+      p[j] = ex(p[j]);
   }
   // one atomic pair per workgroup (the range is an integer min / max: order-free)
   __shared__ uint32_t wk[2][4];
@@ -271,15 +289,22 @@ __global__ __launch_bounds__(256) void tg_hist_kernel(const float* __restrict__ 
   // kPer / 4 rounds of 16-byte loads, each round 4 KB of consecutive pool entries (the pool of
   // a head starts 16-byte aligned when nkv * N is a multiple of 4; else one value at a time)
   if ((per_head & 3) == 0) {
+    for (int q0 = 0; q0 < kPer / 4; q0 += 4) {  // four 16-byte loads in flight per thread
+      float4 v[4];
 #pragma unroll
-    for (int q = 0; q < kPer / 4; ++q) {
-      const int64_t j = base + 4 * (t + 256 * q);
-      if (j < per_head) {
-        const float4 v = *reinterpret_cast<const float4*>(p + j);
-        add(v.x);
-        add(v.y);
-        add(v.z);
-        add(v.w);
+      for (int q = 0; q < 4; ++q) {
+        const int64_t j = base + 4 * (t + 256 * (q0 + q));
+        v[q] = j < per_head ? *reinterpret_cast<const float4*>(p + j)
+                            : make_float4(-1.f, -1.f, -1.f, -1.f);  // key 0: never a candidate
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (base + 4 * (t + 256 * (q0 + q)) < per_head) {
+          add(v[q].x);
+          add(v[q].y);
+          add(v[q].z);
+          add(v[q].w);
+        }
       }
     }
   } else {
@@ -421,14 +446,24 @@ __global__ __launch_bounds__(256) void tg_mark_kernel(const float* __restrict__ 
   for (int rr = wave; rr < nr; rr += 4) {
     const float* row = e + ((size_t)bh * N + r0 + rr) * nkv;
     uint32_t* out = tbits + ((size_t)bh * N + r0 + rr) * nwords;
-    for (int J0 = 0; J0 < nkv; J0 += 64) {
-      const int J = J0 + lane;
-      bool sel = false, bd = false;
-      if (J < nkv) sel = tg_selected(h, row[J], bd);
-      const unsigned long long bal = __ballot(sel);
-      my += __popcll(__ballot(bd));
-      const int w = (J0 >> 5) + lane;
-      if (lane < 2 && w < nwords) out[w] = (uint32_t)(bal >> (32 * lane));
+    for (int J1 = 0; J1 < nkv; J1 += 256) {  // four loads in flight per lane
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int J = J1 + 64 * i + lane;
+        v[i] = J < nkv ? row[J] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int J0 = J1 + 64 * i;
+        if (J0 >= nkv) break;
+        bool sel = false, bd = false;
+        if (J0 + lane < nkv) sel = tg_selected(h, v[i], bd);
+        const unsigned long long bal = __ballot(sel);
+        my += __popcll(__ballot(bd));
+        const int w = (J0 >> 5) + lane;
+        if (lane < 2 && w < nwords) out[w] = (uint32_t)(bal >> (32 * lane));
+      }
     }
   }
   if (lane == 0) sbnd[wave] = my;
