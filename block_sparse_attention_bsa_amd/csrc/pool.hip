@@ -1,11 +1,15 @@
 // Block means of Q or K (pith.science review of VMoBA, "What carries the argument" and the
 // Figure 2 caption: each block is represented by the mean of its token vectors).
 //
-// One workgroup of 256 threads per (block J, head bh). A token row of d elements is read as
-// 16-byte segments: SEGS threads cover one row and 256 / SEGS rows are in flight per pass, so a
-// wavefront reads whole rows (a 4x4x8 tile is 16 runs of 8 contiguous tokens, 2 KiB each for
-// bf16, d = 128). Each thread accumulates its segment over the rows it visits in fp32; the
-// partial sums are combined across row groups in LDS in a fixed order (deterministic).
+// One workgroup of 256 threads per (block J, head bh, d slice). A token row of d elements is read
+// as 16-byte segments: the SEGS / slices segments of the workgroup's d slice are covered by as
+// many threads, and 256 / (SEGS / slices) rows are in flight per pass, so a wavefront reads whole
+// rows or whole slices of rows (a 4x4x8 tile is 16 runs of 8 contiguous tokens, 2 KiB each for
+// bf16, d = 128). Blocks of a few hundred tokens take one slice (the whole row); a side whose
+// blocks reach thousands of tokens (1D and 2D partitions) is split into 2 or 4 d slices, so
+// that its few long blocks spread over more workgroups. Each thread accumulates its segment over
+// the rows it visits in fp32; the partial sums are combined across row groups in LDS in a fixed
+// order (deterministic).
 #include "bsa_internal.h"
 #include "device_common.h"
 
@@ -46,33 +50,26 @@ struct PoolSide {
   const int32_t* perm;
   const int32_t* start;
   int nblk;
+  int slices;  // d slices per block (1, 2 or 4): one workgroup each
 };
 
-// blockIdx.x < a.nblk pools side a, the rest side b (both in one launch: more workgroups in
-// flight than either alone, for the short 480p passes).
-template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_kernel(const PoolSide<T> a, const PoolSide<T> b,
-                                                   int N) {
+// One workgroup's block and d slice (SL slices per block, a compile-time constant so that the
+// thread mapping needs no division).
+template <typename T, int D, int SL>
+__device__ __forceinline__ void pool_block(const PoolSide<T>& sd, int w, int N,
+                                           float (*red)[Seg<T>::kVec + 1]) {
   constexpr int VEC = Seg<T>::kVec;
   constexpr int SEGS = D / VEC;
-  constexpr int GROUPS = 256 / SEGS;
-  constexpr int UNROLL = 8;  // one pass covers a 128-token block: all its rows in flight
-  __shared__ float red[GROUPS][D + 1];
-
-  const bool first = (int)blockIdx.x < a.nblk;
-  const PoolSide<T>& sd = first ? a : b;
-  const T* __restrict__ X = sd.X;
-  float* __restrict__ Xbar = sd.Xbar;
-  const int32_t* __restrict__ perm = sd.perm;
-  const int32_t* __restrict__ start = sd.start;
-  const int nblk = sd.nblk;
-  const int J = first ? (int)blockIdx.x : (int)blockIdx.x - a.nblk;
+  constexpr int SSEG = SEGS / SL;       // segments of this workgroup's d slice
+  constexpr int GROUPS = 256 / SSEG;    // rows in flight per pass
+  constexpr int UNROLL = 8;             // one pass covers a 128-token block: all its rows in flight
+  const int J = w / SL, slice = w - J * SL;
   const int bh = blockIdx.y;
-  const int seg = threadIdx.x % SEGS;
-  const int grp = threadIdx.x / SEGS;
-  const int s0 = start[J];
-  const int cnt = start[J + 1] - s0;
-  const T* __restrict__ Xh = X + (size_t)bh * N * D + seg * VEC;
+  const int seg = slice * SSEG + (int)threadIdx.x % SSEG;
+  const int grp = (int)threadIdx.x / SSEG;
+  const int s0 = sd.start[J];
+  const int cnt = sd.start[J + 1] - s0;
+  const T* __restrict__ Xh = sd.X + (size_t)bh * N * D + seg * VEC;
 
   float acc[VEC];
 #pragma unroll
@@ -84,7 +81,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const PoolSide<T> a, const Po
     for (int u = 0; u < UNROLL; ++u) {
       const int kk = k + u * GROUPS;
       if (kk < cnt) {
-        const int n = perm[s0 + kk];
+        const int n = sd.perm[s0 + kk];
         v[u] = *reinterpret_cast<const uint4*>(Xh + (size_t)n * D);
       } else {
         v[u] = make_uint4(0, 0, 0, 0);
@@ -95,14 +92,34 @@ __global__ __launch_bounds__(256) void pool_kernel(const PoolSide<T> a, const Po
       if (k + u * GROUPS < cnt) Seg<T>::add(acc, v[u]);
   }
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) red[grp][seg * VEC + e] = acc[e];
+  for (int e = 0; e < VEC; ++e) red[threadIdx.x][e] = acc[e];
   __syncthreads();
-  if (threadIdx.x < D) {
+  constexpr int DW = D / SL;  // d values of the slice
+  if ((int)threadIdx.x < DW) {
+    const int c = threadIdx.x, cs = c / VEC, ce = c % VEC;
     float s = 0.f;
 #pragma unroll
-    for (int g = 0; g < GROUPS; ++g) s += red[g][threadIdx.x];
-    Xbar[((size_t)bh * nblk + J) * D + threadIdx.x] = s / (float)cnt;
+    for (int g = 0; g < GROUPS; ++g) s += red[g * SSEG + cs][ce];
+    sd.Xbar[((size_t)bh * sd.nblk + J) * D + slice * DW + c] = s / (float)cnt;
   }
+}
+
+// blockIdx.x < a.nblk * a.slices pools side a, the rest side b (both in one launch: more
+// workgroups in flight than either alone, for the short 480p passes).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_kernel(const PoolSide<T> a, const PoolSide<T> b,
+                                                   int N) {
+  __shared__ float red[256][Seg<T>::kVec + 1];
+  const int na = a.nblk * a.slices;
+  const bool first = (int)blockIdx.x < na;
+  const PoolSide<T>& sd = first ? a : b;
+  const int w = first ? (int)blockIdx.x : (int)blockIdx.x - na;
+  if (sd.slices == 1)
+    pool_block<T, D, 1>(sd, w, N, red);
+  else if (sd.slices == 2)
+    pool_block<T, D, 2>(sd, w, N, red);
+  else
+    pool_block<T, D, 4>(sd, w, N, red);
 }
 
 template <typename T>
@@ -113,6 +130,8 @@ PoolSide<T> side(const bsa_plan& p, int which, const void* X, float* Xbar) {
   sd.perm = which == 0 ? p.qperm : p.kvperm;
   sd.start = which == 0 ? p.qstart : p.kvstart;
   sd.nblk = X ? (which == 0 ? p.nq : p.nkv) : 0;
+  const int mx = which == 0 ? p.max_qblk : p.max_kvblk;
+  sd.slices = mx > 1024 ? 4 : (mx > 512 ? 2 : 1);
   return sd;
 }
 
@@ -121,7 +140,7 @@ template <typename T, int D>
 hipError_t launch(const bsa_plan& p, const void* Q, float* Qbar, const void* K, float* Kbar,
                   hipStream_t s) {
   const PoolSide<T> a = side<T>(p, 0, Q, Qbar), b = side<T>(p, 1, K, Kbar);
-  const dim3 grid(a.nblk + b.nblk, p.prob.B * p.prob.H);
+  const dim3 grid(a.nblk * a.slices + b.nblk * b.slices, p.prob.B * p.prob.H);
   pool_kernel<T, D><<<grid, 256, 0, s>>>(a, b, p.prob.N);
   return hipGetLastError();
 }
