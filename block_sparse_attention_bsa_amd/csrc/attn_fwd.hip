@@ -586,26 +586,28 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
 
 // ------------------------------------------------------- sparse forward on 16x16x32 MFMAs
 
-// The sparse forward (kFwd, kFwdO) on v_mfma_f32_16x16x32_bf16. The work per tile is the body
-// above's, cut into 16 x 16 output tiles: the same FLOPs at the same matrix-pipe rate, but each
+// The sparse forward (kFwd, kFwdO) on v_mfma_f32_16x16x32_bf16. The work is the body above's,
+// cut into 16 x 16 output tiles: the same FLOPs at the same matrix-pipe rate, but each
 // instruction moves a quarter of the accumulator registers of a 32 x 32 x 16 one, and under the
-// chip's power cap that buys clock (a back-to-back loop of each sustains 2.09 vs 1.93 GHz).
+// chip's power cap that buys clock (a back-to-back loop of each sustains 2.09 vs 1.93 GHz). Each
+// step is one 32-token chunk (two 16 KB stages of K and V), which keeps the registers within
+// 168 and lets three workgroups share a CU (4 % faster than two workgroups of 64-token steps).
 //
 // Layouts (lane = 16 g + t, g = lane / 16, t = lane % 16; wavefront w owns query rows
 // 32 w .. +32 of the item, in two 16-row tiles qt):
-//   S^T tile (kv rows 16 mt .. +16 of the 64-token step, queries 16 qt .. +16), K = d in 32s:
+//   S^T tile (kv rows 16 mt .. +16 of the chunk, queries 16 qt .. +16), K = d in 32s:
 //     A = K rows: lane reads row 16 mt + t, d 32 kc + 8 g .. +8 (one 16-byte LDS read; K is
 //     stored in 1 KB fragment tiles so that these reads are contiguous);
 //     B = Q^T from registers: query 16 qt + t, d 32 kc + 8 g .. +8;
 //     lane holds S^T[16 mt + 4 g + e][16 qt + t], e = 0..3.
-//   O^T tile (d rows 16 dt .. +16, queries 16 qt .. +16), K = 32 kv rows of half s of the step,
-//   taken in the order the score tiles left them in the lanes: k = 8 g + i is kv row
-//   32 s + 4 g + i (i < 4) or 32 s + 16 + 4 g + i - 4, so
-//     B = P^T is the lane's own weights of score tiles 2 s and 2 s + 1 (no lane exchange);
-//     A = V^T: two transposing 8-byte LDS reads (ds_read_b64_tr_b16) of rows 32 s + 4 g .. +4
-//     and 32 s + 16 + 4 g .. +4, columns 16 dt .. +16 (lane t gets column 16 dt + t);
+//   O^T tile (d rows 16 dt .. +16, queries 16 qt .. +16), K = the chunk's 32 kv rows taken in
+//   the order the score tiles left them in the lanes: k = 8 g + i is kv row 4 g + i (i < 4) or
+//   16 + 4 g + i - 4, so
+//     B = P^T is the lane's own weights of score tiles 0 and 1 (no lane exchange);
+//     A = V^T: two transposing 8-byte LDS reads (ds_read_b64_tr_b16) of rows 4 g .. +4 and
+//     16 + 4 g .. +4, columns 16 dt .. +16 (lane t gets column 16 dt + t);
 //     lane holds O^T[16 dt + 4 g + e][16 qt + t].
-// A query's 64 scores of a step sit in the four lanes t, t + 16, t + 32, t + 48: its running
+// A query's 32 scores of a step sit in the four lanes t, t + 16, t + 32, t + 48: its running
 // max is kept equal in the four (the exact max of the rare rescale is reduced over them) and its
 // sums are per-lane partials, added over the four at the end.
 //
@@ -616,7 +618,8 @@ template <int MODE, bool PACK>
 __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
   static_assert(MODE == kFwd || MODE == kFwdO, "the sparse forward only");
   constexpr int D = 128;
-  constexpr int kStage = 2 * kTileBytes;  // K and V of one 64-token tile
+  constexpr int kCh = kTileBytes / 2;      // one 32-token chunk of K or V
+  constexpr int kStage = 2 * kCh;
   char* const lds_a = lds;
   char* const lds_b = lds + kStage;
 
@@ -673,7 +676,7 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
 
   // Loader role as in the body above (wave w fills tile rows 16 w + 4 i + lane / 16), with this
   // kernel's LDS key.
-  const int lchunk = wave >> 1, loff = 16 * (wave & 1), lgrp = lane >> 4;
+  const int lgrp = lane >> 4;
   Cursor cur;
   MultiCursor mc;
   if constexpr (PACK) {
@@ -705,22 +708,23 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
   // fragment are 1 KB of consecutive LDS (row-major rows read that way, 16 rows x 4 units,
   // cost 4 bank-conflict cycles per read under any XOR key). V stays row-major under
   // lds_key16 for its transposing reads. Copy i of wave w fills block 4 w + i of either tile.
-  uint32_t koff[4], voff[4];
+  // K: fragment tiles (mt, kc), block 4 mt + kc of the 8 KB chunk; copy i of wave w fills
+  // block 2 w + i. V: row-major under lds_key16; copy i of wave w fills rows 8 w + 4 i .. +4.
+  uint32_t koff[2], voff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    koff[i] = (uint32_t)((loff + (lane & 15)) * kRowBytes) + 16u * (uint32_t)(4 * i + (lane >> 4));
-    voff[i] = (uint32_t)((loff + 4 * i + lgrp) * kRowBytes) +
-              16u * (uint32_t)((lane & 15) ^ lds_key16(16 * wave + 4 * i + lgrp));
+  for (int i = 0; i < 2; ++i) {
+    const int blk = 2 * wave + i, mt = blk >> 2, kc = blk & 3;
+    koff[i] = (uint32_t)((16 * mt + (lane & 15)) * kRowBytes) + 16u * (uint32_t)(4 * kc + (lane >> 4));
+    const int vr = 8 * wave + 4 * i + lgrp;
+    voff[i] = (uint32_t)(vr * kRowBytes) + 16u * (uint32_t)((lane & 15) ^ lds_key16(vr));
   }
-  auto tile_issue = [&](Chunk ca, Chunk cb, uint32_t st_m0) {
-    const int pos = (lchunk && cb.nv > 0) ? cb.pos : ca.pos;
-    const uint16_t* kb = kbase + (size_t)pos * D;
-    const uint16_t* vb = vbase + (size_t)pos * D;
+  auto tile_issue = [&](Chunk ca, uint32_t st_m0) {
+    const uint16_t* kb = kbase + (size_t)ca.pos * D;
+    const uint16_t* vb = vbase + (size_t)ca.pos * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t m0v = st_m0 + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
-      lds_dma16_so(kb, koff[i], m0v);
-      lds_dma16_so(vb, voff[i], m0v + kTileBytes);
+    for (int i = 0; i < 2; ++i) {
+      lds_dma16_so(kb, koff[i], st_m0 + (uint32_t)(1024 * (2 * wave + i)));
+      lds_dma16_so(vb, voff[i], st_m0 + kCh + (uint32_t)(1024 * (2 * wave + i)));
     }
   };
 
@@ -732,82 +736,63 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
     const int vrow = 4 * g + (t >> 2);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      vofs[dt] = kTileBytes + vrow * kRowBytes + lds_swz16(vrow, 2 * dt + ((t & 3) >> 1)) +
+      vofs[dt] = kCh + vrow * kRowBytes + lds_swz16(vrow, 2 * dt + ((t & 3) >> 1)) +
                  8 * (t & 1);
   }
 
   const uint32_t m0_a = lds_addr(lds_a), m0_b = lds_addr(lds_b);
   Chunk a0 = take();
-  Chunk b0 = take();
-  if (a0.nv > 0) tile_issue(a0, b0, m0_a);
+  if (a0.nv > 0) tile_issue(a0, m0_a);
   Chunk a1 = take();
-  Chunk b1 = take();
   vmem_wait_all();
   __syncthreads();
 
   auto step = [&](const char* st, uint32_t nx_m0) {
-    f32x4_t sacc[2][4];  // [qt][mt]
-    bool pa = true, pb = true, act = active;
-    if constexpr (PACK) {  // chunks of blocks this wavefront's query block selected
-      pa = (a0.lmask >> lw) & 1;
-      pb = b0.nv > 0 && ((b0.lmask >> lw) & 1);
-      act = active && (pa || pb);
-    }
+    f32x4_t sacc[2][2];  // [qt][mt]
+    bool act = active;
+    if constexpr (PACK) act = active && ((a0.lmask >> lw) & 1);
     if (act) {
       __builtin_amdgcn_s_setprio(2);
-      bf16x8_t kf[4][4];  // [kc][mt]
+      bf16x8_t kf[4][2];  // [kc][mt]
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
           kf[kc][mt] = *reinterpret_cast<const bf16x8_t*>(st + 4096 * mt + 1024 * kc + 16 * lane);
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) sacc[qt][mt][e] = 0.f;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt)
             sacc[qt][mt] =
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kc][mt], qf[qt][kc], sacc[qt][mt], 0, 0, 0);
-      // eight K reads ahead of the MFMAs, then one read per two MFMAs, then the rest
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      // four K reads ahead of the MFMAs, then one read per two MFMAs, then the rest
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_s_setprio(0);
     }
     const Chunk an = take();
-    const Chunk bn = take();
-    if (a1.nv > 0) tile_issue(a1, b1, nx_m0);
+    if (a1.nv > 0) tile_issue(a1, nx_m0);
 
     if (act) {
-      if (a0.nv < 32 || b0.nv < 32) {  // partial chunk(s): mask padded kv rows
+      if (a0.nv < 32) {  // partial chunk: mask padded kv rows
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const int nv = mt < 2 ? a0.nv : b0.nv;
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (16 * (mt & 1) + 4 * g + e >= nv) {
-              sacc[0][mt][e] = -INFINITY;
-              sacc[1][mt][e] = -INFINITY;
-            }
-        }
-      }
-      if constexpr (PACK) {  // chunks of blocks this wavefront's query block did not select
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          if (!(mt < 2 ? pa : pb))
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            if (16 * mt + 4 * g + e >= a0.nv) {
               sacc[0][mt][e] = -INFINITY;
               sacc[1][mt][e] = -INFINITY;
             }
@@ -822,48 +807,44 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
         const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
         return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
       };
-      bf16x8_t vf0[2];
+      bf16x8_t vf0[1];
       vf0[0] = vfrag(0, 0);
-      vf0[1] = vfrag(0, 1);
       __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the VALU work below
 
       // Weights against the running max as it stands, their bf16 packing (the B operands) and
       // the lane partial sums: fp32 (kFwd, for the LSE) and of the rounded weights.
-      bf16x8_t pbw[2][2];  // [qt][s]
+      bf16x8_t pbw[2][1];  // [qt][s]
       float ls[2], lbs[2];
       auto weights = [&]() {
         const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-          float pv[4][4];
+          float pv[2][4];
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+          for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               pv[mt][e] = __builtin_amdgcn_exp2f(fmaf(sacc[qt][mt][e], c2, -m_run[qt]));
-          uint32_t w[8];
+          uint32_t w[4];
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
+          for (int mt = 0; mt < 2; ++mt) {
             w[2 * mt] = pack_bf16x2(pv[mt][0], pv[mt][1]);
             w[2 * mt + 1] = pack_bf16x2(pv[mt][2], pv[mt][3]);
           }
           float lb0 = 0.f, lb1 = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; i += 2) {
+          for (int i = 0; i < 4; i += 2) {
             lb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), one2, lb0,
                                                   false);
             lb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i + 1]), one2,
                                                   lb1, false);
           }
           lbs[qt] = lb0 + lb1;
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-            pbw[qt][s] = __builtin_bit_cast(
-                bf16x8_t, make_uint4(w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]));
+          pbw[qt][0] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
           if constexpr (MODE == kFwd) {
             float f0 = pv[0][0], f1 = pv[0][1], f2 = pv[0][2], f3 = pv[0][3];
 #pragma unroll
-            for (int mt = 1; mt < 4; ++mt) {
+            for (int mt = 1; mt < 2; ++mt) {
               f0 += pv[mt][0];
               f1 += pv[mt][1];
               f2 += pv[mt][2];
@@ -885,7 +866,7 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
         for (int qt = 0; qt < 2; ++qt) {
           float sm = sacc[qt][0][0];
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+          for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) sm = fmaxf(sm, sacc[qt][mt][e]);
           sm = fmaxf(sm, __shfl_xor(sm, 16, 64));
@@ -912,11 +893,10 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
       __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        bf16x8_t vf[2];
+        bf16x8_t vf[1];
+        vf[0] = dt == 0 ? vf0[0] : vfrag(dt, 0);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) vf[s] = dt == 0 ? vf0[s] : vfrag(dt, s);
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 1; ++s)
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt)
             oacc[qt][dt] =
@@ -925,19 +905,17 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
       // weights first, then the MFMAs with the remaining V reads interleaved, two per MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 200, 0);
 #pragma unroll
-      for (int i = 0; i < 14; ++i) {
+      for (int i = 0; i < 7; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 18, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 9, 0);
       __builtin_amdgcn_s_setprio(0);
     }
     vmem_wait_all();
     __syncthreads();
     a0 = a1;
-    b0 = b1;
     a1 = an;
-    b1 = bn;
   };
   while (true) {
     if (a0.nv <= 0) break;
@@ -989,16 +967,21 @@ template <int MODE>
 __global__ __launch_bounds__(256, 2) void attn_mfma_d128(const MfmaArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[stage_bytes<MODE>()];
   __shared__ int32_t none[1];
-  if constexpr (MODE == kFwd || MODE == kFwdO) {
-    const int total = a.n_fitems * (int)gridDim.y;
-    const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
-    if (ld_ro(a.fitems + kFItemInts * (lin % a.n_fitems)) > 1)
-      attn16_body<MODE, true>(a, lds);
-    else
-      attn16_body<MODE, false>(a, lds);
-  } else {
-    attn_mfma_body<MODE>(a, lds, none);
-  }
+  attn_mfma_body<MODE>(a, lds, none);
+}
+
+// The sparse forward (kFwd, kFwdO): two 16 KB stages of one 32-token chunk each and at most 168
+// VGPRs, so that three workgroups share a CU. A work item is one query block's 128-row chunk
+// or the packed slots of up to four small blocks.
+template <int MODE>
+__global__ __launch_bounds__(256, 3) void attn16_fwd(const MfmaArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kTileBytes];
+  const int total = a.n_fitems * (int)gridDim.y;
+  const int lin = xcd_remap(blockIdx.x + blockIdx.y * gridDim.x, total);
+  if (ld_ro(a.fitems + kFItemInts * (lin % a.n_fitems)) > 1)
+    attn16_body<MODE, true>(a, lds);
+  else
+    attn16_body<MODE, false>(a, lds);
 }
 
 template <int MODE>
@@ -1219,9 +1202,9 @@ hipError_t launch_attn_fwd(const bsa_plan& p, const void* Q, const void* K, cons
     // gridDim.x * gridDim.y is exactly n_fitems * B * H (the XCD remap is a bijection on it).
     const dim3 grid(p.n_fitems, p.prob.B * p.prob.H);
     if (lse)
-      attn_mfma_d128<kFwd><<<grid, 256, 0, s>>>(a);
+      attn16_fwd<kFwd><<<grid, 256, 0, s>>>(a);
     else
-      attn_mfma_d128<kFwdO><<<grid, 256, 0, s>>>(a);
+      attn16_fwd<kFwdO><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
   }
   if (p.prob.dtype == BSA_BF16)

@@ -29,6 +29,10 @@ def _layer(w, head_scale=None):
     ("c1", CONFIGS[1]),
     ("c2-small", replace(CONFIGS[2], grid=(6, 9, 20), H=2)),
     ("c5-1d", replace(CONFIGS[5], grid=(6, 9, 20), H=2, kvpart=("tile", (3, 9, 20)))),
+    # blocks of 640 and 1280 tokens: each pooled in 2 and 4 d slices
+    ("long-blocks", replace(CONFIGS[5], grid=(8, 16, 20), H=2, qpart=("tile", (2, 16, 20)),
+                            kvpart=("tile", (4, 16, 20)))),
+    ("fp32-d64-long", replace(CONFIGS[1], grid=(4, 16, 20), kvpart=("tile", (4, 16, 20)))),
     ("c2-full", CONFIGS[2]),
 ])
 def test_pool_parity(name, w):
