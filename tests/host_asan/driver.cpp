@@ -190,10 +190,14 @@ static void exercise(int B, int H, int d, int dtype, int T, int Hg, int Wg, bsa_
     CHECK(bsa_attn_fwd_token_bits(plan, q.p(), k.p(), v.p(), rp.i(), ci.i(), (uint32_t*)sel.p(),
                                   o.p(), nullptr, ws_f.p(), wsf, nullptr) ==
           (nkv > 768 ? BSA_EUNSUPPORTED : BSA_OK));
-    if (nkv <= 2048)
+    if (nkv <= 2048) {
       CHECK(bsa_attn_fwd_tokens(plan, q.p(), k.p(), v.p(), (int32_t*)rp.p(), (int32_t*)ci.p(),
                                 (int32_t*)sel.p(), 6, o.p(), nullptr, ws_f.p(), wsf,
                                 nullptr) == BSA_OK);
+      CHECK(bsa_attn_fwd_tokens(plan, q.p(), k.p(), v.p(), (int32_t*)rp.p(), (int32_t*)ci.p(),
+                                (int32_t*)sel.p(), 6, o.p(), nullptr, ws_f.p(), wsf - 1,
+                                nullptr) == BSA_ECAPACITY);
+    }
   } else {
     CHECK(bsa_calibrate_mass(plan, q.p(), k.p(), (float*)S.p(), ws_c.p(), wsc, nullptr) ==
           BSA_EUNSUPPORTED);
