@@ -288,8 +288,19 @@ def measured_peaks(tm, copy_mib=1024, reps=3):
             bsa_probe_copy(src, dst, n)
         with tm("probe_torch_copy"):
             dst.copy_(src)
+    # the forward's instruction mix at its occupancy (768 workgroups: three per CU, one
+    # wavefront of each per SIMD): per round 16 MFMAs and/or 32 exponentials or FMAs
+    mix_wgs, mix_iters = 768, 4000
+    mix_names = {2: "mfma", 3: "mfma_exp", 4: "exp", 5: "mfma_fma", 6: "fma"}
+    for _ in range(reps + 1):
+        for shape, name in mix_names.items():
+            with tm("probe_mix_" + name):
+                bsa_probe_mfma(shape, mix_wgs, mix_iters, sink)
     torch.cuda.synchronize()
     best = lambda k: min(a.elapsed_time(b) for a, b in tm.marks[k][1:])  # skip the first call
+    # ns per round of every SIMD (its three wavefronts each run mix_iters rounds)
+    mix = {name: round(best("probe_mix_" + name) * 1e6 / mix_iters, 1)
+           for name in mix_names.values()}
     r32 = flops / (best("probe_mfma") * 1e-3) / 1e12
     r16 = flops / (best("probe_mfma16") * 1e-3) / 1e12
     return {"mfma_bf16_tflops": round(max(r32, r16), 1),
@@ -297,9 +308,12 @@ def measured_peaks(tm, copy_mib=1024, reps=3):
             "copy_kernel_gbs": round(2 * n / (best("probe_copy") * 1e-3) / 1e9, 1),
             "copy_torch_gbs": round(2 * n / (best("probe_torch_copy") * 1e-3) / 1e9, 1),
             "copy_bytes_moved": 2 * n,
+            "mix_ns_per_round": mix,
             "method": "bsa_probe_mfma (v_mfma_f32_32x32x16_bf16 and 16x16x32 loops, 2048 x 256 "
                       "threads; the faster counts) and bsa_probe_copy / torch copy_ of 1 GiB, "
-                      "best of 3 calls after one warm-up"}
+                      "best of 3 calls after one warm-up; mix_ns_per_round: shapes 2-6 at "
+                      "768 x 256 threads (three wavefronts per SIMD), 4000 rounds, ns per round "
+                      "of 3 x 16 MFMAs and/or 3 x 32 exponentials or FMAs per SIMD"}
 
 
 def score_paths(w, L, q, k, mink, tm, calls=10):

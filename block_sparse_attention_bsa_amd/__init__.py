@@ -326,8 +326,10 @@ def bsa_attn_fwd_token_bits(plan: Plan, Q, K, V, row_ptr, col_idx, tbits, O, lse
 
 
 def bsa_probe_mfma(shape: int, workgroups: int, iters: int, sink, stream=None) -> float:
-    """Enqueue the bf16 MFMA peak loop (shape 0: 32x32x16, 1: 16x16x32); returns the FLOPs it
-    issues."""
+    """Enqueue the bf16 MFMA peak loop (shape 0: 32x32x16, 1: 16x16x32) or, at three
+    workgroups per CU, one of the matrix/vector mixes (2: 16x16x32 MFMAs alone, 3: with 32
+    exponentials per round, 4: the exponentials alone, 5: MFMAs with 32 FMAs, 6: the FMAs
+    alone); returns the FLOPs of its MFMAs."""
     f = ctypes.c_double(0.0)
     _check(lib().bsa_probe_mfma(int(shape), int(workgroups), int(iters), _ptr(sink),
                                 ctypes.byref(f), _stream(stream)))

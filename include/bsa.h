@@ -340,9 +340,11 @@ int bsa_attn_bwd(const bsa_plan* plan, const void* Q, const void* K, const void*
 /* Measurement helpers, outside the attention path: the ceilings that benches compare the
  * kernels with, measured on the current GPU. bsa_probe_mfma runs `workgroups` x 256 threads of
  * back-to-back bf16 MFMAs on register operands -- shape 0: v_mfma_f32_32x32x16_bf16 (iters x 8
- * per wavefront), shape 1: v_mfma_f32_16x16x32_bf16 (iters x 16) -- and stores the FLOPs it
- * issues in *flops (host, nullable); sink is device memory of workgroups x 256 floats (not
- * written in practice). bsa_probe_copy copies `bytes` (a multiple of 16) from src to dst with a
+ * per wavefront), shape 1: v_mfma_f32_16x16x32_bf16 (iters x 16) -- or, at three workgroups
+ * per CU, rounds of 16 independent v_mfma_f32_16x16x32_bf16 alone (shape 2), with 32
+ * independent v_exp_f32 (3), the 32 exponentials alone (4), the MFMAs with 32 v_fma_f32 (5) or
+ * the FMAs alone (6), and stores the FLOPs of its MFMAs in *flops (host, nullable; 0 for
+ * shapes 4 and 6); sink is device memory of workgroups x 256 floats (not written in practice). bsa_probe_copy copies `bytes` (a multiple of 16) from src to dst with a
  * grid-stride 16-byte kernel. Both enqueue on `stream` and return BSA_EINVAL on bad arguments. */
 int bsa_probe_mfma(int32_t shape, int32_t workgroups, int32_t iters, float* sink, double* flops,
                    void* stream);

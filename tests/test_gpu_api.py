@@ -163,8 +163,9 @@ def test_backward_is_deterministic():
 
 
 def test_measurement_probes():
-    """The copy probe copies exactly; the MFMA probe reports the FLOPs it issues and rejects
-    bad arguments (the bench's measured ceilings come from these two)."""
+    """The copy probe copies exactly; the MFMA probe (peak loops and matrix/vector mixes) reports
+    the FLOPs of its MFMAs and rejects bad arguments (the bench's measured ceilings come from
+    these two)."""
     import torch
     import block_sparse_attention_bsa_amd as bsa
     src = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
@@ -173,10 +174,10 @@ def test_measurement_probes():
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
     sink = torch.zeros(4 * 256, dtype=torch.float32, device="cuda")
-    for shape in (0, 1):
+    for shape in range(7):  # the two peak loops and the five matrix/vector mixes
         f = bsa.bsa_probe_mfma(shape, 4, 3, sink)
         torch.cuda.synchronize()
-        assert f == 4 * 4 * 3 * 8 * 2 * 32 * 32 * 16
+        assert f == (0 if shape in (4, 6) else 4 * 4 * 3 * 8 * 2 * 32 * 32 * 16)
     assert bsa.lib().bsa_probe_mfma(0, 0, 3, sink.data_ptr(), None, None) == bsa.BSA_EINVAL
-    assert bsa.lib().bsa_probe_mfma(2, 4, 3, sink.data_ptr(), None, None) == bsa.BSA_EINVAL
+    assert bsa.lib().bsa_probe_mfma(7, 4, 3, sink.data_ptr(), None, None) == bsa.BSA_EINVAL
     assert bsa.lib().bsa_probe_copy(src.data_ptr(), dst.data_ptr(), 10, None) == bsa.BSA_EINVAL
