@@ -408,25 +408,49 @@ __global__ __launch_bounds__(256) void mark_row_wave_kernel(const float* __restr
   if (lane == 0) base_counts[r] = (int32_t)count;
 }
 
+// The per-head minimum's top-up and the emission in one pass (row_ptr already holds the scan of
+// the final counts max(base count, k)): a row below its head's k re-reads its scores, takes the
+// top k of the same ranking (by count) and writes its columns from the flags in registers; any
+// other row writes its columns from the marking pass's bitmap. Columns ascend in both cases
+// (value i of lane l is column l + 64 i). Rows of at most 64 * kVpl blocks (nwords <= 64).
 template <int kVpl>
-__global__ __launch_bounds__(256) void topup_wave_kernel(const float* __restrict__ S, int64_t rows,
-                                                         int nq, int nkv, int nwords,
-                                                         const int32_t* __restrict__ base_counts,
-                                                         const int32_t* __restrict__ head_k,
-                                                         uint32_t* __restrict__ bitmap) {
+__global__ __launch_bounds__(256) void topup_emit_wave_kernel(
+    const float* __restrict__ S, int64_t rows, int nq, int nkv, int nwords,
+    const int32_t* __restrict__ base_counts, const int32_t* __restrict__ head_k,
+    const uint32_t* __restrict__ bitmap, const int32_t* __restrict__ row_ptr,
+    int32_t* __restrict__ col_idx) {
   __shared__ WaveHist hist[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-  if (r >= rows) return;
+  if (r >= rows) return;  // whole wavefronts
   const int k = head_k[r / nq];
-  if (base_counts[r] >= k) return;
-  const float* row = S + r * nkv;
-  float v[kVpl];
+  int pos = row_ptr[r];
+  const int end = row_ptr[r + 1];
+  if (base_counts[r] < k) {
+    const float* row = S + r * nkv;
+    float v[kVpl];
 #pragma unroll
-  for (int i = 0; i < kVpl; ++i) v[i] = lane + 64 * i < nkv ? row[lane + 64 * i] : 0.f;
-  bool sel[kVpl];
-  wave_select(v, nkv, (unsigned long long)k, true, false, hist[wave], sel);
-  write_row_bits(sel, nwords, bitmap + r * nwords);
+    for (int i = 0; i < kVpl; ++i) v[i] = lane + 64 * i < nkv ? row[lane + 64 * i] : 0.f;
+    bool sel[kVpl];
+    wave_select(v, nkv, (unsigned long long)k, true, false, hist[wave], sel);
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i) {
+      const unsigned long long m = __ballot(sel[i]);
+      const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
+      if (sel[i] && at < end) col_idx[at] = lane + 64 * i;
+      pos += __popcll(m);
+    }
+    return;
+  }
+  const uint32_t word = lane < nwords ? bitmap[r * nwords + lane] : 0u;
+  for (int g = 0; 2 * g < nwords; ++g) {
+    const uint32_t lo = (uint32_t)__shfl((int)word, 2 * g, 64);
+    const uint32_t hi = (uint32_t)__shfl((int)word, 2 * g + 1, 64);  // 0 past nwords
+    const unsigned long long m = ((unsigned long long)hi << 32) | lo;
+    const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
+    if ((m >> lane) & 1ull && at < end) col_idx[at] = 64 * g + lane;
+    pos += __popcll(m);
+  }
 }
 
 // Local + TopK (VMoBA review: the training-free selection, referee report major comment 2): row
@@ -1250,12 +1274,15 @@ static hipError_t select_finish(const bsa_plan& p, const float* S, const bsa_sel
                                      prm.fixed_k, head_k_ws, head_k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (use_min_k && wave_rows) {
+  if (use_min_k && wave_rows) {  // row_ptr from the final counts, then top-up and emission
+    e = launch_scan(base_counts, head_k_ws, true, rows, p.nq, row_ptr, counts,
+                    reinterpret_cast<int32_t*>(base + L.partial), s);
+    if (e != hipSuccess) return e;
     with_vpl(p.nkv, [&](auto vpl) {
-      topup_wave_kernel<decltype(vpl)::value><<<wgrid, 256, 0, s>>>(
-          S, rows, p.nq, p.nkv, L.nwords, base_counts, head_k_ws, bitmap);
+      topup_emit_wave_kernel<decltype(vpl)::value><<<wgrid, 256, 0, s>>>(
+          S, rows, p.nq, p.nkv, L.nwords, base_counts, head_k_ws, bitmap, row_ptr, col_idx);
     });
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return hipGetLastError();
   } else if (use_min_k) {
     topup_kernel<<<(unsigned)rows, 256, 0, s>>>(S, p.nq, p.nkv, L.nwords, base_counts,
                                                 head_k_ws, bitmap);

@@ -17,13 +17,13 @@ from helpers import dev_to_f64, log, to_dev, to_f64, topp_set_ok
 pytestmark = pytest.mark.gpu
 
 
-def _theta_in_gap(ent, frac=0.5):
-    """A threshold midway between two neighbouring head entropies, at least 1e-4 from each: the
-    usable gap nearest the `frac` quantile."""
+def _theta_in_gap(ent, frac=0.5, margin=1e-4):
+    """A threshold midway between two neighbouring head entropies, at least `margin` from each:
+    the usable gap nearest the `frac` quantile."""
     e = np.sort(ent.reshape(-1))
     k = int(round(frac * (len(e) - 1)))
     for i in sorted(range(len(e) - 1), key=lambda i: abs(i - k)):
-        if e[i + 1] - e[i] > 2e-4:
+        if e[i + 1] - e[i] > 2 * margin:
             return 0.5 * (e[i] + e[i + 1])
     raise AssertionError("no usable entropy gap")
 
@@ -72,18 +72,22 @@ def _check(w, rows_gpu, ent_gpu, pooled_gpu, S_ref, qs, p, theta, G):
     log(f"  sets: exact {exact}, tolerated near-ties {tol}")
 
 
-def _run(w, G, p=None, frac=0.5, theta=None, seed=0):
+def _run(w, G, p=None, frac=0.5, theta=None, seed=0, x=None, S_ref=None, margin=1e-4):
+    """x (the workload's inputs) and S_ref (the oracle's row scores of them) may be passed in by
+    a caller that already has them."""
     import torch
     from block_sparse_attention_bsa_amd.layer import BlockSparseAttention
     p = w.p if p is None else p
-    x = make_inputs(w)
+    x = make_inputs(w) if x is None else x
     hs = x["head_scale"]
-    Q, K = to_f64(x["q"]), to_f64(x["k"])
     qb, kb = oracle.partition(w.grid, w.qpart), oracle.partition(w.grid, w.kvpart)
     qs = oracle.block_sizes(qb)
-    S_ref = oracle.score_row(oracle.pool(Q, qb), oracle.pool(K, kb), hs.astype(np.float64))
+    if S_ref is None:
+        Q, K = to_f64(x["q"]), to_f64(x["k"])
+        S_ref = oracle.score_row(oracle.pool(Q, qb), oracle.pool(K, kb), hs.astype(np.float64))
+        del Q, K
     if theta is None:
-        theta = _theta_in_gap(oracle.head_entropy(S_ref, qs), frac)
+        theta = _theta_in_gap(oracle.head_entropy(S_ref, qs), frac, margin)
     log(f"eg {w.name} grid={w.grid} B={w.B} H={w.H} G={G} p={p} theta={theta:.6f}")
     layer = BlockSparseAttention(w.B, w.H, w.d, w.grid, w.qpart, w.kvpart, dtype=w.dtype,
                                  head_scale=hs)

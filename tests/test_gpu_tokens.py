@@ -19,10 +19,11 @@ from helpers import dev_to_f64, log, to_dev, to_f64
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, k, heads=None, o_sample=None, seed=0):
+def _run(w, k, heads=None, o_sample=None, seed=0, x=None):
+    """x (the workload's inputs) may be passed in by a caller that already has them."""
     import torch
     from block_sparse_attention_bsa_amd.layer import BlockSparseAttention
-    x = make_inputs(w)
+    x = make_inputs(w) if x is None else x
     hs = x["head_scale"].astype(np.float64)
     Q, K, V = (to_f64(x[n]) for n in ("q", "k", "v"))
     qb, kb = oracle.partition(w.grid, w.qpart), oracle.partition(w.grid, w.kvpart)

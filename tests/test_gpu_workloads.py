@@ -27,6 +27,17 @@ def _inputs(cid):
     return make_inputs(w, tensors=tensors)
 
 
+@functools.lru_cache(maxsize=1)
+def _row_scores(cid):
+    """The oracle's row-normalised block scores of the workload's inputs (fp64)."""
+    w = CONFIGS[cid]
+    x = _inputs(cid)
+    Q, K = to_f64(x["q"]), to_f64(x["k"])
+    qb, kb = oracle.partition(w.grid, w.qpart), oracle.partition(w.grid, w.kvpart)
+    return oracle.score_row(oracle.pool(Q, qb), oracle.pool(K, kb),
+                            x["head_scale"].astype(np.float64))
+
+
 def _layer(w, kvpart, x):
     from block_sparse_attention_bsa_amd.layer import BlockSparseAttention
     return BlockSparseAttention(w.B, w.H, w.d, w.grid, w.qpart, kvpart, dtype=w.dtype,
@@ -48,7 +59,7 @@ def test_hybrid_min_k_full_size():
     hs = x["head_scale"].astype(np.float64)
     qb, kb = oracle.partition(w.grid, w.qpart), oracle.partition(w.grid, w.kvpart)
     qs = oracle.block_sizes(qb)
-    S = oracle.score_row(oracle.pool(Q, qb), oracle.pool(K, kb), hs)
+    S = _row_scores(4)
     rows_ref, k_ref = oracle.select_hybrid(S, w.p, qs)
     log(f"head k: gpu {head_k.tolist()}")
     log(f"        ref {k_ref.tolist()}")
@@ -84,6 +95,22 @@ def test_hybrid_min_k_full_size():
     worst = max(float(np.abs(Og[0, h, qb[i]] - O_ref[0, h, qb[i]]).max()) for _, h, i in sample)
     log(f"density {dens:.3f}; O max-abs {worst:.2e} over {len(sample)} q-blocks")
     assert worst <= 1e-2
+
+
+def test_entropy_routed_full_size_720p():
+    """EG-Sparse's entropy-routed selection on the 720p hybrid workload's inputs, groups of four
+    heads, theta between two of the 24 head entropies near their median (the heads' entropies lie
+    within 1e-3 of each other here, so theta keeps 1e-5 from both neighbours; the GPU's entropies
+    are within 1e-7 of the oracle's)."""
+    from test_gpu_select_eg import _run as eg_run
+    eg_run(CONFIGS[4], 4, x=_inputs(4), S_ref=_row_scores(4), margin=1e-5)
+
+
+def test_token_topk_full_size_720p():
+    """Per-token Local + TopK (k = 18, the widest list) on the 720p inputs: every token's list of
+    the first and last head against the oracle's, O and LSE on 256 sampled tokens of each."""
+    from test_gpu_tokens import _run as tok_run
+    tok_run(CONFIGS[4], 18, heads=[0, 23], o_sample=256, x=_inputs(4))
 
 
 def _head_check(W, rows_gpu, rows_ref, nq, tau):
