@@ -1184,7 +1184,7 @@ static hipError_t mark_rows(const bsa_plan& p, const float* S, unsigned long lon
   const int64_t rows = (int64_t)p.prob.B * p.prob.H * p.nq;
   const unsigned wgrid = (unsigned)((rows + 3) / 4);
   if (p.nkv <= kWaveRowMax)
-    with_vpl(p.nkv, [&](auto vpl) {
+    with_sel_vpl(p.nkv, [&](auto vpl) {
       mark_row_wave_kernel<decltype(vpl)::value><<<wgrid, 256, 0, s>>>(
           S, rows, p.nkv, L.nwords, target, all, bitmap, base_counts, p.nq, skip_head);
     });
@@ -1278,7 +1278,7 @@ static hipError_t select_finish(const bsa_plan& p, const float* S, const bsa_sel
     e = launch_scan(base_counts, head_k_ws, true, rows, p.nq, row_ptr, counts,
                     reinterpret_cast<int32_t*>(base + L.partial), s);
     if (e != hipSuccess) return e;
-    with_vpl(p.nkv, [&](auto vpl) {
+    with_sel_vpl(p.nkv, [&](auto vpl) {
       topup_emit_wave_kernel<decltype(vpl)::value><<<wgrid, 256, 0, s>>>(
           S, rows, p.nq, p.nkv, L.nwords, base_counts, head_k_ws, bitmap, row_ptr, col_idx);
     });
