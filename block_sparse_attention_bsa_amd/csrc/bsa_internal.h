@@ -112,7 +112,7 @@ struct TokWs {
 TokWs tok_ws_layout(const bsa_plan& p);
 
 // Per-token global threshold selection (bsa_select_tokens_global): Kbar's two bf16 terms, the
-// head pools' gates (then their exp) [B*H][N][nkv] fp32, per-head radix state and histogram,
+// head pools' gates [B*H][N][nkv] fp32 (field e), per-head radix state and histogram,
 // boundary counts per 32-token chunk, and the per-query-block union (bitmap, counts, scan).
 constexpr size_t kTgHeadBytes = 80;
 struct TgWs {

@@ -5,7 +5,9 @@
 //
 // Per head, the gate of every (query token i, kv block J), g = sigma_h q_i . kbar_J, is formed
 // once on the bf16 matrix cores (kbar split into two bf16 terms, 2^-17 relative, fp32 sums) and
-// kept in the workspace; e = exp(g - max g) then replaces it. The head's weights are e / Z with
+// kept in the workspace with the head's smallest and largest gate; every pass that reads a gate
+// forms e = exp(g - max g) from it (the same expression everywhere, so the same bits), so no pass
+// writes the exponentials back. The head's weights are e / Z with
 // Z = sum e, so "the shortest prefix of the (weight desc, pair index i * nkv + J asc) order whose
 // weights reach tau" is the same set as the prefix of e reaching tau * Z. The head pool (N * nkv
 // candidates) runs the radix select of the other pools on e's bit pattern over many workgroups:
@@ -36,7 +38,8 @@ struct TgHead {
   int32_t done, all, eq_all;
   uint32_t keep, eq_cnt, above_cnt, shift;  // shift: the fixed-point scale 2^shift of e
   unsigned long long above_sum, target, total;
-  int32_t pad[2];
+  uint32_t gmin;  // order-preserving key of the head's smallest gate
+  int32_t pad;
 };
 static_assert(sizeof(TgHead) == kTgHeadBytes, "head state size");
 struct TgHist {
@@ -52,6 +55,21 @@ __device__ __forceinline__ float tg_gate_from_key(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// e = exp(g - max g), as exp2 of the log2 e-scaled difference (v_exp_f32), ml = max g * log2 e;
+// at most 1 (the max gate's rounding could give exp2 of a tiny positive number).
+__device__ __forceinline__ float tg_e(float g, float ml) {
+  return fminf(__builtin_amdgcn_exp2f(fmaf(g, kLog2e, -ml)), 1.f);
+}
+__device__ __forceinline__ float tg_ml(const TgHead& h) {
+  return tg_gate_from_key(h.gmax) * kLog2e;
+}
+// key(e) - kmin, with key(e) held to [kmin, kmax]: the range comes from e of the head's smallest
+// and largest gates, which bound every e as long as exp2 does not decrease anywhere; the clamp
+// keeps every candidate in the pool's first digit even if it did.
+__device__ __forceinline__ uint32_t tg_ukey(const TgHead& h, float e) {
+  return min(max(sel_key(e), h.kmin), h.kmax) - h.kmin;
+}
+
 // e * 2^shift, rounded to nearest (e in [0, 1]).
 __device__ __forceinline__ unsigned long long tg_fix(float e, uint32_t shift) {
   const double x = (double)e * ldexp(1.0, (int)shift);
@@ -65,6 +83,7 @@ __global__ __launch_bounds__(256) void tg_init_kernel(TgHead* __restrict__ heads
   if (t == 0) {
     TgHead h{};
     h.gmax = 0u;
+    h.gmin = 0xffffffffu;
     h.kmin = 0xffffffffu;
     h.kmax = 0u;
     h.shift = shift;
@@ -77,7 +96,7 @@ __global__ __launch_bounds__(256) void tg_init_kernel(TgHead* __restrict__ heads
 // Gates of 128 tokens (one workgroup, a wavefront per 32) against every kv block of the head:
 // per 32-block tile, G^T = Kbar Q^T with Kbar's two bf16 terms as A and Q as B, so each lane
 // holds 16 gates of one token; written as sigma_h * gate (fp32) to g[bh][n][J], and the head's
-// largest gate is raised with an integer atomic on its order-preserving key.
+// largest and smallest gates are updated with integer atomics on their order-preserving keys.
 __global__ __launch_bounds__(256) void tg_gates_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Khi,
     const uint16_t* __restrict__ Klo, const float* __restrict__ scale, int H, int N, int nkv,
@@ -117,7 +136,7 @@ __global__ __launch_bounds__(256) void tg_gates_kernel(
   };
   const int ntiles = (nkv + kTgTile - 1) / kTgTile;
   float* grow = g + ((size_t)bh * N + (valid ? n : 0)) * nkv;
-  float gmax = -INFINITY;
+  float gmax = -INFINITY, gmin = INFINITY;
   load(0);
   store(0);
   __syncthreads();
@@ -149,6 +168,7 @@ __global__ __launch_bounds__(256) void tg_gates_kernel(
                                          sig * acc[4 * q + 2], sig * acc[4 * q + 3]);
             *reinterpret_cast<float4*>(grow + J) = v;
             gmax = fmaxf(gmax, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+            gmin = fminf(gmin, fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
           }
         }
       } else {
@@ -159,6 +179,7 @@ __global__ __launch_bounds__(256) void tg_gates_kernel(
             const float v = sig * acc[e];
             grow[J] = v;
             gmax = fmaxf(gmax, v);
+            gmin = fminf(gmin, v);
           }
         }
       }
@@ -166,72 +187,32 @@ __global__ __launch_bounds__(256) void tg_gates_kernel(
     if (it + 1 < ntiles) store(st ^ 1);
     __syncthreads();
   }
-  // one integer atomic per workgroup on the head's order-preserving max key
-  __shared__ float wmax[4];
+  // one integer atomic per workgroup on each of the head's order-preserving max and min keys
+  __shared__ float wmax[4], wmin[4];
   gmax = wave_max_f32(gmax);
-  if (lane == 0) wmax[wave] = gmax;
+  gmin = -wave_max_f32(-gmin);
+  if (lane == 0) {
+    wmax[wave] = gmax;
+    wmin[wave] = gmin;
+  }
   __syncthreads();
   if (t == 0) {
     const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float mn = fminf(fminf(wmin[0], wmin[1]), fminf(wmin[2], wmin[3]));
+    if (mn < INFINITY) atomicMin(&heads[bh].gmin, tg_gate_key(mn));
     if (m > -INFINITY) atomicMax(&heads[bh].gmax, tg_gate_key(m));
   }
 }
 
-// e = exp(g - max g) in place (as exp2 of the log2 e-scaled difference, v_exp_f32), and the range
-// of e's keys per head (integer atomics, one pair per workgroup).
-__global__ __launch_bounds__(256) void tg_exp_kernel(float* __restrict__ g, int64_t per_head,
-                                                     TgHead* __restrict__ heads) {
-  const int bh = blockIdx.y;
-  const float m = tg_gate_from_key(heads[bh].gmax);
-  float* p = g + (size_t)bh * per_head;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  const float ml = m * kLog2e;
-  // at most 1 (the max gate's rounding could give exp2 of a tiny positive number)
-  auto ex = [&](float g) {
-    const float e = fminf(__builtin_amdgcn_exp2f(fmaf(g, kLog2e, -ml)), 1.f);
-    const uint32_t k = sel_key(e);
-    kmin = min(kmin, k);
-    kmax = max(kmax, k);
-    return e;
-  };
-  if ((per_head & 3) == 0) {  // 16 bytes per lane (rows of the pool start 16-byte aligned)
-    float4* p4 = reinterpret_cast<float4*>(p);
-    const int64_t n4 = per_head / 4;
-    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < n4;
-         j += (int64_t)gridDim.x * 256) {
-      float4 v = p4[j];
-      v.x = ex(v.x);
-      v.y = ex(v.y);
-      v.z = ex(v.z);
-      v.w = ex(v.w);
-      p4[j] = v;
-    }
-  } else {
-    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < per_head;
-         j += (int64_t)gridDim.x * 256)
-      p[j] = ex(p[j]);
-  }
-  // one atomic pair per workgroup (the range is an integer min / max: order-free)
-  __shared__ uint32_t wk[2][4];
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    wk[0][w] = kmin;
-    wk[1][w] = kmax;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    atomicMin(&heads[bh].kmin, min(min(wk[0][0], wk[0][1]), min(wk[0][2], wk[0][3])));
-    atomicMax(&heads[bh].kmax, max(max(wk[1][0], wk[1][1]), max(wk[1][2], wk[1][3])));
-  }
-}
-
-// Per head: the first digit's width from the key range (u = key - kmin has rem bits).
+// Per head: the range of e's keys, from e of the smallest and largest gate, and the first digit's
+// width from it (u = key - kmin has rem bits).
 __global__ __launch_bounds__(64) void tg_setup_kernel(TgHead* __restrict__ heads) {
   const int bh = blockIdx.x;
   if (threadIdx.x != 0) return;
   TgHead h = heads[bh];
+  const float ml = tg_ml(h);
+  h.kmin = sel_key(tg_e(tg_gate_from_key(h.gmin), ml));
+  h.kmax = sel_key(tg_e(tg_gate_from_key(h.gmax), ml));
   const uint32_t spread = h.kmax - h.kmin;
   h.rem = spread ? 32 - __clz(spread) : 0;
   h.hi = 0u;
@@ -244,10 +225,11 @@ __device__ __forceinline__ void tg_digit(const TgHead& h, int& db, int& sh, uint
   dmask = (1u << db) - 1u;
 }
 
-// One digit pass over a chunk of the head pool: the candidates still matching the prefix add
-// their count and fixed-point sum to their digit's bin (LDS histogram, runs of equal bins summed
-// in registers first), then to the head's global histogram.
-__global__ __launch_bounds__(256) void tg_hist_kernel(const float* __restrict__ e,
+// One digit pass over a chunk of the head pool (gates, each turned into e as it is read): the
+// candidates still matching the prefix add their count and fixed-point sum to their digit's bin
+// (LDS histogram, runs of equal bins summed in registers first), then to the head's global
+// histogram.
+__global__ __launch_bounds__(256) void tg_hist_kernel(const float* __restrict__ g,
                                                       int64_t per_head,
                                                       const TgHead* __restrict__ heads,
                                                       TgHist* __restrict__ hist) {
@@ -265,12 +247,14 @@ __global__ __launch_bounds__(256) void tg_hist_kernel(const float* __restrict__ 
   int db, sh;
   uint32_t dmask;
   tg_digit(h, db, sh, dmask);
-  const float* p = e + (size_t)bh * per_head;
+  const float* p = g + (size_t)bh * per_head;
+  const float ml = tg_ml(h);
   constexpr int kPer = kTgChunk / 256;
   uint32_t run_bin = 256u, run_cnt = 0u;
   unsigned long long run_sum = 0ull;
-  auto add = [&](float v) {
-    const uint32_t uk = sel_key(v) - h.kmin;
+  auto add = [&](float gv) {
+    const float v = tg_e(gv, ml);
+    const uint32_t uk = tg_ukey(h, v);
     if ((uk >> h.rem) == h.hi) {
       const uint32_t bin = (uk >> sh) & dmask;
       if (bin != run_bin) {
@@ -295,7 +279,7 @@ __global__ __launch_bounds__(256) void tg_hist_kernel(const float* __restrict__ 
       for (int q = 0; q < 4; ++q) {
         const int64_t j = base + 4 * (t + 256 * (q0 + q));
         v[q] = j < per_head ? *reinterpret_cast<const float4*>(p + j)
-                            : make_float4(-1.f, -1.f, -1.f, -1.f);  // key 0: never a candidate
+                            : make_float4(0.f, 0.f, 0.f, 0.f);  // not added (the test below)
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -416,10 +400,10 @@ __global__ __launch_bounds__(64) void tg_pick_kernel(int pass, double tau,
   heads[bh] = h;
 }
 
-__device__ __forceinline__ bool tg_selected(const TgHead& h, float v, bool& boundary) {
+__device__ __forceinline__ bool tg_selected(const TgHead& h, float e, bool& boundary) {
   boundary = false;
   if (h.all) return true;
-  const uint32_t k = (sel_key(v) - h.kmin) >> h.rem;
+  const uint32_t k = tg_ukey(h, e) >> h.rem;
   if (k > h.hi) return true;
   if (k == h.hi) {
     boundary = !h.eq_all;
@@ -431,7 +415,7 @@ __device__ __forceinline__ bool tg_selected(const TgHead& h, float v, bool& boun
 // Per token row: the bitmap of its kept blocks (every pair above the boundary class, and the
 // whole class when all of it is kept), and per chunk of kTgRows rows the count of boundary-class
 // pairs not yet kept.
-__global__ __launch_bounds__(256) void tg_mark_kernel(const float* __restrict__ e, int N,
+__global__ __launch_bounds__(256) void tg_mark_kernel(const float* __restrict__ g, int N,
                                                       int nkv, int nwords,
                                                       const TgHead* __restrict__ heads,
                                                       uint32_t* __restrict__ tbits,
@@ -439,12 +423,13 @@ __global__ __launch_bounds__(256) void tg_mark_kernel(const float* __restrict__ 
   __shared__ int sbnd[4];
   const int bh = blockIdx.y, c = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const TgHead h = heads[bh];
+  const float ml = tg_ml(h);
   const int r0 = c * kTgRows, nr = min(kTgRows, N - r0);
   // wavefront w takes rows w, w + 4, ...: lane l tests blocks 64 i + l (coalesced reads), a
   // ballot gives two bitmap words per 64 blocks
   int my = 0;
   for (int rr = wave; rr < nr; rr += 4) {
-    const float* row = e + ((size_t)bh * N + r0 + rr) * nkv;
+    const float* row = g + ((size_t)bh * N + r0 + rr) * nkv;
     uint32_t* out = tbits + ((size_t)bh * N + r0 + rr) * nwords;
     for (int J1 = 0; J1 < nkv; J1 += 256) {  // four loads in flight per lane
       float v[4];
@@ -458,7 +443,7 @@ __global__ __launch_bounds__(256) void tg_mark_kernel(const float* __restrict__ 
         const int J0 = J1 + 64 * i;
         if (J0 >= nkv) break;
         bool sel = false, bd = false;
-        if (J0 + lane < nkv) sel = tg_selected(h, v[i], bd);
+        if (J0 + lane < nkv) sel = tg_selected(h, tg_e(v[i], ml), bd);
         const unsigned long long bal = __ballot(sel);
         my += __popcll(__ballot(bd));
         const int w = (J0 >> 5) + lane;
@@ -473,7 +458,7 @@ __global__ __launch_bounds__(256) void tg_mark_kernel(const float* __restrict__ 
 
 // When only part of the boundary class is kept: its members in pool index order (token, then
 // block), chunk by chunk, the counts of the earlier chunks giving each chunk's first rank.
-__global__ __launch_bounds__(64) void tg_boundary_kernel(const float* __restrict__ e, int N,
+__global__ __launch_bounds__(64) void tg_boundary_kernel(const float* __restrict__ g, int N,
                                                          int nkv, int nwords,
                                                          const TgHead* __restrict__ heads,
                                                          const int32_t* __restrict__ bnd,
@@ -491,14 +476,15 @@ __global__ __launch_bounds__(64) void tg_boundary_kernel(const float* __restrict
   if ((uint32_t)before >= h.keep) return;
   const int r0 = c * kTgRows;
   const int64_t n = (int64_t)min(kTgRows, N - r0) * nkv;
-  const float* p = e + ((size_t)bh * N + r0) * nkv;
+  const float* p = g + ((size_t)bh * N + r0) * nkv;
+  const float ml = tg_ml(h);
   uint32_t taken = (uint32_t)before;
   for (int64_t base = 0; base < n && taken < h.keep; base += 64) {
     const int64_t j = base + lane;
     bool eq = false;
     if (j < n) {
       bool bd;
-      tg_selected(h, p[j], bd);
+      tg_selected(h, tg_e(p[j], ml), bd);
       eq = bd;
     }
     const unsigned long long bal = __ballot(eq);
@@ -545,7 +531,7 @@ hipError_t launch_select_tokens_global(const bsa_plan& p, const void* Q, const f
   char* base = static_cast<char*>(ws);
   uint16_t* khi = reinterpret_cast<uint16_t*>(base + L.khi);
   uint16_t* klo = reinterpret_cast<uint16_t*>(base + L.klo);
-  float* e = reinterpret_cast<float*>(base + L.e);
+  float* g = reinterpret_cast<float*>(base + L.e);  // the gates
   TgHead* heads = reinterpret_cast<TgHead*>(base + L.heads);
   TgHist* hist = reinterpret_cast<TgHist*>(base + L.hist);
   int32_t* bnd = reinterpret_cast<int32_t*>(base + L.bnd);
@@ -562,21 +548,19 @@ hipError_t launch_select_tokens_global(const bsa_plan& p, const void* Q, const f
   if (err != hipSuccess) return err;
   tg_init_kernel<<<BH, 256, 0, s>>>(heads, hist, shift);
   tg_gates_kernel<<<dim3((N + 127) / 128, BH), 256, 0, s>>>(
-      static_cast<const uint16_t*>(Q), khi, klo, p.scale, p.prob.H, N, nkv, e, heads);
-  const unsigned egrid = (unsigned)std::min<int64_t>((per_head + 255) / 256, 256);
-  tg_exp_kernel<<<dim3(egrid, BH), 256, 0, s>>>(e, per_head, heads);
+      static_cast<const uint16_t*>(Q), khi, klo, p.scale, p.prob.H, N, nkv, g, heads);
   tg_setup_kernel<<<BH, 64, 0, s>>>(heads);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const unsigned nch = (unsigned)((per_head + kTgChunk - 1) / kTgChunk);
   for (int pass = 0; pass < 5; ++pass) {  // at most 31 key bits in 8-bit digits (or rem = 0)
-    tg_hist_kernel<<<dim3(nch, BH), 256, 0, s>>>(e, per_head, heads, hist);
+    tg_hist_kernel<<<dim3(nch, BH), 256, 0, s>>>(g, per_head, heads, hist);
     tg_pick_kernel<<<BH, 64, 0, s>>>(pass, tau, heads, hist);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int nchunk = (N + kTgRows - 1) / kTgRows;
-  tg_mark_kernel<<<dim3(nchunk, BH), 256, 0, s>>>(e, N, nkv, L.nwords, heads, tbits, bnd,
+  tg_mark_kernel<<<dim3(nchunk, BH), 256, 0, s>>>(g, N, nkv, L.nwords, heads, tbits, bnd,
                                                   nchunk);
-  tg_boundary_kernel<<<dim3(nchunk, BH), 64, 0, s>>>(e, N, nkv, L.nwords, heads, bnd, nchunk,
+  tg_boundary_kernel<<<dim3(nchunk, BH), 64, 0, s>>>(g, N, nkv, L.nwords, heads, bnd, nchunk,
                                                      tbits);
   tg_union_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(tbits, N, p.nq, L.nwords, p.qstart,
                                                              p.qperm, rows, bitmap, counts);
