@@ -186,7 +186,7 @@ TgWs tg_ws_layout(const bsa_plan& p) {
   w.e = w.klo + align_up(kb);
   w.heads = w.e + align_up(BH * N * p.nkv * 4);
   w.hist = w.heads + align_up(BH * kTgHeadBytes);
-  w.bnd = w.hist + align_up(BH * (256 * 4 + 256 * 8));
+  w.bnd = w.hist + align_up(BH * ((size_t)kTgBins * 4 + (size_t)kTgBins * 8));
   w.bitmap = w.bnd + align_up(BH * w.nchunk * 4);
   w.counts = w.bitmap + align_up(rows * w.nwords * 4);
   w.partial = w.counts + align_up(rows * 4);

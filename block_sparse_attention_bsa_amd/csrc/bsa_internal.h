@@ -115,6 +115,10 @@ TokWs tok_ws_layout(const bsa_plan& p);
 // head pools' gates [B*H][N][nkv] fp32 (field e), per-head radix state and histogram,
 // boundary counts per 32-token chunk, and the per-query-block union (bitmap, counts, scan).
 constexpr size_t kTgHeadBytes = 80;
+// The head pool's radix digits: 11 bits (2048 bins), so that two passes decide 22 of a pool's
+// key bits and a third (at most 31 bits in all) is rarely needed.
+constexpr int kTgDigitBits = 11;
+constexpr int kTgBins = 1 << kTgDigitBits;
 struct TgWs {
   size_t khi, klo, e, heads, hist, bnd, bitmap, counts, partial, total;
   int nwords, nchunk;

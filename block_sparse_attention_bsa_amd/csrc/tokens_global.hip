@@ -43,8 +43,8 @@ struct TgHead {
 };
 static_assert(sizeof(TgHead) == kTgHeadBytes, "head state size");
 struct TgHist {
-  unsigned int cnt[256];
-  unsigned long long sum[256];
+  unsigned int cnt[kTgBins];
+  unsigned long long sum[kTgBins];
 };
 
 __device__ __forceinline__ uint32_t tg_gate_key(float g) {
@@ -89,8 +89,10 @@ __global__ __launch_bounds__(256) void tg_init_kernel(TgHead* __restrict__ heads
     h.shift = shift;
     heads[bh] = h;
   }
-  hist[bh].cnt[t] = 0u;
-  hist[bh].sum[t] = 0ull;
+  for (int b = t; b < kTgBins; b += 256) {
+    hist[bh].cnt[b] = 0u;
+    hist[bh].sum[b] = 0ull;
+  }
 }
 
 // Gates of 128 tokens (one workgroup, a wavefront per 32) against every kv block of the head:
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(64) void tg_setup_kernel(TgHead* __restrict__ heads
 }
 
 __device__ __forceinline__ void tg_digit(const TgHead& h, int& db, int& sh, uint32_t& dmask) {
-  db = h.rem < 8 ? h.rem : 8;
+  db = h.rem < kTgDigitBits ? h.rem : kTgDigitBits;
   sh = h.rem - db;
   dmask = (1u << db) - 1u;
 }
@@ -233,16 +235,18 @@ __global__ __launch_bounds__(256) void tg_hist_kernel(const float* __restrict__ 
                                                       int64_t per_head,
                                                       const TgHead* __restrict__ heads,
                                                       TgHist* __restrict__ hist) {
-  __shared__ unsigned int scnt[256];
-  __shared__ unsigned long long ssum[256];
+  __shared__ unsigned int scnt[kTgBins];
+  __shared__ unsigned long long ssum[kTgBins];
   const int bh = blockIdx.y;
   const TgHead h = heads[bh];
   if (h.done) return;
   const int64_t base = (int64_t)blockIdx.x * kTgChunk;
   if (base >= per_head) return;
   const int t = threadIdx.x;
-  scnt[t] = 0u;
-  ssum[t] = 0ull;
+  for (int b = t; b < kTgBins; b += 256) {
+    scnt[b] = 0u;
+    ssum[b] = 0ull;
+  }
   __syncthreads();
   int db, sh;
   uint32_t dmask;
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(256) void tg_hist_kernel(const float* __restrict__ 
   const float* p = g + (size_t)bh * per_head;
   const float ml = tg_ml(h);
   constexpr int kPer = kTgChunk / 256;
-  uint32_t run_bin = 256u, run_cnt = 0u;
+  uint32_t run_bin = (uint32_t)kTgBins, run_cnt = 0u;
   unsigned long long run_sum = 0ull;
   auto add = [&](float gv) {
     const float v = tg_e(gv, ml);
@@ -302,9 +306,11 @@ __global__ __launch_bounds__(256) void tg_hist_kernel(const float* __restrict__ 
     atomicAdd(&ssum[run_bin], run_sum);
   }
   __syncthreads();
-  if (scnt[t]) {
-    atomicAdd(&hist[bh].cnt[t], scnt[t]);
-    atomicAdd(&hist[bh].sum[t], ssum[t]);
+  for (int b = t; b < kTgBins; b += 256) {
+    if (scnt[b]) {
+      atomicAdd(&hist[bh].cnt[b], scnt[b]);
+      atomicAdd(&hist[bh].sum[b], ssum[b]);
+    }
   }
 }
 
@@ -318,13 +324,15 @@ __global__ __launch_bounds__(64) void tg_pick_kernel(int pass, double tau,
   TgHead h = heads[bh];
   if (h.done) return;
   TgHist& hs = hist[bh];
-  unsigned long long bsum[4];
-  unsigned int bcnt[4];
+  // bins in descending order: lane l holds bins kTgBins - 1 - kPerLane l - i
+  constexpr int kPerLane = kTgBins / 64;
+  unsigned long long bsum[kPerLane];
+  unsigned int bcnt[kPerLane];
   unsigned long long lsum = 0;
   int lcnt = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int bin = 255 - 4 * lane - i;
+  for (int i = 0; i < kPerLane; ++i) {
+    const int bin = kTgBins - 1 - kPerLane * lane - i;
     bsum[i] = hs.sum[bin];
     bcnt[i] = hs.cnt[bin];
     lsum += bsum[i];
@@ -333,8 +341,8 @@ __global__ __launch_bounds__(64) void tg_pick_kernel(int pass, double tau,
   const unsigned long long isum = wave_incl_scan_u64(lsum);
   const int icnt = wave_incl_scan_i32(lcnt);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int bin = 255 - 4 * lane - i;
+  for (int i = 0; i < kPerLane; ++i) {
+    const int bin = kTgBins - 1 - kPerLane * lane - i;
     hs.sum[bin] = 0ull;
     hs.cnt[bin] = 0u;
   }
@@ -357,9 +365,9 @@ __global__ __launch_bounds__(64) void tg_pick_kernel(int pass, double tau,
   unsigned long long fsum = 0, fcnt = 0;
   unsigned int feq = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kPerLane; ++i) {
     if (found < 0 && asum < h.target && asum + bsum[i] >= h.target) {
-      found = 255 - 4 * lane - i;
+      found = kTgBins - 1 - kPerLane * lane - i;
       fsum = asum;
       fcnt = acnt;
       feq = bcnt[i];
@@ -552,7 +560,8 @@ hipError_t launch_select_tokens_global(const bsa_plan& p, const void* Q, const f
   tg_setup_kernel<<<BH, 64, 0, s>>>(heads);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const unsigned nch = (unsigned)((per_head + kTgChunk - 1) / kTgChunk);
-  for (int pass = 0; pass < 5; ++pass) {  // at most 31 key bits in 8-bit digits (or rem = 0)
+  // at most 31 key bits in digits of kTgDigitBits (a head stops once its class is decided)
+  for (int pass = 0; pass < (31 + kTgDigitBits - 1) / kTgDigitBits; ++pass) {
     tg_hist_kernel<<<dim3(nch, BH), 256, 0, s>>>(g, per_head, heads, hist);
     tg_pick_kernel<<<BH, 64, 0, s>>>(pass, tau, heads, hist);
   }
