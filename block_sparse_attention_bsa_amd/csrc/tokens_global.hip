@@ -433,29 +433,40 @@ __global__ __launch_bounds__(256) void tg_mark_kernel(const float* __restrict__ 
   const TgHead h = heads[bh];
   const float ml = tg_ml(h);
   const int r0 = c * kTgRows, nr = min(kTgRows, N - r0);
-  // wavefront w takes rows w, w + 4, ...: lane l tests blocks 64 i + l (coalesced reads), a
-  // ballot gives two bitmap words per 64 blocks
+  // wavefront w takes rows w, w + 4, ..., two at a time (rows rr and rr + 4) with up to eight
+  // loads of each in flight: lane l tests blocks 64 i + l (coalesced reads), a ballot gives two
+  // bitmap words per 64 blocks
   int my = 0;
-  for (int rr = wave; rr < nr; rr += 4) {
-    const float* row = g + ((size_t)bh * N + r0 + rr) * nkv;
-    uint32_t* out = tbits + ((size_t)bh * N + r0 + rr) * nwords;
-    for (int J1 = 0; J1 < nkv; J1 += 256) {  // four loads in flight per lane
-      float v[4];
+  for (int rr = wave; rr < nr; rr += 8) {
+    const int nrow = rr + 4 < nr ? 2 : 1;  // wave-uniform
+    const float* row0 = g + ((size_t)bh * N + r0 + rr) * nkv;
+    const float* row1 = row0 + (size_t)4 * nkv;
+    uint32_t* out0 = tbits + ((size_t)bh * N + r0 + rr) * nwords;
+    uint32_t* out1 = out0 + (size_t)4 * nwords;
+    for (int J1 = 0; J1 < nkv; J1 += 512) {
+      float v[2][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int J = J1 + 64 * i + lane;
-        v[i] = J < nkv ? row[J] : 0.f;
-      }
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int J0 = J1 + 64 * i;
-        if (J0 >= nkv) break;
-        bool sel = false, bd = false;
-        if (J0 + lane < nkv) sel = tg_selected(h, tg_e(v[i], ml), bd);
-        const unsigned long long bal = __ballot(sel);
-        my += __popcll(__ballot(bd));
-        const int w = (J0 >> 5) + lane;
-        if (lane < 2 && w < nwords) out[w] = (uint32_t)(bal >> (32 * lane));
+        for (int i = 0; i < 8; ++i) {
+          const int J = J1 + 64 * i + lane;
+          v[q][i] = (q < nrow && J < nkv) ? (q ? row1 : row0)[J] : 0.f;
+        }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (q >= nrow) break;
+        uint32_t* out = q ? out1 : out0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int J0 = J1 + 64 * i;
+          if (J0 >= nkv) break;
+          bool sel = false, bd = false;
+          if (J0 + lane < nkv) sel = tg_selected(h, tg_e(v[q][i], ml), bd);
+          const unsigned long long bal = __ballot(sel);
+          my += __popcll(__ballot(bd));
+          const int w = (J0 >> 5) + lane;
+          if (lane < 2 && w < nwords) out[w] = (uint32_t)(bal >> (32 * lane));
+        }
       }
     }
   }
