@@ -81,9 +81,10 @@ struct MfmaArgs {
   // per-token block lists (the list variant): [B*H][N][tslots], ascending
   const int32_t* tsel;
   int tslots;
-  // per-token block bitmaps (the bitmap variant): [B*H][N][twords]
+  // per-token block bitmaps (the bitmap variant): [B*H][N][twords], staged in LDS rows of
+  // tstride words
   const uint32_t* tbits;
-  int twords;
+  int twords, tstride;
   // forward work items (kFItemInts ints each, see bsa_internal.h): a query block's 128-row
   // chunk, or the 32-row slots of up to four query blocks packed into one workgroup
   const int32_t* fitems;
@@ -254,7 +255,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
       const int row = idx / a.twords, wd = idx - row * a.twords;
       uint32_t v = 0u;
       if (row < nrows) v = a.tbits[((size_t)bh * a.N + a.qperm[q0 + row]) * a.twords + wd];
-      tlist[row * kTokBitsWords + wd] = (int32_t)v;
+      tlist[row * a.tstride + wd] = (int32_t)v;
     }
   }
   vmem_wait_all();
@@ -290,7 +291,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
       if (active) {
         auto picked = [&](int J) {
           if constexpr (TOK == kTokBits) {
-            return ((uint32_t)tlist[qrow * kTokBitsWords + (J >> 5)] >> (J & 31)) & 1u;
+            return ((uint32_t)tlist[qrow * a.tstride + (J >> 5)] >> (J & 31)) & 1u;
           } else {
             while (tcur < J) {
               ++tptr;
@@ -998,6 +999,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_d128_tokbits(const MfmaArgs 
   attn_mfma_body<MODE, kTokBits>(a, lds, tlist);
 }
 
+// The same over rows of up to 2048 blocks: 32 KB of staged bitmaps next to the 64 KB of K/V
+// stages leave room for one workgroup per CU.
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void attn_mfma_d128_tokbits_wide(const MfmaArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[stage_bytes<MODE>()];
+  __shared__ int32_t tlist[kAttnRows * kTokBitsWordsWide];
+  attn_mfma_body<MODE, kTokBits>(a, lds, tlist);
+}
+
 // M[bh, I, J] = (sum over I's work items and their active waves of the block sums) / |I|, in fp64
 // and in a fixed order. Wave w of an item is active iff it holds a valid query row (32 w < rows).
 __global__ __launch_bounds__(256) void mass_combine_kernel(const float* __restrict__ part,
@@ -1259,11 +1269,19 @@ hipError_t launch_attn_fwd_token_bits(const bsa_plan& p, const void* Q, const vo
   a.lse = lse;
   a.tbits = tbits;
   a.twords = (p.nkv + 31) / 32;
+  const bool wide = a.twords > kTokBitsWords;  // at most kTokBitsWordsWide (checked by the API)
+  a.tstride = wide ? kTokBitsWordsWide : kTokBitsWords;
   const dim3 grid(p.n_items, p.prob.B * p.prob.H);
-  if (lse)
+  if (wide) {
+    if (lse)
+      attn_mfma_d128_tokbits_wide<kFwd><<<grid, 256, 0, s>>>(a);
+    else
+      attn_mfma_d128_tokbits_wide<kFwdO><<<grid, 256, 0, s>>>(a);
+  } else if (lse) {
     attn_mfma_d128_tokbits<kFwd><<<grid, 256, 0, s>>>(a);
-  else
+  } else {
     attn_mfma_d128_tokbits<kFwdO><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -189,7 +189,7 @@ static void exercise(int B, int H, int d, int dtype, int T, int Hg, int Wg, bsa_
                                    ci.i(), cap, ws_g.p(), wsg - 1, nullptr) != BSA_OK);
     CHECK(bsa_attn_fwd_token_bits(plan, q.p(), k.p(), v.p(), rp.i(), ci.i(), (uint32_t*)sel.p(),
                                   o.p(), nullptr, ws_f.p(), wsf, nullptr) ==
-          (nkv > 768 ? BSA_EUNSUPPORTED : BSA_OK));
+          (nkv > 2048 ? BSA_EUNSUPPORTED : BSA_OK));
     if (nkv <= 2048) {
       CHECK(bsa_attn_fwd_tokens(plan, q.p(), k.p(), v.p(), (int32_t*)rp.p(), (int32_t*)ci.p(),
                                 (int32_t*)sel.p(), 6, o.p(), nullptr, ws_f.p(), wsf,

@@ -149,11 +149,14 @@ def test_exact_ties_constant_and_duplicated_queries():
         assert ok, f"duplicated queries: {nd} pairs differ"
 
 
-@pytest.mark.parametrize("case", ["small", "ragged_batch2"])
+@pytest.mark.parametrize("case", ["small", "ragged_batch2", "wide"])
 def test_token_bits_attention_on_oracle_sets(case):
     import torch
+    # wide: 1024 kv blocks of 4 tokens, above the 768 blocks whose bitmap rows fit two
+    # workgroups per CU (the kernel for wider rows)
     w = {"small": replace(CONFIGS[2], grid=(5, 8, 16), H=2),
-         "ragged_batch2": replace(CONFIGS[2], B=2, grid=(5, 7, 13), H=2)}[case]
+         "ragged_batch2": replace(CONFIGS[2], B=2, grid=(5, 7, 13), H=2),
+         "wide": replace(CONFIGS[2], grid=(8, 16, 32), H=2, kvpart=("tile", (1, 2, 2)))}[case]
     x = make_inputs(w)
     G, kb = _oracle_gates(w, x)
     sets = oracle.select_tokens_global(G, 0.25)
