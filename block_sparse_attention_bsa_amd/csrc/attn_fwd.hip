@@ -81,10 +81,9 @@ struct MfmaArgs {
   // per-token block lists (the list variant): [B*H][N][tslots], ascending
   const int32_t* tsel;
   int tslots;
-  // per-token block bitmaps (the bitmap variant): [B*H][N][twords], staged in LDS rows of
-  // tstride words
+  // per-token block bitmaps (the bitmap variant): [B*H][N][twords]
   const uint32_t* tbits;
-  int twords, tstride;
+  int twords;
   // forward work items (kFItemInts ints each, see bsa_internal.h): a query block's 128-row
   // chunk, or the 32-row slots of up to four query blocks packed into one workgroup
   const int32_t* fitems;
@@ -250,14 +249,22 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
         v = a.tsel[((size_t)bh * a.N + a.qperm[q0 + row]) * a.tslots + slot];
       tlist[row * kTokSlots + slot] = v;
     }
-  } else if constexpr (TOK == kTokBits) {  // the block bitmaps of this item's rows (0 past them)
-    for (int idx = t; idx < kAttnRows * a.twords; idx += 256) {
-      const int row = idx / a.twords, wd = idx - row * a.twords;
-      uint32_t v = 0u;
-      if (row < nrows) v = a.tbits[((size_t)bh * a.N + a.qperm[q0 + row]) * a.twords + wd];
-      tlist[row * a.tstride + wd] = (int32_t)v;
-    }
   }
+  // kTokBits: a window of kTokBitsWords words (blocks 32 w0 .. 32 (w0 + kTokBitsWords)) of every
+  // row's bitmap (0 past the rows and past twords). The walk ascends, so the window only moves
+  // forward, to the word of a chunk's block past its end: at most a few times per item, at
+  // workgroup-uniform points (the chunks are the same for every wavefront), between barriers.
+  int w0 = 0;
+  auto stage_bits = [&](int wstart) {
+    for (int idx = t; idx < kAttnRows * kTokBitsWords; idx += 256) {
+      const int row = idx / kTokBitsWords, wd = wstart + (idx - row * kTokBitsWords);
+      uint32_t v = 0u;
+      if (row < nrows && wd < a.twords)
+        v = a.tbits[((size_t)bh * a.N + a.qperm[q0 + row]) * a.twords + wd];
+      tlist[idx] = (int32_t)v;
+    }
+  };
+  if constexpr (TOK == kTokBits) stage_bits(0);
   vmem_wait_all();
   __syncthreads();
   // TOK: position in this lane's list and the block there (lists and the CSR row ascend)
@@ -288,19 +295,39 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
       act = active && (pa || pb);
     }
     if constexpr (TOK) {
-      if (active) {
-        auto picked = [&](int J) {
-          if constexpr (TOK == kTokBits) {
-            return ((uint32_t)tlist[qrow * a.tstride + (J >> 5)] >> (J & 31)) & 1u;
-          } else {
-            while (tcur < J) {
-              ++tptr;
-              tcur = tptr < a.tslots ? tlist[qrow * kTokSlots + tptr] : INT_MAX;
-            }
-            return (uint32_t)(tcur == J);
+      auto picked = [&](int J) {
+        if constexpr (TOK == kTokBits) {
+          return ((uint32_t)tlist[qrow * kTokBitsWords + ((J >> 5) - w0)] >> (J & 31)) & 1u;
+        } else {
+          while (tcur < J) {
+            ++tptr;
+            tcur = tptr < a.tslots ? tlist[qrow * kTokSlots + tptr] : INT_MAX;
           }
-        };
-        pa = picked(a0.J);
+          return (uint32_t)(tcur == J);
+        }
+      };
+      // kTokBits: move the window to a chunk's block past its end. Every wavefront takes part
+      // (also the ones past a ragged block's end); the barrier that ended the previous step (or
+      // the one before pb's move, after pa's reads) keeps the old window's readers ahead.
+      auto reach = [&](int J) {
+        if constexpr (TOK == kTokBits) {
+          if (J >= 32 * (w0 + kTokBitsWords)) {  // workgroup-uniform
+            w0 = J >> 5;
+            stage_bits(w0);
+            vmem_wait_all();
+            __syncthreads();
+          }
+        }
+      };
+      reach(a0.J);
+      if (active) pa = picked(a0.J);
+      if constexpr (TOK == kTokBits) {
+        if (b0.nv > 0 && b0.J >= 32 * (w0 + kTokBitsWords)) {  // workgroup-uniform
+          __syncthreads();  // every wavefront has read pa from the old window
+          reach(b0.J);
+        }
+      }
+      if (active) {
         pb = b0.nv > 0 && picked(b0.J);
         act = __ballot(pa || pb) != 0ull;
       }
@@ -999,15 +1026,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_d128_tokbits(const MfmaArgs 
   attn_mfma_body<MODE, kTokBits>(a, lds, tlist);
 }
 
-// The same over rows of up to 2048 blocks: 32 KB of staged bitmaps next to the 64 KB of K/V
-// stages leave room for one workgroup per CU.
-template <int MODE>
-__global__ __launch_bounds__(256, 1) void attn_mfma_d128_tokbits_wide(const MfmaArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[stage_bytes<MODE>()];
-  __shared__ int32_t tlist[kAttnRows * kTokBitsWordsWide];
-  attn_mfma_body<MODE, kTokBits>(a, lds, tlist);
-}
-
 // M[bh, I, J] = (sum over I's work items and their active waves of the block sums) / |I|, in fp64
 // and in a fixed order. Wave w of an item is active iff it holds a valid query row (32 w < rows).
 __global__ __launch_bounds__(256) void mass_combine_kernel(const float* __restrict__ part,
@@ -1269,19 +1287,11 @@ hipError_t launch_attn_fwd_token_bits(const bsa_plan& p, const void* Q, const vo
   a.lse = lse;
   a.tbits = tbits;
   a.twords = (p.nkv + 31) / 32;
-  const bool wide = a.twords > kTokBitsWords;  // at most kTokBitsWordsWide (checked by the API)
-  a.tstride = wide ? kTokBitsWordsWide : kTokBitsWords;
   const dim3 grid(p.n_items, p.prob.B * p.prob.H);
-  if (wide) {
-    if (lse)
-      attn_mfma_d128_tokbits_wide<kFwd><<<grid, 256, 0, s>>>(a);
-    else
-      attn_mfma_d128_tokbits_wide<kFwdO><<<grid, 256, 0, s>>>(a);
-  } else if (lse) {
+  if (lse)
     attn_mfma_d128_tokbits<kFwd><<<grid, 256, 0, s>>>(a);
-  } else {
+  else
     attn_mfma_d128_tokbits<kFwdO><<<grid, 256, 0, s>>>(a);
-  }
   return hipGetLastError();
 }
 

@@ -697,9 +697,9 @@ int bsa_attn_fwd_token_bits(const bsa_plan* plan, const void* Q, const void* K, 
     return fail(BSA_EINVAL, "bsa_attn_fwd_token_bits: NULL argument");
   if (plan->prob.dtype != BSA_BF16 || plan->prob.d != 128)
     return fail(BSA_EUNSUPPORTED, "bsa_attn_fwd_token_bits: bf16 and d = 128 only");
-  if (plan->nkv > 32 * kTokBitsWordsWide)
+  if (plan->nkv > kTokBitsMaxBlocks)
     return fail(BSA_EUNSUPPORTED, "bsa_attn_fwd_token_bits: more than %d kv blocks",
-                32 * kTokBitsWordsWide);
+                kTokBitsMaxBlocks);
   const size_t need = fwd_ws_layout(*plan).total;
   if (!ws || ws_bytes < need)
     return fail(BSA_ECAPACITY, "bsa_attn_fwd_token_bits: workspace %zu < %zu bytes", ws_bytes,

@@ -134,9 +134,9 @@ hipError_t launch_attn_fwd_token_bits(const bsa_plan& p, const void* Q, const vo
                                       const int32_t* col_idx, const uint32_t* tbits, void* O,
                                       float* lse, void* ws, hipStream_t s);
 // Largest kv-block count of the per-token bitmap attention (one LDS row of words per token).
+// The per-token bitmap attention stages a window of this many words of each row's bitmap.
 constexpr int kTokBitsWords = 24;
-// Rows of up to 2048 blocks: the bitmap rows staged with this stride, one workgroup per CU.
-constexpr int kTokBitsWordsWide = 64;
+constexpr int kTokBitsMaxBlocks = 2048;
 
 struct FwdWs {
   size_t kp, vp, total;  // K and V in block order, [B*H][N + kPermPad][d] (bf16, d = 128 path)

@@ -301,8 +301,7 @@ int bsa_select_tokens_global(const bsa_plan* plan, const void* Q, const float* K
  * over the tokens of the blocks set in tbits[b, h, i]; a token with no block gets O = 0 and
  * lse = -inf. Each query block's workgroup walks its union CSR row and masks, per token, the
  * blocks that token did not keep. Numerics and ws as bsa_attn_fwd (ws_fwd bytes). bf16,
- * d = 128 and nkv <= 2048 only (BSA_EUNSUPPORTED otherwise); rows of more than 768 blocks run
- * at one workgroup per CU (their bitmaps take more LDS). */
+ * d = 128 and nkv <= 2048 only (BSA_EUNSUPPORTED otherwise). */
 int bsa_attn_fwd_token_bits(const bsa_plan* plan, const void* Q, const void* K, const void* V,
                             const int32_t* row_ptr, const int32_t* col_idx,
                             const uint32_t* tbits, void* O, float* lse, void* ws,
