@@ -40,10 +40,10 @@ namespace {
 
 // ------------------------------------------------------------------------------- MFMA path
 
-// kFwd: sparse attention with its LSE; kFwdO: sparse attention, output only; kLse / kMass: the
-// two dense calibration passes; kMassO: the second calibration pass that also forms the dense
-// attention output from the same exact weights.
-enum Mode { kFwd = 0, kLse = 1, kMass = 2, kMassO = 3, kFwdO = 4 };
+// kFwd: sparse attention with its LSE; kFwdO: sparse attention, output only; kCal: the dense
+// calibration pass (each query's LSE, and per query and kv block the log-sum of the block's
+// weights); kCalO: the same pass forming the dense attention output as well.
+enum Mode { kFwd = 0, kCal = 1, kCalO = 3, kFwdO = 4 };
 
 
 constexpr int kTileKV = 64;                    // kv tokens per iteration (two chunks)
@@ -72,10 +72,10 @@ struct MfmaArgs {
   const int32_t* kvstart;
   const int32_t* items;
   const float* scale;
-  const float* lse_in;  // kMass, kMassO: per-token log-sum-exp (from the kLse pass)
-  uint16_t* O;          // kFwd, kFwdO, kMassO
-  float* lse;           // kFwd (required), kMassO (nullable), kLse
-  float* part;          // kMass: [bh][item][wave][nkv] per-wave block sums
+  float* lse2;          // kCal, kCalO: per-token log-sum-exp in the log2 domain
+  uint16_t* O;          // kFwd, kFwdO, kCalO
+  float* lse;           // kFwd (required), kCalO (nullable)
+  float* part;          // kCal, kCalO: [bh][item][nkv][128] per-row block log2-sums
   int n_items, H, N, nq, nkv;
   int Npad;  // K and V are permuted into block order: [B*H][Npad][d], Npad = N + kPermPad
   // per-token block lists (the list variant): [B*H][N][tslots], ascending
@@ -111,8 +111,9 @@ constexpr int kTokSlots = kMaxTokenK + 1;
 template <int MODE, int TOK = kTokNone, bool PACK = false>
 __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int32_t* tlist) {
   constexpr int D = 128;
-  constexpr bool kDense = MODE == kLse || MODE == kMass || MODE == kMassO;  // all kv blocks
-  constexpr bool kPV = MODE == kFwd || MODE == kFwdO || MODE == kMassO;  // O = P V is formed
+  constexpr bool kDense = MODE == kCal || MODE == kCalO;  // all kv blocks
+  constexpr bool kCalStats = kDense;  // per-row block log-sums
+  constexpr bool kPV = MODE == kFwd || MODE == kFwdO || MODE == kCalO;  // O = P V is formed
   constexpr bool kNeedV = kPV;
   constexpr int kStage = kNeedV ? 2 * kTileBytes : kTileBytes;
   // the sparse forward reads the forward work items, the other passes one block per item
@@ -174,10 +175,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
   // TOK: a finite floor instead of -inf, so that a tile whose chunks this lane's token did not
   // pick (all scores -inf) gives weights 0, not exp2(-inf + inf)
   float m_run = TOK ? -1e30f : -INFINITY, l_run = 0.f, lb_run = 0.f;
-  // kMass: log2-domain lse of this lane's query (+inf for padding rows, so they add nothing)
-  float nlse2 = 0.f, blk_acc = 0.f;
-  if constexpr (MODE == kMass || MODE == kMassO)
-    nlse2 = qvalid ? -a.lse_in[(size_t)bh * a.N + qtok] * kLog2e : -INFINITY;
+  // kCal, kCalO: this lane's part of the current kv block's weights, against m_run
+  float blk_acc = 0.f;
 
   // Loader role: wave w fills tile rows 16w + 4i + lane/16 (i = 0..3), 16-byte unit lane%16 of
   // the swizzled row, for K (and V), with direct global->LDS copies (no staging registers). K and
@@ -457,40 +456,7 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
         __builtin_amdgcn_s_setprio(0);
       };
 
-      if constexpr (MODE == kMass || MODE == kMassO) {
-        // Exact weights exp(sigma q.k - lse) (the LSE over all N keys is known from the kLse
-        // pass). Block sums: one chunk per M block, flushed at block ends; kMassO also forms
-        // the dense output O from the same weights.
-        float pv[2][16];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) pv[mb][e] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], c2, nlse2));
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const Chunk& c = mb ? b0 : a0;
-          if (c.nv > 0) {
-            float cs0 = 0.f, cs1 = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-              cs0 += pv[mb][e];
-              cs1 += pv[mb][e + 1];
-            }
-            blk_acc += cs0 + cs1;
-            if (c.last) {
-              const float tot = wave_sum_f32(blk_acc);
-              if (lane == 0)
-                a.part[(((size_t)bh * n_items + item) * 4 + wave) * a.nkv + c.J] = tot;
-              blk_acc = 0.f;
-            }
-          }
-        }
-        if constexpr (MODE == kMassO) {
-          bf16x8_t pb[4];
-          lb_run += pack_weights(pv, pb);
-          pv_product(pb);
-        }
-      } else if constexpr (MODE == kFwdO) {
+      if constexpr (MODE == kFwdO) {
         // As the path below, with the bf16-rounded weights' sum (which O is normalised by) as
         // the only sum: it bounds every weight as well, and no LSE is formed.
         float pv[2][16];
@@ -553,7 +519,8 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
           l_run *= alpha;
           lb_run *= alpha;
-          if constexpr (MODE == kFwd) {
+          if constexpr (kCalStats) blk_acc *= alpha;
+          if constexpr (MODE == kFwd || MODE == kCalO) {
 #pragma unroll
             for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
@@ -563,7 +530,32 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
           lsum = weights();
         }
         l_run += lsum;
-        if constexpr (MODE == kFwd) {
+        if constexpr (kCalStats) {
+          // A chunk lies in one kv block; at a block's last chunk the two lane halves' sums give
+          // each query's block sum against m_run, written as m_run + log2(sum) (the block's
+          // log2-sum; -inf when every weight underflowed), rows of an item contiguous.
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const Chunk& c = mb ? b0 : a0;
+            if (c.nv > 0) {
+              float cs0 = 0.f, cs1 = 0.f;
+#pragma unroll
+              for (int e = 0; e < 16; e += 2) {
+                cs0 += pv[mb][e];
+                cs1 += pv[mb][e + 1];
+              }
+              blk_acc += cs0 + cs1;
+              if (c.last) {
+                const float tot = blk_acc + __shfl_xor(blk_acc, 32, 64);
+                if (hl == 0)
+                  a.part[(((size_t)bh * n_items + item) * a.nkv + c.J) * kAttnRows + qrow] =
+                      tot > 0.f ? m_run + log2f(tot) : -INFINITY;
+                blk_acc = 0.f;
+              }
+            }
+          }
+        }
+        if constexpr (MODE == kFwd || MODE == kCalO) {
           bf16x8_t pb[4];
           lb_run += pack_weights(pv, pb);
           pv_product(pb);
@@ -585,7 +577,6 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
     step(lds_b, m0_a);
   }
 
-  if constexpr (MODE == kMass) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
   if constexpr (kPV) {
@@ -602,9 +593,12 @@ __device__ __forceinline__ void attn_mfma_body(const MfmaArgs& a, char* lds, int
         *reinterpret_cast<uint2*>(op + 32 * dm + 8 * g + 4 * hl) = pk;
       }
   }
-  if constexpr (MODE == kMassO) {
-    // the dense step's LSE is the kLse pass's (the weights above are normalised by it)
-    if (a.lse && hl == 0) a.lse[(size_t)bh * a.N + qtok] = a.lse_in[(size_t)bh * a.N + qtok];
+  if constexpr (kCalStats) {
+    if (hl == 0) {
+      const float l2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+      a.lse2[(size_t)bh * a.N + qtok] = l2;
+      if (a.lse) a.lse[(size_t)bh * a.N + qtok] = l_tot > 0.f ? l2 * kLn2 : -INFINITY;
+    }
     return;
   }
   if constexpr (MODE == kFwdO) return;
@@ -986,7 +980,7 @@ __device__ __forceinline__ void attn16_body(const MfmaArgs& a, char* lds) {
 // LDS of the two K (and V) stages.
 template <int MODE>
 constexpr int stage_bytes() {
-  return 2 * ((MODE == kFwd || MODE == kFwdO || MODE == kMassO) ? 2 * kTileBytes : kTileBytes);
+  return 2 * ((MODE == kFwd || MODE == kFwdO || MODE == kCalO) ? 2 * kTileBytes : kTileBytes);
 }
 
 // Two waves per SIMD: two workgroups share a CU. The sparse forward's items are either one
@@ -1026,26 +1020,36 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_d128_tokbits(const MfmaArgs 
   attn_mfma_body<MODE, kTokBits>(a, lds, tlist);
 }
 
-// M[bh, I, J] = (sum over I's work items and their active waves of the block sums) / |I|, in fp64
-// and in a fixed order. Wave w of an item is active iff it holds a valid query row (32 w < rows).
+// M[bh, I, J] = (1/|I|) sum over the query rows i of I of 2^(b_iJ - lse2_i), b_iJ the row's
+// log2-sum of block J's weights and lse2_i its log2-domain LSE, both from the calibration pass:
+// fp64 sums in a fixed order (a work item's rows by lane, then a fixed butterfly; then the items
+// in order). One wavefront per (I, J) at a time.
 __global__ __launch_bounds__(256) void mass_combine_kernel(const float* __restrict__ part,
+                                                           const float* __restrict__ lse2,
+                                                           const int32_t* __restrict__ qperm,
                                                            const int32_t* __restrict__ qstart,
                                                            const int32_t* __restrict__ qitem0,
                                                            const int32_t* __restrict__ items,
-                                                           int n_items, int nq, int nkv,
+                                                           int n_items, int N, int nq, int nkv,
                                                            float* __restrict__ M) {
-  const int I = blockIdx.x, bh = blockIdx.y;
+  const int I = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i0 = qitem0[I], i1 = qitem0[I + 1];
-  const int size = qstart[I + 1] - qstart[I];
+  const int q0 = qstart[I], size = qstart[I + 1] - q0;
   const double inv = 1.0 / (double)size;
-  for (int J = threadIdx.x; J < nkv; J += 256) {
+  const float* l2 = lse2 + (size_t)bh * N;
+  for (int J = wave; J < nkv; J += 4) {
     double s = 0.0;
     for (int it = i0; it < i1; ++it) {
-      const int rows = min(128, size - items[2 * it + 1]);
-      for (int w = 0; 32 * w < rows; ++w)
-        s += part[(((size_t)bh * n_items + it) * 4 + w) * nkv + J];
+      const int off = items[2 * it + 1], rows = min(kAttnRows, size - off);
+      const float* pr = part + (((size_t)bh * n_items + it) * nkv + J) * kAttnRows;
+      double v = 0.0;
+      for (int r = lane; r < rows; r += 64) {
+        const float b = pr[r];
+        if (b > -INFINITY) v += (double)exp2f(b - l2[qperm[q0 + off + r]]);
+      }
+      s += wave_sum_f64(v);
     }
-    M[((size_t)bh * nq + I) * nkv + J] = (float)(s * inv);
+    if (lane == 0) M[((size_t)bh * nq + I) * nkv + J] = (float)(s * inv);
   }
 }
 
@@ -1299,32 +1303,30 @@ hipError_t launch_calibrate(const bsa_plan& p, const void* Q, const void* K, con
                             float* M, void* O, float* lse_out, void* ws, hipStream_t s) {
   const CalibWs L = calib_ws_layout(p);
   char* base = static_cast<char*>(ws);
-  float* lse = reinterpret_cast<float*>(base + L.lse);
+  float* lse2 = reinterpret_cast<float*>(base + L.lse);
   float* part = reinterpret_cast<float*>(base + L.part);
   hipError_t e = launch_permute_rows(p, K, base + L.kp, s);
   if (e == hipSuccess && V) e = launch_permute_rows(p, V, base + L.vp, s);
   if (e != hipSuccess) return e;
+  // One pass: each query's LSE and the per-row log2-sums of every kv block (and, with V, the
+  // dense output), then the masses from them.
   const dim3 grid(p.n_items, p.prob.B * p.prob.H);
   MfmaArgs a = mfma_args(p);
   a.Q = static_cast<const uint16_t*>(Q);
   a.K = reinterpret_cast<const uint16_t*>(base + L.kp);
-  a.lse = lse;
-  attn_mfma_d128<kLse><<<grid, 256, 0, s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  a.lse = nullptr;
-  a.lse_in = lse;
+  a.lse2 = lse2;
   a.part = part;
-  if (V) {  // the masses and the dense output from the same weights
+  if (V) {
     a.V = reinterpret_cast<const uint16_t*>(base + L.vp);
     a.O = static_cast<uint16_t*>(O);
     a.lse = lse_out;
-    attn_mfma_d128<kMassO><<<grid, 256, 0, s>>>(a);
+    attn_mfma_d128<kCalO><<<grid, 256, 0, s>>>(a);
   } else {
-    attn_mfma_d128<kMass><<<grid, 256, 0, s>>>(a);
+    attn_mfma_d128<kCal><<<grid, 256, 0, s>>>(a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mass_combine_kernel<<<dim3(p.nq, p.prob.B * p.prob.H), 256, 0, s>>>(
-      part, p.qstart, p.qitem0, p.items, p.n_items, p.nq, p.nkv, M);
+      part, lse2, p.qperm, p.qstart, p.qitem0, p.items, p.n_items, p.prob.N, p.nq, p.nkv, M);
   return hipGetLastError();
 }
 

@@ -210,7 +210,7 @@ CalibWs calib_ws_layout(const bsa_plan& p) {
   const size_t BH = (size_t)p.prob.B * p.prob.H;
   w.lse = 0;
   w.part = align_up(BH * p.prob.N * 4);
-  w.kp = w.part + align_up(BH * p.n_items * 4 * (size_t)p.nkv * 4);
+  w.kp = w.part + align_up(BH * p.n_items * (size_t)p.nkv * kAttnRows * 4);
   w.vp = w.kp + align_up(BH * (size_t)(p.prob.N + kPermPad) * p.prob.d * 2);
   w.total = w.vp + align_up(BH * (size_t)(p.prob.N + kPermPad) * p.prob.d * 2);
   return w;

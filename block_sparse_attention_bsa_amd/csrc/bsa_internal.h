@@ -90,8 +90,8 @@ struct BwdWs {
 BwdWs bwd_ws_layout(const bsa_plan& p);
 
 struct CalibWs {
-  // per-token log-sum-exp; per (item, wave, kv block) block sums; K and V in block order (V for
-  // the variant that also forms the dense output)
+  // per-token log2-domain log-sum-exp; per (item, kv block, row) log2-sums of the block's
+  // weights; K and V in block order (V for the variant that also forms the dense output)
   size_t lse, part, kp, vp, total;
 };
 CalibWs calib_ws_layout(const bsa_plan& p);

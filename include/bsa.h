@@ -175,15 +175,18 @@ int bsa_score(const bsa_plan* plan, const float* Qbar, const float* Kbar, int32_
 /* Step 2'. Exact block masses of one dense step (LoSA abstract):
  *   M[b, h, I, J] = (1/|I|) sum_{i in I} sum_{j in J} softmax_j(sigma_h q_i . k_j),
  * the softmax taken over all N keys. Q, K [B, H, N, d] of the plan's dtype (bf16 only, d = 128);
- * M fp32 [B, H, nq, nkv]. ws must hold the ws_calib bytes of bsa_plan_info. Rows of M sum to 1. */
+ * M fp32 [B, H, nq, nkv]. ws must hold the ws_calib bytes of bsa_plan_info (mostly the per
+ * query and kv block log-sums of one pass over the keys: B*H*items*nkv*128 floats, items the
+ * 128-row chunks of the query blocks, e.g. 694 MB for the 480p shape). Rows of M sum to 1. */
 int bsa_calibrate_mass(const bsa_plan* plan, const void* Q, const void* K, float* M, void* ws,
                        size_t ws_bytes, void* stream);
 
 /* Step 2' as the dense step itself: the same masses M, plus the dense attention output of that
  * step, O[b, h, i, :] = sum_j softmax_j(sigma_h q_i . k_j) v_j over all N keys, and its LSE
  * (natural log, fp32 [B, H, N]; nullable). The LoSA abstract measures the masses at one early
- * step that runs dense attention; both come from one pass over the same exact weights (the
- * second calibration pass also multiplies them with V). Q, K, V, O [B, H, N, d] bf16 (d = 128),
+ * step that runs dense attention; both come from one online-softmax pass over the keys, whose
+ * weights also multiply V (the masses are formed afterwards from each query's per-block sums and
+ * its LSE, bit-identical to bsa_calibrate_mass). Q, K, V, O [B, H, N, d] bf16 (d = 128),
  * M fp32 [B, H, nq, nkv]; ws as for bsa_calibrate_mass (the ws_calib bytes). O is normalised by
  * the sum of the same bf16-rounded weights that multiply V. Errors as bsa_calibrate_mass. */
 int bsa_calibrate_mass_fwd(const bsa_plan* plan, const void* Q, const void* K, const void* V,
