@@ -1,14 +1,15 @@
-// Sparse attention forward (step 4) and the two dense passes of the exact block-mass calibration
+// Sparse attention forward (step 4) and the dense pass of the exact block-mass calibration
 // (step 2'), on bf16 matrix cores for d = 128, plus a plain VALU path for fp32 and d = 64.
 //
 // Forward: every query of block I attends only to the tokens of the kv blocks listed in CSR row I
 // (pith.science review of VMoBA, Figure 2 caption: attention over the selected blocks only; "What
 // carries the argument": only the highest-scoring blocks contribute their key-value pairs), with
 // a FlashAttention-style online softmax. Calibration (LoSA abstract, scholarbro author page):
-// exact block attention masses from one dense step, computed as a dense log-sum-exp pass over all
-// N keys followed by a dense pass that sums exp(sigma q.k - lse) per (query block, kv block).
+// exact block attention masses from one dense step, computed by one dense online-softmax pass over
+// all N keys that also keeps each query's log-sum of every kv block's weights, and a combine that
+// sums 2^(block log2-sum - log2 lse) per (query block, kv block).
 //
-// KV stream. The kv blocks of a row (the CSR list, or all blocks for the dense passes) are walked
+// KV stream. The kv blocks of a row (the CSR list, or all blocks for the dense pass) are walked
 // as a sequence of 32-token chunks: block J contributes ceil(|J| / 32) chunks, the last one
 // possibly partial. Chunks are padded per block, not concatenated; K and V are first copied into
 // block order (permute_rows_kernel), so a chunk is rows kvstart[J] + 32 * sub .. +32 of that copy

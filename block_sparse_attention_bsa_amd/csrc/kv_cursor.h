@@ -1,4 +1,4 @@
-// Walk over a row's kv blocks (a CSR row, or every block for the dense passes) as 32-token
+// Walk over a row's kv blocks (a CSR row, or every block for the dense pass) as 32-token
 // chunks, padded per block: block J contributes ceil(|J| / 32) chunks, the last possibly partial.
 // Shared by the attention passes (forward, calibration, dQ).
 #pragma once
