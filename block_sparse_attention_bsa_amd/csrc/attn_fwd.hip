@@ -1023,8 +1023,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_d128_tokbits(const MfmaArgs 
 
 // M[bh, I, J] = (1/|I|) sum over the query rows i of I of 2^(b_iJ - lse2_i), b_iJ the row's
 // log2-sum of block J's weights and lse2_i its log2-domain LSE, both from the calibration pass:
-// fp64 sums in a fixed order (a work item's rows by lane, then a fixed butterfly; then the items
-// in order). One wavefront per (I, J) at a time.
+// one thread per kv block J sums the rows of each of I's work items in order (fp64, the item's
+// 128 row values of J contiguous), items in order, with the items' lse2 staged in LDS.
 __global__ __launch_bounds__(256) void mass_combine_kernel(const float* __restrict__ part,
                                                            const float* __restrict__ lse2,
                                                            const int32_t* __restrict__ qperm,
@@ -1033,24 +1033,37 @@ __global__ __launch_bounds__(256) void mass_combine_kernel(const float* __restri
                                                            const int32_t* __restrict__ items,
                                                            int n_items, int N, int nq, int nkv,
                                                            float* __restrict__ M) {
-  const int I = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float l2s[kAttnRows];
+  const int I = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int i0 = qitem0[I], i1 = qitem0[I + 1];
   const int q0 = qstart[I], size = qstart[I + 1] - q0;
   const double inv = 1.0 / (double)size;
   const float* l2 = lse2 + (size_t)bh * N;
-  for (int J = wave; J < nkv; J += 4) {
-    double s = 0.0;
+  for (int J0 = 0; J0 < nkv; J0 += 256) {  // workgroup-uniform
+    const int J = J0 + t;
+    double acc = 0.0;
     for (int it = i0; it < i1; ++it) {
       const int off = items[2 * it + 1], rows = min(kAttnRows, size - off);
-      const float* pr = part + (((size_t)bh * n_items + it) * nkv + J) * kAttnRows;
-      double v = 0.0;
-      for (int r = lane; r < rows; r += 64) {
-        const float b = pr[r];
-        if (b > -INFINITY) v += (double)exp2f(b - l2[qperm[q0 + off + r]]);
+      __syncthreads();  // the previous item's lse2 are read
+      if (t < rows) l2s[t] = l2[qperm[q0 + off + t]];
+      __syncthreads();
+      if (J < nkv) {
+        const float* pr = part + (((size_t)bh * n_items + it) * nkv + J) * kAttnRows;
+        double v = 0.0;
+        int r = 0;
+        for (; r + 4 <= rows; r += 4) {  // 16-byte loads (an item's row block is 512 B aligned)
+          const float4 b4 = *reinterpret_cast<const float4*>(pr + r);
+          const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (bv[e] > -INFINITY) v += (double)exp2f(bv[e] - l2s[r + e]);
+        }
+        for (; r < rows; ++r)
+          if (pr[r] > -INFINITY) v += (double)exp2f(pr[r] - l2s[r]);
+        acc += v;
       }
-      s += wave_sum_f64(v);
     }
-    if (lane == 0) M[((size_t)bh * nq + I) * nkv + J] = (float)(s * inv);
+    if (J < nkv) M[((size_t)bh * nq + I) * nkv + J] = (float)(acc * inv);
   }
 }
 
